@@ -1,0 +1,25 @@
+"""CPU oracle for the paged-KV decode path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the library. It is
+plain float64 NumPy (plus a pure-Python brute force for tiny inputs) and
+shares no code with the HIP path.
+"""
+from .paged_attention import (  # noqa: F401
+    BlockAllocator,
+    InvalidFree,
+    OracleCache,
+    OutOfBlocks,
+    SequenceBlocks,
+    append,
+    attention,
+    attention_split_merge,
+    bf16_bits_to_f64,
+    block_alloc_slots,
+    build_cache,
+    contiguous_attend,
+    gather,
+    kv_bytes_per_token,
+    paged_attention_all,
+    widen,
+)
