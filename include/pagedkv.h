@@ -1,0 +1,250 @@
+/*
+ * pagedkv.h - C ABI of the paged-KV decode-attention library (gfx950).
+ *
+ * The library computes decode-step attention over a paged KV cache:
+ * a pool of fixed-size KV blocks, a per-sequence block table mapping
+ * logical block i of a sequence to a physical block, appends of new
+ * tokens' K/V through that table, and causal scaled-dot-product attention
+ * that gathers every cached block through the table while it computes.
+ *
+ * Sources (the pages this library implements):
+ *  - "Inference Engineering" capstone lab (openarchlab, inference lab):
+ *    class KVPool (write / gather / release) and function forward
+ *    (attention core) in its NumPy listing; mapping-table rows 6-7.
+ *  - foundations-of-llms chapter 5 "Inference & optimisation":
+ *    section 2.1 (KV cache: append k_t, v_t, then attend q_t over K, V),
+ *    section 3.1 (grouped-query attention), section 3.2 (PagedAttention:
+ *    fixed-size blocks allocated on demand, a block table read by the
+ *    attention kernel), section 4.1 (online softmax).
+ *  - LLM inference serving tutorial (ARIS): section 1.7 (idempotent
+ *    reclaim, no double free), section 4.1 (bytes per token),
+ *    section 4.2 (block-table indirection, internal fragmentation).
+ *
+ * Conventions for every entry point
+ *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code. Arguments are
+ *    validated before anything is launched or mutated, so an error leaves
+ *    no partial effect. pkv_strerror() names a code.
+ *  - Device pointers are plain addresses in the current HIP device's
+ *    memory, owned by the caller; the library never allocates, frees or
+ *    retains device memory. Host pointers (kvpool_*) are owned by the
+ *    caller and only read or written during the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream). Kernels are enqueued asynchronously on it; outputs are valid
+ *    once the caller synchronises with the stream. The library keeps no
+ *    per-call state, so calls on different streams may run concurrently as
+ *    long as their output buffers differ.
+ *  - Data the host cannot check without a device round trip (block ids in
+ *    the table, seq_lens, q_start) is checked on the device: an attention
+ *    row whose sequence length is out of range, or whose table holds an id
+ *    outside [0, num_blocks), is written as NaN (out and lse) instead of
+ *    reading out of bounds; kv_append skips a token whose table entry is out
+ *    of range.
+ *
+ * Memory layouts (row-major, innermost last)
+ *  - k_cache, v_cache: [num_blocks][n_kv][block_size][head_dim] elements of
+ *    `dtype` (the lab pool's [block][head][slot][dim] layout): one (block,
+ *    kv head) tile of block_size x head_dim elements is contiguous.
+ *  - block_table: int32 [num_seqs][table_stride]; entry i of row s is the
+ *    physical block holding positions [i*block_size, (i+1)*block_size) of
+ *    sequence s. Entries at or past ceil(seq_lens[s]/block_size) are never
+ *    read (pad them with -1).
+ *  - q, out: [rows][n_q][head_dim] of `dtype`; lse: float [rows][n_q]
+ *    (natural-log log-sum-exp of the scaled scores), nullable.
+ *  - Query head h reads kv head h / (n_q / n_kv) (contiguous groups).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define PKV_OK                       0
+#define PKV_ERR_NULL_POINTER        -1  /* a required pointer is NULL */
+#define PKV_ERR_INVALID_ARGUMENT    -2  /* a size or shape is out of range */
+#define PKV_ERR_UNSUPPORTED         -3  /* no kernel instantiation for this shape/dtype */
+#define PKV_ERR_OUT_OF_BLOCKS       -4  /* the pool has fewer free blocks than requested */
+#define PKV_ERR_INVALID_FREE        -5  /* freeing an id that is out of range, already free, or repeated */
+#define PKV_ERR_WORKSPACE_TOO_SMALL -6  /* workspace_bytes below paged_attn_workspace_size() */
+#define PKV_ERR_TABLE_FULL          -7  /* a sequence needs more blocks than its table row holds */
+#define PKV_ERR_HIP                 -8  /* a HIP launch failed (hipGetLastError) */
+#define PKV_ERR_NO_MEMORY           -9  /* host allocation for the pool object failed */
+
+/* ---- element types ----------------------------------------------------- */
+#define PKV_F32  0   /* IEEE binary32 */
+#define PKV_BF16 1   /* bfloat16 (upper half of binary32), stored as 16 bits */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_strerror(int status);
+
+/* ======================================================================
+ * Block pool (host). The allocator hands out block ids, not bytes; K/V
+ * storage is the caller's k_cache / v_cache.
+ *
+ * Source: lab page, class KVPool - a sorted free list from which a
+ * sequence takes the lowest id each time a position reaches the end of its
+ * last block, with every block returned (and the list re-sorted) when the
+ * sequence ends; chapter 5 section 3.2 (blocks allocated on demand);
+ * serving tutorial section 1.7 (reclaim is idempotent: no double free, no
+ * leak). The lab asserts when the pool runs dry; here that is
+ * PKV_ERR_OUT_OF_BLOCKS with nothing changed.
+ *
+ * Ordering: ids are handed out lowest *rank* first, where alloc_order[i]
+ * has rank i (NULL = identity order 0..num_blocks-1, the lab's policy).
+ * Not thread-safe: one thread owns a pool.
+ * ==================================================================== */
+typedef struct kvpool kvpool_t;
+
+/* Create a pool of num_blocks (>= 1) blocks of block_size (>= 1) tokens.
+ * alloc_order: NULL or a permutation of 0..num_blocks-1 (copied).
+ * Errors: NULL_POINTER (out), INVALID_ARGUMENT (sizes, not a permutation),
+ * NO_MEMORY. */
+int kvpool_create(int32_t num_blocks, int32_t block_size,
+                  const int32_t* alloc_order, kvpool_t** out);
+
+/* Destroy a pool (NULL is accepted and ignored). */
+int kvpool_destroy(kvpool_t* pool);
+
+/* Take the n lowest-rank free blocks, written to out_ids[0..n) in rank
+ * order. All or nothing: OUT_OF_BLOCKS if fewer than n are free. n = 0 is
+ * a no-op. */
+int kvpool_alloc(kvpool_t* pool, int32_t n, int32_t* out_ids);
+
+/* Return n blocks. All or nothing: INVALID_FREE if any id is out of range,
+ * currently free, or listed twice. */
+int kvpool_free(kvpool_t* pool, int32_t n, const int32_t* ids);
+
+/* Number of free blocks. */
+int kvpool_num_free(const kvpool_t* pool, int32_t* out);
+
+/* Free ids in the order they would be handed out (out has room for
+ * num_blocks; *count receives the number written). */
+int kvpool_free_ids(const kvpool_t* pool, int32_t* out, int32_t* count);
+
+/* Sequence helper: grow a table row so it covers `length` tokens, i.e.
+ * holds ceil(length / block_size) blocks. row[0..*num_held) are the blocks
+ * the sequence already holds; new ids are appended in rank order and
+ * *num_held is updated. TABLE_FULL if the row would need more than
+ * row_capacity entries; OUT_OF_BLOCKS if the pool is short (row unchanged
+ * in both cases). */
+int kvpool_ensure(kvpool_t* pool, int32_t* row, int32_t* num_held,
+                  int32_t row_capacity, int32_t length);
+
+/* Sequence helper: return every block of a row, set its entries to -1 and
+ * *num_held to 0. Releasing an empty row is a no-op, so calling this twice
+ * is safe. */
+int kvpool_release(kvpool_t* pool, int32_t* row, int32_t* num_held);
+
+/* ======================================================================
+ * kv_append - write new tokens' K/V into the pool through the table.
+ *
+ * Source: lab page, KVPool.write (token at position p goes to slot p % B
+ * of block table[p / B], for every kv head); chapter 5 section 2.1 (append
+ * k_t, v_t to the cache). Stage 1 of the decode step.
+ *
+ * k_new, v_new: device, [total_new][n_kv][head_dim] of dtype, the new
+ *   tokens of all sequences packed in sequence order.
+ * new_start: device int32 [num_seqs + 1], prefix sums: sequence s owns new
+ *   rows new_start[s] .. new_start[s+1]-1; new_start[num_seqs] == total_new.
+ * start_pos: device int32 [num_seqs], position of sequence s's first new
+ *   token (its cached length before the append).
+ * The table rows must already cover start_pos[s] + (new tokens of s)
+ * (kvpool_ensure). Only the addressed slots are written.
+ * Errors: NULL_POINTER, INVALID_ARGUMENT (negative/zero sizes, dtype),
+ * HIP. total_new == 0 launches nothing. */
+int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+              const int32_t* block_table, int32_t table_stride,
+              const int32_t* start_pos, const int32_t* new_start,
+              int32_t num_seqs, int32_t total_new, int32_t num_blocks,
+              int32_t n_kv, int32_t head_dim, int32_t block_size, int32_t dtype,
+              void* stream);
+
+/* ======================================================================
+ * Attention workspace. Both attention entry points split each sequence's
+ * keys into ranges of split_tokens keys, compute a partial softmax state
+ * per range, and merge the ranges in a second pass (chapter 5 section 4.1:
+ * online softmax; the merged result equals the plain softmax).
+ *
+ * split_tokens: 0 = let the library choose (paged_attn_split_tokens tells
+ *   which); otherwise a positive multiple of block_size.
+ * num_q_rows: decode = num_seqs; chunk = total query rows.
+ * Writes the required byte count to *bytes (may be 0 for shapes that need
+ * no partials). Errors: NULL_POINTER, INVALID_ARGUMENT. */
+int paged_attn_split_tokens(int32_t num_q_rows, int32_t n_kv, int32_t block_size,
+                            int32_t max_seq_len, int32_t requested, int32_t* out);
+int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_t n_kv,
+                              int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                              int32_t split_tokens, size_t* bytes);
+
+/* ======================================================================
+ * paged_attn_decode - one query token per sequence.
+ *
+ * Source: chapter 5 section 2.1 (q_t against every cached key and value),
+ * section 3.1 (query head h uses kv head h / (n_q/n_kv)), section 3.2
+ * (the kernel reads the block table to gather K/V from scattered pages);
+ * lab page, forward (scores scaled by `scale`, max-subtracted softmax,
+ * weighted sum of V). Stages 2 and 3 of the decode step.
+ *
+ * seq_lens: device int32 [num_seqs], keys per sequence *after* the append
+ *   (the new token included); each must be in [1, max_seq_len] and at
+ *   most table_stride * block_size, else that row's output is NaN.
+ * q, out: [num_seqs][n_q][head_dim] of dtype; lse: float [num_seqs][n_q]
+ *   or NULL. scale: multiplies q.k (the lab uses 1/sqrt(head_dim)).
+ * workspace: device, at least paged_attn_workspace_size(num_seqs, ...)
+ *   bytes, 256-byte aligned; contents on entry are ignored.
+ * Supported: dtype PKV_BF16 or PKV_F32; 1 <= head_dim <= 512;
+ *   block_size >= 1; n_q a multiple of n_kv. bf16 with head_dim 128 and
+ *   block_size 16 takes the bandwidth-tuned kernel.
+ * Errors: NULL_POINTER, INVALID_ARGUMENT (n_q % n_kv != 0, sizes, split),
+ * UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP. */
+int paged_attn_decode(void* out, float* lse, const void* q,
+                      const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, int32_t table_stride,
+                      const int32_t* seq_lens,
+                      int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks,
+                      int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                      float scale, int32_t dtype, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * paged_attn_chunk - a chunk of C_s consecutive query tokens per sequence
+ * (chunked prefill), causal.
+ *
+ * Source: lab page, forward called on a prompt chunk at offset `start`
+ * over the gathered cache (mask: key j allowed iff j <= start + i) and its
+ * scheduler's prefill branch; chapter 5 section 4.1 (tiling with online
+ * softmax). Query i of sequence s sits at absolute position
+ * seq_lens[s] - C_s + i and attends keys 0 .. that position.
+ *
+ * q_start: device int32 [num_seqs + 1], prefix sums of C_s; q, out are
+ *   [total_q][n_q][head_dim]; lse float [total_q][n_q] or NULL.
+ * max_q_len: host bound on every C_s. seq_lens[s] >= C_s is required
+ *   (else NaN rows). Other arguments as paged_attn_decode; the workspace
+ *   is sized with num_q_rows = total_q.
+ * Errors: as paged_attn_decode. */
+int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_start,
+                     const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t table_stride,
+                     const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                     int32_t max_seq_len, int32_t num_blocks,
+                     int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                     float scale, int32_t dtype, int32_t split_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * Profiling hook (not part of the computation): when both events are
+ * non-NULL, paged_attn_decode records `before` immediately before and
+ * `after` immediately after its first-pass (split) kernel on the call's
+ * stream, so a caller can time that kernel alone. Pass NULLs to disable.
+ * Events are hipEvent_t passed as void*. Process-wide; not thread-safe. */
+int pkv_set_profile_events(void* before, void* after);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

@@ -17,6 +17,7 @@ from .paged_attention import (  # noqa: F401
     bf16_bits_to_f64,
     block_alloc_slots,
     build_cache,
+    build_tables,
     contiguous_attend,
     gather,
     kv_bytes_per_token,

@@ -394,6 +394,21 @@ def contiguous_attend(wl, s: int, heads=None):
     return _attend_rows(wl, s, K, V, heads)
 
 
+def build_tables(wl) -> np.ndarray:
+    """Only the allocation side of ``build_cache``: the table rows the
+    history-then-step replay produces (no K/V storage)."""
+    alloc = BlockAllocator(wl.num_blocks, wl.alloc_order)
+    seqs = [SequenceBlocks(wl.block_size) for _ in range(wl.num_seqs)]
+    for s in range(wl.num_seqs):
+        seqs[s].ensure(alloc, int(wl.hist_lens[s]))
+    for s in range(wl.num_seqs):
+        seqs[s].ensure(alloc, int(wl.seq_lens[s]))
+    t = np.full((wl.num_seqs, wl.table_stride), -1, dtype=np.int32)
+    for s, sb in enumerate(seqs):
+        t[s, :len(sb.blocks)] = sb.blocks
+    return t
+
+
 def build_cache(wl, fill=None) -> OracleCache:
     c = OracleCache(wl, fill)
     c.fill_history()

@@ -1,0 +1,23 @@
+"""Paged-KV decode attention for AMD MI355X (gfx950).
+
+The computation lives in the C-ABI library ``libpagedkv.so`` (hand-written
+HIP kernels plus a host block allocator, declared in ``include/pagedkv.h``);
+this package is its thin Python binding. Functions raise if the library has
+not been built (``python -m paged_kv_cache_17_amd.build``).
+"""
+from .binding import (  # noqa: F401
+    EXPORTED,
+    KVPool,
+    PKV_BF16,
+    PKV_F32,
+    PagedKVError,
+    kv_append,
+    load_library,
+    paged_attn_chunk,
+    paged_attn_decode,
+    paged_attn_split_tokens,
+    paged_attn_workspace_size,
+    pkv_set_profile_events,
+    strerror,
+)
+from .cache import PagedKVCache  # noqa: F401

@@ -1,0 +1,76 @@
+"""A paged KV cache object built on the C ABI.
+
+Holds the device K/V pools (torch tensors used as plain device memory), a
+host block table with per-sequence block counts maintained by the
+library's ``kvpool_*`` allocator, its device mirror, and a reusable
+attention workspace. Every method only marshals arguments into
+``libpagedkv.so`` calls.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+
+torch = B.torch
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks: int, n_kv: int, head_dim: int, block_size: int, dtype,
+                 num_seqs: int, table_stride: int, alloc_order=None, device="cuda", fill_nan=False):
+        self.num_blocks, self.n_kv, self.head_dim, self.block_size = num_blocks, n_kv, head_dim, block_size
+        self.dtype = dtype
+        self.device = device
+        shape = (num_blocks, n_kv, block_size, head_dim)
+        if fill_nan:
+            self.k_cache = torch.full(shape, float("nan"), dtype=dtype, device=device)
+            self.v_cache = torch.full(shape, float("nan"), dtype=dtype, device=device)
+        else:
+            self.k_cache = torch.empty(shape, dtype=dtype, device=device)
+            self.v_cache = torch.empty(shape, dtype=dtype, device=device)
+        self.pool = B.KVPool(num_blocks, block_size, alloc_order)
+        self.table = np.full((num_seqs, table_stride), -1, dtype=np.int32)
+        self.held = np.zeros(num_seqs, dtype=np.int32)
+        self.table_dev = torch.from_numpy(self.table).to(device)
+        self._ws = None
+
+    # ---- host bookkeeping -------------------------------------------------
+    def ensure(self, s: int, length: int) -> None:
+        self.pool.kvpool_ensure(self.table, self.held, s, length)
+
+    def release(self, s: int) -> None:
+        self.pool.kvpool_release(self.table, self.held, s)
+
+    def upload_table(self, stream=None) -> None:
+        self.table_dev.copy_(torch.from_numpy(self.table), non_blocking=False)
+
+    # ---- device calls -----------------------------------------------------
+    def append(self, k_new, v_new, start_pos, new_start, stream=None) -> None:
+        B.kv_append(self.k_cache, self.v_cache, k_new, v_new, self.table_dev, start_pos, new_start,
+                    stream=stream)
+
+    def workspace(self, num_q_rows: int, n_q: int, max_seq_len: int, split_tokens: int = 0):
+        need = B.paged_attn_workspace_size(num_q_rows, n_q, self.n_kv, self.head_dim, self.block_size,
+                                           max_seq_len, split_tokens)
+        need = max(need, 256)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, q, seq_lens, max_seq_len: int, scale: float, out=None, lse=None,
+               split_tokens: int = 0, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens)
+        B.paged_attn_decode(out, lse, q, self.k_cache, self.v_cache, self.table_dev, seq_lens,
+                            max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
+        return out
+
+    def chunk(self, q, q_start, seq_lens, max_q_len: int, max_seq_len: int, scale: float, out=None,
+              lse=None, split_tokens: int = 0, stream=None):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens)
+        B.paged_attn_chunk(out, lse, q, q_start, self.k_cache, self.v_cache, self.table_dev, seq_lens,
+                           max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
+        return out

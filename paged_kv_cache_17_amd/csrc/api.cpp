@@ -1,0 +1,263 @@
+// C ABI entry points: argument validation, workspace layout and dispatch.
+//
+// Every check runs before the first launch, so an error return leaves the
+// caller's buffers untouched. Kernels run asynchronously on the caller's
+// stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "pagedkv.h"
+
+namespace {
+
+constexpr int kMaxHeadDim = 512;
+constexpr int kMaxSplitTokens = 8192;
+constexpr size_t kAlign = 256;
+
+hipEvent_t g_prof_before = nullptr;
+hipEvent_t g_prof_after = nullptr;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dtype) {
+    if (dtype == PKV_F32) return 4;
+    if (dtype == PKV_BF16) return 2;
+    return 0;
+}
+
+// Auto split size: the largest of 1024/512/256 tokens (rounded to whole
+// blocks) that still gives the launch enough (row, kv head, range)
+// workgroups to cover the chip several times over.
+int auto_split(int rows, int n_kv, int block_size, int max_seq_len) {
+    const long long pairs = static_cast<long long>(rows) * n_kv;
+    int chosen = 0;
+    for (int cand : {1024, 512, 256}) {
+        int sp = (cand + block_size - 1) / block_size * block_size;
+        if (sp > kMaxSplitTokens) sp = kMaxSplitTokens / block_size * block_size;
+        if (sp < block_size) sp = block_size;
+        chosen = sp;
+        const long long ranges = (max_seq_len + sp - 1) / sp;
+        if (pairs * ranges >= 2048) break;
+    }
+    return chosen;
+}
+
+int resolve_split(int rows, int n_kv, int block_size, int max_seq_len, int requested, int* out) {
+    if (requested < 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (requested == 0) {
+        *out = auto_split(rows, n_kv, block_size, max_seq_len);
+        return PKV_OK;
+    }
+    if (requested % block_size || requested > kMaxSplitTokens) return PKV_ERR_INVALID_ARGUMENT;
+    *out = requested;
+    return PKV_OK;
+}
+
+struct Layout {
+    size_t ml_bytes;
+    size_t o_offset;
+    size_t total;
+};
+
+Layout ws_layout(int rows, int n_q, int head_dim, int max_splits) {
+    const size_t parts = static_cast<size_t>(rows) * n_q * max_splits;
+    Layout w;
+    w.ml_bytes = parts * sizeof(pkv::PartialML);
+    w.o_offset = align_up(w.ml_bytes);
+    w.total = w.o_offset + parts * head_dim * sizeof(float);
+    return w;
+}
+
+int check_shape(int num_seqs, int max_seq_len, int num_blocks, int n_q, int n_kv, int head_dim,
+                int block_size, int table_stride, int dtype, float scale) {
+    if (num_seqs < 0 || max_seq_len < 1 || num_blocks < 1 || n_q < 1 || n_kv < 1 ||
+        head_dim < 1 || block_size < 1 || table_stride < 1)
+        return PKV_ERR_INVALID_ARGUMENT;
+    if (n_q % n_kv) return PKV_ERR_INVALID_ARGUMENT;
+    if (!elem_bytes(dtype)) return PKV_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARGUMENT;
+    if (head_dim > kMaxHeadDim) return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decode,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (a.num_rows == 0) return PKV_OK;
+    if (!workspace) return PKV_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
+    const Layout w = ws_layout(a.num_rows, a.n_q, a.head_dim, a.max_splits);
+    if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    a.ws_ml = static_cast<pkv::PartialML*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_offset);
+    const bool bf16 = dtype == PKV_BF16;
+
+    const bool fast = decode && bf16 &&
+                      pkv::decode_fast_supported(a.n_q, a.n_kv, a.head_dim, a.block_size, a.split_tokens) &&
+                      aligned16(a.q) && aligned16(a.k_cache) && aligned16(a.v_cache);
+    hipError_t e;
+    if (fast) {
+        if (g_prof_before && g_prof_after) hipEventRecord(g_prof_before, stream);
+        e = pkv::launch_decode_fast(a, stream);
+        if (g_prof_before && g_prof_after) hipEventRecord(g_prof_after, stream);
+    } else {
+        e = pkv::launch_split_generic(a, bf16, stream);
+    }
+    if (e != hipSuccess) return PKV_ERR_HIP;
+    e = pkv::launch_merge(a, out, lse, bf16, stream);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" const char* pkv_strerror(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL_POINTER: return "null pointer";
+        case PKV_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case PKV_ERR_OUT_OF_BLOCKS: return "out of KV blocks";
+        case PKV_ERR_INVALID_FREE: return "invalid free (out of range, already free, or repeated)";
+        case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case PKV_ERR_TABLE_FULL: return "block table row full";
+        case PKV_ERR_HIP: return "HIP launch error";
+        case PKV_ERR_NO_MEMORY: return "out of host memory";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int pkv_set_profile_events(void* before, void* after) {
+    g_prof_before = static_cast<hipEvent_t>(before);
+    g_prof_after = static_cast<hipEvent_t>(after);
+    return PKV_OK;
+}
+
+extern "C" int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                         const int32_t* block_table, int32_t table_stride,
+                         const int32_t* start_pos, const int32_t* new_start,
+                         int32_t num_seqs, int32_t total_new, int32_t num_blocks,
+                         int32_t n_kv, int32_t head_dim, int32_t block_size, int32_t dtype,
+                         void* stream) {
+    if (num_seqs < 0 || total_new < 0 || num_blocks < 1 || n_kv < 1 || head_dim < 1 ||
+        block_size < 1 || table_stride < 1)
+        return PKV_ERR_INVALID_ARGUMENT;
+    const int eb = elem_bytes(dtype);
+    if (!eb) return PKV_ERR_INVALID_ARGUMENT;
+    if (total_new == 0) return PKV_OK;
+    if (num_seqs == 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (!k_cache || !v_cache || !k_new || !v_new || !block_table || !start_pos || !new_start)
+        return PKV_ERR_NULL_POINTER;
+    hipError_t e = pkv::launch_kv_append(k_cache, v_cache, k_new, v_new, block_table, table_stride,
+                                         start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
+                                         head_dim * eb, block_size, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_attn_split_tokens(int32_t num_q_rows, int32_t n_kv, int32_t block_size,
+                                       int32_t max_seq_len, int32_t requested, int32_t* out) {
+    if (!out) return PKV_ERR_NULL_POINTER;
+    if (num_q_rows < 0 || n_kv < 1 || block_size < 1 || max_seq_len < 1) return PKV_ERR_INVALID_ARGUMENT;
+    return resolve_split(num_q_rows, n_kv, block_size, max_seq_len, requested, out);
+}
+
+extern "C" int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_t n_kv,
+                                         int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                         int32_t split_tokens, size_t* bytes) {
+    if (!bytes) return PKV_ERR_NULL_POINTER;
+    if (num_q_rows < 0 || n_q < 1 || n_kv < 1 || head_dim < 1 || block_size < 1 || max_seq_len < 1)
+        return PKV_ERR_INVALID_ARGUMENT;
+    int split = 0;
+    int rc = resolve_split(num_q_rows, n_kv, block_size, max_seq_len, split_tokens, &split);
+    if (rc != PKV_OK) return rc;
+    const int max_splits = (max_seq_len + split - 1) / split;
+    *bytes = ws_layout(num_q_rows, n_q, head_dim, max_splits).total;
+    return PKV_OK;
+}
+
+extern "C" int paged_attn_decode(void* out, float* lse, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, int32_t table_stride,
+                                 const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks,
+                                 int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                 float scale, int32_t dtype, int32_t split_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size,
+                         table_stride, dtype, scale);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_table || !seq_lens) return PKV_ERR_NULL_POINTER;
+    int split = 0;
+    rc = resolve_split(num_seqs, n_kv, block_size, max_seq_len, split_tokens, &split);
+    if (rc != PKV_OK) return rc;
+    pkv::AttnArgs a{};
+    a.q = q;
+    a.q_start = nullptr;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.table = block_table;
+    a.seq_lens = seq_lens;
+    a.table_stride = table_stride;
+    a.num_seqs = num_seqs;
+    a.num_rows = num_seqs;
+    a.max_q_len = 1;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_blocks;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.split_tokens = split;
+    a.max_splits = (max_seq_len + split - 1) / split;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    return run_attention(a, out, lse, dtype, true, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_start,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t table_stride,
+                                const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                int32_t max_seq_len, int32_t num_blocks,
+                                int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                float scale, int32_t dtype, int32_t split_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size,
+                         table_stride, dtype, scale);
+    if (rc != PKV_OK) return rc;
+    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len) return PKV_ERR_INVALID_ARGUMENT;
+    if (total_q == 0) return PKV_OK;
+    if (num_seqs == 0 || max_q_len == 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (!out || !q || !q_start || !k_cache || !v_cache || !block_table || !seq_lens)
+        return PKV_ERR_NULL_POINTER;
+    int split = 0;
+    rc = resolve_split(total_q, n_kv, block_size, max_seq_len, split_tokens, &split);
+    if (rc != PKV_OK) return rc;
+    pkv::AttnArgs a{};
+    a.q = q;
+    a.q_start = q_start;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.table = block_table;
+    a.seq_lens = seq_lens;
+    a.table_stride = table_stride;
+    a.num_seqs = num_seqs;
+    a.num_rows = total_q;
+    a.max_q_len = max_q_len;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_blocks;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.split_tokens = split;
+    a.max_splits = (max_seq_len + split - 1) / split;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    return run_attention(a, out, lse, dtype, false, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}

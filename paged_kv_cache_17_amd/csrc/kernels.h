@@ -1,0 +1,52 @@
+// Host-side launch wrappers for the paged-KV kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Partial softmax state of one (row, query head, key range): max of the
+// scaled scores in log2 units, and the sum of 2^(score - max).
+struct PartialML {
+    float m;
+    float l;
+};
+
+struct AttnArgs {
+    const void* q;
+    const int32_t* q_start;      // nullptr: one query row per sequence
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* table;
+    const int32_t* seq_lens;
+    int table_stride;
+    int num_seqs;
+    int num_rows;                // decode: num_seqs; chunk: total query rows
+    int max_q_len;
+    int max_seq_len;
+    int num_blocks;
+    int n_q, n_kv, head_dim, block_size;
+    int split_tokens, max_splits;
+    float scale_log2;            // scale * log2(e)
+    float* ws_o;                 // [rows][n_q][max_splits][head_dim]
+    PartialML* ws_ml;            // [rows][n_q][max_splits]
+};
+
+hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* table, int table_stride, const int32_t* start_pos,
+                            const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
+                            int n_kv, int row_bytes, int block_size, hipStream_t stream);
+
+// Split pass for any shape/dtype (one wave per row, head and key range).
+hipError_t launch_split_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
+
+// Split pass tuned for decode with bf16, head_dim 128, block_size 16.
+bool decode_fast_supported(int n_q, int n_kv, int head_dim, int block_size, int split_tokens);
+hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream);
+
+// Merge pass: combines each row's partial states into out (and lse).
+hipError_t launch_merge(const AttnArgs& a, void* out, float* lse, bool bf16, hipStream_t stream);
+
+}  // namespace pkv

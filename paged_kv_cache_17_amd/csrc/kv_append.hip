@@ -1,0 +1,80 @@
+// kv_append: scatter new tokens' K/V into the block pool through the table.
+//
+// Lab page (Inference Engineering), KVPool.write: the token at position p
+// of a sequence is stored in slot p % B of block table[p / B], for every kv
+// head. One thread moves one UNIT-byte piece of one (token, kv head) row,
+// so consecutive threads write consecutive bytes of a pool slot.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+template <int UNIT> struct Piece;
+template <> struct Piece<16> { using T = uint4; };
+template <> struct Piece<8> { using T = uint2; };
+template <> struct Piece<4> { using T = uint32_t; };
+template <> struct Piece<2> { using T = uint16_t; };
+
+template <int UNIT>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    char* __restrict__ kc, char* __restrict__ vc,
+    const char* __restrict__ kn, const char* __restrict__ vn,
+    const int32_t* __restrict__ table, int table_stride,
+    const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start,
+    int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs) {
+    using P = typename Piece<UNIT>::T;
+    const int units = row_bytes / UNIT;
+    const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<long long>(total_new) * n_kv * units) return;
+    const int u = static_cast<int>(idx % units);
+    const long long th = idx / units;
+    const int h = static_cast<int>(th % n_kv);
+    const int t = static_cast<int>(th / n_kv);
+    const int s = seq_of_row(new_start, num_seqs, t);
+    const int pos = start_pos[s] + (t - new_start[s]);
+    if (pos < 0 || pos / bs >= table_stride) return;
+    const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
+    if (blk < 0 || blk >= num_blocks) return;   // unmapped slot: nothing is written
+    const size_t dst = ((static_cast<size_t>(blk) * n_kv + h) * bs + pos % bs) * row_bytes +
+                       static_cast<size_t>(u) * UNIT;
+    const size_t src = (static_cast<size_t>(t) * n_kv + h) * row_bytes + static_cast<size_t>(u) * UNIT;
+    *reinterpret_cast<P*>(kc + dst) = *reinterpret_cast<const P*>(kn + src);
+    *reinterpret_cast<P*>(vc + dst) = *reinterpret_cast<const P*>(vn + src);
+}
+
+template <int UNIT>
+hipError_t launch_unit(void* kc, void* vc, const void* kn, const void* vn, const int32_t* table,
+                       int table_stride, const int32_t* start_pos, const int32_t* new_start,
+                       int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs,
+                       hipStream_t stream) {
+    const long long work = static_cast<long long>(total_new) * n_kv * (row_bytes / UNIT);
+    const unsigned grid = static_cast<unsigned>((work + 255) / 256);
+    hipLaunchKernelGGL(kv_append_kernel<UNIT>, dim3(grid), dim3(256), 0, stream,
+                       static_cast<char*>(kc), static_cast<char*>(vc),
+                       static_cast<const char*>(kn), static_cast<const char*>(vn), table,
+                       table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
+                       row_bytes, bs);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* table, int table_stride, const int32_t* start_pos,
+                            const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
+                            int n_kv, int row_bytes, int block_size, hipStream_t stream) {
+    const uintptr_t align = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+                            reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new);
+#define PKV_APPEND(U)                                                                          \
+    return launch_unit<U>(k_cache, v_cache, k_new, v_new, table, table_stride, start_pos,      \
+                          new_start, num_seqs, total_new, num_blocks, n_kv, row_bytes,         \
+                          block_size, stream)
+    if (row_bytes % 16 == 0 && align % 16 == 0) PKV_APPEND(16);
+    if (row_bytes % 8 == 0 && align % 8 == 0) PKV_APPEND(8);
+    if (row_bytes % 4 == 0 && align % 4 == 0) PKV_APPEND(4);
+    PKV_APPEND(2);
+#undef PKV_APPEND
+}
+
+}  // namespace pkv

@@ -1,0 +1,114 @@
+"""Helpers for the GPU parity tests: run a workload through the C ABI and
+compare with the oracle. Imported by tests only."""
+from __future__ import annotations
+
+import numpy as np
+
+from workloads import BF16
+
+try:
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+# Tolerances (also stated in the tests that use them):
+#  fp32 K/V: max |out - ref| <= 1e-5 per element;
+#  bf16 K/V: per (query row, head), max_d |out - ref| <= 2e-2 * max_d |ref|;
+#  lse: |lse - ref| <= 1e-4 (fp32) / 1e-2 (bf16), i.e. sum_j exp(s_j - lse)
+#  is 1 to that accuracy.
+TOL_F32 = 1e-5
+TOL_BF16_REL = 2e-2
+TOL_LSE = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def torch_dtype(dtype):
+    return torch.bfloat16 if dtype == BF16 else torch.float32
+
+
+def raw_to_torch(raw, dtype, device="cuda"):
+    raw = np.ascontiguousarray(raw)
+    if dtype == BF16:
+        return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(raw.astype(np.float32, copy=False)).to(device)
+
+
+def torch_to_raw(t, dtype):
+    t = t.detach().cpu().contiguous()
+    if dtype == BF16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def i32(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def build_gpu_cache(wl, fill_nan=True, alloc_order=None):
+    """Replay history then step through the library: tables grown by
+    ``kvpool_ensure`` in sequence order, K/V written by ``kv_append``."""
+    import paged_kv_cache_17_amd as pkv
+    order = wl.alloc_order if alloc_order is None else alloc_order
+    c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size, torch_dtype(wl.dtype),
+                         wl.num_seqs, wl.table_stride, alloc_order=order, fill_nan=fill_nan)
+    for s in range(wl.num_seqs):
+        c.ensure(s, int(wl.hist_lens[s]))
+    c.upload_table()
+    kh, vh = wl.packed_hist_kv()
+    if len(kh):
+        hs = np.zeros(wl.num_seqs + 1, dtype=np.int64)
+        np.cumsum(wl.hist_lens, out=hs[1:])
+        c.append(raw_to_torch(kh, wl.dtype), raw_to_torch(vh, wl.dtype),
+                 i32(np.zeros(wl.num_seqs)), i32(hs))
+    for s in range(wl.num_seqs):
+        c.ensure(s, int(wl.seq_lens[s]))
+    c.upload_table()
+    kn, vn = wl.packed_new_kv()
+    if len(kn):
+        c.append(raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype), i32(wl.hist_lens), i32(wl.q_offsets))
+    torch.cuda.synchronize()
+    return c
+
+
+def run_decode(c, wl, split_tokens=0, with_lse=True):
+    q = raw_to_torch(wl.q, wl.dtype)
+    lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda") if with_lse else None
+    out = c.decode(q, i32(wl.seq_lens), wl.max_seq_len, wl.scale, lse=lse, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_chunk(c, wl, split_tokens=0, with_lse=True):
+    q = raw_to_torch(wl.q, wl.dtype)
+    lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda") if with_lse else None
+    out = c.chunk(q, i32(wl.q_offsets), i32(wl.seq_lens), wl.max_new, wl.max_seq_len, wl.scale,
+                  lse=lse, split_tokens=split_tokens)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def out_f64(out, dtype):
+    import oracle
+    return oracle.widen(torch_to_raw(out, dtype), dtype)
+
+
+def check_rows(got, ref, dtype, where=""):
+    """Compare ``[rows, n_q, d]`` outputs to the oracle at the stated tolerance.
+    Returns the worst error (absolute for fp32, relative-to-row-max for bf16)."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"non-finite output {where}"
+    err = np.abs(got - ref).max(axis=-1)
+    if dtype == BF16:
+        scale = np.abs(ref).max(axis=-1)
+        rel = err / scale
+        worst = float(rel.max())
+        assert worst <= TOL_BF16_REL, f"bf16 row error {worst:.3e} > {TOL_BF16_REL} {where}"
+        return worst
+    worst = float(err.max())
+    assert worst <= TOL_F32, f"fp32 error {worst:.3e} > {TOL_F32} {where}"
+    return worst
+
+
+def check_lse(got, ref, dtype, where=""):
+    d = float(np.abs(got - ref).max())
+    assert d <= TOL_LSE[dtype], f"lse error {d:.3e} {where}"
+    return d

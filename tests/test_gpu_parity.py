@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (from the oracle-vs-page pins and the stated tolerances):
+  * block tables and pool bytes: bit-exact (including NaN-poisoned slots
+    nobody wrote);
+  * fp32 K/V: max |out - ref| <= 1e-5;
+  * bf16 K/V: per (row, head) max_d |out - ref| <= 2e-2 * max_d |ref|;
+  * lse within 1e-4 (fp32) / 1e-2 (bf16) of the oracle's;
+  * same input, same split size: bit-identical outputs; relabelled blocks:
+    bit-identical outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import BF16, F32, build_workload, config_workload
+
+from gpu_harness import (build_gpu_cache, check_lse, check_rows, i32, out_f64, raw_to_torch, run_chunk,
+                         run_decode, torch_to_raw)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_17_amd as pkv
+    pkv.load_library()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _full_check(wl, mode="decode", split_tokens=0, check_pool=True):
+    """Build both sides, compare tables, pools and every output row."""
+    c = build_gpu_cache(wl)
+    ora = oracle.build_cache(wl)
+    assert np.array_equal(c.table, ora.tables())
+    if check_pool:
+        assert np.array_equal(torch_to_raw(c.k_cache, wl.dtype).view(np.uint8), ora.pool_k.view(np.uint8))
+        assert np.array_equal(torch_to_raw(c.v_cache, wl.dtype).view(np.uint8), ora.pool_v.view(np.uint8))
+    out, lse = (run_decode if mode == "decode" else run_chunk)(c, wl, split_tokens)
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(out_f64(out, wl.dtype), ref, wl.dtype, f"{wl.name} {mode} split={split_tokens}")
+    lerr = check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, wl.dtype)
+    return c, out, err, lerr
+
+
+# ------------------------------------------------------------ small shapes ---
+
+
+def test_config1_lab_scale_decode_and_chunk():
+    wl = config_workload(1)
+    say("config 1 decode", wl.seq_lens.tolist())
+    _, _, err, lerr = _full_check(wl, "decode")
+    say(f"  max abs err {err:.2e} lse {lerr:.2e}")
+    _full_check(wl, "chunk")
+
+
+def test_append_that_opens_a_block():
+    # cached lengths that are multiples of the block size: the new token
+    # takes a freshly allocated block during the step
+    wl = build_workload(n_q=2, n_kv=2, head_dim=4, block_size=4, dtype=F32, hist_lens=[8, 4, 3, 0],
+                        new_lens=[1, 1, 1, 1], num_blocks=12, table_stride=6, seed=7)
+    say("append opens block", wl.seq_lens.tolist())
+    c, _, _, _ = _full_check(wl, "decode")
+    assert c.held.tolist() == [3, 2, 1, 1]
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 33, 255, 256, 257, 511, 512, 513, 1000, 1023, 1025, 2047, 2049, 3000]
+
+
+@pytest.mark.parametrize("split", [0, 16, 256, 1024, 2048])
+def test_gqa_bf16_ragged_lengths_fast_path(split):
+    L = np.array(RAGGED)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=3)
+    say("gqa bf16 ragged split", split)
+    c, out, err, lerr = _full_check(wl, "decode", split, check_pool=(split == 0))
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+    out2, _ = run_decode(c, wl, split)
+    assert torch.equal(out, out2), "repeat run not bit-identical"
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(8, 8), (16, 8), (32, 4), (6, 3)])
+def test_group_sizes(n_q, n_kv):
+    L = np.array([1, 40, 700, 1500])
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=5)
+    say("group sizes", n_q, n_kv)
+    _full_check(wl, "decode", 256)
+
+
+@pytest.mark.parametrize("dtype,d,bs,n_q,n_kv", [
+    (F32, 128, 16, 32, 8), (BF16, 64, 16, 8, 2), (BF16, 128, 8, 8, 2), (BF16, 96, 32, 4, 2),
+    (F32, 1, 1, 1, 1), (BF16, 4, 2, 4, 2), (F32, 256, 4, 2, 1)])
+def test_generic_shapes(dtype, d, bs, n_q, n_kv):
+    L = np.array([1, 3, bs, bs + 1, 5 * bs + 3, 300])
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=d, block_size=bs, dtype=dtype, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=9)
+    say("generic", dtype, d, bs, n_q, n_kv)
+    _full_check(wl, "decode", 0)
+    _full_check(wl, "decode", bs * 8)
+
+
+def test_relabelled_blocks_give_bit_identical_output():
+    L = np.array([5, 77, 600, 1400])
+    kw = dict(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+              new_lens=np.ones_like(L), seed=12)
+    wl = build_workload(**kw)
+    say("relabelling")
+    a = build_gpu_cache(wl, alloc_order=np.arange(wl.num_blocks, dtype=np.int32))
+    b = build_gpu_cache(wl, alloc_order=np.random.default_rng(1).permutation(wl.num_blocks).astype(np.int32))
+    assert not np.array_equal(a.table, b.table)
+    for split in (0, 256):
+        oa, la = run_decode(a, wl, split)
+        ob, lb = run_decode(b, wl, split)
+        assert torch.equal(oa, ob) and torch.equal(la, lb)
+        ca, _ = run_chunk(a, wl, split)
+        cb, _ = run_chunk(b, wl, split)
+        assert torch.equal(ca, cb)
+
+
+def test_chunk_mix_and_c1_equals_decode():
+    hist = [299, 999, 4095, 0, 17, 100, 511, 0, 2000]
+    new = [1, 1, 1, 64, 64, 33, 1, 1, 100]
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist,
+                        new_lens=new, seed=4)
+    say("chunk mix")
+    _full_check(wl, "chunk", 0)
+    _full_check(wl, "chunk", 64)
+    # every sequence with one new token: the chunk path equals the decode path
+    L = np.array([1, 17, 300, 2100])
+    wl1 = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                         new_lens=np.ones_like(L), seed=6)
+    c = build_gpu_cache(wl1)
+    od, _ = run_decode(c, wl1)
+    oc, _ = run_chunk(c, wl1)
+    check_rows(out_f64(oc, BF16), out_f64(od, BF16), BF16, "chunk C=1 vs decode")
+
+
+def test_lab_prompt_as_chunks_5_then_4():
+    """The lab's 9-token prompt run as chunks [5, 4] equals one 9-token chunk."""
+    one = build_workload(n_q=2, n_kv=2, head_dim=4, block_size=4, dtype=F32, hist_lens=[0], new_lens=[9],
+                         num_blocks=12, table_stride=6, seed=7)
+    say("lab chunks [5, 4]")
+    c_one, out_one, _, _ = _full_check(one, "chunk")
+    import paged_kv_cache_17_amd as pkv
+    c = pkv.PagedKVCache(12, 2, 4, 4, torch.float32, 1, 6, alloc_order=one.alloc_order, fill_nan=True)
+    q_all = raw_to_torch(one.q, F32)
+    outs, lo = [], 0
+    for n in (5, 4):
+        c.ensure(0, lo + n)
+        c.upload_table()
+        k = raw_to_torch(one.k_seq[lo:lo + n], F32)
+        v = raw_to_torch(one.v_seq[lo:lo + n], F32)
+        c.append(k, v, i32([lo]), i32([0, n]))
+        outs.append(c.chunk(q_all[lo:lo + n].contiguous(), i32([0, n]), i32([lo + n]), n, 9, one.scale))
+        lo += n
+    torch.cuda.synchronize()
+    assert np.array_equal(c.table, c_one.table)
+    got = torch.cat(outs).cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - out_one.cpu().numpy())) <= 1e-5
+    c.release(0)
+    c.release(0)
+    assert c.pool.kvpool_num_free() == 12
+
+
+@pytest.mark.parametrize("fast", [True, False])
+def test_invalid_rows_become_nan_and_leave_others_alone(fast):
+    L = np.array([40, 50, 60, 70, 80])
+    d, bs = (128, 16) if fast else (64, 16)
+    wl = build_workload(n_q=8, n_kv=2, head_dim=d, block_size=bs, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=2)
+    say("invalid rows fast" if fast else "invalid rows generic")
+    c = build_gpu_cache(wl)
+    ora = oracle.build_cache(wl)
+    lens = wl.seq_lens.copy()
+    lens[1] = 0                          # empty sequence
+    lens[2] = 10 ** 6                    # beyond max_seq_len and the table
+    c.table_dev[3, 1] = 10 ** 6          # block id outside the pool
+    q = raw_to_torch(wl.q, BF16)
+    lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.decode(q, i32(lens), wl.max_seq_len, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    got = out_f64(out, BF16)
+    ref, _ = oracle.paged_attention_all(ora)
+    for s in (1, 2, 3):
+        assert np.isnan(got[s]).all() and np.isnan(lse[s].cpu().numpy()).all()
+    keep = [0, 4]
+    check_rows(got[keep], ref[keep], BF16, "valid rows next to invalid ones")
+
+
+# ----------------------------------------------------- full-size configs ---
+
+
+def _sample_seqs(wl, k=6):
+    order = np.argsort(wl.seq_lens, kind="stable")
+    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    rng = np.random.default_rng(0)
+    pick |= set(rng.choice(wl.num_seqs, size=min(k, wl.num_seqs), replace=False).tolist())
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_config_sampled(cfg):
+    wl = config_workload(cfg)
+    say(f"config {cfg}: {wl.num_seqs} seqs, {int(wl.seq_lens.sum())} keys, {wl.num_blocks} blocks")
+    c = build_gpu_cache(wl, fill_nan=True)
+    assert np.array_equal(c.table, oracle.build_tables(wl))
+    kpool = torch_to_raw(c.k_cache, wl.dtype)
+    vpool = torch_to_raw(c.v_cache, wl.dtype)
+    picks = _sample_seqs(wl)
+    for s in picks:
+        L = int(wl.seq_lens[s])
+        k, v = wl.rows(s, 0, L)
+        blocks = c.table[s, :c.held[s]]
+        assert np.array_equal(oracle.gather(kpool, blocks, L, wl.block_size).view(np.uint16),
+                              k.transpose(1, 0, 2).view(np.uint16))
+        assert np.array_equal(oracle.gather(vpool, blocks, L, wl.block_size).view(np.uint16),
+                              v.transpose(1, 0, 2).view(np.uint16))
+    del kpool, vpool
+    if cfg == 5:
+        dec = np.nonzero(wl.new_lens == 1)[0]
+        pre = np.nonzero(wl.new_lens > 1)[0]
+        assert dec.tolist() == list(range(len(dec)))      # decode rows come first
+        nd = len(dec)
+        q = raw_to_torch(wl.q, BF16)
+        lens = i32(wl.seq_lens)
+        lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
+        import paged_kv_cache_17_amd as pkv
+        ws = c.workspace(int(q.shape[0]), wl.n_q, wl.max_seq_len)
+        out = torch.empty_like(q)
+        pkv.paged_attn_decode(out[:nd], lse[:nd], q[:nd], c.k_cache, c.v_cache, c.table_dev[:nd], lens[:nd],
+                              int(wl.seq_lens[:nd].max()), wl.scale, ws)
+        qs = wl.q_offsets[nd:] - wl.q_offsets[nd]
+        ws2 = torch.empty_like(ws)
+        pkv.paged_attn_chunk(out[nd:], lse[nd:], q[nd:], i32(qs), c.k_cache, c.v_cache, c.table_dev[nd:],
+                             lens[nd:], int(wl.new_lens[nd:].max()), int(wl.seq_lens[nd:].max()), wl.scale, ws2)
+        torch.cuda.synchronize()
+    else:
+        out, lse = run_decode(c, wl)
+    got = out_f64(out, wl.dtype)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for s in picks:
+        a, b = int(wl.q_offsets[s]), int(wl.q_offsets[s + 1])
+        rows = range(a, b) if b - a <= 8 else [a, a + 1, (a + b) // 2, b - 2, b - 1]
+        ref, ref_lse = oracle.contiguous_attend(wl, s)
+        for r in rows:
+            worst = max(worst, check_rows(got[r:r + 1], ref[r - a:r - a + 1], wl.dtype, f"cfg {cfg} seq {s}"))
+            check_lse(got_lse[r], ref_lse[r - a], wl.dtype, f"cfg {cfg} seq {s}")
+    assert np.isfinite(got).all()
+    say(f"  sampled {len(picks)} seqs, worst row rel err {worst:.2e}")

@@ -6,14 +6,18 @@ histories and queries drawn from N(0, 1). bf16 data is produced from fp32
 draws by round-to-nearest-even and kept as raw uint16 bit patterns, so a
 consumer decides itself how to widen it.
 
-Draw order for one workload (all from ``numpy.random.default_rng(seed)``):
-lengths -> pool permutation -> for each sequence in index order its K rows
-then its V rows (history and new tokens together) -> all query rows.
+Draw order for one workload: lengths, then the pool permutation, from
+``numpy.random.default_rng(seed)``; sequence ``s``'s K rows then V rows
+(history and new tokens together) from ``default_rng([seed, 1, s])``; all
+query rows from ``default_rng([seed, 2])``. Per-sequence streams make the
+draw independent of how many threads fill the arrays.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -33,7 +37,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
-    bits = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    bits = t.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         bits[nan] = np.uint16(0x7FC0)
@@ -143,6 +152,14 @@ def _draw(rng, shape, dtype):
     return f32_to_bf16_bits(x) if dtype == BF16 else x
 
 
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def build_workload(*, n_q, n_kv, head_dim, block_size, dtype, hist_lens, new_lens,
                    num_blocks=None, table_stride=None, order="random", seed=7,
                    rng=None, name="custom", scale=None) -> Workload:
@@ -175,13 +192,17 @@ def build_workload(*, n_q, n_kv, head_dim, block_size, dtype, hist_lens, new_len
     sd = storage_dtype(dtype)
     k_seq = np.empty((int(kv_offsets[-1]), n_kv, head_dim), dtype=sd)
     v_seq = np.empty_like(k_seq)
-    for s, L in enumerate(total):
+    def fill(s):
         a, b = int(kv_offsets[s]), int(kv_offsets[s + 1])
-        k_seq[a:b] = _draw(rng, (int(L), n_kv, head_dim), dtype)
-        v_seq[a:b] = _draw(rng, (int(L), n_kv, head_dim), dtype)
+        srng = np.random.default_rng([seed, 1, s])
+        k_seq[a:b] = _draw(srng, (b - a, n_kv, head_dim), dtype)
+        v_seq[a:b] = _draw(srng, (b - a, n_kv, head_dim), dtype)
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(len(total))))
     q_offsets = np.zeros(len(new) + 1, dtype=np.int64)
     np.cumsum(new, out=q_offsets[1:])
-    q = _draw(rng, (int(q_offsets[-1]), n_q, head_dim), dtype)
+    q = _draw(np.random.default_rng([seed, 2]), (int(q_offsets[-1]), n_q, head_dim), dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     return Workload(name=name, n_q=n_q, n_kv=n_kv, head_dim=head_dim, block_size=block_size,
