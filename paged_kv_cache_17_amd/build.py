@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["kvpool.cpp", "api.cpp", "kv_append.hip", "attn_generic.hip", "attn_merge.hip",
-           "decode_bf16.hip"]
+           "decode_bf16.hip", "decode_balanced.hip"]
 
 
 def hipcc() -> str:

@@ -17,7 +17,8 @@ torch = B.torch
 
 class PagedKVCache:
     def __init__(self, num_blocks: int, n_kv: int, head_dim: int, block_size: int, dtype,
-                 num_seqs: int, table_stride: int, alloc_order=None, device="cuda", fill_nan=False):
+                 num_seqs: int, table_stride: int, alloc_order=None, device="cuda", fill_nan=False,
+                 poison_workspace=False):
         self.num_blocks, self.n_kv, self.head_dim, self.block_size = num_blocks, n_kv, head_dim, block_size
         self.dtype = dtype
         self.device = device
@@ -33,6 +34,10 @@ class PagedKVCache:
         self.held = np.zeros(num_seqs, dtype=np.int32)
         self.table_dev = torch.from_numpy(self.table).to(device)
         self._ws = None
+        # Debug aid: fill the workspace with 0xFF bytes (NaN floats) before
+        # every call, so a partial slot the first pass failed to write shows
+        # up as NaN output instead of reading stale memory.
+        self.poison_workspace = poison_workspace
 
     # ---- host bookkeeping -------------------------------------------------
     def ensure(self, s: int, length: int) -> None:
@@ -55,6 +60,8 @@ class PagedKVCache:
         need = max(need, 256)
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        if self.poison_workspace:
+            self._ws.fill_(0xFF)
         return self._ws
 
     def decode(self, q, seq_lens, max_seq_len: int, scale: float, out=None, lse=None,

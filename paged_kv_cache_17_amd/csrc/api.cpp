@@ -59,6 +59,7 @@ int resolve_split(int rows, int n_kv, int block_size, int max_seq_len, int reque
 struct Layout {
     size_t ml_bytes;
     size_t o_offset;
+    size_t prefix_offset;
     size_t total;
 };
 
@@ -67,8 +68,36 @@ Layout ws_layout(int rows, int n_q, int head_dim, int max_splits) {
     Layout w;
     w.ml_bytes = parts * sizeof(pkv::PartialML);
     w.o_offset = align_up(w.ml_bytes);
-    w.total = w.o_offset + parts * head_dim * sizeof(float);
+    w.prefix_offset = align_up(w.o_offset + parts * head_dim * sizeof(float));
+    w.total = w.prefix_offset;
     return w;
+}
+
+// Balanced decode: W + S*n_kv partial slots of G heads, then the prefix.
+Layout ws_layout_balanced(int num_seqs, int n_q, int n_kv, int head_dim, int waves) {
+    const size_t parts = (static_cast<size_t>(waves) + static_cast<size_t>(num_seqs) * n_kv) * (n_q / n_kv);
+    Layout w;
+    w.ml_bytes = parts * sizeof(pkv::PartialML);
+    w.o_offset = align_up(w.ml_bytes);
+    w.prefix_offset = align_up(w.o_offset + parts * head_dim * sizeof(float));
+    w.total = w.prefix_offset + align_up((static_cast<size_t>(num_seqs) + 1) * sizeof(int));
+    return w;
+}
+
+// Grid size of the balanced pass for the current device (cached for the
+// last shape asked about).
+int balanced_waves(int n_q, int n_kv, int num_seqs) {
+    static thread_local int last_dev = -1, last_g = 0, last_s = 0, last_w = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const int g = n_q / n_kv;
+    if (dev != last_dev || g != last_g || num_seqs != last_s) {
+        last_w = pkv::decode_balanced_waves(n_q, n_kv, num_seqs);
+        last_dev = dev;
+        last_g = g;
+        last_s = num_seqs;
+    }
+    return last_w;
 }
 
 int check_shape(int num_seqs, int max_seq_len, int num_blocks, int n_q, int n_kv, int head_dim,
@@ -85,31 +114,45 @@ int check_shape(int num_seqs, int max_seq_len, int num_blocks, int n_q, int n_kv
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decode,
+int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decode, bool balanced,
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (a.num_rows == 0) return PKV_OK;
     if (!workspace) return PKV_ERR_NULL_POINTER;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
-    const Layout w = ws_layout(a.num_rows, a.n_q, a.head_dim, a.max_splits);
+    const Layout w = balanced ? ws_layout_balanced(a.num_seqs, a.n_q, a.n_kv, a.head_dim, a.waves)
+                              : ws_layout(a.num_rows, a.n_q, a.head_dim, a.max_splits);
     if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
-    a.ws_ml = static_cast<pkv::PartialML*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.o_offset);
+    char* ws = static_cast<char*>(workspace);
+    a.ws_ml = reinterpret_cast<pkv::PartialML*>(ws);
+    a.ws_o = reinterpret_cast<float*>(ws + w.o_offset);
+    a.prefix = balanced ? reinterpret_cast<int*>(ws + w.prefix_offset) : nullptr;
+    if (!balanced) a.waves = 0;
     const bool bf16 = dtype == PKV_BF16;
+    const bool aligned = aligned16(a.q) && aligned16(a.k_cache) && aligned16(a.v_cache);
 
-    const bool fast = decode && bf16 &&
-                      pkv::decode_fast_supported(a.n_q, a.n_kv, a.head_dim, a.block_size, a.split_tokens) &&
-                      aligned16(a.q) && aligned16(a.k_cache) && aligned16(a.v_cache);
     hipError_t e;
-    if (fast) {
-        if (g_prof_before && g_prof_after) hipEventRecord(g_prof_before, stream);
+    const bool timed = g_prof_before && g_prof_after;
+    if (balanced) {
+        if (timed) hipEventRecord(g_prof_before, stream);
+        e = pkv::launch_decode_balanced(a, stream);
+        if (timed) hipEventRecord(g_prof_after, stream);
+    } else if (decode && bf16 && aligned &&
+               pkv::decode_fast_supported(a.n_q, a.n_kv, a.head_dim, a.block_size, a.split_tokens)) {
+        if (timed) hipEventRecord(g_prof_before, stream);
         e = pkv::launch_decode_fast(a, stream);
-        if (g_prof_before && g_prof_after) hipEventRecord(g_prof_after, stream);
+        if (timed) hipEventRecord(g_prof_after, stream);
     } else {
         e = pkv::launch_split_generic(a, bf16, stream);
     }
     if (e != hipSuccess) return PKV_ERR_HIP;
     e = pkv::launch_merge(a, out, lse, bf16, stream);
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+bool balanced_eligible(int dtype, int split_tokens, int num_seqs, int n_q, int n_kv, int head_dim,
+                       int block_size) {
+    return dtype == PKV_BF16 && split_tokens == 0 &&
+           pkv::decode_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs);
 }
 
 }  // namespace
@@ -174,7 +217,14 @@ extern "C" int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_
     int rc = resolve_split(num_q_rows, n_kv, block_size, max_seq_len, split_tokens, &split);
     if (rc != PKV_OK) return rc;
     const int max_splits = (max_seq_len + split - 1) / split;
-    *bytes = ws_layout(num_q_rows, n_q, head_dim, max_splits).total;
+    size_t need = ws_layout(num_q_rows, n_q, head_dim, max_splits).total;
+    if (n_q % n_kv == 0 && balanced_eligible(PKV_BF16, split_tokens, num_q_rows, n_q, n_kv, head_dim, block_size)) {
+        const int waves = balanced_waves(n_q, n_kv, num_q_rows);
+        if (waves < 1) return PKV_ERR_HIP;
+        const size_t b = ws_layout_balanced(num_q_rows, n_q, n_kv, head_dim, waves).total;
+        if (b > need) need = b;
+    }
+    *bytes = need;
     return PKV_OK;
 }
 
@@ -194,7 +244,13 @@ extern "C" int paged_attn_decode(void* out, float* lse, const void* q,
     int split = 0;
     rc = resolve_split(num_seqs, n_kv, block_size, max_seq_len, split_tokens, &split);
     if (rc != PKV_OK) return rc;
+    const bool balanced = balanced_eligible(dtype, split_tokens, num_seqs, n_q, n_kv, head_dim, block_size) &&
+                          aligned16(q) && aligned16(k_cache) && aligned16(v_cache);
     pkv::AttnArgs a{};
+    if (balanced) {
+        a.waves = balanced_waves(n_q, n_kv, num_seqs);
+        if (a.waves < 1) return PKV_ERR_HIP;
+    }
     a.q = q;
     a.q_start = nullptr;
     a.k_cache = k_cache;
@@ -214,7 +270,7 @@ extern "C" int paged_attn_decode(void* out, float* lse, const void* q,
     a.split_tokens = split;
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
-    return run_attention(a, out, lse, dtype, true, workspace, workspace_bytes,
+    return run_attention(a, out, lse, dtype, true, balanced, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -258,6 +314,6 @@ extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int3
     a.split_tokens = split;
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
-    return run_attention(a, out, lse, dtype, false, workspace, workspace_bytes,
+    return run_attention(a, out, lse, dtype, false, false, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }

@@ -1,0 +1,234 @@
+// Balanced decode pass for bf16 K/V, head_dim 128, block_size 16.
+//
+// Decode reads every cached K/V byte once per step (chapter 5 section 2.2),
+// so the kernel is a gathered stream (section 3.2: blocks found through the
+// block table) and its speed is set by how evenly and how continuously the
+// chip's waves keep HBM busy. This pass therefore ignores sequence
+// boundaries when it hands out work:
+//
+//  * all (sequence s, kv head g, block b) tiles of the batch are numbered in
+//    one sequence: s-major, then g, then b (a "segment" is the run of tiles
+//    of one (s, g));
+//  * the grid is W single-wave workgroups, W = what the chip holds at once;
+//    with W' = min(W, T), wave w < W' streams tiles
+//    [floor(w T / W'), floor((w+1) T / W')) of the T tiles - every wave
+//    reads the same number of bytes to within one tile and none is empty
+//    (waves w >= W' have nothing to do);
+//  * a wave keeps the running softmax state of decode_tile.h for the segment
+//    it is in; when it leaves a segment it writes that state as one partial.
+//    The partial of wave w for segment sigma goes to slot w + sigma: both
+//    grow along the tile order, so slots never collide, a segment's partials
+//    fill a contiguous run of slots (no wave between two that touch a
+//    segment can skip it, since no wave is empty), and W + S * n_kv slots
+//    always suffice;
+//  * the next tile's loads are issued before the current tile is computed,
+//    so every wave always has a tile in flight.
+//
+// Per-sequence block counts (ceil(L / 16), 0 for an invalid length) and
+// their prefix sums are built by every wave in LDS from seq_lens; wave 0
+// also stores the prefix for the merge pass. A tile whose table entry is
+// outside the pool is not used and its segment's partial is NaN.
+#include "decode_tile.h"
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+template <int G>
+__global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
+    extern __shared__ int s_mem[];
+    const int S = a.num_seqs;
+    int* P = s_mem;              // [S + 1] prefix sums of per-sequence block counts
+    int* Ls = s_mem + S + 1;     // [S] lengths (0 when invalid)
+    const int lane = threadIdx.x;
+    const int w = blockIdx.x;
+    const int table_tokens = a.table_stride * kTileB;
+
+    int carry = 0;
+    for (int base = 0; base < S; base += kWave) {
+        const int s = base + lane;
+        int nb = 0;
+        if (s < S) {
+            int L = a.seq_lens[s];
+            if (seq_len_ok(L, 1, a.max_seq_len, table_tokens)) nb = (L + kTileB - 1) / kTileB;
+            else L = 0;
+            Ls[s] = L;
+        }
+        int x = nb;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(x, o, kWave);
+            if (lane >= o) x += y;
+        }
+        if (s < S) P[s + 1] = carry + x;
+        carry += __shfl(x, kWave - 1, kWave);
+    }
+    if (lane == 0) P[0] = 0;
+    __syncthreads();
+    if (w == 0)
+        for (int s = lane; s <= S; s += kWave) a.prefix[s] = P[s];
+
+    const int n_kv = a.n_kv;
+    const long long T = static_cast<long long>(n_kv) * P[S];
+    const long long W = T < gridDim.x ? T : static_cast<long long>(gridDim.x);
+    if (w >= W) return;
+    const int t0 = static_cast<int>(static_cast<long long>(w) * T / W);
+    const int t1 = static_cast<int>(static_cast<long long>(w + 1) * T / W);
+    if (t0 >= t1) return;
+    const int n = t1 - t0;
+
+    // Per-lane description of tile c0 + lane: segment, tile index
+    // (block * n_kv + g) and valid tokens (-1: bad table entry).
+    int i_seg = -1, i_tile = 0, i_ntok = 0;
+    auto describe = [&](int c0) {
+        const int t = c0 + lane;
+        i_seg = -1;
+        i_tile = 0;
+        i_ntok = 0;
+        if (t < t1) {
+            int lo = 0, hi = S - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (n_kv * P[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int nb = P[lo + 1] - P[lo];
+            const int rr = t - n_kv * P[lo];
+            const int g = rr / nb;
+            const int bi = rr - g * nb;
+            int blk = a.table[static_cast<size_t>(lo) * a.table_stride + bi];
+            if (blk < 0 || blk >= a.num_blocks) {
+                blk = 0;
+                i_ntok = -1;
+            } else {
+                i_ntok = min(kTileB, Ls[lo] - bi * kTileB);
+            }
+            i_seg = lo * n_kv + g;
+            i_tile = blk * n_kv + g;
+        }
+    };
+
+    const int c = lane & 15;
+    const int r = lane >> 4;
+    const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + lane * 8;
+    const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + lane * 8;
+    const uint16_t* qc = static_cast<const uint16_t*>(a.q) + c * 8;
+    const float sl2 = a.scale_log2;
+
+    DecodeState<G> st;
+    st.reset();
+    u32x4 qv[G];
+    int cur_seg = -1;
+    bool cur_bad = false;
+
+    auto flush = [&]() {
+        st.merge_rows();
+        const size_t p = static_cast<size_t>(w) + cur_seg;
+        if (r == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float4* o = reinterpret_cast<float4*>(a.ws_o + (p * G + h) * kTileD + c * 8);
+                o[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+                o[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+                if (c == 0) a.ws_ml[p * G + h] = cur_bad ? PartialML{NAN, NAN} : PartialML{st.m[h], st.l[h]};
+            }
+        }
+    };
+
+    auto tile_ptr_off = [&](int tile) { return static_cast<size_t>(tile) * kTileElems; };
+
+    describe(t0);
+    u32x4 ka[4], va[4], kb[4], vb[4];
+    {
+        const size_t off = tile_ptr_off(__builtin_amdgcn_readlane(i_tile, 0));
+        load_tile(kc + off, vc + off, ka, va);
+    }
+
+    // One step: tile i is in (kcur, vcur); issue tile i+1 into (knext, vnext),
+    // then compute tile i.
+    auto step = [&](int i, u32x4 (&kcur)[4], u32x4 (&vcur)[4], u32x4 (&knext)[4], u32x4 (&vnext)[4]) {
+        const int li = i & (kWave - 1);
+        const int seg = __builtin_amdgcn_readlane(i_seg, li);
+        const int ntok = __builtin_amdgcn_readlane(i_ntok, li);
+        if (i + 1 < n) {
+            if (li == kWave - 1) describe(t0 + i + 1);
+            const size_t off = tile_ptr_off(__builtin_amdgcn_readlane(i_tile, (i + 1) & (kWave - 1)));
+            load_tile(kc + off, vc + off, knext, vnext);
+        }
+        if (seg != cur_seg) {
+            if (cur_seg >= 0) flush();
+            const int s = seg / n_kv;
+            const int g = seg - s * n_kv;
+            const uint16_t* qs = qc + (static_cast<size_t>(s) * n_kv * G + g * G) * kTileD;
+#pragma unroll
+            for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(qs + h * kTileD);
+            st.reset();
+            cur_seg = seg;
+            cur_bad = false;
+        }
+        if (ntok < 0) cur_bad = true;
+        else st.tile(kcur, vcur, qv, r, ntok, sl2);
+    };
+
+    for (int i = 0; i < n; i += 2) {
+        step(i, ka, va, kb, vb);
+        if (i + 1 < n) step(i + 1, kb, vb, ka, va);
+    }
+    flush();
+}
+
+template <int G>
+hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
+    const size_t lds = sizeof(int) * (2 * static_cast<size_t>(a.num_seqs) + 1);
+    hipLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int G>
+int occupancy(size_t lds) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<G>, kWave, lds) != hipSuccess)
+        return 0;
+    return blocks;
+}
+
+}  // namespace
+
+// Largest batch the balanced pass takes: its per-wave LDS holds two ints per
+// sequence.
+constexpr int kBalancedMaxSeqs = 8192;
+
+bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs) {
+    if (head_dim != kTileD || block_size != kTileB || n_kv < 1 || n_q % n_kv) return false;
+    if (num_seqs < 1 || num_seqs > kBalancedMaxSeqs) return false;
+    const int G = n_q / n_kv;
+    return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+int decode_balanced_waves(int n_q, int n_kv, int num_seqs) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const size_t lds = sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1);
+    int per_cu = 0;
+    switch (n_q / n_kv) {
+        case 1: per_cu = occupancy<1>(lds); break;
+        case 2: per_cu = occupancy<2>(lds); break;
+        case 4: per_cu = occupancy<4>(lds); break;
+        case 8: per_cu = occupancy<8>(lds); break;
+        default: return 0;
+    }
+    if (per_cu < 1) per_cu = 1;
+    return cus * per_cu;
+}
+
+hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream) {
+    switch (a.n_q / a.n_kv) {
+        case 1: return launch_g<1>(a, stream);
+        case 2: return launch_g<2>(a, stream);
+        case 4: return launch_g<4>(a, stream);
+        case 8: return launch_g<8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pkv

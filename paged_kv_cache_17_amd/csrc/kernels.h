@@ -30,8 +30,11 @@ struct AttnArgs {
     int n_q, n_kv, head_dim, block_size;
     int split_tokens, max_splits;
     float scale_log2;            // scale * log2(e)
-    float* ws_o;                 // [rows][n_q][max_splits][head_dim]
-    PartialML* ws_ml;            // [rows][n_q][max_splits]
+    float* ws_o;                 // fixed split: [rows][n_q][max_splits][head_dim]
+                                 // balanced: [waves + S*n_kv][G][head_dim]
+    PartialML* ws_ml;            // same slots as ws_o, without the head_dim axis
+    int waves;                   // balanced decode: grid size W (0 = fixed split)
+    int* prefix;                 // balanced decode: [S+1] block-count prefix sums
 };
 
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
@@ -45,6 +48,12 @@ hipError_t launch_split_generic(const AttnArgs& a, bool bf16, hipStream_t stream
 // Split pass tuned for decode with bf16, head_dim 128, block_size 16.
 bool decode_fast_supported(int n_q, int n_kv, int head_dim, int block_size, int split_tokens);
 hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream);
+
+// Balanced decode pass (bf16, head_dim 128, block_size 16): equal tile
+// ranges per wave across sequence boundaries.
+bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs);
+int decode_balanced_waves(int n_q, int n_kv, int num_seqs);
+hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream);
 
 // Merge pass: combines each row's partial states into out (and lse).
 hipError_t launch_merge(const AttnArgs& a, void* out, float* lse, bool bf16, hipStream_t stream);

@@ -49,7 +49,8 @@ def build_gpu_cache(wl, fill_nan=True, alloc_order=None):
     import paged_kv_cache_17_amd as pkv
     order = wl.alloc_order if alloc_order is None else alloc_order
     c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size, torch_dtype(wl.dtype),
-                         wl.num_seqs, wl.table_stride, alloc_order=order, fill_nan=fill_nan)
+                         wl.num_seqs, wl.table_stride, alloc_order=order, fill_nan=fill_nan,
+                         poison_workspace=fill_nan)
     for s in range(wl.num_seqs):
         c.ensure(s, int(wl.hist_lens[s]))
     c.upload_table()
