@@ -22,7 +22,9 @@
 //    segment can skip it, since no wave is empty), and W + S * n_kv slots
 //    always suffice;
 //  * the next tile's loads are issued before the current tile is computed,
-//    so every wave always has a tile in flight.
+//    so every wave always has a tile in flight;
+//  * with four query heads per kv head the per-tile math is the
+//    reduce-scatter / one-exponential-per-lane form (DecodeStateG4).
 //
 // Per-sequence block counts (ceil(L / 16), 0 for an invalid length) and
 // their prefix sums are built by every wave in LDS from seq_lens; wave 0
@@ -34,12 +36,27 @@
 namespace pkv {
 namespace {
 
+// Dynamic LDS of one workgroup: prefix [S+1], lengths [S], then a 64-float
+// slot (16-byte aligned) for handing weights between lanes.
+__host__ __device__ inline size_t balanced_lds_ints(int num_seqs) {
+    return (2 * static_cast<size_t>(num_seqs) + 1 + 3) / 4 * 4;
+}
+__host__ inline size_t balanced_lds_bytes(int num_seqs) {
+    return sizeof(int) * (balanced_lds_ints(num_seqs) + kWave);
+}
+
+template <int G>
+struct BalancedState { using T = DecodeState<G>; };
+template <>
+struct BalancedState<4> { using T = DecodeStateG4; };
+
 template <int G>
 __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
     extern __shared__ int s_mem[];
     const int S = a.num_seqs;
     int* P = s_mem;              // [S + 1] prefix sums of per-sequence block counts
     int* Ls = s_mem + S + 1;     // [S] lengths (0 when invalid)
+    float* s_p = reinterpret_cast<float*>(s_mem + balanced_lds_ints(S));
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
     const int table_tokens = a.table_stride * kTileB;
@@ -114,14 +131,24 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
     const uint16_t* qc = static_cast<const uint16_t*>(a.q) + c * 8;
     const float sl2 = a.scale_log2;
 
-    DecodeState<G> st;
+    typename BalancedState<G>::T st;
     st.reset();
     u32x4 qv[G];
     int cur_seg = -1;
     bool cur_bad = false;
 
     auto flush = [&]() {
-        st.merge_rows();
+        float fm[G], fl[G];
+        if constexpr (G == 4) {
+            st.finish(lane, fm, fl);
+        } else {
+            st.merge_rows();
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                fm[h] = st.m[h];
+                fl[h] = st.l[h];
+            }
+        }
         const size_t p = static_cast<size_t>(w) + cur_seg;
         if (r == 0) {
 #pragma unroll
@@ -129,7 +156,7 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
                 float4* o = reinterpret_cast<float4*>(a.ws_o + (p * G + h) * kTileD + c * 8);
                 o[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
                 o[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
-                if (c == 0) a.ws_ml[p * G + h] = cur_bad ? PartialML{NAN, NAN} : PartialML{st.m[h], st.l[h]};
+                if (c == 0) a.ws_ml[p * G + h] = cur_bad ? PartialML{NAN, NAN} : PartialML{fm[h], fl[h]};
             }
         }
     };
@@ -165,8 +192,12 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
             cur_seg = seg;
             cur_bad = false;
         }
-        if (ntok < 0) cur_bad = true;
-        else st.tile(kcur, vcur, qv, r, ntok, sl2);
+        if (ntok < 0) {
+            cur_bad = true;
+        } else {
+            if constexpr (G == 4) st.tile(kcur, vcur, qv, lane, ntok, sl2, s_p);
+            else st.tile(kcur, vcur, qv, r, ntok, sl2);
+        }
     };
 
     for (int i = 0; i < n; i += 2) {
@@ -178,8 +209,8 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
 
 template <int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
-    const size_t lds = sizeof(int) * (2 * static_cast<size_t>(a.num_seqs) + 1);
-    hipLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), lds, stream, a);
+    hipLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), balanced_lds_bytes(a.num_seqs),
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -208,7 +239,7 @@ int decode_balanced_waves(int n_q, int n_kv, int num_seqs) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    const size_t lds = sizeof(int) * (2 * static_cast<size_t>(num_seqs) + 1);
+    const size_t lds = balanced_lds_bytes(num_seqs);
     int per_cu = 0;
     switch (n_q / n_kv) {
         case 1: per_cu = occupancy<1>(lds); break;

@@ -16,6 +16,11 @@ template <> struct Piece<8> { using T = uint2; };
 template <> struct Piece<4> { using T = uint32_t; };
 template <> struct Piece<2> { using T = uint16_t; };
 
+// Sequences whose prefix array fits this many entries have it staged in LDS
+// once per workgroup, so the per-thread search for a token's sequence does
+// not chain global loads.
+constexpr int kStagedSeqs = 4096;
+
 template <int UNIT>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     char* __restrict__ kc, char* __restrict__ vc,
@@ -24,6 +29,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start,
     int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs) {
     using P = typename Piece<UNIT>::T;
+    __shared__ int s_start[kStagedSeqs + 1];
+    const bool staged = num_seqs <= kStagedSeqs;
+    if (staged)
+        for (int i = threadIdx.x; i <= num_seqs; i += blockDim.x) s_start[i] = new_start[i];
+    __syncthreads();
     const int units = row_bytes / UNIT;
     const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= static_cast<long long>(total_new) * n_kv * units) return;
@@ -31,8 +41,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const long long th = idx / units;
     const int h = static_cast<int>(th % n_kv);
     const int t = static_cast<int>(th / n_kv);
-    const int s = seq_of_row(new_start, num_seqs, t);
-    const int pos = start_pos[s] + (t - new_start[s]);
+    const int32_t* starts = staged ? s_start : new_start;
+    const int s = seq_of_row(starts, num_seqs, t);
+    const int pos = start_pos[s] + (t - starts[s]);
     if (pos < 0 || pos / bs >= table_stride) return;
     const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
     if (blk < 0 || blk >= num_blocks) return;   // unmapped slot: nothing is written
