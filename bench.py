@@ -42,7 +42,58 @@ def parse():
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--copies", type=int, default=2, help="independent cache copies used in turn")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
+
+
+# Source files of the split kernel; the counter figures in COUNTERS are valid
+# only while their hash matches.
+KERNEL_SOURCES = ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_tile.h",
+                  "paged_kv_cache_17_amd/csrc/device_common.h"]
+COUNTERS = os.path.join(ROOT, "profiles", "decode_split_c2_counters.txt")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size), or None if absent or stale."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            line = line.strip()
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != kernel_source_hash() or kv.get("workload") != config_name:
+        return None
+    fetch = float(kv["fetch_kib_per_launch"]) * float(kv["fetch_scale"])
+    write = float(kv["write_kib_per_launch"]) * float(kv["write_scale"])
+    return (fetch + write) * 1024.0
+
+
+def copy_probe(mib):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5, "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n}), flush=True)
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -74,6 +125,10 @@ def main():
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}); "
               "multi-GPU sharding is described but not run", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     import paged_kv_cache_17_amd as pkv
@@ -161,7 +216,8 @@ def main():
         "step_kv_frac_of_peak": ideal / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {"kernel": "decode split pass", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None, "avg_launch_ms": kern_avg},
+                     "traffic": measured_traffic(CONFIG_NAMES[args.config]), "avg_launch_ms": kern_avg,
+                     "algorithmic_bytes": ideal, "source_sha": kernel_source_hash()},
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
