@@ -31,6 +31,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "decode tokens/s and achieved KV-read HBM GB/s (% of peak), paged attention, 1 GPU"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix-core peak
 
 
 def parse():
@@ -138,28 +139,45 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.load_library()
     wl = config_workload(args.config)
-    if (wl.new_lens != 1).any():
-        raise SystemExit("bench.py times decode steps; this workload has multi-token chunks")
     caches = [build_gpu_cache(wl, fill_nan=False) for _ in range(args.copies)]
     S = wl.num_seqs
+    nd = int(np.argmax(wl.new_lens != 1)) if (wl.new_lens != 1).any() else S   # decode rows come first
+    assert (wl.new_lens[:nd] == 1).all() and (wl.new_lens[nd:] > 1).all()
     q = raw_to_torch(wl.q, wl.dtype)
     kn, vn = wl.packed_new_kv()
     k_new, v_new = raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype)
     start_pos, new_start = i32(wl.hist_lens), i32(wl.q_offsets)
     seq_lens = i32(wl.seq_lens)
-    split = args.split     # 0: the library's balanced partition (bf16, d 128, block 16)
+    qd = wl.q_offsets[nd]                       # first chunk query row
+    q_dec, q_chk = q[:qd], q[qd:]
+    chunk_start = i32(wl.q_offsets[nd:] - qd)
+    max_dec = int(wl.seq_lens[:nd].max()) if nd else 0
+    max_chk = int(wl.seq_lens[nd:].max()) if nd < S else 0
+    max_c = int(wl.new_lens[nd:].max()) if nd < S else 0
+    split = args.split     # 0: the library's balanced partition / matrix-core chunk kernel
     outs = [torch.empty_like(q) for _ in caches]
-    for c in caches:
-        c.workspace(S, wl.n_q, wl.max_seq_len, split)
+    def workspace(rows, max_len):
+        n = pkv.paged_attn_workspace_size(rows, wl.n_q, wl.n_kv, wl.head_dim, wl.block_size, max_len, split)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    ws = [(workspace(nd, max_dec) if nd else None, workspace(len(q_chk), max_chk) if nd < S else None)
+          for _ in caches]
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        c = caches[i % len(caches)]
-        if ev is not None:
-            pkv.pkv_set_profile_events(*ev)
+    def step(i, ev_dec=None, ev_chk=None):
+        j = i % len(caches)
+        c, out = caches[j], outs[j]
         c.append(k_new, v_new, start_pos, new_start, stream=stream)
-        c.decode(q, seq_lens, wl.max_seq_len, wl.scale, out=outs[i % len(caches)], split_tokens=split,
-                 stream=stream)
+        if nd:
+            if ev_dec is not None:
+                pkv.pkv_set_profile_events(*ev_dec)
+            pkv.paged_attn_decode(out[:qd], None, q_dec, c.k_cache, c.v_cache, c.table_dev[:nd], seq_lens[:nd],
+                                  max_dec, wl.scale, ws[j][0], split_tokens=split, stream=stream)
+        if nd < S:
+            pkv.pkv_set_profile_events(*ev_chk) if ev_chk is not None else pkv.pkv_set_profile_events(None, None)
+            pkv.paged_attn_chunk(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, c.table_dev[nd:],
+                                 seq_lens[nd:], max_c, max_chk, wl.scale, ws[j][1], split_tokens=split,
+                                 stream=stream)
+        pkv.pkv_set_profile_events(None, None)
 
     for i in range(args.warmup):
         step(i)
@@ -175,26 +193,33 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
 
-    # Timed region 2: the same steps with an event pair around every launch
-    # of the split kernel (recorded by the library on the launch stream) ->
-    # that kernel's average duration for the roofline. Kept apart because
-    # each recorded event adds a few microseconds between launches.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for b, a in evs:      # torch creates events on first record; the library re-records them
-        b.record(stream)
-        a.record(stream)
+    # Timed region 2: the same steps with an event pair recorded by the
+    # library around the decode split pass and around the chunk kernel ->
+    # their average durations for the roofline. Kept apart because each
+    # recorded event adds a few microseconds between launches.
+    def pairs():
+        ps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for b, a in ps:   # torch creates events on first record; the library re-records them
+            b.record(stream)
+            a.record(stream)
+        return ps
+    ev_dec = pairs() if nd else [None] * args.steps
+    ev_chk = pairs() if nd < S else [None] * args.steps
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, ev_dec[i], ev_chk[i])
     torch.cuda.synchronize()
-    pkv.pkv_set_profile_events(None, None)
-    kern_ms = [b.elapsed_time(a) for b, a in evs]
     ms_step = total_ms / args.steps
-    kern_avg = float(np.mean(kern_ms))
-    ideal = wl.ideal_kv_bytes()          # 2 (K,V) x n_kv x d x 2 B x sum of context lengths
-    achieved = ideal / (kern_avg * 1e-3) / 1e9
     tokens = int(wl.new_lens.sum())
+
+    # Algorithmic work: decode rows read every cached K/V byte once
+    # (2 x n_kv x d x 2 B per key); chunk rows do 4 x n_q x d FLOPs per
+    # allowed (query, key) pair (scores and weighted sum).
+    dec_bytes = int(wl.seq_lens[:nd].sum()) * wl.n_kv * wl.head_dim * 2 * 2
+    pairs_allowed = sum(int(C) * int(P) + int(C) * (int(C) + 1) // 2
+                        for P, C in zip(wl.hist_lens[nd:], wl.new_lens[nd:]))
+    chk_flops = 4 * wl.n_q * wl.head_dim * pairs_allowed
     line = {
         "metric": METRIC,
         "value": tokens * args.steps / (total_ms * 1e-3),
@@ -208,17 +233,30 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config], "num_seqs": S, "n_q": wl.n_q, "n_kv": wl.n_kv,
-                   "head_dim": wl.head_dim, "block_size": wl.block_size, "context_tokens": int(wl.seq_lens.sum()),
-                   "kv_bytes": ideal, "cache_copies": len(caches),
+        "config": {"workload": CONFIG_NAMES[args.config], "num_seqs": S, "decode_seqs": nd, "chunk_seqs": S - nd,
+                   "n_q": wl.n_q, "n_kv": wl.n_kv, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "context_tokens": int(wl.seq_lens.sum()), "kv_bytes": wl.ideal_kv_bytes(),
+                   "cache_copies": len(caches),
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
-        "step_kv_gbps": ideal / (ms_step * 1e-3) / 1e9,
-        "step_kv_frac_of_peak": ideal / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "decode split pass", "bound": "hbm", "achieved": achieved,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(CONFIG_NAMES[args.config]), "avg_launch_ms": kern_avg,
-                     "algorithmic_bytes": ideal, "source_sha": kernel_source_hash()},
     }
+    if nd:
+        kern_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_dec]))
+        achieved = dec_bytes / (kern_avg * 1e-3) / 1e9
+        line["step_kv_gbps"] = wl.ideal_kv_bytes() / (ms_step * 1e-3) / 1e9
+        line["step_kv_frac_of_peak"] = line["step_kv_gbps"] / PEAK_HBM_GBPS
+        line["roofline"] = {"kernel": "decode split pass", "bound": "hbm", "achieved": achieved,
+                            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                            "traffic": measured_traffic(CONFIG_NAMES[args.config]), "avg_launch_ms": kern_avg,
+                            "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash()}
+    if nd < S:
+        chk_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_chk]))
+        tflops = chk_flops / (chk_avg * 1e-3) / 1e12
+        line["chunk_roofline"] = {"kernel": "chunk attention (matrix cores)", "bound": "mfma",
+                                  "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None, "avg_launch_ms": chk_avg,
+                                  "algorithmic_flops": chk_flops}
+        if not nd:
+            line["roofline"] = line.pop("chunk_roofline")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

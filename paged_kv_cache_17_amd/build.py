@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["kvpool.cpp", "api.cpp", "kv_append.hip", "attn_generic.hip", "attn_merge.hip",
-           "decode_bf16.hip", "decode_balanced.hip"]
+           "decode_bf16.hip", "decode_balanced.hip",
+           "chunk_mfma.hip"]
 
 
 def hipcc() -> str:

@@ -294,6 +294,9 @@ extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int3
     int split = 0;
     rc = resolve_split(total_q, n_kv, block_size, max_seq_len, split_tokens, &split);
     if (rc != PKV_OK) return rc;
+    const bool mfma = dtype == PKV_BF16 && split_tokens == 0 &&
+                      pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size) &&
+                      aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out);
     pkv::AttnArgs a{};
     a.q = q;
     a.q_start = q_start;
@@ -314,6 +317,13 @@ extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int3
     a.split_tokens = split;
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
+    if (mfma) {
+        const bool timed = g_prof_before && g_prof_after;
+        if (timed) hipEventRecord(g_prof_before, static_cast<hipStream_t>(stream));
+        const hipError_t e = pkv::launch_chunk_mfma(a, out, lse, static_cast<hipStream_t>(stream));
+        if (timed) hipEventRecord(g_prof_after, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    }
     return run_attention(a, out, lse, dtype, false, false, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }

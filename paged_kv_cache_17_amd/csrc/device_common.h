@@ -15,11 +15,15 @@ constexpr float kLog2e = 1.44269504088896340736f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Round to bf16 (nearest even) with the hardware pack-convert instruction.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // keep NaN a NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                      // round to nearest even
-    return static_cast<uint16_t>(u >> 16);
+    return static_cast<uint16_t>(pack2_bf16(f, 0.0f) & 0xffffu);
 }
 
 template <typename T> struct Elem;

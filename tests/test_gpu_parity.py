@@ -142,6 +142,19 @@ def test_chunk_mix_and_c1_equals_decode():
     check_rows(out_f64(oc, BF16), out_f64(od, BF16), BF16, "chunk C=1 vs decode")
 
 
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 8), (64, 8)])
+def test_chunk_matrix_core_path_shapes(n_q, n_kv):
+    """Chunks whose lengths straddle the 32/64/128-row query tiles and whose
+    priors straddle block (16) and key-tile (64) boundaries."""
+    hist = [0, 1, 15, 16, 17, 63, 64, 65, 700, 0, 129]
+    new = [1, 5, 31, 32, 33, 100, 128, 129, 300, 64, 2]
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist,
+                        new_lens=new, seed=13)
+    say("chunk mfma shapes", n_q, n_kv)
+    _, _, err, lerr = _full_check(wl, "chunk", 0, check_pool=False)
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+
+
 def test_lab_prompt_as_chunks_5_then_4():
     """The lab's 9-token prompt run as chunks [5, 4] equals one 9-token chunk."""
     one = build_workload(n_q=2, n_kv=2, head_dim=4, block_size=4, dtype=F32, hist_lens=[0], new_lens=[9],
