@@ -146,24 +146,46 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const size_t gstride = static_cast<size_t>(g) * kBS * kD;
     u32x4 stage[8];
 
-    // K: key rows st/16 + 8m (m = 0..7), dims 8*(st%16)..+7.
-    // V: keys 8*(st/16) + m (m = 0..7), dims 8*(st%16)..+7.
+    // K threads: key rows st/16 + 8m (m = 0..7), dims 8*(st%16)..+7 (a
+    // wave's load covers whole 256-byte key rows).
+    // V threads: keys 8*(st%8) + m (m = 0..7), dims 8*(st/8)..+7, so the 8
+    // lanes that write LDS together hold different key groups of one row
+    // of V^T (different banks).
+    const int k_row0 = st >> 4, k_dim = 8 * (st & 15);
+    const int v_key0 = 8 * (st & 7), v_dim = 8 * (st >> 3);
+    const size_t blk_elems = static_cast<size_t>(n_kv) * kBS * kD;
+    auto block_ptr = [&](int bi) {
+        const int blk = bi < kTblCache ? s_tbl[bi] : trow[bi];
+        return (stage_k ? kc : vc) + static_cast<size_t>(blk) * blk_elems + gstride;
+    };
     auto load_tile = [&](int kt) {
         const int kbase = kt * kKeys;
+        if (stage_k) {
+            // rows k_row0 + 8m: m = 0,1 in block 0 of the tile, 2,3 in block 1, ...
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int key = stage_k ? kbase + (st >> 4) + 8 * m : kbase + 8 * (st >> 4) + m;
-            u32x4 v = {0, 0, 0, 0};
-            if (key <= kmax) {
-                const int bi = key / kBS;
-                const int blk = bi < kTblCache ? s_tbl[bi] : trow[bi];
-                const uint16_t* src = (stage_k ? kc : vc) +
-                                      (static_cast<size_t>(blk) * n_kv * kBS * kD + gstride) +
-                                      (key % kBS) * kD + 8 * (st & 15);
-                v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-                if (!stage_k && key >= L) v = u32x4{0, 0, 0, 0};
+            for (int b = 0; b < 4; ++b) {
+                const int key0 = kbase + 16 * b + k_row0;
+                const uint16_t* base = key0 <= kmax ? block_ptr(key0 / kBS) + k_dim : nullptr;
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int key = key0 + 8 * m2;
+                    stage[2 * b + m2] = key <= kmax
+                        ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (key % kBS) * kD))
+                        : u32x4{0, 0, 0, 0};
+                }
             }
-            stage[m] = v;
+        } else {
+            // keys v_key0 .. v_key0 + 7 lie in one block
+            const int key0 = kbase + v_key0;
+            const uint16_t* base = key0 <= kmax ? block_ptr(key0 / kBS) + v_dim : nullptr;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int key = key0 + m;
+                u32x4 v = {0, 0, 0, 0};
+                if (key <= kmax && key < L)
+                    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (key % kBS) * kD));
+                stage[m] = v;
+            }
         }
     };
     auto store_tile = [&](int buf) {
@@ -179,9 +201,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
                 *reinterpret_cast<u32x4*>(s_k + row * kKPitch + 8 * (st & 15)) = stage[m];
             }
         } else {
-            // 8 x 8 transpose: column e (dim 8*(st%16) + e) over keys m = 0..7.
-            const int kb = 8 * (st >> 4);
-            const int db = 8 * (st & 15);
+            // 8 x 8 transpose: column e (dim v_dim + e) over keys v_key0 + m.
+            const int kb = v_key0;
+            const int db = v_dim;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int w = e >> 1;
