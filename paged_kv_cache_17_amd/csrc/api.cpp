@@ -295,7 +295,7 @@ extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int3
     rc = resolve_split(total_q, n_kv, block_size, max_seq_len, split_tokens, &split);
     if (rc != PKV_OK) return rc;
     const bool mfma = dtype == PKV_BF16 && split_tokens == 0 &&
-                      pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size) &&
+                      pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size, max_seq_len) &&
                       aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out);
     pkv::AttnArgs a{};
     a.q = q;

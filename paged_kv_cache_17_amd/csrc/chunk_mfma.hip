@@ -16,20 +16,28 @@
 // 3.1). Query tiles are dispatched longest-first.
 //
 // Per 64-key tile (4 cache blocks gathered through the table):
-//  * K is staged row-major in LDS, V transposed (an 8 x 8 bf16 transpose in
-//    registers per thread), both padded against bank conflicts and double
-//    buffered; the next tile's global loads are in flight while the current
-//    tile is computed;
-//  * S^T = K Q^T: A = K rows read in a permuted order pi, B = the wave's
-//    queries (kept in registers). With pi(8i+4h+j) = 16(i/2)+8h+4(i%2)+j the
-//    accumulator registers of S^T already hold, for each 16-key step, the
-//    8 consecutive keys the next product needs in its B operand;
+//  * each wave copies one cache block of K and of V straight from global
+//    memory into LDS (global_load_lds, 16 bytes per lane, no registers);
+//    the copy of tile kt + 1 runs while tile kt is computed, into the other
+//    of two buffers. LDS rows are 256 bytes, unpadded; the 16-byte granule
+//    c of row r is stored at position c ^ sw(r), which makes both read
+//    patterns below free of bank conflicts;
+//  * S^T = K Q^T: A = K rows, B = the wave's queries (kept in registers).
+//    LDS row n of a 32-key subtile holds key pi(n) = n with bits 2 and 3
+//    swapped; then the accumulator registers of S^T already hold, for each
+//    16-key step, the 8 consecutive keys the next product needs in its B
+//    operand;
 //  * each lane owns whole query rows (one column of S^T), so the online
 //    softmax is lane-local plus one exchange with the other half-wave; the
 //    reference max moves only when a score exceeds it by 2^8 (exact, rare
-//    rescaling of the accumulators);
-//  * O^T += V^T P^T: A = V^T from LDS, B = P^T packed to bf16 from registers.
-// Keys past the sequence end get weight 0 and their V is zeroed in LDS.
+//    rescaling of the accumulators). Only tiles that reach past a row's
+//    position evaluate the causal mask;
+//  * O^T += V^T P^T: A = V^T read from the row-major V tile with the
+//    transposing LDS load ds_read_b64_tr_b16 (in each 16-lane group, lane j
+//    element e comes from lane 4e + j/4, element j%4), B = P^T packed to
+//    bf16 from registers.
+// Keys past the last one a tile needs are loaded as copies of that key
+// (finite cache data) and get weight 0.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -41,33 +49,39 @@ constexpr int kBS = 16;
 constexpr int kKeys = 64;                 // keys per staged tile
 constexpr int kRows = 128;                // (head, query) rows per workgroup
 constexpr int kThreads = 256;
-constexpr int kKPitch = kD + 8;           // bf16 elements per K row in LDS
-constexpr int kVPitch = kKeys + 8;        // bf16 elements per V^T row in LDS
+constexpr int kRowBytes = kD * 2;         // one K or V row in LDS (unpadded)
 constexpr float kLazy = 8.0f;
 constexpr int kXcds = 8;                  // dispatch round-robin width
-constexpr int kTblCache = 2048;           // table entries cached in LDS (32768 keys)
+constexpr int kTblCache = 2048;           // table entries held in LDS (32768 keys)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack2_bf16(lo, hi); }
+// Granule swizzle of LDS row r (granule = 16 bytes = 8 elements).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// Row of S^T (key index within a 32-key subtile) held by accumulator
-// register r of a lane in half h, given the permuted K-row order.
-__device__ __forceinline__ int key_of_reg(int r, int h) {
-    const int i = r >> 2, j = r & 3;
-    return 16 * (i >> 1) + 8 * h + 4 * (i & 1) + j;
+// Offset (within a 32-key subtile, before adding 8h) of the key held by
+// accumulator register r of S^T.
+__device__ __forceinline__ constexpr int key_of_reg(int r) {
+    return 16 * ((r >> 2) >> 1) + 4 * ((r >> 2) & 1) + (r & 3);
 }
 
 template <int G>
 __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uint16_t* __restrict__ out,
                                                                  float* __restrict__ lse) {
     constexpr int QT = kRows / G;                 // queries per workgroup
-    __shared__ __align__(16) uint16_t s_kbuf[2][kKeys * kKPitch];
-    __shared__ __align__(16) uint16_t s_vbuf[2][kD * kVPitch];
+    __shared__ __align__(16) uint16_t s_k0[kKeys * kD];
+    __shared__ __align__(16) uint16_t s_k1[kKeys * kD];
+    __shared__ __align__(16) uint16_t s_v0[kKeys * kD];
+    __shared__ __align__(16) uint16_t s_v1[kKeys * kD];
     __shared__ int s_bad;
     __shared__ int s_tbl[kTblCache];
 
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int tile_rev = k_on_xcd % nq_max;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;                      // column of S^T / O^T = this lane's row
     const int h = lane >> 5;                      // half-wave
 
@@ -115,14 +129,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int32_t* trow = a.table + static_cast<size_t>(s) * a.table_stride;
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    if (ok)
+    if (ok && nblk <= kTblCache)
         for (int b = tid; b < nblk; b += kThreads) {
             const int id = trow[b];
             if (id < 0 || id >= a.num_blocks) s_bad = 1;
-            if (b < kTblCache) s_tbl[b] = id;
+            s_tbl[b] = id;
         }
     __syncthreads();
-    if (!ok || s_bad) {
+    if (!ok || nblk > kTblCache || s_bad) {
         if (active) {
             for (int e = h; e < kD; e += 2) Elem<uint16_t>::store(out + orow * kD + e, NAN);
             if (lse && h == 0) lse[orow] = NAN;
@@ -138,87 +152,55 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int t = 0; t < 8; ++t) qv[t] = active ? qp[2 * t] : u32x4{0, 0, 0, 0};
     }
 
-    // Staging roles: threads 0..127 copy K rows, 128..255 transpose V blocks.
-    const bool stage_k = tid < 128;
-    const int st = tid & 127;
-    const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-    const size_t gstride = static_cast<size_t>(g) * kBS * kD;
-    u32x4 stage[8];
+    // Copy of one tile: wave w fetches cache block 4kt + w (keys 16w..16w+15
+    // of the tile) into LDS rows 16w..16w+15, four rows per instruction.
+    // Lane l writes granule l%16 of row 16w + 4i + l/16.
+    const char* kc = static_cast<const char*>(a.k_cache);
+    const char* vc = static_cast<const char*>(a.v_cache);
+    const size_t blk_bytes = static_cast<size_t>(n_kv) * kBS * kRowBytes;
+    const size_t head_bytes = static_cast<size_t>(g) * kBS * kRowBytes;
+    const int lr = lane >> 4;
+    const int lc = lane & 15;
+    const int last_blk = kmax / kBS;
+    auto issue_tile = [&](int kt, uint16_t* sk, uint16_t* sv) {
+        const int bi = 4 * kt + wave;
+        const int bsrc = min(bi, last_blk);
+        // rows past key kmax are replaced by a row <= kmax of block bsrc
+        const int cap = bi > last_blk ? (kmax & (kBS - 1)) : min(kmax - kBS * bi, kBS - 1);
+        const int id = __builtin_amdgcn_readfirstlane(s_tbl[bsrc]);
+        const char* kb = kc + static_cast<size_t>(id) * blk_bytes + head_bytes;
+        const char* vb = vc + static_cast<size_t>(id) * blk_bytes + head_bytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gran = lc ^ ((lr << 1) | (i & 1));          // logical granule of this lane's slot
+            const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), cap);  // key pi(4i + lr)
+            const int rv = min(4 * i + lr, cap);
+            __builtin_amdgcn_global_load_lds(kb + rk * kRowBytes + gran * 16,
+                                             (lds_void*)(sk + (16 * wave + 4 * i) * kD), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + rv * kRowBytes + gran * 16,
+                                             (lds_void*)(sv + (16 * wave + 4 * i) * kD), 16, 0, 0);
+        }
+    };
 
-    // K threads: key rows st/16 + 8m (m = 0..7), dims 8*(st%16)..+7 (a
-    // wave's load covers whole 256-byte key rows).
-    // V threads: keys 8*(st%8) + m (m = 0..7), dims 8*(st/8)..+7, so the 8
-    // lanes that write LDS together hold different key groups of one row
-    // of V^T (different banks).
-    const int k_row0 = st >> 4, k_dim = 8 * (st & 15);
-    const int v_key0 = 8 * (st & 7), v_dim = 8 * (st >> 3);
-    const size_t blk_elems = static_cast<size_t>(n_kv) * kBS * kD;
-    auto block_ptr = [&](int bi) {
-        const int blk = bi < kTblCache ? s_tbl[bi] : trow[bi];
-        return (stage_k ? kc : vc) + static_cast<size_t>(blk) * blk_elems + gstride;
-    };
-    auto load_tile = [&](int kt) {
-        const int kbase = kt * kKeys;
-        if (stage_k) {
-            // rows k_row0 + 8m: m = 0,1 in block 0 of the tile, 2,3 in block 1, ...
+    // K read offsets (bytes, within a subtile): row n, logical granule 2t + h.
+    int koff[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int key0 = kbase + 16 * b + k_row0;
-                const uint16_t* base = key0 <= kmax ? block_ptr(key0 / kBS) + k_dim : nullptr;
+    for (int t = 0; t < 4; ++t) koff[t] = n * kRowBytes + (((2 * t + h) ^ swz(n)) * 16);
+    // V^T read offsets: lane (group gq = lane/16, j = lane%16) reads row
+    // 8(gq/2) + 4a + j/4 of a 16-key step, elements 4(j%4)..+3 of the 16 dims
+    // 16(gq%2).. of a 32-dim tile; the swizzle depends on the tile's parity.
+    int voff[2][2];
+    {
+        const int gq = lane >> 4, j = lane & 15;
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) {
-                    const int key = key0 + 8 * m2;
-                    stage[2 * b + m2] = key <= kmax
-                        ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (key % kBS) * kD))
-                        : u32x4{0, 0, 0, 0};
-                }
+        for (int dp = 0; dp < 2; ++dp)
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa) {
+                const int r = 8 * (gq >> 1) + 4 * aa + (j >> 2);
+                const int gran = 4 * dp + 2 * (gq & 1) + ((j >> 1) & 1);
+                voff[dp][aa] = r * kRowBytes + ((gran ^ swz(r)) * 16) + (j & 1) * 8;
             }
-        } else {
-            // keys v_key0 .. v_key0 + 7 lie in one block
-            const int key0 = kbase + v_key0;
-            const uint16_t* base = key0 <= kmax ? block_ptr(key0 / kBS) + v_dim : nullptr;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int key = key0 + m;
-                u32x4 v = {0, 0, 0, 0};
-                if (key <= kmax && key < L)
-                    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (key % kBS) * kD));
-                stage[m] = v;
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t* s_k = s_kbuf[buf];
-        uint16_t* s_vt = s_vbuf[buf];
-        if (stage_k) {
-            // key k goes to row k with bits 2 and 3 swapped: the product reads
-            // key pi(n) for lane n, so lane n then reads row n (no bank conflicts)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int k = (st >> 4) + 8 * m;
-                const int row = (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-                *reinterpret_cast<u32x4*>(s_k + row * kKPitch + 8 * (st & 15)) = stage[m];
-            }
-        } else {
-            // 8 x 8 transpose: column e (dim v_dim + e) over keys v_key0 + m.
-            const int kb = v_key0;
-            const int db = v_dim;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1;
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 col;
-#pragma unroll
-                for (int d2 = 0; d2 < 4; ++d2) {
-                    const uint32_t lo = stage[2 * d2][w];
-                    const uint32_t hi = stage[2 * d2 + 1][w];
-                    col[d2] = __builtin_amdgcn_perm(hi, lo, sel);
-                }
-                *reinterpret_cast<u32x4*>(s_vt + (db + e) * kVPitch + kb) = col;
-            }
-        }
-    };
+    }
 
     f32x16 o[4];                                  // O^T tiles: dims 32dt + C-layout rows
 #pragma unroll
@@ -227,48 +209,37 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const float sl2 = a.scale_log2;
     const int ntiles = kmax / kKeys + 1;
     const int pmin = P + q0;                      // smallest position in the tile
+    const int kt_diag = (pmin + 1) / kKeys;       // tiles before this one need no mask
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-    // Double-buffered tiles: tile kt is computed from buffer kt % 2 while
-    // the loads of tile kt + 1 are in flight; those are written to the
-    // other buffer after the compute, and one barrier per tile separates a
-    // buffer's readers from its next writers.
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const uint16_t* s_k = s_kbuf[kt & 1];
-        const uint16_t* s_vt = s_vbuf[kt & 1];
-        if (kt + 1 < ntiles) load_tile(kt + 1);
+    auto step = [&](int kt, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv, bool mask) {
+        if (kt + 1 < ntiles) issue_tile(kt + 1, nk, nv);
+        const char* skb = reinterpret_cast<const char*>(sk);
+        const char* svb = reinterpret_cast<const char*>(sv);
 
         // S^T for the two 32-key subtiles.
         f32x16 sacc[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             sacc[u] = f32x16{};
-            // A row m = n is key pi(n), stored at LDS row n of the subtile
-            const uint16_t* kp = s_k + (32 * u + n) * kKPitch + 8 * h;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const u32x4 av = *reinterpret_cast<const u32x4*>(kp + 16 * t);
+                const u32x4 av = *reinterpret_cast<const u32x4*>(skb + 32 * u * kRowBytes + koff[t & 3] + (t >> 2) * 128);
                 sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(qv[t]), sacc[u], 0, 0, 0);
             }
         }
 
-        // Mask, max, lazy rescale, weights.
-        const int kbase = kt * kKeys;
-        const bool need_mask = kbase + kKeys - 1 > pmin || !active;
-        float sv[2][16];
+        // Causal mask (diagonal tiles only), max, lazy rescale, weights.
+        float sv2[2][16];
         float mx = -INFINITY;
+        const int lim = pos - kt * kKeys - 8 * h;   // key offsets <= lim are allowed
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float x = sacc[u][r];
-                if (need_mask) {
-                    const int key = kbase + 32 * u + key_of_reg(r, h);
-                    x = (active && key <= pos) ? x : -INFINITY;
-                }
-                sv[u][r] = x;
+                if (mask) x = (32 * u + key_of_reg(r) <= lim) ? x : -INFINITY;
+                sv2[u][r] = x;
                 mx = fmaxf(mx, x);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
@@ -289,15 +260,16 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                float p[8];
+                uint32_t w[4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * half + e;   // registers 8*half .. 8*half+7: i = 2*half, 2*half+1
-                    p[e] = __builtin_amdgcn_exp2f(fmaf(sv[u][r], sl2, -mref_safe));
-                    lsum += p[e];
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 8 * half + 2 * e;
+                    w[e] = pack2_bf16(__builtin_amdgcn_exp2f(fmaf(sv2[u][r], sl2, -mref_safe)),
+                                      __builtin_amdgcn_exp2f(fmaf(sv2[u][r + 1], sl2, -mref_safe)));
+                    // the normaliser sums the same rounded weights the product uses
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
                 }
-                pb[2 * u + half] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
-                                         pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+                pb[2 * u + half] = u32x4{w[0], w[1], w[2], w[3]};
             }
 
         // O^T += V^T P^T over the tile's four 16-key steps.
@@ -305,11 +277,29 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const u32x4 av = *reinterpret_cast<const u32x4*>(s_vt + (32 * dt + n) * kVPitch + 16 * t + 8 * h);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pb[t]), o[dt], 0, 0, 0);
+                const char* base = svb + t * 16 * kRowBytes + (dt >> 1) * 128;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + voff[dt & 1][0]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + voff[dt & 1][1]));
+                const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                as_bf16x8(pb[t]), o[dt], 0, 0, 0);
             }
-        if (kt + 1 < ntiles) store_tile((kt + 1) & 1);
+        // the next tile's copies have landed (the barrier waits for them) and
+        // every wave is done reading this tile's buffers
         __syncthreads();
+    };
+
+    issue_tile(0, s_k0, s_v0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const bool mask = kt >= kt_diag;
+        if (kt & 1) {
+            if (mask) step(kt, s_k1, s_v1, s_k0, s_v0, true);
+            else step(kt, s_k1, s_v1, s_k0, s_v0, false);
+        } else {
+            if (mask) step(kt, s_k0, s_v0, s_k1, s_v1, true);
+            else step(kt, s_k0, s_v0, s_k1, s_v1, false);
+        }
     }
 
     // Epilogue: combine the half-waves' sums, normalise, store.
@@ -323,8 +313,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int i = 0; i < 4; ++i) {
             const int d0 = 32 * dt + 8 * i + 4 * h;
             uint2 w;
-            w.x = pack_bf16(o[dt][4 * i + 0] * inv, o[dt][4 * i + 1] * inv);
-            w.y = pack_bf16(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
+            w.x = pack2_bf16(o[dt][4 * i + 0] * inv, o[dt][4 * i + 1] * inv);
+            w.y = pack2_bf16(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
             *reinterpret_cast<uint2*>(op + d0) = w;
         }
     if (lse && h == 0) lse[orow] = kLn2 * (mref + log2f(ltot));
@@ -343,8 +333,9 @@ hipError_t launch_g(const AttnArgs& a, void* out, float* lse, hipStream_t stream
 
 }  // namespace
 
-bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size) {
+bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size, int max_seq_len) {
     if (head_dim != kD || block_size != kBS || n_kv < 1 || n_q % n_kv) return false;
+    if (max_seq_len > kTblCache * kBS) return false;
     const int G = n_q / n_kv;
     return G == 1 || G == 2 || G == 4 || G == 8;
 }

@@ -55,9 +55,9 @@ bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, 
 int decode_balanced_waves(int n_q, int n_kv, int num_seqs);
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream);
 
-// Chunk attention on MFMA (bf16, head_dim 128, block_size 16): writes out
-// and lse directly, no workspace.
-bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size);
+// Chunk attention on MFMA (bf16, head_dim 128, block_size 16, sequences of
+// at most 32768 keys): writes out and lse directly, no workspace.
+bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size, int max_seq_len);
 hipError_t launch_chunk_mfma(const AttnArgs& a, void* out, float* lse, hipStream_t stream);
 
 // Merge pass: combines each row's partial states into out (and lse).
