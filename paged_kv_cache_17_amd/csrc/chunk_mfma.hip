@@ -18,8 +18,8 @@
 // Per 64-key tile (4 cache blocks gathered through the table):
 //  * each wave copies one cache block of K and of V straight from global
 //    memory into LDS (global_load_lds, 16 bytes per lane, no registers);
-//    the copy of tile kt + 1 runs while tile kt is computed, into the other
-//    of two buffers. LDS rows are 256 bytes, unpadded; the 16-byte granule
+//    the copy of tile kt + 1 runs while the weights and the second product
+//    of tile kt are computed, into the other of two buffers. LDS rows are 256 bytes, unpadded; the 16-byte granule
 //    c of row r is stored at position c ^ sw(r), which makes both read
 //    patterns below free of bank conflicts;
 //  * S^T = K Q^T: A = K rows, B = the wave's queries (kept in registers).
@@ -61,12 +61,28 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Granule swizzle of LDS row r (granule = 16 bytes = 8 elements).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Where one wave copies a tile's cache block from: K and V base of the
+// block (this kv head) and the largest row it may read.
+struct TileSrc {
+    const char* kb;
+    const char* vb;
+    int cap;
+};
+
+// Granule swizzle of LDS row r (granule = 16 bytes = 8 elements). Bits of
+// the result: r2, r0, r1, r0^r1^r3. Reads of 8 or 16 consecutive rows at one
+// granule, and of 4 consecutive rows at 2 or 4 adjacent granules, then hit
+// distinct banks whether a read phase covers 128 or 256 bytes.
+__device__ __forceinline__ int swz(int r) {
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    return r2 | (r0 << 1) | (r1 << 2) | ((r0 ^ r1 ^ r3) << 3);
+}
 
 // Offset (within a 32-key subtile, before adding 8h) of the key held by
 // accumulator register r of S^T.
@@ -162,43 +178,52 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int lr = lane >> 4;
     const int lc = lane & 15;
     const int last_blk = kmax / kBS;
-    auto issue_tile = [&](int kt, uint16_t* sk, uint16_t* sv) {
+    // Source of the copies for tile kt: per-wave block base (K, V) and the
+    // row bound. Rows past key kmax are replaced by a row <= kmax of block bsrc.
+    auto tile_src = [&](int kt) {
         const int bi = 4 * kt + wave;
         const int bsrc = min(bi, last_blk);
-        // rows past key kmax are replaced by a row <= kmax of block bsrc
         const int cap = bi > last_blk ? (kmax & (kBS - 1)) : min(kmax - kBS * bi, kBS - 1);
         const int id = __builtin_amdgcn_readfirstlane(s_tbl[bsrc]);
-        const char* kb = kc + static_cast<size_t>(id) * blk_bytes + head_bytes;
-        const char* vb = vc + static_cast<size_t>(id) * blk_bytes + head_bytes;
+        const size_t off = static_cast<size_t>(id) * blk_bytes + head_bytes;
+        return TileSrc{kc + off, vc + off, cap};
+    };
+    auto issue_k = [&](const TileSrc& src, uint16_t* sk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int gran = lc ^ ((lr << 1) | (i & 1));          // logical granule of this lane's slot
-            const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), cap);  // key pi(4i + lr)
-            const int rv = min(4 * i + lr, cap);
-            __builtin_amdgcn_global_load_lds(kb + rk * kRowBytes + gran * 16,
+            const int gran = lc ^ swz(4 * i + lr);                 // logical granule of this lane's slot
+            const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), src.cap);  // key pi(4i + lr)
+            __builtin_amdgcn_global_load_lds(src.kb + rk * kRowBytes + gran * 16,
                                              (lds_void*)(sk + (16 * wave + 4 * i) * kD), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vb + rv * kRowBytes + gran * 16,
+        }
+    };
+    auto issue_v = [&](const TileSrc& src, uint16_t* sv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gran = lc ^ swz(4 * i + lr);
+            const int rv = min(4 * i + lr, src.cap);
+            __builtin_amdgcn_global_load_lds(src.vb + rv * kRowBytes + gran * 16,
                                              (lds_void*)(sv + (16 * wave + 4 * i) * kD), 16, 0, 0);
         }
     };
 
     // K read offsets (bytes, within a subtile): row n, logical granule 2t + h.
-    int koff[4];
+    int koff[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) koff[t] = n * kRowBytes + (((2 * t + h) ^ swz(n)) * 16);
-    // V^T read offsets: lane (group gq = lane/16, j = lane%16) reads row
-    // 8(gq/2) + 4a + j/4 of a 16-key step, elements 4(j%4)..+3 of the 16 dims
-    // 16(gq%2).. of a 32-dim tile; the swizzle depends on the tile's parity.
-    int voff[2][2];
+    for (int t = 0; t < 8; ++t) koff[t] = n * kRowBytes + (((2 * t + h) ^ swz(n)) * 16);
+    // V^T read offsets (within a 16-key step): lane (group gq = lane/16,
+    // j = lane%16) reads row 8(gq/2) + 4a + j/4, elements 4(j%4)..+3 of the
+    // 16 dims 32dt + 16(gq%2)...
+    int voff[4][2];
     {
         const int gq = lane >> 4, j = lane & 15;
 #pragma unroll
-        for (int dp = 0; dp < 2; ++dp)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int aa = 0; aa < 2; ++aa) {
                 const int r = 8 * (gq >> 1) + 4 * aa + (j >> 2);
-                const int gran = 4 * dp + 2 * (gq & 1) + ((j >> 1) & 1);
-                voff[dp][aa] = r * kRowBytes + ((gran ^ swz(r)) * 16) + (j & 1) * 8;
+                const int gran = 4 * dt + 2 * (gq & 1) + ((j >> 1) & 1);
+                voff[dt][aa] = r * kRowBytes + ((gran ^ swz(r)) * 16) + (j & 1) * 8;
             }
     }
 
@@ -212,21 +237,55 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int kt_diag = (pmin + 1) / kKeys;       // tiles before this one need no mask
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-    auto step = [&](int kt, const uint16_t* sk, const uint16_t* sv, uint16_t* nk, uint16_t* nv, bool mask) {
-        if (kt + 1 < ntiles) issue_tile(kt + 1, nk, nv);
-        const char* skb = reinterpret_cast<const char*>(sk);
-        const char* svb = reinterpret_cast<const char*>(sv);
+    {
+        const TileSrc src = tile_src(0);
+        issue_k(src, s_k0);
+        issue_v(src, s_v0);
+    }
+    __syncthreads();
+    // One tile: compute from (sk, sv) while the next tile is copied into
+    // (nk, nv). Called with fixed buffers on even and odd tiles so every LDS
+    // address is a per-lane register plus an immediate.
+    auto tile = [&](int kt, uint16_t* sk, uint16_t* sv, uint16_t* nk, uint16_t* nv) {
+        const lds_char* skb = (const lds_char*)sk;
+        const lds_char* svb = (const lds_char*)sv;
 
-        // S^T for the two 32-key subtiles.
+        // S^T for the two 32-key subtiles; all K operands are requested
+        // before the first product so the LDS latency is paid once.
+        u32x4 kop[2][8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                kop[u][t] = *(const lds_u32x4*)(skb + koff[t] + 32 * u * kRowBytes);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 sacc[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             sacc[u] = f32x16{};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const u32x4 av = *reinterpret_cast<const u32x4*>(skb + 32 * u * kRowBytes + koff[t & 3] + (t >> 2) * 128);
-                sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(qv[t]), sacc[u], 0, 0, 0);
-            }
+            for (int t = 0; t < 8; ++t)
+                sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[u][t]), as_bf16x8(qv[t]), sacc[u], 0, 0, 0);
+        }
+        // V^T operands for the second product, requested while the weights
+        // are computed.
+        i16x4 vop[4][4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa)
+                    vop[t][dt][aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(svb + voff[dt][aa] + t * 16 * kRowBytes));
+        __builtin_amdgcn_sched_barrier(0);
+        // The copies of the next tile start only now: the compiler cannot tell
+        // the transposing reads above apart from them and would make those
+        // reads wait for the copies.
+        if (kt + 1 < ntiles) {
+            const TileSrc nsrc = tile_src(kt + 1);
+            issue_k(nsrc, nk);
+            issue_v(nsrc, nv);
         }
 
         // Causal mask (diagonal tiles only), max, lazy rescale, weights.
@@ -237,11 +296,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = sacc[u][r];
-                if (mask) x = (32 * u + key_of_reg(r) <= lim) ? x : -INFINITY;
-                sv2[u][r] = x;
-                mx = fmaxf(mx, x);
+                sv2[u][r] = sacc[u][r];
             }
+        if (kt >= kt_diag) {
+            // tile reaches past some row's position
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sv2[u][r] = (32 * u + key_of_reg(r) <= lim) ? sv2[u][r] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv2[u][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
         const bool need = mx > mref + kLazy;
         if (__builtin_amdgcn_ballot_w64(need)) {
@@ -277,10 +345,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const char* base = svb + t * 16 * kRowBytes + (dt >> 1) * 128;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + voff[dt & 1][0]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + voff[dt & 1][1]));
-                const i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const i16x8 av = __builtin_shufflevector(vop[t][dt][0], vop[t][dt][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                 as_bf16x8(pb[t]), o[dt], 0, 0, 0);
             }
@@ -288,18 +353,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         // every wave is done reading this tile's buffers
         __syncthreads();
     };
-
-    issue_tile(0, s_k0, s_v0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const bool mask = kt >= kt_diag;
-        if (kt & 1) {
-            if (mask) step(kt, s_k1, s_v1, s_k0, s_v0, true);
-            else step(kt, s_k1, s_v1, s_k0, s_v0, false);
-        } else {
-            if (mask) step(kt, s_k0, s_v0, s_k1, s_v1, true);
-            else step(kt, s_k0, s_v0, s_k1, s_v1, false);
-        }
+    for (int kt = 0; kt < ntiles; kt += 2) {
+        tile(kt, s_k0, s_v0, s_k1, s_v1);
+        if (kt + 1 < ntiles) tile(kt + 1, s_k1, s_v1, s_k0, s_v0);
     }
 
     // Epilogue: combine the half-waves' sums, normalise, store.
