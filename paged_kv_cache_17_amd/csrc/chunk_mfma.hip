@@ -18,8 +18,8 @@
 // Per 64-key tile (4 cache blocks gathered through the table):
 //  * each wave copies one cache block of K and of V straight from global
 //    memory into LDS (global_load_lds, 16 bytes per lane, no registers);
-//    the copy of tile kt + 1 runs while the weights and the second product
-//    of tile kt are computed, into the other of two buffers. LDS rows are 256 bytes, unpadded; the 16-byte granule
+//    the copy of tile kt + 1 runs while tile kt is computed, into the other
+//    of two buffers. LDS rows are 256 bytes, unpadded; the 16-byte granule
 //    c of row r is stored at position c ^ sw(r), which makes both read
 //    patterns below free of bank conflicts;
 //  * S^T = K Q^T: A = K rows, B = the wave's queries (kept in registers).
@@ -74,6 +74,38 @@ struct TileSrc {
     const char* vb;
     int cap;
 };
+
+// Transposing LDS read, issued as inline assembly so the compiler does not
+// order it after the asynchronous global-to-LDS copies in flight (it cannot
+// prove they touch other buffers). The compiler therefore does not track its
+// completion either: callers wait with lds_wait_all() before using the data.
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_read_tr16(uint32_t addr) {
+    i16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// Waits for every outstanding LDS read of this wave; the eight values pass
+// through the statement, so their uses cannot be scheduled before the wait.
+__device__ __forceinline__ void lds_wait_all(i16x4& a, i16x4& b, i16x4& c, i16x4& d,
+                                             i16x4& e, i16x4& f, i16x4& g, i16x4& h) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+__device__ __forceinline__ void lds_pin(i16x4& a, i16x4& b, i16x4& c, i16x4& d,
+                                        i16x4& e, i16x4& f, i16x4& g, i16x4& h) {
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
+}
+
+// Maximum of a value over lanes l and l ^ 32.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Granule swizzle of LDS row r (granule = 16 bytes = 8 elements). Bits of
 // the result: r2, r0, r1, r0^r1^r3. Reads of 8 or 16 consecutive rows at one
@@ -249,6 +281,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     auto tile = [&](int kt, uint16_t* sk, uint16_t* sv, uint16_t* nk, uint16_t* nv) {
         const lds_char* skb = (const lds_char*)sk;
         const lds_char* svb = (const lds_char*)sv;
+        // copies of the next tile: in flight during the whole tile
+        if (kt + 1 < ntiles) {
+            const TileSrc nsrc = tile_src(kt + 1);
+            issue_k(nsrc, nk);
+            issue_v(nsrc, nv);
+        }
 
         // S^T for the two 32-key subtiles; all K operands are requested
         // before the first product so the LDS latency is paid once.
@@ -271,22 +309,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         // are computed.
         i16x4 vop[4][4][2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int aa = 0; aa < 2; ++aa)
-                    vop[t][dt][aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(svb + voff[dt][aa] + t * 16 * kRowBytes));
-        __builtin_amdgcn_sched_barrier(0);
-        // The copies of the next tile start only now: the compiler cannot tell
-        // the transposing reads above apart from them and would make those
-        // reads wait for the copies.
-        if (kt + 1 < ntiles) {
-            const TileSrc nsrc = tile_src(kt + 1);
-            issue_k(nsrc, nk);
-            issue_v(nsrc, nv);
-        }
+            for (int aa = 0; aa < 2; ++aa) {
+                const uint32_t va = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(svb + voff[dt][aa]));
+                vop[0][dt][aa] = lds_read_tr16<0 * 16 * kRowBytes>(va);
+                vop[1][dt][aa] = lds_read_tr16<1 * 16 * kRowBytes>(va);
+                vop[2][dt][aa] = lds_read_tr16<2 * 16 * kRowBytes>(va);
+                vop[3][dt][aa] = lds_read_tr16<3 * 16 * kRowBytes>(va);
+            }
 
         // Causal mask (diagonal tiles only), max, lazy rescale, weights.
         float sv2[2][16];
@@ -310,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv2[u][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * sl2;
+        mx = max_halves(mx) * sl2;
         const bool need = mx > mref + kLazy;
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float nref = need ? mx : mref;
@@ -341,6 +372,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
             }
 
         // O^T += V^T P^T over the tile's four 16-key steps.
+        lds_wait_all(vop[0][0][0], vop[0][0][1], vop[0][1][0], vop[0][1][1],
+                     vop[0][2][0], vop[0][2][1], vop[0][3][0], vop[0][3][1]);
+#pragma unroll
+        for (int t = 1; t < 4; ++t)
+            lds_pin(vop[t][0][0], vop[t][0][1], vop[t][1][0], vop[t][1][1],
+                    vop[t][2][0], vop[t][2][1], vop[t][3][0], vop[t][3][1]);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -359,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     }
 
     // Epilogue: combine the half-waves' sums, normalise, store.
-    const float ltot = lsum + __shfl_xor(lsum, 32, kWave);
+    const float ltot = sum_halves(lsum);
     if (!active) return;
     const float inv = 1.0f / ltot;
     uint16_t* op = out + orow * kD;
