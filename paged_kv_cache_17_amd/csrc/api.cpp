@@ -245,7 +245,7 @@ extern "C" int paged_attn_decode(void* out, float* lse, const void* q,
     rc = resolve_split(num_seqs, n_kv, block_size, max_seq_len, split_tokens, &split);
     if (rc != PKV_OK) return rc;
     const bool balanced = balanced_eligible(dtype, split_tokens, num_seqs, n_q, n_kv, head_dim, block_size) &&
-                          aligned16(q) && aligned16(k_cache) && aligned16(v_cache);
+                          aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out);
     pkv::AttnArgs a{};
     if (balanced) {
         a.waves = balanced_waves(n_q, n_kv, num_seqs);

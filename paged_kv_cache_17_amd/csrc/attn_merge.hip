@@ -94,26 +94,29 @@ __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a, T* __restrict__ 
     if (lse && threadIdx.x == 0) lse[static_cast<size_t>(row) * a.n_q + h] = kLn2 * (M + log2f(den));
 }
 
-// Balanced-decode merge: one workgroup per (sequence, kv head) combines the
-// G heads' partials. Everything a row needs is fetched in three dependent
-// rounds: the sequence's length and prefix entries, the partials' (m, l)
-// (their weights staged in LDS), then the partial outputs (one element per
-// thread and partial). A segment spread over more than kMergeMaxParts waves
-// recomputes the weights on the fly instead of staging them.
-constexpr int kMergeMaxParts = 256;
+// Balanced-decode merge: one workgroup of 256 threads per (sequence, kv
+// head) combines the G heads' partials in three rounds of independent
+// loads: (1) the sequence's length and prefix entries; (2) every partial's
+// (m, l) for the G heads, one partial per thread, staged in LDS, then per
+// head a wave reduces the maximum and the weighted sum; (3) the partial
+// outputs, four dims per thread, all partials' loads in flight together.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxParts = 256;   // partials staged at once in LDS
 
 template <int G>
-__global__ __launch_bounds__(256) void merge_balanced_kernel(AttnArgs a, uint16_t* __restrict__ out,
-                                                             float* __restrict__ lse) {
+__global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs a, uint16_t* __restrict__ out,
+                                                                       float* __restrict__ lse) {
     constexpr int D = 128;
-    __shared__ float s_w[kMergeMaxParts][G];     // weights 2^(m_j - M_h)
+    __shared__ float s_m[kMergeMaxParts][G];     // m_j, then the weight 2^(m_j - M)
+    __shared__ float s_l[kMergeMaxParts][G];
     __shared__ float s_M[G];
-    __shared__ float s_inv[G];
-    __shared__ float s_lse[G];
+    __shared__ float s_den[G];
     __shared__ int s_info[3];                    // count, first slot, ok
     const int s = blockIdx.x;
     const int g = blockIdx.y;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     if (tid == 0) {
         const int L = a.seq_lens[s];
         const long long P = a.prefix[s];
@@ -135,51 +138,107 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(AttnArgs a, uint16_
         s_info[1] = static_cast<int>(first);
         s_info[2] = ok;
     }
+    if (tid < G) {
+        s_M[tid] = -INFINITY;
+        s_den[tid] = 0.0f;
+    }
     __syncthreads();
     const int count = s_info[0];
     const size_t first = static_cast<size_t>(s_info[1]);
     const bool ok = s_info[2];
+
+    // Per-head maximum over all partials; a NaN partial makes it NaN.
+    for (int j0 = 0; j0 < count; j0 += kMergeMaxParts) {
+        const int n = min(count - j0, kMergeMaxParts);
+        if (tid < n) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const PartialML p = a.ws_ml[(first + j0 + tid) * G + h];
+                s_m[tid][h] = p.m;
+                s_l[tid][h] = p.l;
+            }
+        }
+        __syncthreads();
+        for (int h = wave; h < G; h += kMergeThreads / kWave) {
+            float M = -INFINITY;
+            bool bad = false;
+            for (int j = lane; j < n; j += kWave) {
+                bad |= isnan(s_m[j][h]);
+                M = fmaxf(M, s_m[j][h]);
+            }
+            M = wave_max(M);
+            bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+            if (lane == 0) s_M[h] = (bad || isnan(s_M[h])) ? NAN : fmaxf(s_M[h], M);
+        }
+        __syncthreads();
+    }
+    // Weights and their sum (the staged block is still in LDS when
+    // count <= kMergeMaxParts; otherwise they are recomputed below).
     const bool staged = count <= kMergeMaxParts;
-    if (ok && tid < G) {
-        const int h = tid;
-        float M = -INFINITY;
-        bool nan = false;
-        for (int j = 0; j < count; ++j) {
-            const float m = a.ws_ml[(first + j) * G + h].m;
-            nan |= isnan(m);
-            M = fmaxf(M, m);
-        }
+    for (int h = wave; h < G; h += kMergeThreads / kWave) {
+        const float M = s_M[h];
         float den = 0.0f;
-        for (int j = 0; j < count; ++j) {
-            const PartialML p = a.ws_ml[(first + j) * G + h];
-            const float w = exp2f(p.m - M);
-            if (staged) s_w[j][h] = w;
-            den = fmaf(w, p.l, den);
+        for (int j = lane; j < count; j += kWave) {
+            float m, l;
+            if (staged) {
+                m = s_m[j][h];
+                l = s_l[j][h];
+            } else {
+                const PartialML p = a.ws_ml[(first + j) * G + h];
+                m = p.m;
+                l = p.l;
+            }
+            const float w = exp2f(m - M);
+            if (staged) s_m[j][h] = w;
+            den = fmaf(w, l, den);
         }
-        s_M[h] = M;
-        s_inv[h] = nan ? NAN : 1.0f / den;
-        s_lse[h] = nan ? NAN : kLn2 * (M + log2f(den));
+        den = wave_sum(den);
+        if (lane == 0) s_den[h] = den;
     }
     __syncthreads();
+
+    // Outputs: thread -> (head, 4 dims); partials' loads issued in groups of 8.
     uint16_t* obase = out + (static_cast<size_t>(s) * a.n_q + g * G) * D;
-    for (int e = tid; e < G * D; e += 256) {
-        const int h = e / D;
-        const int k = e - h * D;
-        float num = 0.0f;
-        float inv = NAN;
-        if (ok && staged) {
-#pragma unroll 4
-            for (int j = 0; j < count; ++j) num = fmaf(s_w[j][h], a.ws_o[((first + j) * G + h) * D + k], num);
-            inv = s_inv[h];
-        } else if (ok) {
-            const float M = s_M[h];
-            for (int j = 0; j < count; ++j)
-                num = fmaf(exp2f(a.ws_ml[(first + j) * G + h].m - M), a.ws_o[((first + j) * G + h) * D + k], num);
-            inv = s_inv[h];
+    for (int e = tid; e < G * D / 4; e += kMergeThreads) {
+        const int h = e / (D / 4);
+        const int k = 4 * (e - h * (D / 4));
+        const float M = s_M[h];
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float* ob = a.ws_o + (first * G + h) * D + k;
+        int j = 0;
+        for (; j + 8 <= count; j += 8) {
+            float4 v[8];
+            float wv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(j + u) * G * D);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) wv[u] = staged ? s_m[j + u][h] : exp2f(a.ws_ml[(first + j + u) * G + h].m - M);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                acc.x = fmaf(wv[u], v[u].x, acc.x);
+                acc.y = fmaf(wv[u], v[u].y, acc.y);
+                acc.z = fmaf(wv[u], v[u].z, acc.z);
+                acc.w = fmaf(wv[u], v[u].w, acc.w);
+            }
         }
-        obase[e] = f32_to_bf16(num * inv);
+        for (; j < count; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(j) * G * D);
+            const float wj = staged ? s_m[j][h] : exp2f(a.ws_ml[(first + j) * G + h].m - M);
+            acc.x = fmaf(wj, v.x, acc.x);
+            acc.y = fmaf(wj, v.y, acc.y);
+            acc.z = fmaf(wj, v.z, acc.z);
+            acc.w = fmaf(wj, v.w, acc.w);
+        }
+        const float inv = (ok && !isnan(M)) ? 1.0f / s_den[h] : NAN;
+        uint2 w2;
+        w2.x = pack2_bf16(acc.x * inv, acc.y * inv);
+        w2.y = pack2_bf16(acc.z * inv, acc.w * inv);
+        *reinterpret_cast<uint2*>(obase + h * D + k) = w2;
     }
-    if (lse && tid < G) lse[static_cast<size_t>(s) * a.n_q + g * G + tid] = ok ? s_lse[tid] : NAN;
+    if (lse && tid < G) {
+        const float M = s_M[tid];
+        lse[static_cast<size_t>(s) * a.n_q + g * G + tid] = (ok && !isnan(M)) ? kLn2 * (M + log2f(s_den[tid])) : NAN;
+    }
 }
 
 }  // namespace

@@ -91,7 +91,50 @@ def test_group_sizes(n_q, n_kv):
     wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
                         new_lens=np.ones_like(L), seed=5)
     say("group sizes", n_q, n_kv)
-    _full_check(wl, "decode", 256)
+    _full_check(wl, "decode", 0)       # balanced split pass + its merge
+    _full_check(wl, "decode", 256)     # fixed split + merge pass
+
+
+def test_balanced_many_short_sequences():
+    """Hundreds of short sequences: most (sequence, kv head) segments lie
+    inside one wave's tile range (a single partial); the rest span several
+    waves and their partials are merged."""
+    L = np.random.default_rng(21).integers(1, 301, size=700)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=21)
+    say("balanced, 700 short sequences")
+    _, _, err, lerr = _full_check(wl, "decode", 0, check_pool=False)
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+
+
+def test_balanced_workspace_reuse_and_stale_contents():
+    """Workspace contents on entry are ignored: back-to-back calls on one
+    workspace, and calls on a workspace holding arbitrary bytes or zeros,
+    give bit-identical results."""
+    import paged_kv_cache_17_amd as pkv
+    L = np.array([3, 900, 2500, 4000, 17, 1300, 64, 3333])
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=22)
+    say("balanced workspace reuse")
+    c = build_gpu_cache(wl, fill_nan=False)
+    q = raw_to_torch(wl.q, BF16)
+    lens = i32(wl.seq_lens)
+    ws = c.workspace(wl.num_seqs, wl.n_q, wl.max_seq_len)
+    outs = []
+    for trial in range(5):
+        if trial == 3:
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=ws.device))
+        if trial == 4:
+            ws.zero_()
+        out = torch.empty_like(q)
+        lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda")
+        pkv.paged_attn_decode(out, lse, q, c.k_cache, c.v_cache, c.table_dev, lens, wl.max_seq_len, wl.scale, ws)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    for out, lse in outs[1:]:
+        assert torch.equal(out, outs[0][0]) and torch.equal(lse, outs[0][1])
+    ref, _ = oracle.paged_attention_all(oracle.build_cache(wl))
+    check_rows(out_f64(outs[0][0], BF16), ref, BF16, "workspace reuse")
 
 
 @pytest.mark.parametrize("dtype,d,bs,n_q,n_kv", [
