@@ -48,36 +48,44 @@ def parse():
     return p.parse_args()
 
 
-# Source files of the split kernel; the counter figures in COUNTERS are valid
-# only while their hash matches.
-KERNEL_SOURCES = ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_tile.h",
-                  "paged_kv_cache_17_amd/csrc/device_common.h"]
-COUNTERS = os.path.join(ROOT, "profiles", "decode_split_c2_counters.txt")
+# Counter summaries (FETCH_SIZE / WRITE_SIZE per launch) committed under
+# profiles/, one per timed kernel; a summary is used only while the hash of
+# that kernel's sources matches the one it records.
+COUNTERS = {
+    "decode": (os.path.join(ROOT, "profiles", "decode_split_c2_counters.txt"),
+               ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_tile.h",
+                "paged_kv_cache_17_amd/csrc/device_common.h"]),
+    "chunk": (os.path.join(ROOT, "profiles", "chunk_mfma_c5_counters.txt"),
+              ["paged_kv_cache_17_amd/csrc/chunk_mfma.hip", "paged_kv_cache_17_amd/csrc/device_common.h"]),
+}
 
 
-def kernel_source_hash():
+def kernel_source_hash(kind="decode"):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in COUNTERS[kind][1]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config_name):
-    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
-    for a plain copy of known size), or None if absent or stale."""
-    if not os.path.exists(COUNTERS):
+def measured_traffic(config_name, kind="decode"):
+    """HBM bytes per launch of the decode split kernel (kind "decode") or the
+    chunk kernel (kind "chunk") from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a
+    plain copy of known size), or None if absent, stale or for another
+    workload."""
+    path = COUNTERS[kind][0]
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(COUNTERS) as f:
+    with open(path) as f:
         for line in f:
             line = line.strip()
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != kernel_source_hash() or kv.get("workload") != config_name:
+    if kv.get("source_sha") != kernel_source_hash(kind) or kv.get("workload") != config_name:
         return None
     fetch = float(kv["fetch_kib_per_launch"]) * float(kv["fetch_scale"])
     write = float(kv["write_kib_per_launch"]) * float(kv["write_scale"])
@@ -97,26 +105,62 @@ def copy_probe(mib):
                       "bytes_written_per_launch": n}), flush=True)
 
 
+_ORACLE_CACHE = None     # the oracle's cache, shared with forked workers
+
+
+def _attend_some(seqs):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for s in seqs:
+            _ORACLE_CACHE.attend(s)
+        return time.perf_counter() - t0
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """Time the float64 oracle on the same decode step (gather through its own
-    pool + widening + attention, all sequences), repeated until about
-    ``budget_s`` seconds of CPU work; reports the median step."""
+    pool + widening + attention, all sequences), each setting repeated until
+    about ``budget_s`` seconds of work; reports the median step:
+
+    * one core: the sequences in turn, BLAS limited to one thread;
+    * all host cores (capped at 16, the GPU machine's CPU share): a pool of
+      forked worker processes, one BLAS thread each, the sequences dealt
+      round-robin; the step time is the wall time until the last worker is
+      done.
+    """
+    import multiprocessing as mp
+
     import oracle
-    cache = oracle.build_cache(wl, fill=0)
-    times = []
-    t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 50):
-        t0 = time.perf_counter()
-        for s in range(wl.num_seqs):
-            cache.attend(s)
-        times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
+    from threadpoolctl import threadpool_limits
+    global _ORACLE_CACHE
+    _ORACLE_CACHE = oracle.build_cache(wl, fill=0)
     tokens = int(wl.new_lens.sum())
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    seqs = list(range(wl.num_seqs))
+
+    def repeat(fn):
+        times = []
+        t_start = time.perf_counter()
+        while not times or (time.perf_counter() - t_start < budget_s and len(times) < 50):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    with threadpool_limits(1):
+        dt1, n1 = repeat(lambda: _attend_some(seqs))
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    with mp.get_context("fork").Pool(cores) as pool:
+        parts = [seqs[i::cores] for i in range(cores)]
+        pool.map(_attend_some, parts)               # warm the workers
+        dtn, nn = repeat(lambda: pool.map(_attend_some, parts))
+    kv = wl.ideal_kv_bytes()
+    return {"value": tokens / dtn, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole decode step ({wl.num_seqs} sequences, {int(wl.seq_lens.sum())} keys): "
-                      f"table gather, bf16->float64 widening and attention in NumPy float64, one thread; "
-                      f"median of {len(times)} repeats",
-            "seconds_per_step": dt, "kv_gbps": wl.ideal_kv_bytes() / dt / 1e9}
+                      f"table gather, bf16->float64 widening and attention in NumPy float64; {cores} forked "
+                      f"worker processes with one BLAS thread each, median of {nn} repeats",
+            "seconds_per_step": dtn, "kv_gbps": kv / dtn / 1e9,
+            "one_core": {"value": tokens / dt1, "unit": "tokens/s", "cores": 1, "seconds_per_step": dt1,
+                         "kv_gbps": kv / dt1 / 1e9, "repeats": n1}}
 
 
 def main():
@@ -193,10 +237,11 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
 
-    # Timed region 2: the same steps with an event pair recorded by the
-    # library around the decode split pass and around the chunk kernel ->
-    # their average durations for the roofline. Kept apart because each
-    # recorded event adds a few microseconds between launches.
+    # Timed region 2: the same steps, with the library launching the decode
+    # split pass and the chunk kernel so that their own dispatches record an
+    # event pair (kernel start, kernel end) -> their average durations for
+    # the roofline. Kept apart from region 1 so the value is measured on
+    # plain launches.
     def pairs():
         ps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
@@ -247,14 +292,16 @@ def main():
         line["roofline"] = {"kernel": "decode split pass", "bound": "hbm", "achieved": achieved,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                             "traffic": measured_traffic(CONFIG_NAMES[args.config]), "avg_launch_ms": kern_avg,
-                            "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash()}
+                            "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash("decode")}
     if nd < S:
         chk_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_chk]))
         tflops = chk_flops / (chk_avg * 1e-3) / 1e12
         line["chunk_roofline"] = {"kernel": "chunk attention (matrix cores)", "bound": "mfma",
                                   "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None, "avg_launch_ms": chk_avg,
-                                  "algorithmic_flops": chk_flops}
+                                  "frac": tflops / PEAK_BF16_TFLOPS,
+                                  "traffic": measured_traffic(CONFIG_NAMES[args.config], "chunk"),
+                                  "avg_launch_ms": chk_avg, "algorithmic_flops": chk_flops,
+                                  "source_sha": kernel_source_hash("chunk")}
         if not nd:
             line["roofline"] = line.pop("chunk_roofline")
     if not args.no_cpu:

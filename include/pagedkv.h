@@ -238,11 +238,13 @@ int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_star
 
 /* ======================================================================
  * Profiling hook (not part of the computation): when both events are
- * non-NULL, paged_attn_decode records `before` immediately before and
- * `after` immediately after its first-pass (split) kernel on the call's
- * stream, and paged_attn_chunk does the same around its matrix-core kernel,
- * so a caller can time that kernel alone. Pass NULLs to disable. Events
- * are hipEvent_t passed as void*. Process-wide; not thread-safe. */
+ * non-NULL, paged_attn_decode launches its first-pass (split) kernel and
+ * paged_attn_chunk its matrix-core kernel so that the kernel's own dispatch
+ * records `before` when the kernel starts executing and `after` when it
+ * has finished (hipExtLaunchKernel's event pair); elapsed time between them
+ * is that kernel's duration, without the latency of separate event
+ * packets. Pass NULLs to disable. Events are hipEvent_t passed as void*.
+ * Process-wide; not thread-safe. */
 int pkv_set_profile_events(void* before, void* after);
 
 #ifdef __cplusplus

@@ -20,6 +20,17 @@ constexpr size_t kAlign = 256;
 hipEvent_t g_prof_before = nullptr;
 hipEvent_t g_prof_after = nullptr;
 
+// The profiling pair, when both events are set: recorded by the timed
+// kernel's own dispatch.
+pkv::KernelEvents profile_events() {
+    pkv::KernelEvents ev;
+    if (g_prof_before && g_prof_after) {
+        ev.start = g_prof_before;
+        ev.stop = g_prof_after;
+    }
+    return ev;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int elem_bytes(int dtype) {
@@ -131,16 +142,11 @@ int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decod
     const bool aligned = aligned16(a.q) && aligned16(a.k_cache) && aligned16(a.v_cache);
 
     hipError_t e;
-    const bool timed = g_prof_before && g_prof_after;
     if (balanced) {
-        if (timed) hipEventRecord(g_prof_before, stream);
-        e = pkv::launch_decode_balanced(a, stream);
-        if (timed) hipEventRecord(g_prof_after, stream);
+        e = pkv::launch_decode_balanced(a, stream, profile_events());
     } else if (decode && bf16 && aligned &&
                pkv::decode_fast_supported(a.n_q, a.n_kv, a.head_dim, a.block_size, a.split_tokens)) {
-        if (timed) hipEventRecord(g_prof_before, stream);
-        e = pkv::launch_decode_fast(a, stream);
-        if (timed) hipEventRecord(g_prof_after, stream);
+        e = pkv::launch_decode_fast(a, stream, profile_events());
     } else {
         e = pkv::launch_split_generic(a, bf16, stream);
     }
@@ -318,10 +324,7 @@ extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int3
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
     if (mfma) {
-        const bool timed = g_prof_before && g_prof_after;
-        if (timed) hipEventRecord(g_prof_before, static_cast<hipStream_t>(stream));
-        const hipError_t e = pkv::launch_chunk_mfma(a, out, lse, static_cast<hipStream_t>(stream));
-        if (timed) hipEventRecord(g_prof_after, static_cast<hipStream_t>(stream));
+        const hipError_t e = pkv::launch_chunk_mfma(a, out, lse, static_cast<hipStream_t>(stream), profile_events());
         return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
     }
     return run_attention(a, out, lse, dtype, false, false, workspace, workspace_bytes,

@@ -414,13 +414,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
 }
 
 template <int G>
-hipError_t launch_g(const AttnArgs& a, void* out, float* lse, hipStream_t stream) {
+hipError_t launch_g(const AttnArgs& a, void* out, float* lse, hipStream_t stream, KernelEvents ev) {
     constexpr int QT = kRows / G;
     const int nq = (a.max_q_len + QT - 1) / QT;
     const int pairs = a.num_seqs * a.n_kv;
     const int per_xcd = (pairs + kXcds - 1) / kXcds;
     const dim3 grid(per_xcd * nq * kXcds);
-    hipLaunchKernelGGL(chunk_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, a, static_cast<uint16_t*>(out), lse);
+    uint16_t* o = static_cast<uint16_t*>(out);
+    if (ev.on())
+        hipExtLaunchKernelGGL(chunk_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a, o, lse);
+    else
+        hipLaunchKernelGGL(chunk_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, a, o, lse);
     return hipGetLastError();
 }
 
@@ -433,12 +437,12 @@ bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size, int m
     return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
-hipError_t launch_chunk_mfma(const AttnArgs& a, void* out, float* lse, hipStream_t stream) {
+hipError_t launch_chunk_mfma(const AttnArgs& a, void* out, float* lse, hipStream_t stream, KernelEvents ev) {
     switch (a.n_q / a.n_kv) {
-        case 1: return launch_g<1>(a, out, lse, stream);
-        case 2: return launch_g<2>(a, out, lse, stream);
-        case 4: return launch_g<4>(a, out, lse, stream);
-        case 8: return launch_g<8>(a, out, lse, stream);
+        case 1: return launch_g<1>(a, out, lse, stream, ev);
+        case 2: return launch_g<2>(a, out, lse, stream, ev);
+        case 4: return launch_g<4>(a, out, lse, stream, ev);
+        case 8: return launch_g<8>(a, out, lse, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

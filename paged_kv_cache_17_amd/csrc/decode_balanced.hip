@@ -208,9 +208,13 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
 }
 
 template <int G>
-hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), balanced_lds_bytes(a.num_seqs),
-                       stream, a);
+hipError_t launch_g(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
+    const size_t lds = balanced_lds_bytes(a.num_seqs);
+    if (ev.on())
+        hipExtLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), lds, stream, ev.start, ev.stop, 0,
+                              a);
+    else
+        hipLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -252,12 +256,12 @@ int decode_balanced_waves(int n_q, int n_kv, int num_seqs) {
     return cus * per_cu;
 }
 
-hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     switch (a.n_q / a.n_kv) {
-        case 1: return launch_g<1>(a, stream);
-        case 2: return launch_g<2>(a, stream);
-        case 4: return launch_g<4>(a, stream);
-        case 8: return launch_g<8>(a, stream);
+        case 1: return launch_g<1>(a, stream, ev);
+        case 2: return launch_g<2>(a, stream, ev);
+        case 4: return launch_g<4>(a, stream, ev);
+        case 8: return launch_g<8>(a, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

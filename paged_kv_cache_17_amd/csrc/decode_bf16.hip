@@ -106,10 +106,14 @@ __global__ __launch_bounds__(kWave * WAVES) void decode_split_kernel(AttnArgs a)
 }
 
 template <int G>
-hipError_t launch_g(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_g(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     constexpr int kWaves = 4;
     const dim3 grid(a.max_splits, a.n_kv, a.num_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<G, kWaves>), grid, dim3(kWave * kWaves), 0, stream, a);
+    if (ev.on())
+        hipExtLaunchKernelGGL((decode_split_kernel<G, kWaves>), grid, dim3(kWave * kWaves), 0, stream, ev.start,
+                              ev.stop, 0, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<G, kWaves>), grid, dim3(kWave * kWaves), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -122,12 +126,12 @@ bool decode_fast_supported(int n_q, int n_kv, int head_dim, int block_size, int 
     return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
-hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     switch (a.n_q / a.n_kv) {
-        case 1: return launch_g<1>(a, stream);
-        case 2: return launch_g<2>(a, stream);
-        case 4: return launch_g<4>(a, stream);
-        case 8: return launch_g<8>(a, stream);
+        case 1: return launch_g<1>(a, stream, ev);
+        case 2: return launch_g<2>(a, stream, ev);
+        case 4: return launch_g<4>(a, stream, ev);
+        case 8: return launch_g<8>(a, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,6 +37,14 @@ struct AttnArgs {
     int* prefix;                 // balanced decode: [S+1] block-count prefix sums
 };
 
+// Optional event pair recorded by the kernel's own dispatch (start and end
+// of its execution), for timing one kernel without extra stream packets.
+struct KernelEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+    bool on() const { return start || stop; }
+};
+
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* table, int table_stride, const int32_t* start_pos,
                             const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
@@ -47,18 +55,19 @@ hipError_t launch_split_generic(const AttnArgs& a, bool bf16, hipStream_t stream
 
 // Split pass tuned for decode with bf16, head_dim 128, block_size 16.
 bool decode_fast_supported(int n_q, int n_kv, int head_dim, int block_size, int split_tokens);
-hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
 
 // Balanced decode pass (bf16, head_dim 128, block_size 16): equal tile
 // ranges per wave across sequence boundaries.
 bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs);
 int decode_balanced_waves(int n_q, int n_kv, int num_seqs);
-hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
 
 // Chunk attention on MFMA (bf16, head_dim 128, block_size 16, sequences of
 // at most 32768 keys): writes out and lse directly, no workspace.
 bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size, int max_seq_len);
-hipError_t launch_chunk_mfma(const AttnArgs& a, void* out, float* lse, hipStream_t stream);
+hipError_t launch_chunk_mfma(const AttnArgs& a, void* out, float* lse, hipStream_t stream,
+                             KernelEvents ev = {});
 
 // Merge pass: combines each row's partial states into out (and lse).
 hipError_t launch_merge(const AttnArgs& a, void* out, float* lse, bool bf16, hipStream_t stream);
