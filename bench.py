@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--copies", type=int, default=2, help="independent cache copies used in turn")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--bestof", action="store_true",
+                   help="time the best-of-8 decode step over shared prompts (and the same step without sharing)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -163,6 +165,100 @@ def cpu_baseline(wl, budget_s=10.0):
                          "kv_gbps": kv / dt1 / 1e9, "repeats": n1}}
 
 
+def bench_bestof(args):
+    """Best-of-8 decode step over shared prompts (8 prompts x 2048 tokens, 8
+    branches each with 64 own tokens): every branch's table points at its
+    prompt's blocks, the shared tail block having been copied on write. A
+    step re-appends each branch's last own token (idempotent) and runs
+    paged_attn_decode over the 64 branches. The same step over a cache in
+    which every branch holds a private copy of its prompt is timed beside
+    it. Cache copies are used in turn so the data of one step is not in the
+    last-level cache at the next."""
+    import torch
+    import paged_kv_cache_17_amd as pkv
+    from gpu_harness import build_gpu_fork_cache, i32, raw_to_torch
+    from workloads import best_of_n_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.load_library()
+    fw = best_of_n_workload()
+    NP, NB = fw.num_prompts, fw.num_branches
+    lens = fw.branch_lens()
+    q = raw_to_torch(fw.q, fw.dtype)
+    last_k = raw_to_torch(np.stack([k[-1] for k in fw.own_k]), fw.dtype)
+    last_v = raw_to_torch(np.stack([v[-1] for v in fw.own_v]), fw.dtype)
+    start_pos = i32(np.concatenate([np.zeros(NP), lens - 1]))
+    new_start = i32(np.concatenate([np.zeros(NP + 1), np.arange(1, NB + 1)]))
+    seq_lens = i32(lens)
+    stream = torch.cuda.current_stream()
+    copies = max(args.copies, 4)
+    # distinct K+V bytes behind the branches' tables: each prompt once, each
+    # branch's own tokens once
+    unique = (int(fw.prompt_lens.sum()) + int(fw.own_lens.sum())) * fw.n_kv * fw.head_dim * 2 * 2
+
+    def run(share):
+        caches = [build_gpu_fork_cache(fw, fill_nan=False, share=share)[0] for _ in range(copies)]
+        outs = [torch.empty_like(q) for _ in caches]
+        wss = [c.workspace(NB, fw.n_q, int(lens.max())).clone() for c in caches]
+
+        def step(i, ev=None):
+            j = i % len(caches)
+            c = caches[j]
+            c.append(last_k, last_v, start_pos, new_start, stream=stream)
+            if ev is not None:
+                pkv.pkv_set_profile_events(*ev)
+            pkv.paged_attn_decode(outs[j], None, q, c.k_cache, c.v_cache, c.table_dev[NP:], seq_lens,
+                                  int(lens.max()), fw.scale, wss[j], stream=stream)
+            pkv.pkv_set_profile_events(None, None)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for b, a in evs:
+            b.record(stream)
+            a.record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        kern = float(np.mean([b.elapsed_time(a) for b, a in evs]))
+        used = fw.num_blocks - caches[0].pool.kvpool_num_free()
+        del caches
+        torch.cuda.empty_cache()
+        return ms, kern, used
+
+    ms_s, kern_s, used_s = run(True)
+    ms_u, kern_u, used_u = run(False)
+    logical = fw.logical_kv_bytes()
+    line = {
+        "metric": METRIC, "value": NB * args.steps / (ms_s * args.steps * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_s, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": fw.name, "prompts": NP, "branches_per_prompt": fw.branches,
+                   "prompt_tokens": int(fw.prompt_lens[0]), "own_tokens": int(fw.own_lens[0]), "n_q": fw.n_q,
+                   "n_kv": fw.n_kv, "head_dim": fw.head_dim, "block_size": fw.block_size,
+                   "cache_copies": copies},
+        "roofline": {"kernel": "decode split pass over shared prompts", "bound": "hbm",
+                     "achieved": unique / (kern_s * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": unique / (kern_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
+                     "avg_launch_ms": kern_s, "algorithmic_bytes": unique,
+                     "logical_bytes": logical, "logical_gbps": logical / (kern_s * 1e-3) / 1e9},
+        "blocks_held": {"shared": used_s, "unshared": used_u},
+        "unshared": {"value": NB / (ms_u * 1e-3), "ms_per_step": ms_u, "avg_launch_ms": kern_u,
+                     "kv_gbps": logical / (kern_u * 1e-3) / 1e9},
+        "sharing_speedup": ms_u / ms_s,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,6 +269,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.bestof:
+        bench_bestof(args)
         return
 
     import torch

@@ -73,6 +73,7 @@ extern "C" {
 #define PKV_ERR_TABLE_FULL          -7  /* a sequence needs more blocks than its table row holds */
 #define PKV_ERR_HIP                 -8  /* a HIP launch failed (hipGetLastError) */
 #define PKV_ERR_NO_MEMORY           -9  /* host allocation for the pool object failed */
+#define PKV_ERR_INVALID_BLOCK      -10  /* a block id to share or copy is out of range, not allocated, or repeated */
 
 /* ---- element types ----------------------------------------------------- */
 #define PKV_F32  0   /* IEEE binary32 */
@@ -114,9 +115,54 @@ int kvpool_destroy(kvpool_t* pool);
  * a no-op. */
 int kvpool_alloc(kvpool_t* pool, int32_t n, int32_t* out_ids);
 
-/* Return n blocks. All or nothing: INVALID_FREE if any id is out of range,
- * currently free, or listed twice. */
+/* Drop one reference to each of n blocks; a block whose last reference
+ * goes rejoins the free set (a block from kvpool_alloc has one reference).
+ * All or nothing: INVALID_FREE if any id is out of range, currently free,
+ * or listed twice. */
 int kvpool_free(kvpool_t* pool, int32_t n, const int32_t* ids);
+
+/* ----------------------------------------------------------------------
+ * Shared blocks. Source: serving tutorial section 4.2 (a physical block
+ * can be shared through reference counts by a common prefix or by beam /
+ * parallel-sampling branches; a shared, still-writable tail block that one
+ * holder is about to change is copied and that holder's table remapped
+ * instead of writing the shared copy), section 1.7 (a shared block goes
+ * back to the allocator only when its last holder releases it), and its
+ * question on best-of-n (the prompt's KV is held once, only the branches'
+ * own tokens grow with the number of branches); lab-scale demo D08 (two
+ * sequences of 6 and 7 tokens with block size 4 sharing one full block
+ * need 3 physical blocks instead of 4). The attention entry points need
+ * nothing extra: table rows may name the same block.
+ * -------------------------------------------------------------------- */
+
+/* Add one reference to each of n allocated blocks. All or nothing:
+ * INVALID_BLOCK if an id is out of range, free, or listed twice. */
+int kvpool_share(kvpool_t* pool, int32_t n, const int32_t* ids);
+
+/* Holders of block `id` (0 = free). INVALID_ARGUMENT if out of range. */
+int kvpool_refcount(const kvpool_t* pool, int32_t id, int32_t* out);
+
+/* Sequence helper: make an empty row (*dst_held == 0) share the first
+ * ceil(length / block_size) blocks of another row (its first `length`
+ * tokens), one more reference each; *dst_held is set to that count. A
+ * length that ends inside a block shares that block too; the first write
+ * into it goes through kvpool_cow. Errors: INVALID_ARGUMENT (dst not
+ * empty, length past the source's blocks), TABLE_FULL, INVALID_BLOCK. */
+int kvpool_fork(kvpool_t* pool, const int32_t* src_row, int32_t src_held,
+                int32_t* dst_row, int32_t* dst_held, int32_t row_capacity, int32_t length);
+
+/* Sequence helper, before writing positions [start, start + count) of a
+ * row: every block of the row in that range held by more than one row is
+ * replaced in this row by a newly allocated block (lowest rank first, in
+ * row order), dropping one reference to the old block. The (old, new)
+ * pairs go to copy_src / copy_dst (capacity entries each; at most
+ * ceil(count / block_size) + 1 are needed) and *num_copies; the caller
+ * copies their contents with kv_copy_blocks before appending. All or
+ * nothing: INVALID_BLOCK (a row entry in range is not an allocated block),
+ * INVALID_ARGUMENT (capacity too small), OUT_OF_BLOCKS. Blocks past
+ * num_held are not touched (kvpool_ensure allocates them unshared). */
+int kvpool_cow(kvpool_t* pool, int32_t* row, int32_t num_held, int32_t start, int32_t count,
+               int32_t* copy_src, int32_t* copy_dst, int32_t capacity, int32_t* num_copies);
 
 /* Number of free blocks. */
 int kvpool_num_free(const kvpool_t* pool, int32_t* out);
@@ -134,7 +180,8 @@ int kvpool_free_ids(const kvpool_t* pool, int32_t* out, int32_t* count);
 int kvpool_ensure(kvpool_t* pool, int32_t* row, int32_t* num_held,
                   int32_t row_capacity, int32_t length);
 
-/* Sequence helper: return every block of a row, set its entries to -1 and
+/* Sequence helper: drop the row's reference to each of its blocks (blocks
+ * no other row holds rejoin the free set), set its entries to -1 and
  * *num_held to 0. Releasing an empty row is a no-op, so calling this twice
  * is safe. */
 int kvpool_release(kvpool_t* pool, int32_t* row, int32_t* num_held);
@@ -162,6 +209,24 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
               int32_t num_seqs, int32_t total_new, int32_t num_blocks,
               int32_t n_kv, int32_t head_dim, int32_t block_size, int32_t dtype,
               void* stream);
+
+/* ======================================================================
+ * kv_copy_blocks - copy whole blocks inside both pools: block src_ids[i]'s
+ * K and V (all kv heads, all slots) onto block dst_ids[i], i < n.
+ *
+ * Source: serving tutorial section 4.2 (copy-on-write: the holder about to
+ * write a shared block gets a copy of it). Pair the call with kvpool_cow,
+ * whose (old, new) pairs it takes, before kv_append into those blocks.
+ *
+ * src_ids, dst_ids: device int32 [n]. Every dst must differ from every
+ * other dst and from every src of the call (kvpool_cow's pairs do), else
+ * the result is undefined. A pair naming an id outside [0, num_blocks), or
+ * the same block twice, is skipped. Shapes as kv_append.
+ * Errors: NULL_POINTER, INVALID_ARGUMENT (sizes, dtype), HIP. n == 0
+ * launches nothing. */
+int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
+                   int32_t n, int32_t num_blocks, int32_t n_kv, int32_t head_dim,
+                   int32_t block_size, int32_t dtype, void* stream);
 
 /* ======================================================================
  * Attention workspace. Both attention entry points split each sequence's

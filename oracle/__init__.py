@@ -7,7 +7,9 @@ shares no code with the HIP path.
 """
 from .paged_attention import (  # noqa: F401
     BlockAllocator,
+    InvalidBlock,
     InvalidFree,
+    copy_blocks,
     OracleCache,
     OutOfBlocks,
     SequenceBlocks,

@@ -72,7 +72,7 @@ class InvalidFree(OracleError):
 
 
 class BlockAllocator:
-    """Free set of block ids handed out lowest rank first.
+    """Free set of block ids handed out lowest rank first, with holder counts.
 
     The lab's pool keeps a sorted free list, pops index 0 when a sequence
     needs a block and re-sorts after a release, so it always hands out the
@@ -85,8 +85,14 @@ class BlockAllocator:
     changes nothing. The serving tutorial (section 1.7) requires reclaim to
     be free of double frees, so ``free`` validates every id (in range,
     currently allocated, no duplicates) before returning any of them.
-    Pinned against the tutorial's block-slot demo, the lab's 7-of-12 peak
-    and a brute-force model of the sorted list.
+
+    Shared blocks (serving tutorial, section 4.2: a common prefix or beam
+    branches point at the same physical block, counted by reference;
+    section 1.7: the block goes back only when its last holder lets go):
+    ``alloc`` gives a block one holder, ``share`` adds one, ``free`` drops
+    one and returns the block to the free set when none is left.
+    Pinned against the tutorial's block-slot and sharing demos, the lab's
+    7-of-12 peak and a brute-force model of the sorted list.
     """
 
     def __init__(self, num_blocks: int, order=None):
@@ -99,6 +105,7 @@ class BlockAllocator:
         self.rank = {blk: i for i, blk in enumerate(order)}
         self.free_ranks = sorted(range(self.num_blocks))   # ranks of free ids
         self.order = order
+        self.refs = {}                                      # allocated id -> holders
 
     @property
     def num_free(self) -> int:
@@ -108,25 +115,49 @@ class BlockAllocator:
         """Free ids in the order they would be handed out."""
         return [self.order[r] for r in self.free_ranks]
 
+    def refcount(self, blk: int) -> int:
+        return self.refs.get(int(blk), 0)
+
     def alloc(self, n: int) -> list:
         if n < 0:
             raise ValueError("negative count")
         if n > len(self.free_ranks):
             raise OutOfBlocks(f"need {n} blocks, {len(self.free_ranks)} free")
         taken, self.free_ranks = self.free_ranks[:n], self.free_ranks[n:]
-        return [self.order[r] for r in taken]
+        ids = [self.order[r] for r in taken]
+        for b in ids:
+            self.refs[b] = 1
+        return ids
+
+    def _check_held(self, ids, exc):
+        if len(set(ids)) != len(ids):
+            raise exc("duplicate id in one call")
+        for b in ids:
+            if not (0 <= b < self.num_blocks):
+                raise exc(f"id {b} out of range")
+            if self.refs.get(b, 0) == 0:
+                raise exc(f"id {b} is free")
 
     def free(self, ids) -> None:
         ids = [int(x) for x in ids]
-        if len(set(ids)) != len(ids):
-            raise InvalidFree("duplicate id in one free call")
-        free_set = set(self.free_ranks)
+        self._check_held(ids, InvalidFree)
+        back = []
         for b in ids:
-            if not (0 <= b < self.num_blocks):
-                raise InvalidFree(f"id {b} out of range")
-            if self.rank[b] in free_set:
-                raise InvalidFree(f"id {b} is already free")
-        self.free_ranks = sorted(self.free_ranks + [self.rank[b] for b in ids])
+            self.refs[b] -= 1
+            if self.refs[b] == 0:
+                del self.refs[b]
+                back.append(self.rank[b])
+        self.free_ranks = sorted(self.free_ranks + back)
+
+    def share(self, ids) -> None:
+        ids = [int(x) for x in ids]
+        self._check_held(ids, InvalidBlock)
+        for b in ids:
+            self.refs[b] += 1
+
+
+class InvalidBlock(OracleError):
+    pass
 
 
 class SequenceBlocks:
@@ -135,8 +166,15 @@ class SequenceBlocks:
     ``ensure(L)`` grows the row to ceil(L / B) blocks, taking one new block
     each time a position reaches ``len(blocks) * B``; taking them in one
     ``alloc`` call gives the same ids as the lab's one-at-a-time pops.
-    ``release`` returns the row's blocks and empties it, so a second release
-    is a no-op (serving tutorial, section 1.7: reclaim must be idempotent).
+    ``release`` drops the row's hold on its blocks and empties it, so a
+    second release is a no-op (serving tutorial, section 1.7: reclaim must
+    be idempotent).
+
+    ``fork`` and ``cow`` are the sharing side (serving tutorial, section
+    4.2): a new row points at another row's first ceil(L / B) blocks; before
+    a row writes positions in a block that other rows also hold, it swaps in
+    a fresh block (lowest rank first, in row order) holding a copy, and the
+    others keep the original.
     """
 
     def __init__(self, block_size: int):
@@ -151,6 +189,41 @@ class SequenceBlocks:
     def release(self, allocator: BlockAllocator) -> None:
         blocks, self.blocks = self.blocks, []
         allocator.free(blocks)
+
+    def fork(self, allocator: BlockAllocator, src: "SequenceBlocks", length: int) -> None:
+        if self.blocks:
+            raise ValueError("fork into a non-empty row")
+        need = -(-int(length) // self.block_size)
+        if need > len(src.blocks):
+            raise ValueError("fork past the source's blocks")
+        allocator.share(src.blocks[:need])
+        self.blocks = list(src.blocks[:need])
+
+    def cow(self, allocator: BlockAllocator, start: int, count: int) -> list:
+        """Make the blocks holding positions [start, start + count) private to
+        this row; returns the (old, new) pairs whose contents must be copied."""
+        if count <= 0 or not self.blocks:
+            return []
+        first = int(start) // self.block_size
+        last = min((int(start) + int(count) - 1) // self.block_size, len(self.blocks) - 1)
+        shared = [i for i in range(first, last + 1) if allocator.refcount(self.blocks[i]) > 1]
+        if len(shared) > allocator.num_free:
+            raise OutOfBlocks("no room for the copies")
+        pairs = []
+        for i in shared:
+            old = self.blocks[i]
+            new = allocator.alloc(1)[0]
+            allocator.refs[old] -= 1
+            self.blocks[i] = new
+            pairs.append((old, new))
+        return pairs
+
+
+def copy_blocks(pool_k, pool_v, pairs) -> None:
+    """Copy-on-write's data side: block ``new`` receives block ``old``'s K and V."""
+    for old, new in pairs:
+        pool_k[new] = pool_k[old]
+        pool_v[new] = pool_v[old]
 
 
 # --------------------------------------------------------------------------

@@ -41,6 +41,11 @@ _SIGNATURES = {
     "kvpool_free_ids": ([_p, _pi32, _pi32], ctypes.c_int),
     "kvpool_ensure": ([_p, _pi32, _pi32, _i32, _i32], ctypes.c_int),
     "kvpool_release": ([_p, _pi32, _pi32], ctypes.c_int),
+    "kvpool_share": ([_p, _i32, _pi32], ctypes.c_int),
+    "kvpool_refcount": ([_p, _i32, _pi32], ctypes.c_int),
+    "kvpool_fork": ([_p, _pi32, _i32, _pi32, _pi32, _i32, _i32], ctypes.c_int),
+    "kvpool_cow": ([_p, _pi32, _i32, _i32, _i32, _pi32, _pi32, _i32, _pi32], ctypes.c_int),
+    "kv_copy_blocks": ([_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p], ctypes.c_int),
     "kv_append": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p],
                   ctypes.c_int),
     "paged_attn_split_tokens": ([_i32, _i32, _i32, _i32, _i32, _pi32], ctypes.c_int),
@@ -156,6 +161,35 @@ class KVPool:
         _check("kvpool_release", load_library().kvpool_release(
             self._h, _i32_ptr(table, s * stride), _i32_ptr(held, s)))
 
+    def kvpool_share(self, ids) -> None:
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        _check("kvpool_share", load_library().kvpool_share(self._h, int(len(ids)), _i32_ptr(ids)))
+
+    def kvpool_refcount(self, block: int) -> int:
+        n = _i32()
+        _check("kvpool_refcount", load_library().kvpool_refcount(self._h, int(block), ctypes.byref(n)))
+        return n.value
+
+    def kvpool_fork(self, table: np.ndarray, held: np.ndarray, src: int, dst: int, length: int) -> None:
+        """Row ``dst`` (empty) shares the blocks of row ``src`` covering ``length`` tokens."""
+        stride = table.shape[1]
+        _check("kvpool_fork", load_library().kvpool_fork(
+            self._h, _i32_ptr(table, src * stride), int(held[src]), _i32_ptr(table, dst * stride),
+            _i32_ptr(held, dst), int(stride), int(length)))
+
+    def kvpool_cow(self, table: np.ndarray, held: np.ndarray, s: int, start: int, count: int):
+        """Unshare row ``s``'s blocks covering ``[start, start + count)``; returns the
+        ``(src, dst)`` id arrays of the block copies the caller must make."""
+        stride = table.shape[1]
+        cap = -(-int(count) // self.block_size) + 1
+        src = np.zeros(cap, dtype=np.int32)
+        dst = np.zeros(cap, dtype=np.int32)
+        n = _i32()
+        _check("kvpool_cow", load_library().kvpool_cow(
+            self._h, _i32_ptr(table, s * stride), int(held[s]), int(start), int(count), _i32_ptr(src),
+            _i32_ptr(dst), int(cap), ctypes.byref(n)))
+        return src[:n.value], dst[:n.value]
+
 
 # --------------------------------------------------------------------------
 # Device entry points
@@ -199,6 +233,15 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, start_pos, new_start,
         int(block_table.shape[1]), _ptr(start_pos), _ptr(new_start), int(start_pos.shape[0]),
         int(k_new.shape[0]), int(num_blocks), int(n_kv), int(d), int(bs), _dtype_code(k_cache),
         _stream(stream)))
+
+
+def kv_copy_blocks(k_cache, v_cache, src_ids, dst_ids, stream=None):
+    """Copy whole blocks ``src_ids[i] -> dst_ids[i]`` (device int32) in both pools."""
+    _dev(k_cache, v_cache, src_ids, dst_ids)
+    num_blocks, n_kv, bs, d = k_cache.shape
+    _check("kv_copy_blocks", load_library().kv_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(src_ids), _ptr(dst_ids), int(src_ids.shape[0]), int(num_blocks),
+        int(n_kv), int(d), int(bs), _dtype_code(k_cache), _stream(stream)))
 
 
 def paged_attn_split_tokens(num_q_rows, n_kv, block_size, max_seq_len, requested=0) -> int:

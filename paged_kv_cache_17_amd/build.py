@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["kvpool.cpp", "api.cpp", "kv_append.hip", "attn_generic.hip", "attn_merge.hip",
+SOURCES = ["kvpool.cpp", "api.cpp", "kv_append.hip", "kv_copy.hip", "attn_generic.hip", "attn_merge.hip",
            "decode_bf16.hip", "decode_balanced.hip",
            "chunk_mfma.hip"]
 

@@ -46,6 +46,21 @@ class PagedKVCache:
     def release(self, s: int) -> None:
         self.pool.kvpool_release(self.table, self.held, s)
 
+    def fork(self, src: int, dst: int, length: int) -> None:
+        """Row ``dst`` (empty) shares row ``src``'s blocks for its first ``length`` tokens."""
+        self.pool.kvpool_fork(self.table, self.held, src, dst, length)
+
+    def unshare_for_write(self, s: int, start: int, count: int, stream=None) -> int:
+        """Copy-on-write before appending ``count`` tokens at ``start`` to row ``s``:
+        shared blocks in that range are replaced by private copies (host table
+        updated, contents copied on the device). Returns the number of copies;
+        call ``upload_table`` before the next device call that reads the table."""
+        src, dst = self.pool.kvpool_cow(self.table, self.held, s, start, count)
+        if len(src):
+            B.kv_copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(src).to(self.device),
+                             torch.from_numpy(dst).to(self.device), stream=stream)
+        return len(src)
+
     def upload_table(self, stream=None) -> None:
         self.table_dev.copy_(torch.from_numpy(self.table), non_blocking=False)
 

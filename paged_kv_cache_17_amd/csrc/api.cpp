@@ -175,6 +175,7 @@ extern "C" const char* pkv_strerror(int status) {
         case PKV_ERR_TABLE_FULL: return "block table row full";
         case PKV_ERR_HIP: return "HIP launch error";
         case PKV_ERR_NO_MEMORY: return "out of host memory";
+        case PKV_ERR_INVALID_BLOCK: return "invalid block (out of range, not allocated, or repeated)";
         default: return "unknown status";
     }
 }
@@ -203,6 +204,20 @@ extern "C" int kv_append(void* k_cache, void* v_cache, const void* k_new, const 
     hipError_t e = pkv::launch_kv_append(k_cache, v_cache, k_new, v_new, block_table, table_stride,
                                          start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
                                          head_dim * eb, block_size, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
+                              int32_t n, int32_t num_blocks, int32_t n_kv, int32_t head_dim,
+                              int32_t block_size, int32_t dtype, void* stream) {
+    if (n < 0 || num_blocks < 1 || n_kv < 1 || head_dim < 1 || block_size < 1) return PKV_ERR_INVALID_ARGUMENT;
+    const int eb = elem_bytes(dtype);
+    if (!eb) return PKV_ERR_INVALID_ARGUMENT;
+    if (n == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !src_ids || !dst_ids) return PKV_ERR_NULL_POINTER;
+    const size_t block_bytes = static_cast<size_t>(n_kv) * block_size * head_dim * eb;
+    const hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, src_ids, dst_ids, n, num_blocks, block_bytes,
+                                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -50,6 +50,11 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
                             const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
                             int n_kv, int row_bytes, int block_size, hipStream_t stream);
 
+// Whole-block copies (src_ids[i] -> dst_ids[i], both pools) for
+// copy-on-write; block_bytes = n_kv * block_size * head_dim * element size.
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
+                              int n, int num_blocks, size_t block_bytes, hipStream_t stream);
+
 // Split pass for any shape/dtype (one wave per row, head and key range).
 hipError_t launch_split_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
 

@@ -9,6 +9,14 @@
 // The free set is a bitmap over *ranks* (rank i <-> id order[i]), so the
 // next block to hand out is the lowest set bit: O(num_blocks / 64) per
 // call in the worst case, no allocation after creation.
+//
+// Blocks are reference counted (serving tutorial section 4.2: physical
+// blocks shared between a common prefix or beam branches through their
+// tables; section 1.7: a shared block goes back to the allocator only when
+// its last holder releases it). A block is free exactly when its count is
+// 0. A shared block that is about to be written is replaced, in the writing
+// sequence's row only, by a fresh copy (copy-on-write, section 4.2).
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -25,6 +33,7 @@ struct kvpool {
     std::vector<int32_t> order;    // rank -> id
     std::vector<int32_t> rank;     // id -> rank
     std::vector<uint64_t> free_bits;  // bit r set <=> rank r is free
+    std::vector<int32_t> refs;     // id -> holders (0 <=> free)
 };
 
 namespace {
@@ -62,6 +71,7 @@ extern "C" int kvpool_create(int32_t num_blocks, int32_t block_size,
             p->order[r] = id;
             p->rank[id] = r;
         }
+        p->refs.assign(num_blocks, 0);
         p->free_bits.assign((num_blocks + 63) / 64, 0);
         for (int32_t r = 0; r < num_blocks; ++r) set_free(p, r);
         p->num_free = num_blocks;
@@ -93,6 +103,7 @@ extern "C" int kvpool_alloc(kvpool_t* p, int32_t n, int32_t* out_ids) {
             int32_t r = w * 64 + __builtin_ctzll(bits);
             bits &= bits - 1;
             clear_free(p, r);
+            p->refs[p->order[r]] = 1;
             out_ids[got++] = p->order[r];
         }
         if (p->free_bits[w] == 0) p->scan_from = w + 1;
@@ -101,30 +112,59 @@ extern "C" int kvpool_alloc(kvpool_t* p, int32_t n, int32_t* out_ids) {
     return PKV_OK;
 }
 
+namespace {
+
+// True when ids[0..n) are in range, allocated and pairwise distinct. Uses
+// the free bits of the listed ranks as scratch marks and restores them.
+bool valid_held_ids(kvpool* p, int32_t n, const int32_t* ids) {
+    int32_t i = 0;
+    for (; i < n; ++i) {
+        const int32_t id = ids[i];
+        if (id < 0 || id >= p->num_blocks) break;
+        const int32_t r = p->rank[id];
+        if (is_free(p, r)) break;   // free, or listed earlier in this call
+        set_free(p, r);
+    }
+    for (int32_t j = 0; j < i; ++j) clear_free(p, p->rank[ids[j]]);
+    return i == n;
+}
+
+}  // namespace
+
 extern "C" int kvpool_free(kvpool_t* p, int32_t n, const int32_t* ids) {
     if (!p) return PKV_ERR_NULL_POINTER;
     if (n < 0) return PKV_ERR_INVALID_ARGUMENT;
     if (n == 0) return PKV_OK;
     if (!ids) return PKV_ERR_NULL_POINTER;
-    // Validate everything first, marking as we go so a repeated id is seen;
-    // undo the marks on failure so the call has no effect.
-    int32_t i = 0;
-    for (; i < n; ++i) {
-        int32_t id = ids[i];
-        if (id < 0 || id >= p->num_blocks) break;
-        int32_t r = p->rank[id];
-        if (is_free(p, r)) break;
-        set_free(p, r);
-    }
-    if (i < n) {
-        for (int32_t j = 0; j < i; ++j) clear_free(p, p->rank[ids[j]]);
-        return PKV_ERR_INVALID_FREE;
-    }
+    // Validate everything first so a failing call has no effect.
+    if (!valid_held_ids(p, n, ids)) return PKV_ERR_INVALID_FREE;
+    int32_t freed = 0;
     for (int32_t j = 0; j < n; ++j) {
-        int32_t w = p->rank[ids[j]] >> 6;
-        if (w < p->scan_from) p->scan_from = w;
+        const int32_t id = ids[j];
+        if (--p->refs[id] > 0) continue;   // other holders keep it
+        const int32_t r = p->rank[id];
+        set_free(p, r);
+        if ((r >> 6) < p->scan_from) p->scan_from = r >> 6;
+        ++freed;
     }
-    p->num_free += n;
+    p->num_free += freed;
+    return PKV_OK;
+}
+
+extern "C" int kvpool_share(kvpool_t* p, int32_t n, const int32_t* ids) {
+    if (!p) return PKV_ERR_NULL_POINTER;
+    if (n < 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (n == 0) return PKV_OK;
+    if (!ids) return PKV_ERR_NULL_POINTER;
+    if (!valid_held_ids(p, n, ids)) return PKV_ERR_INVALID_BLOCK;
+    for (int32_t j = 0; j < n; ++j) ++p->refs[ids[j]];
+    return PKV_OK;
+}
+
+extern "C" int kvpool_refcount(const kvpool_t* p, int32_t id, int32_t* out) {
+    if (!p || !out) return PKV_ERR_NULL_POINTER;
+    if (id < 0 || id >= p->num_blocks) return PKV_ERR_INVALID_ARGUMENT;
+    *out = p->refs[id];
     return PKV_OK;
 }
 
@@ -166,5 +206,60 @@ extern "C" int kvpool_release(kvpool_t* p, int32_t* row, int32_t* num_held) {
     if (rc != PKV_OK) return rc;
     for (int32_t i = 0; i < *num_held; ++i) row[i] = -1;
     *num_held = 0;
+    return PKV_OK;
+}
+
+extern "C" int kvpool_fork(kvpool_t* p, const int32_t* src_row, int32_t src_held, int32_t* dst_row,
+                           int32_t* dst_held, int32_t row_capacity, int32_t length) {
+    if (!p || !dst_held) return PKV_ERR_NULL_POINTER;
+    if (length < 0 || src_held < 0 || row_capacity < 0 || *dst_held != 0) return PKV_ERR_INVALID_ARGUMENT;
+    const int64_t need = (static_cast<int64_t>(length) + p->block_size - 1) / p->block_size;
+    if (need > src_held) return PKV_ERR_INVALID_ARGUMENT;
+    if (need > row_capacity) return PKV_ERR_TABLE_FULL;
+    if (need == 0) return PKV_OK;
+    if (!src_row || !dst_row) return PKV_ERR_NULL_POINTER;
+    const int32_t n = static_cast<int32_t>(need);
+    const int rc = kvpool_share(p, n, src_row);
+    if (rc != PKV_OK) return rc;
+    for (int32_t i = 0; i < n; ++i) dst_row[i] = src_row[i];
+    *dst_held = n;
+    return PKV_OK;
+}
+
+extern "C" int kvpool_cow(kvpool_t* p, int32_t* row, int32_t num_held, int32_t start, int32_t count,
+                          int32_t* copy_src, int32_t* copy_dst, int32_t capacity, int32_t* num_copies) {
+    if (!p || !num_copies) return PKV_ERR_NULL_POINTER;
+    *num_copies = 0;
+    if (num_held < 0 || start < 0 || count < 0 || capacity < 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (count == 0 || num_held == 0) return PKV_OK;
+    if (!row) return PKV_ERR_NULL_POINTER;
+    const int64_t first = start / p->block_size;
+    const int64_t last = std::min<int64_t>((static_cast<int64_t>(start) + count - 1) / p->block_size,
+                                           static_cast<int64_t>(num_held) - 1);
+    // Check first: every id in range and allocated, enough copy slots and
+    // enough free blocks; nothing changes on failure.
+    int32_t shared = 0;
+    for (int64_t i = first; i <= last; ++i) {
+        const int32_t id = row[i];
+        if (id < 0 || id >= p->num_blocks || p->refs[id] < 1) return PKV_ERR_INVALID_BLOCK;
+        if (p->refs[id] > 1) ++shared;
+    }
+    if (shared == 0) return PKV_OK;
+    if (!copy_src || !copy_dst) return PKV_ERR_NULL_POINTER;
+    if (shared > capacity) return PKV_ERR_INVALID_ARGUMENT;
+    if (shared > p->num_free) return PKV_ERR_OUT_OF_BLOCKS;
+    int32_t c = 0;
+    for (int64_t i = first; i <= last; ++i) {
+        const int32_t id = row[i];
+        if (p->refs[id] < 2) continue;
+        int32_t fresh = -1;
+        kvpool_alloc(p, 1, &fresh);
+        --p->refs[id];
+        copy_src[c] = id;
+        copy_dst[c] = fresh;
+        row[i] = fresh;
+        ++c;
+    }
+    *num_copies = c;
     return PKV_OK;
 }

@@ -113,3 +113,56 @@ def check_lse(got, ref, dtype, where=""):
     d = float(np.abs(got - ref).max())
     assert d <= TOL_LSE[dtype], f"lse error {d:.3e} {where}"
     return d
+
+
+def build_gpu_fork_cache(fw, fill_nan=True, share=True):
+    """Forked sequences through the library: prompts written once (rows
+    0..P-1), each forked into its branches (rows P..P+n*P-1), the prompt rows
+    released, then for every branch copy-on-write of the shared tail block
+    and its own tokens appended. Returns (cache, number of block copies).
+    With share=False every branch row instead gets a private copy of its
+    prompt (the no-sharing baseline)."""
+    import paged_kv_cache_17_amd as pkv
+    NP, NB = fw.num_prompts, fw.num_branches
+    c = pkv.PagedKVCache(fw.num_blocks, fw.n_kv, fw.head_dim, fw.block_size, torch_dtype(fw.dtype), NP + NB,
+                         fw.table_stride, alloc_order=fw.alloc_order, fill_nan=fill_nan,
+                         poison_workspace=fill_nan)
+    if not share:
+        lens = fw.branch_lens()
+        for b in range(NB):
+            c.ensure(NP + b, int(lens[b]))
+        c.upload_table()
+        counts = np.concatenate([np.zeros(NP, dtype=np.int64), lens])
+        starts = np.zeros(NP + NB + 1, dtype=np.int64)
+        np.cumsum(counts, out=starts[1:])
+        ks = np.concatenate([np.concatenate([fw.prompt_k[fw.prompt_of(b)], fw.own_k[b]]) for b in range(NB)])
+        vs = np.concatenate([np.concatenate([fw.prompt_v[fw.prompt_of(b)], fw.own_v[b]]) for b in range(NB)])
+        c.append(raw_to_torch(ks, fw.dtype), raw_to_torch(vs, fw.dtype), i32(np.zeros(NP + NB)), i32(starts))
+        torch.cuda.synchronize()
+        return c, 0
+    for p, P in enumerate(fw.prompt_lens):
+        c.ensure(p, int(P))
+    c.upload_table()
+    counts = np.concatenate([fw.prompt_lens, np.zeros(NB, dtype=np.int64)])
+    starts = np.zeros(NP + NB + 1, dtype=np.int64)
+    np.cumsum(counts, out=starts[1:])
+    c.append(raw_to_torch(np.concatenate(fw.prompt_k), fw.dtype), raw_to_torch(np.concatenate(fw.prompt_v), fw.dtype),
+             i32(np.zeros(NP + NB)), i32(starts))
+    for b in range(NB):
+        c.fork(fw.prompt_of(b), NP + b, int(fw.prompt_lens[fw.prompt_of(b)]))
+    for p in range(NP):
+        c.release(p)
+    copies = 0
+    for b in range(NB):
+        P, g = int(fw.prompt_lens[fw.prompt_of(b)]), int(fw.own_lens[b])
+        copies += c.unshare_for_write(NP + b, P, g)
+        c.ensure(NP + b, P + g)
+    c.upload_table()
+    counts = np.concatenate([np.zeros(NP, dtype=np.int64), fw.own_lens])
+    starts = np.zeros(NP + NB + 1, dtype=np.int64)
+    np.cumsum(counts, out=starts[1:])
+    pos = np.concatenate([np.zeros(NP, dtype=np.int64), [fw.prompt_lens[fw.prompt_of(b)] for b in range(NB)]])
+    c.append(raw_to_torch(np.concatenate(fw.own_k), fw.dtype), raw_to_torch(np.concatenate(fw.own_v), fw.dtype),
+             i32(pos), i32(starts))
+    torch.cuda.synchronize()
+    return c, copies

@@ -1,0 +1,146 @@
+"""Host checks of the library's shared blocks against the oracle (no GPU).
+
+The C pool's reference counts, forks and copy-on-write must reproduce the
+oracle's allocator exactly: the same ids in the same rows, the same counts,
+the same free list, the same copy pairs, and errors that change nothing.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_17_amd as pkv
+
+
+def _state(pool, table, held, n):
+    return (table.copy(), held.copy(), pool.kvpool_free_ids().tolist(),
+            [pool.kvpool_refcount(b) for b in range(n)])
+
+
+def _script(seed):
+    rng = random.Random(seed)
+    n, B = rng.choice([(12, 4), (40, 2), (70, 16)])
+    S, cap = 6, 12
+    order = np.array(rng.sample(range(n), n), dtype=np.int32)
+    pool = pkv.KVPool(n, B, order)
+    table = np.full((S, cap), -1, dtype=np.int32)
+    held = np.zeros(S, dtype=np.int32)
+    ora = oracle.BlockAllocator(n, order)
+    rows = [oracle.SequenceBlocks(B) for _ in range(S)]
+    lens = [0] * S
+    for _ in range(150):
+        op = rng.random()
+        s = rng.randrange(S)
+        before = _state(pool, table, held, n)
+        if op < 0.3:
+            L = min(lens[s] + rng.randint(0, 3 * B), cap * B)
+            try:
+                rows[s].ensure(ora, L)
+                ok = True
+            except oracle.OutOfBlocks:
+                ok = False
+            if ok:
+                pool.kvpool_ensure(table, held, s, L)
+                lens[s] = max(lens[s], L)
+            else:
+                with pytest.raises(pkv.PagedKVError) as ei:
+                    pool.kvpool_ensure(table, held, s, L)
+                assert ei.value.status == -4
+        elif op < 0.45:
+            t = rng.randrange(S)
+            if t != s and held[s] == 0 and held[t] > 0:
+                L = rng.randint(0, lens[t])
+                rows[s].fork(ora, rows[t], L)
+                pool.kvpool_fork(table, held, t, s, L)
+                lens[s] = L
+            elif held[s] > 0 and held[t] > 0:
+                with pytest.raises(pkv.PagedKVError) as ei:      # destination not empty
+                    pool.kvpool_fork(table, held, t, s, 1)
+                assert ei.value.status == -2
+        elif op < 0.62:
+            if lens[s]:
+                start = rng.randint(0, lens[s])
+                count = rng.randint(1, 2 * B)
+                try:
+                    want = rows[s].cow(ora, start, count)
+                    ok = True
+                except oracle.OutOfBlocks:
+                    ok = False
+                if ok:
+                    src, dst = pool.kvpool_cow(table, held, s, start, count)
+                    assert list(zip(src.tolist(), dst.tolist())) == want
+                else:
+                    with pytest.raises(pkv.PagedKVError) as ei:
+                        pool.kvpool_cow(table, held, s, start, count)
+                    assert ei.value.status == -4
+        elif op < 0.75:
+            rows[s].release(ora)
+            pool.kvpool_release(table, held, s)
+            pool.kvpool_release(table, held, s)           # idempotent
+            lens[s] = 0
+        elif op < 0.85:
+            # share, then free, a block some row holds (net zero)
+            if held[s]:
+                b = int(table[s, rng.randrange(held[s])])
+                pool.kvpool_share([b])
+                ora.share([b])
+                assert pool.kvpool_refcount(b) == ora.refcount(b)
+                pool.kvpool_free([b])
+                ora.free([b])
+        else:
+            free_ids = ora.free_ids()
+            bad = rng.choice([[n], [-1], free_ids[:1] or [n + 1],
+                              [int(table[s, 0])] * 2 if held[s] else [n]])
+            with pytest.raises(pkv.PagedKVError) as ei:
+                pool.kvpool_share(bad)
+            assert ei.value.status == -10
+            with pytest.raises(pkv.PagedKVError) as ei:
+                pool.kvpool_free(bad)
+            assert ei.value.status == -5
+            assert _state(pool, table, held, n)[2:] == before[2:]
+        for r in range(S):
+            assert table[r, :held[r]].tolist() == rows[r].blocks
+            assert (table[r, held[r]:] == -1).all()
+        assert pool.kvpool_free_ids().tolist() == ora.free_ids()
+        assert [pool.kvpool_refcount(b) for b in range(n)] == [ora.refcount(b) for b in range(n)]
+    for r in range(S):
+        pool.kvpool_release(table, held, r)
+    assert pool.kvpool_num_free() == n
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_sharing_scripts_match_the_oracle(seed):
+    _script(seed)
+
+
+def test_demo_d08_through_the_library():
+    pool = pkv.KVPool(16, 4)
+    table = np.full((2, 4), -1, dtype=np.int32)
+    held = np.zeros(2, dtype=np.int32)
+    pool.kvpool_ensure(table, held, 0, 6)
+    pool.kvpool_fork(table, held, 0, 1, 4)
+    pool.kvpool_ensure(table, held, 1, 7)
+    used = {int(b) for r in range(2) for b in table[r, :held[r]]}
+    assert len(used) == 3 and 16 - pool.kvpool_num_free() == 3
+    assert pool.kvpool_refcount(int(table[0, 0])) == 2
+
+
+def test_cow_errors_change_nothing():
+    pool = pkv.KVPool(3, 4)
+    table = np.full((3, 2), -1, dtype=np.int32)
+    held = np.zeros(3, dtype=np.int32)
+    pool.kvpool_ensure(table, held, 0, 8)          # 2 blocks, 1 free
+    pool.kvpool_fork(table, held, 0, 1, 8)
+    pool.kvpool_fork(table, held, 0, 2, 8)
+    before = (table.copy(), pool.kvpool_free_ids().tolist())
+    with pytest.raises(pkv.PagedKVError) as ei:    # needs 2 fresh blocks, 1 free
+        pool.kvpool_cow(table, held, 1, 0, 8)
+    assert ei.value.status == -4
+    assert np.array_equal(table, before[0]) and pool.kvpool_free_ids().tolist() == before[1]
+    src, dst = pool.kvpool_cow(table, held, 1, 4, 1)   # one block: fits
+    assert src.tolist() == [int(table[0, 1])] and dst.tolist() == [int(table[1, 1])]
+    assert pool.kvpool_refcount(int(table[0, 1])) == 2
+    with pytest.raises(pkv.PagedKVError) as ei:    # fork past the source's blocks
+        pool.kvpool_fork(table, np.zeros(3, dtype=np.int32), 0, 1, 9)
+    assert ei.value.status == -2

@@ -15,3 +15,4 @@ from .synth import (  # noqa: F401
     f32_to_bf16_bits,
     poison_bits,
 )
+from .forks import ForkWorkload, best_of_n_workload, build_fork_workload  # noqa: F401
