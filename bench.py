@@ -231,12 +231,30 @@ def bench_bestof(args):
         torch.cuda.synchronize()
         kern = float(np.mean([b.elapsed_time(a) for b, a in evs]))
         used = fw.num_blocks - caches[0].pool.kvpool_num_free()
+        copy = copy_timing(caches[0]) if share else None
         del caches
         torch.cuda.empty_cache()
-        return ms, kern, used
+        return ms, kern, used, copy
 
-    ms_s, kern_s, used_s = run(True)
-    ms_u, kern_u, used_u = run(False)
+    def copy_timing(c, n=512, reps=20):
+        # copy-on-write's data side: n whole blocks (both pools) onto free blocks
+        held = sorted({int(x) for x in c.table[NP:].ravel() if x >= 0})[:n]
+        free = c.pool.kvpool_free_ids()[:len(held)]
+        src, dst = i32(held), i32(free)
+        pkv.kv_copy_blocks(c.k_cache, c.v_cache, src, dst, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            pkv.kv_copy_blocks(c.k_cache, c.v_cache, src, dst, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = len(held) * fw.n_kv * fw.block_size * fw.head_dim * 2 * 2 * 2   # K and V, read and write
+        return {"blocks": len(held), "bytes_moved": nbytes, "ms": ms, "gbps": nbytes / (ms * 1e-3) / 1e9}
+
+    ms_s, kern_s, used_s, copy = run(True)
+    ms_u, kern_u, used_u, _ = run(False)
     logical = fw.logical_kv_bytes()
     line = {
         "metric": METRIC, "value": NB * args.steps / (ms_s * args.steps * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -255,6 +273,7 @@ def bench_bestof(args):
         "unshared": {"value": NB / (ms_u * 1e-3), "ms_per_step": ms_u, "avg_launch_ms": kern_u,
                      "kv_gbps": logical / (kern_u * 1e-3) / 1e9},
         "sharing_speedup": ms_u / ms_s,
+        "cow_copy": copy,
     }
     print(json.dumps(line), flush=True)
 

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     PKV_F32,
     PagedKVError,
     kv_append,
+    kv_copy_blocks,
     load_library,
     paged_attn_chunk,
     paged_attn_decode,
