@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     p.add_argument("--copies", type=int, default=2, help="independent cache copies used in turn")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--kv", choices=["bf16", "int8"], default="bf16",
+                   help="K/V format of the cache: bf16, or 8-bit codes with one fp32 scale per token and kv head")
     p.add_argument("--bestof", action="store_true",
                    help="time the best-of-8 decode step over shared prompts (and the same step without sharing)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -119,7 +121,7 @@ def _attend_some(seqs):
         return time.perf_counter() - t0
 
 
-def cpu_baseline(wl, budget_s=10.0):
+def cpu_baseline(wl, budget_s=10.0, quant=False):
     """Time the float64 oracle on the same decode step (gather through its own
     pool + widening + attention, all sequences), each setting repeated until
     about ``budget_s`` seconds of work; reports the median step:
@@ -135,7 +137,7 @@ def cpu_baseline(wl, budget_s=10.0):
     import oracle
     from threadpoolctl import threadpool_limits
     global _ORACLE_CACHE
-    _ORACLE_CACHE = oracle.build_cache(wl, fill=0)
+    _ORACLE_CACHE = oracle.build_quant_cache(wl) if quant else oracle.build_cache(wl, fill=0)
     tokens = int(wl.new_lens.sum())
     seqs = list(range(wl.num_seqs))
 
@@ -301,10 +303,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.load_library()
     wl = config_workload(args.config)
-    caches = [build_gpu_cache(wl, fill_nan=False) for _ in range(args.copies)]
+    quant = args.kv == "int8"
+    caches = [build_gpu_cache(wl, fill_nan=False, quantized=quant) for _ in range(args.copies)]
     S = wl.num_seqs
     nd = int(np.argmax(wl.new_lens != 1)) if (wl.new_lens != 1).any() else S   # decode rows come first
     assert (wl.new_lens[:nd] == 1).all() and (wl.new_lens[nd:] > 1).all()
+    if quant and (nd < S or args.split):
+        sys.exit("the 8-bit cache has decode rows only, with the balanced partition")
     q = raw_to_torch(wl.q, wl.dtype)
     kn, vn = wl.packed_new_kv()
     k_new, v_new = raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype)
@@ -332,8 +337,12 @@ def main():
         if nd:
             if ev_dec is not None:
                 pkv.pkv_set_profile_events(*ev_dec)
-            pkv.paged_attn_decode(out[:qd], None, q_dec, c.k_cache, c.v_cache, c.table_dev[:nd], seq_lens[:nd],
-                                  max_dec, wl.scale, ws[j][0], split_tokens=split, stream=stream)
+            if quant:
+                pkv.paged_attn_decode_q8(out[:qd], None, q_dec, c.k_cache, c.v_cache, c.k_scale, c.v_scale,
+                                         c.table_dev[:nd], seq_lens[:nd], max_dec, wl.scale, ws[j][0], stream=stream)
+            else:
+                pkv.paged_attn_decode(out[:qd], None, q_dec, c.k_cache, c.v_cache, c.table_dev[:nd], seq_lens[:nd],
+                                      max_dec, wl.scale, ws[j][0], split_tokens=split, stream=stream)
         if nd < S:
             pkv.pkv_set_profile_events(*ev_chk) if ev_chk is not None else pkv.pkv_set_profile_events(None, None)
             pkv.paged_attn_chunk(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, c.table_dev[nd:],
@@ -377,9 +386,11 @@ def main():
     tokens = int(wl.new_lens.sum())
 
     # Algorithmic work: decode rows read every cached K/V byte once
-    # (2 x n_kv x d x 2 B per key); chunk rows do 4 x n_q x d FLOPs per
+    # (2 x n_kv x d x 2 B per key for bf16; 2 x n_kv x (d + 4) B for 8-bit
+    # codes plus their fp32 scale); chunk rows do 4 x n_q x d FLOPs per
     # allowed (query, key) pair (scores and weighted sum).
-    dec_bytes = int(wl.seq_lens[:nd].sum()) * wl.n_kv * wl.head_dim * 2 * 2
+    key_bytes = 2 * wl.n_kv * ((wl.head_dim + 4) if quant else wl.head_dim * 2)
+    dec_bytes = int(wl.seq_lens[:nd].sum()) * key_bytes
     pairs_allowed = sum(int(C) * int(P) + int(C) * (int(C) + 1) // 2
                         for P, C in zip(wl.hist_lens[nd:], wl.new_lens[nd:]))
     chk_flops = 4 * wl.n_q * wl.head_dim * pairs_allowed
@@ -394,22 +405,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "int8 K/V, bf16 q/out, fp32 accumulate" if quant else "bf16",
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config], "num_seqs": S, "decode_seqs": nd, "chunk_seqs": S - nd,
+        "config": {"workload": CONFIG_NAMES[args.config] + ("-kv-int8" if quant else ""), "num_seqs": S, "decode_seqs": nd, "chunk_seqs": S - nd,
                    "n_q": wl.n_q, "n_kv": wl.n_kv, "head_dim": wl.head_dim, "block_size": wl.block_size,
-                   "context_tokens": int(wl.seq_lens.sum()), "kv_bytes": wl.ideal_kv_bytes(),
+                   "context_tokens": int(wl.seq_lens.sum()),
+                   "kv_bytes": int(wl.seq_lens.sum()) * key_bytes if quant else wl.ideal_kv_bytes(),
                    "cache_copies": len(caches),
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
     }
     if nd:
         kern_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_dec]))
         achieved = dec_bytes / (kern_avg * 1e-3) / 1e9
-        line["step_kv_gbps"] = wl.ideal_kv_bytes() / (ms_step * 1e-3) / 1e9
+        line["step_kv_gbps"] = line["config"]["kv_bytes"] / (ms_step * 1e-3) / 1e9
         line["step_kv_frac_of_peak"] = line["step_kv_gbps"] / PEAK_HBM_GBPS
         line["roofline"] = {"kernel": "decode split pass", "bound": "hbm", "achieved": achieved,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                            "traffic": measured_traffic(CONFIG_NAMES[args.config]), "avg_launch_ms": kern_avg,
+                            "traffic": None if quant else measured_traffic(CONFIG_NAMES[args.config]),
+                            "avg_launch_ms": kern_avg,
                             "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash("decode")}
     if nd < S:
         chk_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_chk]))
@@ -423,7 +436,7 @@ def main():
         if not nd:
             line["roofline"] = line.pop("chunk_roofline")
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline"] = cpu_baseline(wl, quant=quant)
     print(json.dumps(line), flush=True)
 
 

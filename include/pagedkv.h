@@ -302,6 +302,59 @@ int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_star
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * 8-bit K/V (quantised cache).
+ *
+ * Source: chapter 5 section 4 (post-training quantisation, symmetric
+ * absmax onto the integer grid [-q_max, q_max], q_max = 2^(b-1) - 1 = 127
+ * for 8 bits: s = max|w| / q_max, w_q = clamp(round(w / s)), the value is
+ * read back as s * w_q; group-wise: one scale per group of consecutive
+ * elements, group sizes 32/64/128), applied here to the cache with one
+ * group per (token, kv head) - the head_dim values a token writes for one
+ * kv head; serving tutorial section 7 (KV-cache quantisation is a design
+ * point of its own: per-token granularity, capacity and bandwidth) and
+ * section 4.1 (scales are storage beyond the ideal K/V payload); the lab
+ * page notes it did not run a quantised KV cache.
+ *
+ * Layout: k_codes, v_codes int8 [num_blocks][n_kv][block_size][head_dim]
+ * (two's complement codes in [-127, 127]); k_scale, v_scale float
+ * [num_blocks][n_kv][block_size], the scale of each (block, kv head, slot).
+ * Storage per token and kv head: head_dim + 4 bytes for K and the same for
+ * V (264 bytes at head_dim 128, against 512 for bf16).
+ * ==================================================================== */
+
+/* kv_append_q8 - quantise new tokens' K/V and write them through the table
+ * (kv_append's addressing; its argument meanings). For every new token and
+ * kv head, separately for K and V: s = max(max_i |x_i|, 1e-8) / 127 and
+ * code_i = clamp(rint(x_i / s), -127, 127), computed in fp32 with correctly
+ * rounded division and ties-to-even rounding; the codes go to the slot's
+ * row, s to its scale. new_dtype: PKV_BF16 or PKV_F32 (k_new, v_new
+ * [total_new][n_kv][head_dim]); inputs must be finite. Any head_dim and
+ * block_size. Errors: NULL_POINTER, INVALID_ARGUMENT, HIP. */
+int kv_append_q8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                 const void* k_new, const void* v_new, int32_t new_dtype,
+                 const int32_t* block_table, int32_t table_stride,
+                 const int32_t* start_pos, const int32_t* new_start,
+                 int32_t num_seqs, int32_t total_new, int32_t num_blocks,
+                 int32_t n_kv, int32_t head_dim, int32_t block_size, void* stream);
+
+/* paged_attn_decode_q8 - paged_attn_decode over an 8-bit cache: keys and
+ * values are read as s * code; q and out are bf16; fp32 accumulation.
+ * Supported: head_dim 128, block_size 16, n_q / n_kv in {1, 2, 4, 8},
+ * 1..8192 sequences (else UNSUPPORTED); q and out 16-byte aligned, code
+ * pools 8-byte aligned (else INVALID_ARGUMENT). The workspace is sized by
+ * paged_attn_workspace_size with split_tokens 0 (the size covers both the
+ * bf16 and the 8-bit pass). Invalid lengths or table entries give NaN rows
+ * as in paged_attn_decode. Other arguments as paged_attn_decode. */
+int paged_attn_decode_q8(void* out, float* lse, const void* q,
+                         const void* k_codes, const void* v_codes,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, int32_t table_stride,
+                         const int32_t* seq_lens,
+                         int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks,
+                         int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * Profiling hook (not part of the computation): when both events are
  * non-NULL, paged_attn_decode launches its first-pass (split) kernel and
  * paged_attn_chunk its matrix-core kernel so that the kernel's own dispatch

@@ -12,6 +12,7 @@ from .paged_attention import (  # noqa: F401
     copy_blocks,
     OracleCache,
     OutOfBlocks,
+    QuantOracleCache,
     SequenceBlocks,
     append,
     attention,
@@ -19,10 +20,14 @@ from .paged_attention import (  # noqa: F401
     bf16_bits_to_f64,
     block_alloc_slots,
     build_cache,
+    build_quant_cache,
     build_tables,
     contiguous_attend,
+    dequantize,
     gather,
     kv_bytes_per_token,
     paged_attention_all,
+    quant_bytes,
+    quantize_absmax,
     widen,
 )

@@ -467,6 +467,109 @@ def contiguous_attend(wl, s: int, heads=None):
     return _attend_rows(wl, s, K, V, heads)
 
 
+# --------------------------------------------------------------------------
+# 8-bit cache (symmetric absmax quantisation, one scale per token and kv head)
+# --------------------------------------------------------------------------
+
+QUANT_POISON_CODE = np.int8(-128)   # outside the code range: marks unwritten slots
+
+
+def quantize_absmax(x, q_max: int = 127, eps: float = 1e-8):
+    """Symmetric absmax quantisation of each row (last axis) of ``x``.
+
+    Chapter 5, section 4: scale ``s = max|x| / q_max`` (the exercise clamps
+    ``max|x|`` below at 1e-8), code ``clamp(round(x / s), -q_max, q_max)``,
+    value read back as ``s * code``; group-wise form with one scale per group
+    of consecutive elements - here a row is one token's head_dim values for
+    one kv head. The scale and the codes are computed in float32 (the
+    exercise's precision), rounding ties to even, so the integer decision is
+    the one a float32 implementation with correctly rounded division makes.
+    Returns ``(codes int8 [..., g], scales float32 [...])``. Pinned by the
+    half-step bound, exact grids, symmetry and the chapter's byte counts.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1, keepdims=True)
+    s = np.maximum(amax, np.float32(eps)) / np.float32(q_max)
+    codes = np.clip(np.rint(x / s), -q_max, q_max).astype(np.int8)
+    return codes, s[..., 0]
+
+
+def dequantize(codes, scales) -> np.ndarray:
+    """``s * code`` in float64 (exact: an 8-bit code times a float32 scale)."""
+    return np.asarray(codes).astype(np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def quant_bytes(n_elements: int, bits: int, groups: int, scale_bytes: int) -> int:
+    """Storage of a quantised tensor: ``bits`` per element plus one scale per
+    group (chapter 5, section 4: the exercise's memory column counts the
+    codes and FP16 scales the same way)."""
+    return n_elements * bits // 8 + groups * scale_bytes
+
+
+class QuantOracleCache(OracleCache):
+    """The oracle's 8-bit pool: codes ``[num_blocks, n_kv, B, d]`` and one
+    float32 scale per (block, kv head, slot), for K and for V. Tokens are
+    quantised row by row (``quantize_absmax``) as they are appended, through
+    the same allocator and table replay as ``OracleCache``; attention reads
+    ``s * code``. Unwritten codes hold -128 and unwritten scales NaN."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        shape = (wl.num_blocks, wl.n_kv, wl.block_size, wl.head_dim)
+        self.pool_k = np.full(shape, QUANT_POISON_CODE, dtype=np.int8)
+        self.pool_v = self.pool_k.copy()
+        self.scale_k = np.full(shape[:3], np.nan, dtype=np.float32)
+        self.scale_v = self.scale_k.copy()
+        self.allocator = BlockAllocator(wl.num_blocks, wl.alloc_order)
+        self.seqs = [SequenceBlocks(wl.block_size) for _ in range(wl.num_seqs)]
+
+    def _append(self, s, start, k, v):
+        B = self.wl.block_size
+        ck, sk = quantize_absmax(widen(k, self.wl.dtype))
+        cv, sv = quantize_absmax(widen(v, self.wl.dtype))
+        blocks = self.seqs[s].blocks
+        for i in range(len(k)):
+            p = start + i
+            blk = blocks[p // B]
+            self.pool_k[blk, :, p % B, :] = ck[i]
+            self.pool_v[blk, :, p % B, :] = cv[i]
+            self.scale_k[blk, :, p % B] = sk[i]
+            self.scale_v[blk, :, p % B] = sv[i]
+
+    def fill_history(self):
+        wl = self.wl
+        for s in range(wl.num_seqs):
+            self.seqs[s].ensure(self.allocator, int(wl.hist_lens[s]))
+            k, v = wl.hist_rows(s)
+            self._append(s, 0, k, v)
+
+    def append_step(self):
+        wl = self.wl
+        for s in range(wl.num_seqs):
+            self.seqs[s].ensure(self.allocator, int(wl.seq_lens[s]))
+            k, v = wl.new_rows(s)
+            self._append(s, int(wl.hist_lens[s]), k, v)
+
+    def sequence_kv(self, s: int):
+        wl = self.wl
+        L = int(wl.seq_lens[s])
+        B = wl.block_size
+        blocks = self.seqs[s].blocks
+        K = gather(self.pool_k, blocks, L, B)
+        V = gather(self.pool_v, blocks, L, B)
+        nb = -(-L // B)
+        sk = np.concatenate([self.scale_k[blocks[i]] for i in range(nb)], axis=1)[:, :L]
+        sv = np.concatenate([self.scale_v[blocks[i]] for i in range(nb)], axis=1)[:, :L]
+        return dequantize(K, sk), dequantize(V, sv)
+
+
+def build_quant_cache(wl) -> QuantOracleCache:
+    c = QuantOracleCache(wl)
+    c.fill_history()
+    c.append_step()
+    return c
+
+
 def build_tables(wl) -> np.ndarray:
     """Only the allocation side of ``build_cache``: the table rows the
     history-then-step replay produces (no K/V storage)."""

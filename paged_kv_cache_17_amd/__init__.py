@@ -12,10 +12,12 @@ from .binding import (  # noqa: F401
     PKV_F32,
     PagedKVError,
     kv_append,
+    kv_append_q8,
     kv_copy_blocks,
     load_library,
     paged_attn_chunk,
     paged_attn_decode,
+    paged_attn_decode_q8,
     paged_attn_split_tokens,
     paged_attn_workspace_size,
     pkv_set_profile_events,

@@ -46,6 +46,10 @@ _SIGNATURES = {
     "kvpool_fork": ([_p, _pi32, _i32, _pi32, _pi32, _i32, _i32], ctypes.c_int),
     "kvpool_cow": ([_p, _pi32, _i32, _i32, _i32, _pi32, _pi32, _i32, _pi32], ctypes.c_int),
     "kv_copy_blocks": ([_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p], ctypes.c_int),
+    "kv_append_q8": ([_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p],
+                     ctypes.c_int),
+    "paged_attn_decode_q8": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                              ctypes.c_float, _p, _size_t, _p], ctypes.c_int),
     "kv_append": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p],
                   ctypes.c_int),
     "paged_attn_split_tokens": ([_i32, _i32, _i32, _i32, _i32, _pi32], ctypes.c_int),
@@ -242,6 +246,29 @@ def kv_copy_blocks(k_cache, v_cache, src_ids, dst_ids, stream=None):
     _check("kv_copy_blocks", load_library().kv_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(src_ids), _ptr(dst_ids), int(src_ids.shape[0]), int(num_blocks),
         int(n_kv), int(d), int(bs), _dtype_code(k_cache), _stream(stream)))
+
+
+def kv_append_q8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_table, start_pos, new_start, stream=None):
+    """Quantise ``k_new``/``v_new`` ``[T, n_kv, d]`` (bf16 or fp32) into the 8-bit pool."""
+    _dev(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_table, start_pos, new_start)
+    num_blocks, n_kv, bs, d = k_codes.shape
+    _check("kv_append_q8", load_library().kv_append_q8(
+        _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(start_pos), _ptr(new_start), int(start_pos.shape[0]),
+        int(k_new.shape[0]), int(num_blocks), int(n_kv), int(d), int(bs), _stream(stream)))
+
+
+def paged_attn_decode_q8(out, lse, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                         scale, workspace, stream=None):
+    """Decode attention over the 8-bit pool: ``q``/``out`` bf16 ``[S, n_q, d]``."""
+    _dev(out, lse, q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, workspace)
+    num_blocks, n_kv, bs, d = k_codes.shape
+    S, n_q, _ = q.shape
+    _check("paged_attn_decode_q8", load_library().paged_attn_decode_q8(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(S), int(max_seq_len), int(num_blocks),
+        int(n_q), int(n_kv), int(d), int(bs), float(scale), _ptr(workspace),
+        int(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def paged_attn_split_tokens(num_q_rows, n_kv, block_size, max_seq_len, requested=0) -> int:

@@ -23,7 +23,17 @@ class PagedKVCache:
         self.dtype = dtype
         self.device = device
         shape = (num_blocks, n_kv, block_size, head_dim)
-        if fill_nan:
+        # dtype torch.int8: 8-bit codes plus one fp32 scale per (block, kv head,
+        # slot) for K and for V (kv_append_q8 / paged_attn_decode_q8)
+        self.quantized = dtype == torch.int8
+        if self.quantized:
+            # poison: code -128 (outside the code range) and NaN scales
+            self.k_cache = torch.full(shape, -128, dtype=torch.int8, device=device)
+            self.v_cache = torch.full(shape, -128, dtype=torch.int8, device=device)
+            fill = float("nan") if fill_nan else 0.0
+            self.k_scale = torch.full(shape[:3], fill, dtype=torch.float32, device=device)
+            self.v_scale = torch.full(shape[:3], fill, dtype=torch.float32, device=device)
+        elif fill_nan:
             self.k_cache = torch.full(shape, float("nan"), dtype=dtype, device=device)
             self.v_cache = torch.full(shape, float("nan"), dtype=dtype, device=device)
         else:
@@ -55,6 +65,8 @@ class PagedKVCache:
         shared blocks in that range are replaced by private copies (host table
         updated, contents copied on the device). Returns the number of copies;
         call ``upload_table`` before the next device call that reads the table."""
+        if self.quantized:
+            raise NotImplementedError("copy-on-write of an 8-bit cache (codes and scales) is not provided")
         src, dst = self.pool.kvpool_cow(self.table, self.held, s, start, count)
         if len(src):
             B.kv_copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(src).to(self.device),
@@ -66,6 +78,10 @@ class PagedKVCache:
 
     # ---- device calls -----------------------------------------------------
     def append(self, k_new, v_new, start_pos, new_start, stream=None) -> None:
+        if self.quantized:
+            B.kv_append_q8(self.k_cache, self.v_cache, self.k_scale, self.v_scale, k_new, v_new, self.table_dev,
+                           start_pos, new_start, stream=stream)
+            return
         B.kv_append(self.k_cache, self.v_cache, k_new, v_new, self.table_dev, start_pos, new_start,
                     stream=stream)
 
@@ -84,6 +100,12 @@ class PagedKVCache:
         if out is None:
             out = torch.empty_like(q)
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens)
+        if self.quantized:
+            if split_tokens:
+                raise ValueError("the 8-bit decode uses the balanced partition only (split_tokens=0)")
+            B.paged_attn_decode_q8(out, lse, q, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
+                                   self.table_dev, seq_lens, max_seq_len, scale, ws, stream=stream)
+            return out
         B.paged_attn_decode(out, lse, q, self.k_cache, self.v_cache, self.table_dev, seq_lens,
                             max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
         return out
@@ -92,6 +114,8 @@ class PagedKVCache:
               lse=None, split_tokens: int = 0, stream=None):
         if out is None:
             out = torch.empty_like(q)
+        if self.quantized:
+            raise NotImplementedError("chunk attention over an 8-bit cache is not provided")
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens)
         B.paged_attn_chunk(out, lse, q, q_start, self.k_cache, self.v_cache, self.table_dev, seq_lens,
                            max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)

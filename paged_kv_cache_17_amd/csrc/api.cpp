@@ -96,19 +96,20 @@ Layout ws_layout_balanced(int num_seqs, int n_q, int n_kv, int head_dim, int wav
 }
 
 // Grid size of the balanced pass for the current device (cached for the
-// last shape asked about).
-int balanced_waves(int n_q, int n_kv, int num_seqs) {
-    static thread_local int last_dev = -1, last_g = 0, last_s = 0, last_w = 0;
+// last shape asked about, per K/V format).
+int balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv = false) {
+    static thread_local int last_dev[2] = {-1, -1}, last_g[2] = {0, 0}, last_s[2] = {0, 0}, last_w[2] = {0, 0};
+    const int f = int8_kv ? 1 : 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     const int g = n_q / n_kv;
-    if (dev != last_dev || g != last_g || num_seqs != last_s) {
-        last_w = pkv::decode_balanced_waves(n_q, n_kv, num_seqs);
-        last_dev = dev;
-        last_g = g;
-        last_s = num_seqs;
+    if (dev != last_dev[f] || g != last_g[f] || num_seqs != last_s[f]) {
+        last_w[f] = pkv::decode_balanced_waves(n_q, n_kv, num_seqs, int8_kv);
+        last_dev[f] = dev;
+        last_g[f] = g;
+        last_s[f] = num_seqs;
     }
-    return last_w;
+    return last_w[f];
 }
 
 int check_shape(int num_seqs, int max_seq_len, int num_blocks, int n_q, int n_kv, int head_dim,
@@ -240,10 +241,12 @@ extern "C" int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_
     const int max_splits = (max_seq_len + split - 1) / split;
     size_t need = ws_layout(num_q_rows, n_q, head_dim, max_splits).total;
     if (n_q % n_kv == 0 && balanced_eligible(PKV_BF16, split_tokens, num_q_rows, n_q, n_kv, head_dim, block_size)) {
-        const int waves = balanced_waves(n_q, n_kv, num_q_rows);
-        if (waves < 1) return PKV_ERR_HIP;
-        const size_t b = ws_layout_balanced(num_q_rows, n_q, n_kv, head_dim, waves).total;
-        if (b > need) need = b;
+        for (bool int8_kv : {false, true}) {   // bf16 and 8-bit K/V (paged_attn_decode_q8)
+            const int waves = balanced_waves(n_q, n_kv, num_q_rows, int8_kv);
+            if (waves < 1) return PKV_ERR_HIP;
+            const size_t b = ws_layout_balanced(num_q_rows, n_q, n_kv, head_dim, waves).total;
+            if (b > need) need = b;
+        }
     }
     *bytes = need;
     return PKV_OK;
@@ -292,6 +295,70 @@ extern "C" int paged_attn_decode(void* out, float* lse, const void* q,
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
     return run_attention(a, out, lse, dtype, true, balanced, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kv_append_q8(void* k_codes, void* v_codes, float* k_scale, float* v_scale, const void* k_new,
+                            const void* v_new, int32_t new_dtype, const int32_t* block_table, int32_t table_stride,
+                            const int32_t* start_pos, const int32_t* new_start, int32_t num_seqs, int32_t total_new,
+                            int32_t num_blocks, int32_t n_kv, int32_t head_dim, int32_t block_size, void* stream) {
+    if (num_seqs < 0 || total_new < 0 || num_blocks < 1 || n_kv < 1 || head_dim < 1 || block_size < 1 ||
+        table_stride < 1)
+        return PKV_ERR_INVALID_ARGUMENT;
+    if (!elem_bytes(new_dtype)) return PKV_ERR_INVALID_ARGUMENT;
+    if (total_new == 0) return PKV_OK;
+    if (num_seqs == 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (!k_codes || !v_codes || !k_scale || !v_scale || !k_new || !v_new || !block_table || !start_pos ||
+        !new_start)
+        return PKV_ERR_NULL_POINTER;
+    const hipError_t e = pkv::launch_kv_append_q8(
+        static_cast<int8_t*>(k_codes), static_cast<int8_t*>(v_codes), k_scale, v_scale, k_new, v_new,
+        new_dtype == PKV_BF16, block_table, table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
+        head_dim, block_size, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_attn_decode_q8(void* out, float* lse, const void* q, const void* k_codes, const void* v_codes,
+                                    const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                    int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                    int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
+                                    int32_t head_dim, int32_t block_size, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size, table_stride, PKV_BF16,
+                         scale);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_codes || !v_codes || !k_scale || !v_scale || !block_table || !seq_lens)
+        return PKV_ERR_NULL_POINTER;
+    if (!pkv::decode_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs)) return PKV_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(k_codes) & 7) ||
+        (reinterpret_cast<uintptr_t>(v_codes) & 7))
+        return PKV_ERR_INVALID_ARGUMENT;
+    pkv::AttnArgs a{};
+    a.waves = balanced_waves(n_q, n_kv, num_seqs, true);
+    if (a.waves < 1) return PKV_ERR_HIP;
+    a.q = q;
+    a.q_start = nullptr;
+    a.k_cache = k_codes;
+    a.v_cache = v_codes;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.table = block_table;
+    a.seq_lens = seq_lens;
+    a.table_stride = table_stride;
+    a.num_seqs = num_seqs;
+    a.num_rows = num_seqs;
+    a.max_q_len = 1;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_blocks;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.split_tokens = block_size;
+    a.max_splits = 1;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    return run_attention(a, out, lse, PKV_BF16, true, true, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }
 

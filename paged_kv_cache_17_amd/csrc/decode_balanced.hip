@@ -24,7 +24,10 @@
 //  * the next tile's loads are issued before the current tile is computed,
 //    so every wave always has a tile in flight;
 //  * with four query heads per kv head the per-tile math is the
-//    reduce-scatter / one-exponential-per-lane form (DecodeStateG4).
+//    reduce-scatter / one-exponential-per-lane form (DecodeStateG4);
+//  * the K/V format is a template parameter: bf16 tiles, or 8-bit codes
+//    with one fp32 scale per (token, kv head) (half the bytes; the scales
+//    are folded into the scores and the weights, see decode_tile.h).
 //
 // Per-sequence block counts (ceil(L / 16), 0 for an invalid length) and
 // their prefix sums are built by every wave in LDS from seq_lens; wave 0
@@ -50,7 +53,73 @@ struct BalancedState { using T = DecodeState<G>; };
 template <>
 struct BalancedState<4> { using T = DecodeStateG4; };
 
+// bf16 K/V: per tile, eight 16-byte loads per lane (decode_tile.h layout).
 template <int G>
+struct Bf16Kv {
+    struct Regs {
+        u32x4 k[4], v[4];
+    };
+    const uint16_t* kc;
+    const uint16_t* vc;
+    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane)
+        : kc(static_cast<const uint16_t*>(a.k_cache) + lane * 8), vc(static_cast<const uint16_t*>(a.v_cache) + lane * 8) {}
+    __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
+        const size_t off = static_cast<size_t>(tile) * kTileElems;
+        load_tile(kc + off, vc + off, t.k, t.v);
+    }
+    __device__ __forceinline__ void compute(typename BalancedState<G>::T& st, const Regs& t, const u32x4 (&qv)[G],
+                                            int lane, int ntok, float sl2, float* s_p) const {
+        if constexpr (G == 4) st.tile(t.k, t.v, qv, lane, ntok, sl2, s_p);
+        else st.tile(t.k, t.v, qv, lane >> 4, ntok, sl2);
+    }
+};
+
+// 8-bit codes + fp32 scales: per tile, eight 8-byte code loads and the
+// scales this lane's scores and weights need.
+template <int G>
+struct Int8Kv {
+    static constexpr int kScales = G == 4 ? 1 : 4;
+    struct Regs {
+        u32x2 k[4], v[4];
+        float sk[kScales], sv[kScales];
+    };
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* ks;
+    const float* vs;
+    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane)
+        : kc(static_cast<const int8_t*>(a.k_cache) + lane * 8), vc(static_cast<const int8_t*>(a.v_cache) + lane * 8),
+          ks(a.k_scale), vs(a.v_scale) {}
+    __device__ __forceinline__ void load(Regs& t, int tile, int lane) const {
+        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
+        const u32x2* kp = reinterpret_cast<const u32x2*>(kc + off);
+        const u32x2* vp = reinterpret_cast<const u32x2*>(vc + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t.k[i] = __builtin_nontemporal_load(kp + i * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t.v[i] = __builtin_nontemporal_load(vp + i * 64);
+        const size_t so = static_cast<size_t>(tile) * kTileB;
+        const int r = lane >> 4;
+        if constexpr (G == 4) {
+            const int tok = 4 * (lane & 3) + r;        // token of this lane's score
+            t.sk[0] = ks[so + tok];
+            t.sv[0] = vs[so + tok];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                t.sk[i] = ks[so + 4 * i + r];
+                t.sv[i] = vs[so + 4 * i + r];
+            }
+        }
+    }
+    __device__ __forceinline__ void compute(typename BalancedState<G>::T& st, const Regs& t, const u32x4 (&qv)[G],
+                                            int lane, int ntok, float sl2, float* s_p) const {
+        if constexpr (G == 4) st.tile_q8(t.k, t.v, t.sk[0], t.sv[0], qv, lane, ntok, sl2, s_p);
+        else st.tile_q8(t.k, t.v, t.sk, t.sv, qv, lane >> 4, ntok, sl2);
+    }
+};
+
+template <int G, class Kv>
 __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
     extern __shared__ int s_mem[];
     const int S = a.num_seqs;
@@ -126,8 +195,7 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
 
     const int c = lane & 15;
     const int r = lane >> 4;
-    const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + lane * 8;
-    const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + lane * 8;
+    const Kv kv(a, lane);
     const uint16_t* qc = static_cast<const uint16_t*>(a.q) + c * 8;
     const float sl2 = a.scale_log2;
 
@@ -161,25 +229,19 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
         }
     };
 
-    auto tile_ptr_off = [&](int tile) { return static_cast<size_t>(tile) * kTileElems; };
-
     describe(t0);
-    u32x4 ka[4], va[4], kb[4], vb[4];
-    {
-        const size_t off = tile_ptr_off(__builtin_amdgcn_readlane(i_tile, 0));
-        load_tile(kc + off, vc + off, ka, va);
-    }
+    typename Kv::Regs ta, tb;
+    kv.load(ta, __builtin_amdgcn_readlane(i_tile, 0), lane);
 
-    // One step: tile i is in (kcur, vcur); issue tile i+1 into (knext, vnext),
-    // then compute tile i.
-    auto step = [&](int i, u32x4 (&kcur)[4], u32x4 (&vcur)[4], u32x4 (&knext)[4], u32x4 (&vnext)[4]) {
+    // One step: tile i is in cur; issue tile i+1 into nxt, then compute
+    // tile i.
+    auto step = [&](int i, const typename Kv::Regs& cur, typename Kv::Regs& nxt) {
         const int li = i & (kWave - 1);
         const int seg = __builtin_amdgcn_readlane(i_seg, li);
         const int ntok = __builtin_amdgcn_readlane(i_ntok, li);
         if (i + 1 < n) {
             if (li == kWave - 1) describe(t0 + i + 1);
-            const size_t off = tile_ptr_off(__builtin_amdgcn_readlane(i_tile, (i + 1) & (kWave - 1)));
-            load_tile(kc + off, vc + off, knext, vnext);
+            kv.load(nxt, __builtin_amdgcn_readlane(i_tile, (i + 1) & (kWave - 1)), lane);
         }
         if (seg != cur_seg) {
             if (cur_seg >= 0) flush();
@@ -195,35 +257,64 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
         if (ntok < 0) {
             cur_bad = true;
         } else {
-            if constexpr (G == 4) st.tile(kcur, vcur, qv, lane, ntok, sl2, s_p);
-            else st.tile(kcur, vcur, qv, r, ntok, sl2);
+            kv.compute(st, cur, qv, lane, ntok, sl2, s_p);
         }
     };
 
     for (int i = 0; i < n; i += 2) {
-        step(i, ka, va, kb, vb);
-        if (i + 1 < n) step(i + 1, kb, vb, ka, va);
+        step(i, ta, tb);
+        if (i + 1 < n) step(i + 1, tb, ta);
     }
     flush();
 }
 
-template <int G>
+template <int G, class Kv>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     const size_t lds = balanced_lds_bytes(a.num_seqs);
     if (ev.on())
-        hipExtLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), lds, stream, ev.start, ev.stop, 0,
-                              a);
+        hipExtLaunchKernelGGL(decode_balanced_kernel<G, Kv>, dim3(a.waves), dim3(kWave), lds, stream, ev.start,
+                              ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(decode_balanced_kernel<G>, dim3(a.waves), dim3(kWave), lds, stream, a);
+        hipLaunchKernelGGL((decode_balanced_kernel<G, Kv>), dim3(a.waves), dim3(kWave), lds, stream, a);
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, class Kv>
 int occupancy(size_t lds) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<G>, kWave, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<G, Kv>, kWave, lds) !=
+        hipSuccess)
         return 0;
     return blocks;
+}
+
+template <template <int> class Kv>
+int waves_for(int n_q, int n_kv, int num_seqs) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const size_t lds = balanced_lds_bytes(num_seqs);
+    int per_cu = 0;
+    switch (n_q / n_kv) {
+        case 1: per_cu = occupancy<1, Kv<1>>(lds); break;
+        case 2: per_cu = occupancy<2, Kv<2>>(lds); break;
+        case 4: per_cu = occupancy<4, Kv<4>>(lds); break;
+        case 8: per_cu = occupancy<8, Kv<8>>(lds); break;
+        default: return 0;
+    }
+    if (per_cu < 1) per_cu = 1;
+    return cus * per_cu;
+}
+
+template <template <int> class Kv>
+hipError_t launch_kv(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
+    switch (a.n_q / a.n_kv) {
+        case 1: return launch_g<1, Kv<1>>(a, stream, ev);
+        case 2: return launch_g<2, Kv<2>>(a, stream, ev);
+        case 4: return launch_g<4, Kv<4>>(a, stream, ev);
+        case 8: return launch_g<8, Kv<8>>(a, stream, ev);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -239,31 +330,12 @@ bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, 
     return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
-int decode_balanced_waves(int n_q, int n_kv, int num_seqs) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    const size_t lds = balanced_lds_bytes(num_seqs);
-    int per_cu = 0;
-    switch (n_q / n_kv) {
-        case 1: per_cu = occupancy<1>(lds); break;
-        case 2: per_cu = occupancy<2>(lds); break;
-        case 4: per_cu = occupancy<4>(lds); break;
-        case 8: per_cu = occupancy<8>(lds); break;
-        default: return 0;
-    }
-    if (per_cu < 1) per_cu = 1;
-    return cus * per_cu;
+int decode_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv) {
+    return int8_kv ? waves_for<Int8Kv>(n_q, n_kv, num_seqs) : waves_for<Bf16Kv>(n_q, n_kv, num_seqs);
 }
 
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
-    switch (a.n_q / a.n_kv) {
-        case 1: return launch_g<1>(a, stream, ev);
-        case 2: return launch_g<2>(a, stream, ev);
-        case 4: return launch_g<4>(a, stream, ev);
-        case 8: return launch_g<8>(a, stream, ev);
-        default: return hipErrorInvalidValue;
-    }
+    return a.k_scale ? launch_kv<Int8Kv>(a, stream, ev) : launch_kv<Bf16Kv>(a, stream, ev);
 }
 
 }  // namespace pkv

@@ -20,6 +20,7 @@ constexpr int kTileElems = kTileD * kTileB;   // elements of K (or V) per tile
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Each element is copied to a scalar before the bit cast: bit-casting a
 // vector element accessor directly (k.y) has been seen to read element 0.
@@ -40,6 +41,34 @@ __device__ __forceinline__ void widen8_bf16(const u32x4 v, float (&f)[8]) {
     f[2] = bf16_lo(v1); f[3] = bf16_hi(v1);
     f[4] = bf16_lo(v2); f[5] = bf16_hi(v2);
     f[6] = bf16_lo(v3); f[7] = bf16_hi(v3);
+}
+
+// Quantised tiles (8-bit codes, symmetric absmax, one fp32 scale per token
+// and kv head): lane l holds 8 codes (8 bytes) of token 4i + r, dims 8c..8c+7,
+// in load i, the same positions as the bf16 layout. A code is a signed
+// integer of magnitude <= 127, so it is exact in bf16 and in fp32.
+__device__ __forceinline__ float code_at(uint32_t w, int byte) {
+    return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w >> (8 * byte))));
+}
+
+// Eight codes as four bf16 pairs (exact), for the bf16 dot instruction.
+__device__ __forceinline__ u32x4 codes8_to_bf16x8(const u32x2 w) {
+    const uint32_t a = w[0], b = w[1];
+    u32x4 r;
+    r[0] = pack2_bf16(code_at(a, 0), code_at(a, 1));
+    r[1] = pack2_bf16(code_at(a, 2), code_at(a, 3));
+    r[2] = pack2_bf16(code_at(b, 0), code_at(b, 1));
+    r[3] = pack2_bf16(code_at(b, 2), code_at(b, 3));
+    return r;
+}
+
+__device__ __forceinline__ void widen8_codes(const u32x2 w, float (&f)[8]) {
+    const uint32_t a = w[0], b = w[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = code_at(a, e);
+        f[4 + e] = code_at(b, e);
+    }
 }
 
 // Issue the eight 16-byte loads of one tile (K then V). `k`/`v` point at the
@@ -105,6 +134,54 @@ struct DecodeState {
 #pragma unroll
             for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i][h] - mu);
             l[h] = fmaf(l[h], alpha, (p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float x = acc[h][k] * alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x = fmaf(p[i], vf[i][k], x);
+                acc[h][k] = x;
+            }
+            m[h] = mn;
+        }
+    }
+
+    // The same for a quantised tile: scores are code dot products times the
+    // token's K scale; V's scale is folded into the weight of each token
+    // (the normaliser keeps the unscaled weights). sk[i], sv[i]: scales of
+    // token 4i + r. Past the end of the sequence the weight is 0 and the V
+    // scale (possibly never written) is not used.
+    __device__ __forceinline__ void tile_q8(const u32x2 (&kr)[4], const u32x2 (&vr)[4], const float (&sk)[4],
+                                            const float (&sv)[4], const u32x4 (&qv)[G], int r, int ntok,
+                                            float sl2) {
+        float sc[4][G];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool valid = 4 * i + r < ntok;
+            const u32x4 kb = codes8_to_bf16x8(kr[i]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float full = row16_sum(dot8_bf16(kb, qv[h]));
+                sc[i][h] = valid ? full * sk[i] * sl2 : -INFINITY;
+            }
+        }
+        float vf[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) widen8_codes(vr[i], vf[i]);
+        float svv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) svv[i] = (4 * i + r < ntok) ? sv[i] : 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mx = fmaxf(fmaxf(sc[0][h], sc[1][h]), fmaxf(sc[2][h], sc[3][h]));
+            const float mn = fmaxf(m[h], mx);
+            const float mu = (mn == -INFINITY) ? 0.0f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - mu);
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i][h] - mu);
+            l[h] = fmaf(l[h], alpha, (p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] *= svv[i];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 float x = acc[h][k] * alpha;
@@ -265,6 +342,70 @@ struct DecodeStateG4 {
                 for (int k = 0; k < 8; ++k) vf[i][k] = ok ? vf[i][k] : 0.0f;
             }
         }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float x = acc[h][k];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x = fmaf(pw[h * 4 + i], vf[i][k], x);
+                acc[h][k] = x;
+            }
+    }
+
+    // The same for a quantised tile. sk, sv: the K and V scales of the token
+    // this lane's score belongs to (4 (c % 4) + r). The score is the code dot
+    // product times sk; the weight handed to the row is p * sv, so the P.V
+    // products run on the codes; the normaliser keeps p.
+    __device__ __forceinline__ void tile_q8(const u32x2 (&kr)[4], const u32x2 (&vr)[4], float sk, float sv,
+                                            const u32x4 (&qv)[G], int lane, int ntok, float sl2, float* s_p) {
+        const int c = lane & 15;
+        const int r = lane >> 4;
+        float part[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 kb = codes8_to_bf16x8(kr[i]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) part[h * 4 + i] = dot8_bf16(kb, qv[h]);
+        }
+        const int i_own = c & 3;
+        const bool valid = 4 * i_own + r < ntok;
+        const float red = row16_reduce_scatter(part, c);
+        const float s = valid ? red * sk * sl2 : -INFINITY;
+        float mx = fmaxf(s, __builtin_amdgcn_update_dpp(0.0f, s, 0xB1, 0xF, 0xF, false));
+        mx = fmaxf(mx, __builtin_amdgcn_update_dpp(0.0f, mx, 0x4E, 0xF, 0xF, false));
+        const bool need = mx > mref + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float nref = need ? mx : mref;
+            const float alpha = (nref == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
+            l *= alpha;
+            float al[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) al[h] = __shfl(alpha, (lane & 48) | (h << 2), kWave);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[h][k] *= al[h];
+            mref = nref;
+            mref_safe = (nref == -INFINITY) ? 0.0f : nref;
+        }
+        const float p = __builtin_amdgcn_exp2f(s - mref_safe);
+        l += p;
+        s_p[lane] = valid ? p * sv : 0.0f;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float pw[16];
+        const float4* row = reinterpret_cast<const float4*>(s_p + (lane & 48));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 t = row[q];
+            pw[4 * q + 0] = t.x; pw[4 * q + 1] = t.y; pw[4 * q + 2] = t.z; pw[4 * q + 3] = t.w;
+        }
+        __builtin_amdgcn_wave_barrier();   // all lanes read before the next tile overwrites
+        float vf[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) widen8_codes(vr[i], vf[i]);
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll

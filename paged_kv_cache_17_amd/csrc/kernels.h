@@ -17,8 +17,10 @@ struct PartialML {
 struct AttnArgs {
     const void* q;
     const int32_t* q_start;      // nullptr: one query row per sequence
-    const void* k_cache;
+    const void* k_cache;         // bf16 / fp32 elements, or 8-bit codes when k_scale is set
     const void* v_cache;
+    const float* k_scale;        // 8-bit K/V: [num_blocks][n_kv][block_size] scales; nullptr otherwise
+    const float* v_scale;
     const int32_t* table;
     const int32_t* seq_lens;
     int table_stride;
@@ -50,6 +52,12 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
                             const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
                             int n_kv, int row_bytes, int block_size, hipStream_t stream);
 
+// Quantising append (8-bit codes + one fp32 scale per token and kv head).
+hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,
+                               const void* v_new, bool bf16_in, const int32_t* table, int table_stride,
+                               const int32_t* start_pos, const int32_t* new_start, int num_seqs, int total_new,
+                               int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream);
+
 // Whole-block copies (src_ids[i] -> dst_ids[i], both pools) for
 // copy-on-write; block_bytes = n_kv * block_size * head_dim * element size.
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
@@ -65,7 +73,7 @@ hipError_t launch_decode_fast(const AttnArgs& a, hipStream_t stream, KernelEvent
 // Balanced decode pass (bf16, head_dim 128, block_size 16): equal tile
 // ranges per wave across sequence boundaries.
 bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs);
-int decode_balanced_waves(int n_q, int n_kv, int num_seqs);
+int decode_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv = false);
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
 
 // Chunk attention on MFMA (bf16, head_dim 128, block_size 16, sequences of

@@ -69,7 +69,70 @@ hipError_t launch_unit(void* kc, void* vc, const void* kn, const void* vn, const
     return hipGetLastError();
 }
 
+// Quantising append: one wave per (new token, kv head) row of K and of V.
+// Symmetric absmax quantisation (chapter 5 section 4, group-wise: one scale
+// per group of consecutive elements, here the head_dim values of one token
+// and kv head): s = max(max_i |x_i|, 1e-8) / 127, code_i =
+// clamp(rint(x_i / s), -127, 127) (ties to even), all in fp32 with
+// correctly rounded division; the pool keeps the 8-bit codes and s.
+template <typename TIn>
+__global__ __launch_bounds__(256) void kv_append_q8_kernel(
+    int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
+    const TIn* __restrict__ kn, const TIn* __restrict__ vn, const int32_t* __restrict__ table, int table_stride,
+    const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start, int num_seqs, int total_new,
+    int num_blocks, int n_kv, int d, int bs) {
+    __shared__ int s_start[kStagedSeqs + 1];
+    const bool staged = num_seqs <= kStagedSeqs;
+    if (staged)
+        for (int i = threadIdx.x; i <= num_seqs; i += blockDim.x) s_start[i] = new_start[i];
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row = static_cast<long long>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (row >= 2LL * total_new * n_kv) return;                // whole wave exits together
+    const bool is_v = row & 1;
+    const long long th = row >> 1;
+    const int h = static_cast<int>(th % n_kv);
+    const int t = static_cast<int>(th / n_kv);
+    const int32_t* starts = staged ? s_start : new_start;
+    const int s = seq_of_row(starts, num_seqs, t);
+    const int pos = start_pos[s] + (t - starts[s]);
+    if (pos < 0 || pos / bs >= table_stride) return;
+    const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
+    if (blk < 0 || blk >= num_blocks) return;                 // unmapped slot: nothing is written
+    const TIn* src = (is_v ? vn : kn) + (static_cast<size_t>(t) * n_kv + h) * d;
+    float amax = 0.0f;
+    for (int e = lane; e < d; e += kWave) amax = fmaxf(amax, fabsf(Elem<TIn>::load(src + e)));
+    amax = wave_max(amax);
+    const float scale = fmaxf(amax, 1e-8f) / 127.0f;
+    const size_t slot = (static_cast<size_t>(blk) * n_kv + h) * bs + pos % bs;
+    int8_t* dst = (is_v ? vc : kc) + slot * d;
+    for (int e = lane; e < d; e += kWave) {
+        const float c = fminf(fmaxf(rintf(Elem<TIn>::load(src + e) / scale), -127.0f), 127.0f);
+        dst[e] = static_cast<int8_t>(c);
+    }
+    if (lane == 0) (is_v ? vs : ks)[slot] = scale;
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,
+                               const void* v_new, bool bf16_in, const int32_t* table, int table_stride,
+                               const int32_t* start_pos, const int32_t* new_start, int num_seqs, int total_new,
+                               int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream) {
+    const long long rows = 2LL * total_new * n_kv;
+    const unsigned grid = static_cast<unsigned>((rows + 3) / 4);     // four waves per workgroup
+    if (bf16_in)
+        hipLaunchKernelGGL(kv_append_q8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, k_cache, v_cache,
+                           k_scale, v_scale, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                           table, table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
+                           head_dim, block_size);
+    else
+        hipLaunchKernelGGL(kv_append_q8_kernel<float>, dim3(grid), dim3(256), 0, stream, k_cache, v_cache, k_scale,
+                           v_scale, static_cast<const float*>(k_new), static_cast<const float*>(v_new), table,
+                           table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv, head_dim,
+                           block_size);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* table, int table_stride, const int32_t* start_pos,

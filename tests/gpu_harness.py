@@ -43,12 +43,14 @@ def i32(a, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
 
 
-def build_gpu_cache(wl, fill_nan=True, alloc_order=None):
+def build_gpu_cache(wl, fill_nan=True, alloc_order=None, quantized=False):
     """Replay history then step through the library: tables grown by
-    ``kvpool_ensure`` in sequence order, K/V written by ``kv_append``."""
+    ``kvpool_ensure`` in sequence order, K/V written by ``kv_append`` (or
+    quantised by ``kv_append_q8`` into an 8-bit cache)."""
     import paged_kv_cache_17_amd as pkv
     order = wl.alloc_order if alloc_order is None else alloc_order
-    c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size, torch_dtype(wl.dtype),
+    c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size,
+                         torch.int8 if quantized else torch_dtype(wl.dtype),
                          wl.num_seqs, wl.table_stride, alloc_order=order, fill_nan=fill_nan,
                          poison_workspace=fill_nan)
     for s in range(wl.num_seqs):

@@ -1,0 +1,121 @@
+"""GPU parity of the 8-bit K/V path (kv_append_q8, paged_attn_decode_q8).
+
+Bars: the pool's codes and scales bit-exact against the oracle's
+quantiser (both take the integer decision in fp32 with correctly rounded
+division, ties to even; unwritten slots keep code -128 and a NaN scale);
+decode outputs per (row, head) within 2e-2 of the row maximum of the
+oracle's attention over the same dequantised cache (bf16 output); lse
+within 1e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import BF16, F32, build_workload, config_workload
+
+from gpu_harness import build_gpu_cache, check_lse, check_rows, i32, out_f64, raw_to_torch
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_17_amd as pkv
+    pkv.load_library()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _pools_match(c, ora):
+    assert np.array_equal(c.table, ora.tables())
+    assert np.array_equal(c.k_cache.cpu().numpy(), ora.pool_k)
+    assert np.array_equal(c.v_cache.cpu().numpy(), ora.pool_v)
+    # scales bit for bit, NaN poison included
+    assert np.array_equal(c.k_scale.cpu().numpy().view(np.uint32), ora.scale_k.view(np.uint32))
+    assert np.array_equal(c.v_scale.cpu().numpy().view(np.uint32), ora.scale_v.view(np.uint32))
+
+
+def _decode(c, wl):
+    q = raw_to_torch(wl.q, BF16)
+    lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.decode(q, i32(wl.seq_lens), wl.max_seq_len, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    return out_f64(out, BF16), lse.cpu().numpy().astype(np.float64)
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 33, 255, 256, 257, 1000, 2049, 3000]
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 8), (64, 8), (6, 3)])
+def test_q8_append_and_decode_match_the_oracle(n_q, n_kv):
+    L = np.array(RAGGED)
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=41)
+    say("q8 decode", n_q, n_kv)
+    c = build_gpu_cache(wl, quantized=True)
+    ora = oracle.build_quant_cache(wl)
+    _pools_match(c, ora)
+    got, got_lse = _decode(c, wl)
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(got, ref, BF16, f"q8 {n_q}/{n_kv}")
+    check_lse(got_lse, ref_lse, BF16, "q8 lse")
+    say(f"  worst row rel err {err:.2e}")
+    got2, _ = _decode(c, wl)
+    assert np.array_equal(got, got2), "repeat run not bit-identical"
+
+
+@pytest.mark.parametrize("dtype,d,bs", [(F32, 128, 16), (F32, 8, 4), (BF16, 64, 8), (BF16, 5, 3)])
+def test_q8_append_any_shape_is_bit_exact(dtype, d, bs):
+    """The quantising append takes any head_dim / block_size and fp32 or
+    bf16 inputs; codes and scales equal the oracle's bit for bit."""
+    L = np.array([1, bs, bs + 1, 3 * bs + 2, 70])
+    wl = build_workload(n_q=4, n_kv=2, head_dim=d, block_size=bs, dtype=dtype, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=42)
+    say("q8 append", dtype, d, bs)
+    c = build_gpu_cache(wl, quantized=True)
+    _pools_match(c, oracle.build_quant_cache(wl))
+
+
+def test_q8_invalid_rows_become_nan():
+    L = np.array([40, 50, 60, 70, 80])
+    wl = build_workload(n_q=8, n_kv=2, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=43)
+    c = build_gpu_cache(wl, quantized=True)
+    lens = wl.seq_lens.copy()
+    lens[1] = 0
+    lens[2] = 10 ** 6
+    c.table_dev[3, 1] = 10 ** 6
+    q = raw_to_torch(wl.q, BF16)
+    lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.decode(q, i32(lens), wl.max_seq_len, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    got = out_f64(out, BF16)
+    for s in (1, 2, 3):
+        assert np.isnan(got[s]).all() and np.isnan(lse[s].cpu().numpy()).all()
+    ref, _ = oracle.paged_attention_all(oracle.build_quant_cache(wl))
+    check_rows(got[[0, 4]], ref[[0, 4]], BF16, "valid q8 rows next to invalid ones")
+
+
+def test_q8_full_size_decode_batch_sampled():
+    """The 64-sequence decode batch (lengths 512..4096) through the 8-bit
+    path: whole pools bit-exact, sampled sequences' rows within tolerance."""
+    wl = config_workload(2)
+    say(f"q8 config 2: {wl.num_seqs} seqs, {int(wl.seq_lens.sum())} keys")
+    c = build_gpu_cache(wl, quantized=True)
+    ora = oracle.build_quant_cache(wl)
+    _pools_match(c, ora)
+    got, got_lse = _decode(c, wl)
+    order = np.argsort(wl.seq_lens, kind="stable")
+    picks = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3, 17, 40})
+    worst = 0.0
+    for s in picks:
+        ref, ref_lse = ora.attend(s)
+        worst = max(worst, check_rows(got[s:s + 1], ref, BF16, f"q8 cfg2 seq {s}"))
+        check_lse(got_lse[s], ref_lse[0], BF16, f"q8 cfg2 seq {s}")
+    assert np.isfinite(got).all()
+    say(f"  sampled {len(picks)} seqs, worst row rel err {worst:.2e}")
