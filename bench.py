@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kv", choices=["bf16", "int8"], default="bf16",
                    help="K/V format of the cache: bf16, or 8-bit codes with one fp32 scale per token and kv head")
+    p.add_argument("--verify", action="store_true",
+                   help="time a speculative verification step: gamma + 1 = 5 tokens per sequence of the "
+                        "64-sequence batch appended and attended as one causal chunk")
     p.add_argument("--bestof", action="store_true",
                    help="time the best-of-8 decode step over shared prompts (and the same step without sharing)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -280,6 +283,87 @@ def bench_bestof(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_verify(args):
+    """Speculative verification step over the 64-sequence batch (lengths
+    512..4096 after the append, gamma = 4): append the 5 tokens of every
+    sequence (the pending token and 4 drafts; re-appending the same tokens
+    is idempotent) and verify them with one causal chunk of 5 queries per
+    sequence. Timed with the matrix-core chunk kernel (the library's choice)
+    and with the VALU split path (split_tokens 256) beside it. The chunk
+    reads each sequence's K/V once: the roofline is HBM."""
+    import torch
+    import paged_kv_cache_17_amd as pkv
+    from gpu_harness import GpuSpec
+    from workloads import verify_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.load_library()
+    sw = verify_workload()
+    g1 = sw.gamma + 1
+    gpus = [GpuSpec(sw, fill_nan=False) for _ in range(args.copies)]
+    for g in gpus:
+        g.append_cycle(0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    lens = gpus[0].lens + g1
+    kv_bytes = int(lens.sum()) * sw.n_kv * sw.head_dim * 2 * 2
+    flops = 4 * sw.n_q * sw.head_dim * sum(g1 * (int(L) - g1) + g1 * (g1 + 1) // 2 for L in lens)
+
+    def run(split):
+        def step(i, ev=None):
+            g = gpus[i % len(gpus)]
+            k, v, _ = g.cyc[0]
+            g.c.append(k, v, i32_lens[i % len(gpus)], g.q_start, stream=stream)
+            if ev is not None:
+                pkv.pkv_set_profile_events(*ev)
+            g.verify(0, split_tokens=split, stream=stream)
+            pkv.pkv_set_profile_events(None, None)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        kern = None
+        if split == 0:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for b, a in evs:
+                b.record(stream)
+                a.record(stream)
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                step(i, evs[i])
+            torch.cuda.synchronize()
+            kern = float(np.mean([b.elapsed_time(a) for b, a in evs]))
+        return ms, kern
+
+    from gpu_harness import i32
+    i32_lens = [i32(g.lens) for g in gpus]
+    ms_m, kern_m = run(0)
+    ms_v, _ = run(256)
+    tokens = sw.num_seqs * g1
+    line = {
+        "metric": METRIC, "value": tokens / (ms_m * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_m, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": sw.name, "num_seqs": sw.num_seqs, "chunk": g1, "n_q": sw.n_q, "n_kv": sw.n_kv,
+                   "head_dim": sw.head_dim, "block_size": sw.block_size, "context_tokens": int(lens.sum()),
+                   "kv_bytes": kv_bytes, "cache_copies": len(gpus)},
+        "roofline": {"kernel": "chunk attention (matrix cores), 5-query chunks", "bound": "hbm",
+                     "achieved": kv_bytes / (kern_m * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": kv_bytes / (kern_m * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
+                     "avg_launch_ms": kern_m, "algorithmic_bytes": kv_bytes, "algorithmic_flops": flops},
+        "valu_split_path": {"value": tokens / (ms_v * 1e-3), "ms_per_step": ms_v, "split_tokens": 256},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,6 +377,9 @@ def main():
         return
     if args.bestof:
         bench_bestof(args)
+        return
+    if args.verify:
+        bench_verify(args)
         return
 
     import torch

@@ -121,6 +121,20 @@ int kvpool_alloc(kvpool_t* pool, int32_t n, int32_t* out_ids);
  * or listed twice. */
 int kvpool_free(kvpool_t* pool, int32_t n, const int32_t* ids);
 
+/* Sequence helper: roll a row back to `length` tokens - keep its first
+ * ceil(length / block_size) blocks and drop the row's reference to every
+ * block after them (blocks no other row holds rejoin the free set); their
+ * entries become -1 and *num_held is updated. A row already that short is
+ * unchanged, so repeating the call is a no-op. Source: chapter 5 section 5
+ * (speculative decoding: the target model verifies gamma drafted tokens in
+ * one pass; a rejected draft and every draft after it are discarded) and
+ * the serving tutorial's question on speculative decoding (the KV of
+ * rejected candidates is rolled back and never counted as committed).
+ * Positions past the new length inside the last kept block keep their old
+ * contents; attention never reads past seq_lens and the next append
+ * overwrites them. Errors: NULL_POINTER, INVALID_ARGUMENT, INVALID_FREE. */
+int kvpool_truncate(kvpool_t* pool, int32_t* row, int32_t* num_held, int32_t length);
+
 /* ----------------------------------------------------------------------
  * Shared blocks. Source: serving tutorial section 4.2 (a physical block
  * can be shared through reference counts by a common prefix or by beam /

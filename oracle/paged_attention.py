@@ -190,6 +190,16 @@ class SequenceBlocks:
         blocks, self.blocks = self.blocks, []
         allocator.free(blocks)
 
+    def truncate(self, allocator: BlockAllocator, length: int) -> None:
+        """Roll the row back to ``length`` tokens: keep ceil(length / B) blocks
+        and let go of the rest (chapter 5 section 5: drafts after the first
+        rejected one are discarded; serving tutorial, question on speculative
+        decoding: their KV is rolled back, not committed)."""
+        keep = -(-int(length) // self.block_size)
+        if keep < len(self.blocks):
+            tail, self.blocks = self.blocks[keep:], self.blocks[:keep]
+            allocator.free(tail)
+
     def fork(self, allocator: BlockAllocator, src: "SequenceBlocks", length: int) -> None:
         if self.blocks:
             raise ValueError("fork into a non-empty row")

@@ -41,6 +41,7 @@ _SIGNATURES = {
     "kvpool_free_ids": ([_p, _pi32, _pi32], ctypes.c_int),
     "kvpool_ensure": ([_p, _pi32, _pi32, _i32, _i32], ctypes.c_int),
     "kvpool_release": ([_p, _pi32, _pi32], ctypes.c_int),
+    "kvpool_truncate": ([_p, _pi32, _pi32, _i32], ctypes.c_int),
     "kvpool_share": ([_p, _i32, _pi32], ctypes.c_int),
     "kvpool_refcount": ([_p, _i32, _pi32], ctypes.c_int),
     "kvpool_fork": ([_p, _pi32, _i32, _pi32, _pi32, _i32, _i32], ctypes.c_int),
@@ -164,6 +165,12 @@ class KVPool:
         stride = table.shape[1]
         _check("kvpool_release", load_library().kvpool_release(
             self._h, _i32_ptr(table, s * stride), _i32_ptr(held, s)))
+
+    def kvpool_truncate(self, table: np.ndarray, held: np.ndarray, s: int, length: int) -> None:
+        """Roll row ``s`` back to ``length`` tokens (blocks past it are released)."""
+        stride = table.shape[1]
+        _check("kvpool_truncate", load_library().kvpool_truncate(
+            self._h, _i32_ptr(table, s * stride), _i32_ptr(held, s), int(length)))
 
     def kvpool_share(self, ids) -> None:
         ids = np.ascontiguousarray(ids, dtype=np.int32)

@@ -56,6 +56,11 @@ class PagedKVCache:
     def release(self, s: int) -> None:
         self.pool.kvpool_release(self.table, self.held, s)
 
+    def truncate(self, s: int, length: int) -> None:
+        """Roll row ``s`` back to ``length`` tokens (rejected speculative drafts);
+        call ``upload_table`` before the next device call that reads the table."""
+        self.pool.kvpool_truncate(self.table, self.held, s, length)
+
     def fork(self, src: int, dst: int, length: int) -> None:
         """Row ``dst`` (empty) shares row ``src``'s blocks for its first ``length`` tokens."""
         self.pool.kvpool_fork(self.table, self.held, src, dst, length)

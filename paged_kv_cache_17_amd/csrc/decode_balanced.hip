@@ -56,6 +56,7 @@ struct BalancedState<4> { using T = DecodeStateG4; };
 // bf16 K/V: per tile, eight 16-byte loads per lane (decode_tile.h layout).
 template <int G>
 struct Bf16Kv {
+    static constexpr int kDepth = 2;   // tiles in flight + 1
     struct Regs {
         u32x4 k[4], v[4];
     };
@@ -78,6 +79,8 @@ struct Bf16Kv {
 // scales this lane's scores and weights need.
 template <int G>
 struct Int8Kv {
+    // a tile is half the bytes of a bf16 one: keep two in flight
+    static constexpr int kDepth = 3;
     static constexpr int kScales = G == 4 ? 1 : 4;
     struct Regs {
         u32x2 k[4], v[4];
@@ -119,8 +122,11 @@ struct Int8Kv {
     }
 };
 
+// At least two waves per SIMD (at most 256 registers per lane): fewer
+// waves would halve the bytes the chip keeps in flight.
 template <int G, class Kv>
-__global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_balanced_kernel(AttnArgs a) {
     extern __shared__ int s_mem[];
     const int S = a.num_seqs;
     int* P = s_mem;              // [S + 1] prefix sums of per-sequence block counts
@@ -229,20 +235,29 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
         }
     };
 
+    // Tiles stream through Kv::kDepth buffers: tile j is issued kDepth - 1
+    // tiles before it is computed. Each buffer keeps its tile's segment and
+    // valid-token count, so the descriptor window may move ahead of the
+    // tile being computed.
+    constexpr int D = Kv::kDepth;
+    struct Buf {
+        typename Kv::Regs t;
+        int seg, ntok;
+    };
     describe(t0);
-    typename Kv::Regs ta, tb;
-    kv.load(ta, __builtin_amdgcn_readlane(i_tile, 0), lane);
+    auto issue = [&](int j, Buf& b) {
+        const int lj = j & (kWave - 1);
+        if (lj == 0 && j > 0) describe(t0 + j);
+        b.seg = __builtin_amdgcn_readlane(i_seg, lj);
+        b.ntok = __builtin_amdgcn_readlane(i_ntok, lj);
+        kv.load(b.t, __builtin_amdgcn_readlane(i_tile, lj), lane);
+    };
 
-    // One step: tile i is in cur; issue tile i+1 into nxt, then compute
-    // tile i.
-    auto step = [&](int i, const typename Kv::Regs& cur, typename Kv::Regs& nxt) {
-        const int li = i & (kWave - 1);
-        const int seg = __builtin_amdgcn_readlane(i_seg, li);
-        const int ntok = __builtin_amdgcn_readlane(i_ntok, li);
-        if (i + 1 < n) {
-            if (li == kWave - 1) describe(t0 + i + 1);
-            kv.load(nxt, __builtin_amdgcn_readlane(i_tile, (i + 1) & (kWave - 1)), lane);
-        }
+    // One step: issue tile i + D - 1 into fut, then compute tile i (in cur).
+    auto step = [&](int i, const Buf& cur, Buf& fut) {
+        if (i + D - 1 < n) issue(i + D - 1, fut);
+        const int seg = cur.seg;
+        const int ntok = cur.ntok;
         if (seg != cur_seg) {
             if (cur_seg >= 0) flush();
             const int s = seg / n_kv;
@@ -257,13 +272,26 @@ __global__ __launch_bounds__(kWave) void decode_balanced_kernel(AttnArgs a) {
         if (ntok < 0) {
             cur_bad = true;
         } else {
-            kv.compute(st, cur, qv, lane, ntok, sl2, s_p);
+            kv.compute(st, cur.t, qv, lane, ntok, sl2, s_p);
         }
     };
 
-    for (int i = 0; i < n; i += 2) {
-        step(i, ta, tb);
-        if (i + 1 < n) step(i + 1, tb, ta);
+    Buf b0, b1;
+    issue(0, b0);
+    if constexpr (D == 2) {
+        for (int i = 0; i < n; i += 2) {
+            step(i, b0, b1);
+            if (i + 1 < n) step(i + 1, b1, b0);
+        }
+    } else {
+        static_assert(D == 3, "pipeline depth 2 or 3");
+        Buf b2;
+        if (n > 1) issue(1, b1);
+        for (int i = 0; i < n; i += 3) {
+            step(i, b0, b2);
+            if (i + 1 < n) step(i + 1, b1, b0);
+            if (i + 2 < n) step(i + 2, b2, b1);
+        }
     }
     flush();
 }

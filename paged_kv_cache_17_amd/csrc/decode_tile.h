@@ -403,18 +403,16 @@ struct DecodeStateG4 {
             pw[4 * q + 0] = t.x; pw[4 * q + 1] = t.y; pw[4 * q + 2] = t.z; pw[4 * q + 3] = t.w;
         }
         __builtin_amdgcn_wave_barrier();   // all lanes read before the next tile overwrites
-        float vf[4][8];
+        // token by token, so only one token's widened codes are live
 #pragma unroll
-        for (int i = 0; i < 4; ++i) widen8_codes(vr[i], vf[i]);
+        for (int i = 0; i < 4; ++i) {
+            float vf[8];
+            widen8_codes(vr[i], vf);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float x = acc[h][k];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x = fmaf(pw[h * 4 + i], vf[i][k], x);
-                acc[h][k] = x;
-            }
+                for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(pw[h * 4 + i], vf[k], acc[h][k]);
+        }
     }
 
     // Per-head (m, l) of this row, in every lane of the row, then the

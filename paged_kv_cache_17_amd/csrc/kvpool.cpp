@@ -263,3 +263,17 @@ extern "C" int kvpool_cow(kvpool_t* p, int32_t* row, int32_t num_held, int32_t s
     *num_copies = c;
     return PKV_OK;
 }
+
+extern "C" int kvpool_truncate(kvpool_t* p, int32_t* row, int32_t* num_held, int32_t length) {
+    if (!p || !num_held) return PKV_ERR_NULL_POINTER;
+    if (length < 0 || *num_held < 0) return PKV_ERR_INVALID_ARGUMENT;
+    const int64_t keep = (static_cast<int64_t>(length) + p->block_size - 1) / p->block_size;
+    if (keep >= *num_held) return PKV_OK;
+    if (!row) return PKV_ERR_NULL_POINTER;
+    const int32_t k = static_cast<int32_t>(keep);
+    const int rc = kvpool_free(p, *num_held - k, row + k);
+    if (rc != PKV_OK) return rc;
+    for (int32_t i = k; i < *num_held; ++i) row[i] = -1;
+    *num_held = k;
+    return PKV_OK;
+}

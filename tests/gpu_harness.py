@@ -168,3 +168,55 @@ def build_gpu_fork_cache(fw, fill_nan=True, share=True):
              i32(pos), i32(starts))
     torch.cuda.synchronize()
     return c, copies
+
+
+class GpuSpec:
+    """Speculative-decoding cycles through the library: history appended
+    once, then per cycle gamma + 1 tokens appended (kv_append), verified as
+    one causal chunk (paged_attn_chunk) and rolled back to the committed
+    length (kvpool_truncate)."""
+
+    def __init__(self, sw, fill_nan=True):
+        import paged_kv_cache_17_amd as pkv
+        self.sw = sw
+        S = sw.num_seqs
+        self.c = pkv.PagedKVCache(sw.num_blocks, sw.n_kv, sw.head_dim, sw.block_size, torch_dtype(sw.dtype), S,
+                                  sw.table_stride, alloc_order=sw.alloc_order, fill_nan=fill_nan,
+                                  poison_workspace=fill_nan)
+        self.lens = np.array(sw.hist_lens, dtype=np.int64)
+        for s in range(S):
+            self.c.ensure(s, int(self.lens[s]))
+        self.c.upload_table()
+        starts = np.zeros(S + 1, dtype=np.int64)
+        np.cumsum(self.lens, out=starts[1:])
+        self.c.append(raw_to_torch(np.concatenate(sw.hist_k), sw.dtype), raw_to_torch(np.concatenate(sw.hist_v), sw.dtype),
+                      i32(np.zeros(S)), i32(starts))
+        g1 = sw.gamma + 1
+        self.q_start = i32(np.arange(S + 1) * g1)
+        self.cyc = [(raw_to_torch(np.concatenate(sw.cyc_k[c]), sw.dtype), raw_to_torch(np.concatenate(sw.cyc_v[c]), sw.dtype),
+                     raw_to_torch(sw.cyc_q[c], sw.dtype)) for c in range(sw.cycles)]
+        torch.cuda.synchronize()
+
+    def append_cycle(self, c, stream=None):
+        sw = self.sw
+        g1 = sw.gamma + 1
+        for s in range(sw.num_seqs):
+            self.c.ensure(s, int(self.lens[s]) + g1)
+        self.c.upload_table()
+        k, v, _ = self.cyc[c]
+        self.c.append(k, v, i32(self.lens), self.q_start, stream=stream)
+
+    def verify(self, c, split_tokens=0, stream=None):
+        sw = self.sw
+        g1 = sw.gamma + 1
+        lens = self.lens + g1
+        return self.c.chunk(self.cyc[c][2], self.q_start, i32(lens), g1, int(lens.max()), sw.scale,
+                            split_tokens=split_tokens, stream=stream)
+
+    def rollback(self, c):
+        sw = self.sw
+        for s in range(sw.num_seqs):
+            keep = int(sw.accepted[c, s]) + 1
+            self.c.truncate(s, int(self.lens[s]) + keep)
+            self.lens[s] += keep
+        self.c.upload_table()

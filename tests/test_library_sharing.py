@@ -144,3 +144,43 @@ def test_cow_errors_change_nothing():
     with pytest.raises(pkv.PagedKVError) as ei:    # fork past the source's blocks
         pool.kvpool_fork(table, np.zeros(3, dtype=np.int32), 0, 1, 9)
     assert ei.value.status == -2
+
+
+def test_truncate_matches_the_oracle():
+    """Rollback (kvpool_truncate) on random rows, some of them sharing blocks."""
+    for seed in range(20):
+        rng = random.Random(seed)
+        n, B, S, cap = 60, rng.choice([1, 4, 16]), 5, 20
+        order = np.array(rng.sample(range(n), n), dtype=np.int32)
+        pool = pkv.KVPool(n, B, order)
+        table = np.full((S, cap), -1, dtype=np.int32)
+        held = np.zeros(S, dtype=np.int32)
+        ora = oracle.BlockAllocator(n, order)
+        rows = [oracle.SequenceBlocks(B) for _ in range(S)]
+        lens = [0] * S
+        for _ in range(80):
+            s = rng.randrange(S)
+            op = rng.random()
+            if op < 0.45:
+                L = min(lens[s] + rng.randint(0, 3 * B), cap * B)
+                if -(-L // B) - len(rows[s].blocks) <= ora.num_free:
+                    rows[s].ensure(ora, L)
+                    pool.kvpool_ensure(table, held, s, L)
+                    lens[s] = max(lens[s], L)
+            elif op < 0.6:
+                t = rng.randrange(S)
+                if t != s and not rows[s].blocks and rows[t].blocks:
+                    L = rng.randint(0, lens[t])
+                    rows[s].fork(ora, rows[t], L)
+                    pool.kvpool_fork(table, held, t, s, L)
+                    lens[s] = L
+            else:
+                L = rng.randint(0, lens[s])
+                rows[s].truncate(ora, L)
+                pool.kvpool_truncate(table, held, s, L)
+                pool.kvpool_truncate(table, held, s, L)
+                lens[s] = L
+            for r in range(S):
+                assert table[r, :held[r]].tolist() == rows[r].blocks
+                assert (table[r, held[r]:] == -1).all()
+            assert pool.kvpool_free_ids().tolist() == ora.free_ids()

@@ -16,3 +16,4 @@ from .synth import (  # noqa: F401
     poison_bits,
 )
 from .forks import ForkWorkload, best_of_n_workload, build_fork_workload  # noqa: F401
+from .speculative import SpecWorkload, build_spec_workload, verify_workload  # noqa: F401
