@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kv", choices=["bf16", "int8"], default="bf16",
                    help="K/V format of the cache: bf16, or 8-bit codes with one fp32 scale per token and kv head")
+    p.add_argument("--sample", action="store_true",
+                   help="time token sampling (temperature 0.8, top-k 50, top-p 0.9) over 64 rows of a "
+                        "128256-entry vocabulary")
     p.add_argument("--verify", action="store_true",
                    help="time a speculative verification step: gamma + 1 = 5 tokens per sequence of the "
                         "64-sequence batch appended and attended as one causal chunk")
@@ -283,6 +286,48 @@ def bench_bestof(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_sample(args):
+    """Token sampling after the LM head: 64 rows x 128256 logits (fp32),
+    temperature 0.8, top-k 50, top-p 0.9, one uniform number per row. A step
+    is one sample_tokens launch; the algorithmic bytes are the logits read
+    once (the kernel's passes over a row after the first hit in L2)."""
+    import torch
+    import paged_kv_cache_17_amd as pkv
+    from workloads import lm_head_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.load_library()
+    sw = lm_head_workload()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    copies = [dev(sw.logits) for _ in range(max(args.copies, 2))]
+    T, k, p, u = dev(sw.temperature), dev(sw.top_k), dev(sw.top_p), dev(sw.u)
+    tok = torch.empty(len(sw.u), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        pkv.sample_tokens(copies[i % len(copies)], T, k, p, u, token=tok, stream=stream)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        pkv.sample_tokens(copies[i % len(copies)], T, k, p, u, token=tok, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    rows, vocab = sw.logits.shape
+    nbytes = rows * vocab * 4
+    line = {
+        "metric": "sampled tokens/s and logits read GB/s, token sampling after the LM head, 1 GPU",
+        "value": rows / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": sw.name, "rows": rows, "vocab": vocab, "logit_bytes": nbytes},
+        "roofline": {"kernel": "sample_tokens", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "traffic": None, "avg_launch_ms": ms, "algorithmic_bytes": nbytes},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_verify(args):
     """Speculative verification step over the 64-sequence batch (lengths
     512..4096 after the append, gamma = 4): append the 5 tokens of every
@@ -380,6 +425,9 @@ def main():
         return
     if args.verify:
         bench_verify(args)
+        return
+    if args.sample:
+        bench_sample(args)
         return
 
     import torch

@@ -369,6 +369,37 @@ int paged_attn_decode_q8(void* out, float* lse, const void* q,
                          float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * sample_tokens - pick the next token of each row of logits.
+ *
+ * Source: lab page, function sample (temperature 0 = greedy, softmax of
+ * logits / T, top-k, then top-p on the renormalised result, then a draw
+ * with the filtered probabilities); chapter 5's filter-and-sample listing
+ * (sort the scaled logits, mask past k, mask where the cumulative
+ * probability before a token reaches p - never the first); serving
+ * tutorial demos D01/D02 (greedy takes the lowest index among tied maxima;
+ * top-k keeps exactly k; top-p keeps the shortest prefix reaching p, the
+ * boundary token included; top-k then top-p is not top-p then top-k).
+ *
+ * Per row: T = temperature[row] (0: greedy on the raw logits; < 0 or NaN:
+ * token -1); z = logit / T in fp32; order by decreasing z, ties to the
+ * lower index; top_k[row] > 0 keeps the first k of that order; masses
+ * exp(z - max z); top_p[row] < 1 keeps the prefix of the order up to the
+ * first token at which the cumulative mass reaches top_p times the kept
+ * total; token = the first index, in vocabulary order, whose cumulative
+ * kept mass exceeds u[row] times the kept total. u is the caller's uniform
+ * random number in [0, 1) (the only randomness; this call draws none).
+ *
+ * logits: device float [rows][ld] (the first vocab entries of each row are
+ *   used; finite values); temperature, top_p, u: device float [rows];
+ *   top_k: device int32 [rows]; token: device int32 [rows] (output);
+ *   kept: device int32 [rows][2] or NULL - tokens kept after top-k and
+ *   after top-p. Errors: NULL_POINTER, INVALID_ARGUMENT (vocab < 1,
+ *   ld < vocab), HIP. */
+int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t rows, int32_t vocab,
+                  int64_t ld, const float* temperature, const int32_t* top_k, const float* top_p,
+                  const float* u, void* stream);
+
+/* ======================================================================
  * Profiling hook (not part of the computation): when both events are
  * non-NULL, paged_attn_decode launches its first-pass (split) kernel and
  * paged_attn_chunk its matrix-core kernel so that the kernel's own dispatch

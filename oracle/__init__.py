@@ -31,3 +31,4 @@ from .paged_attention import (  # noqa: F401
     quantize_absmax,
     widen,
 )
+from . import sampling  # noqa: F401,E402

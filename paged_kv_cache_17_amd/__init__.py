@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     paged_attn_split_tokens,
     paged_attn_workspace_size,
     pkv_set_profile_events,
+    sample_tokens,
     strerror,
 )
 from .cache import PagedKVCache  # noqa: F401

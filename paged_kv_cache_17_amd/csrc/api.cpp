@@ -222,6 +222,17 @@ extern "C" int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_i
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+extern "C" int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t rows, int32_t vocab,
+                             int64_t ld, const float* temperature, const int32_t* top_k, const float* top_p,
+                             const float* u, void* stream) {
+    if (rows < 0 || vocab < 1 || ld < vocab) return PKV_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return PKV_OK;
+    if (!token || !logits || !temperature || !top_k || !top_p || !u) return PKV_ERR_NULL_POINTER;
+    pkv::SampleArgs a{logits, vocab, static_cast<size_t>(ld), temperature, top_k, top_p, u, token, kept};
+    const hipError_t e = pkv::launch_sample(a, rows, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 extern "C" int paged_attn_split_tokens(int32_t num_q_rows, int32_t n_kv, int32_t block_size,
                                        int32_t max_seq_len, int32_t requested, int32_t* out) {
     if (!out) return PKV_ERR_NULL_POINTER;

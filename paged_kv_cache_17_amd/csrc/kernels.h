@@ -58,6 +58,20 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
                                const int32_t* start_pos, const int32_t* new_start, int num_seqs, int total_new,
                                int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream);
 
+// Token sampling after the LM head (one workgroup per row of logits).
+struct SampleArgs {
+    const float* logits;         // [rows][ld], the first vocab entries used
+    int vocab;
+    size_t ld;
+    const float* temperature;    // [rows]
+    const int32_t* top_k;        // [rows], 0 = off
+    const float* top_p;          // [rows], >= 1 = off
+    const float* u;              // [rows] uniform numbers in [0, 1)
+    int32_t* token;              // [rows]
+    int32_t* kept;               // [rows][2] tokens kept by top-k and by top-p, or nullptr
+};
+hipError_t launch_sample(const SampleArgs& a, int rows, hipStream_t stream);
+
 // Whole-block copies (src_ids[i] -> dst_ids[i], both pools) for
 // copy-on-write; block_bytes = n_kv * block_size * head_dim * element size.
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,

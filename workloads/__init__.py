@@ -17,3 +17,4 @@ from .synth import (  # noqa: F401
 )
 from .forks import ForkWorkload, best_of_n_workload, build_fork_workload  # noqa: F401
 from .speculative import SpecWorkload, build_spec_workload, verify_workload  # noqa: F401
+from .sampling import SampleWorkload, build_sample_workload, lm_head_workload  # noqa: F401
