@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--sample", action="store_true",
                    help="time token sampling (temperature 0.8, top-k 50, top-p 0.9) over 64 rows of a "
                         "128256-entry vocabulary")
+    p.add_argument("--sample-topk", type=int, default=50,
+                   help="top-k of the --sample workload (0 = off: every row takes the whole-row path)")
     p.add_argument("--verify", action="store_true",
                    help="time a speculative verification step: gamma + 1 = 5 tokens per sequence of the "
                         "64-sequence batch appended and attended as one causal chunk")
@@ -288,28 +290,30 @@ def bench_bestof(args):
 
 def bench_sample(args):
     """Token sampling after the LM head: 64 rows x 128256 logits (fp32),
-    temperature 0.8, top-k 50, top-p 0.9, one uniform number per row. A step
-    is one sample_tokens launch; the algorithmic bytes are the logits read
-    once (the kernel's passes over a row after the first hit in L2)."""
+    temperature 0.8, top-k 50 (``--sample-topk``; 0 = off), top-p 0.9, one
+    uniform number per row. A step is one sample_tokens call (its candidate
+    kernel, finishing kernel and whole-row kernel, each doing nothing for the
+    rows of the other path); the algorithmic bytes are the logits read once."""
     import torch
     import paged_kv_cache_17_amd as pkv
     from workloads import lm_head_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.load_library()
-    sw = lm_head_workload()
+    sw = lm_head_workload(top_k=args.sample_topk)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     copies = [dev(sw.logits) for _ in range(max(args.copies, 2))]
     T, k, p, u = dev(sw.temperature), dev(sw.top_k), dev(sw.top_p), dev(sw.u)
     tok = torch.empty(len(sw.u), dtype=torch.int32, device="cuda")
+    ws = torch.empty(pkv.sample_workspace_size(*sw.logits.shape), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        pkv.sample_tokens(copies[i % len(copies)], T, k, p, u, token=tok, stream=stream)
+        pkv.sample_tokens(copies[i % len(copies)], T, k, p, u, token=tok, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(args.steps):
-        pkv.sample_tokens(copies[i % len(copies)], T, k, p, u, token=tok, stream=stream)
+        pkv.sample_tokens(copies[i % len(copies)], T, k, p, u, token=tok, workspace=ws, stream=stream)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
@@ -321,7 +325,7 @@ def bench_sample(args):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": sw.name, "rows": rows, "vocab": vocab, "logit_bytes": nbytes},
-        "roofline": {"kernel": "sample_tokens", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+        "roofline": {"kernel": "sample_tokens (all three kernels)", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                      "traffic": None, "avg_launch_ms": ms, "algorithmic_bytes": nbytes},
     }

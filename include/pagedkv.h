@@ -393,11 +393,24 @@ int paged_attn_decode_q8(void* out, float* lse, const void* q,
  *   used; finite values); temperature, top_p, u: device float [rows];
  *   top_k: device int32 [rows]; token: device int32 [rows] (output);
  *   kept: device int32 [rows][2] or NULL - tokens kept after top-k and
- *   after top-p. Errors: NULL_POINTER, INVALID_ARGUMENT (vocab < 1,
- *   ld < vocab), HIP. */
+ *   after top-p. workspace: device memory of at least
+ *   sample_workspace_size(rows, vocab) bytes, 8-byte aligned, owned by the
+ *   caller, holding per-chunk candidates between the call's two kernels
+ *   (contents on entry are ignored; calls sharing one workspace must not
+ *   overlap). Rows with a top-k of at most 256 tokens (and greedy rows) are
+ *   finished from those candidates, other rows by one workgroup over the
+ *   whole row; both give the result defined above. Errors: NULL_POINTER,
+ *   INVALID_ARGUMENT (vocab < 1 or above 8192 x 8192, ld < vocab,
+ *   rows x ceil(vocab / 8192) above INT32_MAX, workspace not 8-byte
+ *   aligned), WORKSPACE_TOO_SMALL, HIP. */
 int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t rows, int32_t vocab,
                   int64_t ld, const float* temperature, const int32_t* top_k, const float* top_p,
-                  const float* u, void* stream);
+                  const float* u, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace sample_tokens needs: rows x ceil(vocab / 8192) chunks,
+ * each with 256 candidate slots of 8 bytes.
+ * Errors: NULL_POINTER, INVALID_ARGUMENT (as for sample_tokens). */
+int sample_workspace_size(int32_t rows, int32_t vocab, size_t* bytes);
 
 /* ======================================================================
  * Profiling hook (not part of the computation): when both events are

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     paged_attn_workspace_size,
     pkv_set_profile_events,
     sample_tokens,
+    sample_workspace_size,
     strerror,
 )
 from .cache import PagedKVCache  # noqa: F401

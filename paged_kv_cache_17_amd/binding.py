@@ -61,7 +61,8 @@ _SIGNATURES = {
     "paged_attn_chunk": ([_p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, ctypes.c_float, _i32, _i32, _p, _size_t, _p], ctypes.c_int),
     "pkv_set_profile_events": ([_p, _p], ctypes.c_int),
-    "sample_tokens": ([_p, _p, _p, _i32, _i32, ctypes.c_int64, _p, _p, _p, _p, _p], ctypes.c_int),
+    "sample_workspace_size": ([_i32, _i32, ctypes.POINTER(_size_t)], ctypes.c_int),
+    "sample_tokens": ([_p, _p, _p, _i32, _i32, ctypes.c_int64, _p, _p, _p, _p, _p, _size_t, _p], ctypes.c_int),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -323,19 +324,31 @@ def paged_attn_chunk(out, lse, q, q_start, k_cache, v_cache, block_table, seq_le
         _stream(stream)))
 
 
-def sample_tokens(logits, temperature, top_k, top_p, u, token=None, kept=None, stream=None):
+def sample_workspace_size(rows, vocab) -> int:
+    """Bytes of device workspace sample_tokens needs for ``rows`` x ``vocab``."""
+    n = _size_t(0)
+    _check("sample_workspace_size", load_library().sample_workspace_size(int(rows), int(vocab), ctypes.byref(n)))
+    return int(n.value)
+
+
+def sample_tokens(logits, temperature, top_k, top_p, u, token=None, kept=None, workspace=None, stream=None):
     """Next token per row of ``logits`` ``[rows, vocab]`` (float32); per-row
     ``temperature``, ``top_k`` (int32), ``top_p``, ``u`` device tensors.
-    Returns the int32 token tensor (and fills ``kept`` [rows, 2] if given)."""
+    ``workspace``: device uint8 tensor of at least sample_workspace_size
+    bytes (allocated here when omitted). Returns the int32 token tensor (and
+    fills ``kept`` [rows, 2] if given)."""
     rows, vocab = logits.shape
     if token is None:
         token = torch.empty(rows, dtype=torch.int32, device=logits.device)
-    _dev(logits, temperature, top_k, top_p, u, token, kept)
+    if workspace is None:
+        workspace = torch.empty(max(1, sample_workspace_size(rows, vocab)), dtype=torch.uint8, device=logits.device)
+    _dev(logits, temperature, top_k, top_p, u, token, kept, workspace)
     if logits.dtype != torch.float32 or top_k.dtype != torch.int32:
         raise TypeError("float32 logits and int32 top_k required")
     _check("sample_tokens", load_library().sample_tokens(
         _ptr(token), _ptr(kept), _ptr(logits), int(rows), int(vocab), int(logits.stride(0)), _ptr(temperature),
-        _ptr(top_k), _ptr(top_p), _ptr(u), _stream(stream)))
+        _ptr(top_k), _ptr(top_p), _ptr(u), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+        _stream(stream)))
     return token
 
 

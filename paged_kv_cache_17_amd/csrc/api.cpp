@@ -222,13 +222,25 @@ extern "C" int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_i
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+extern "C" int sample_workspace_size(int32_t rows, int32_t vocab, size_t* bytes) {
+    if (!bytes) return PKV_ERR_NULL_POINTER;
+    if (rows < 0 || vocab < 1 || vocab > pkv::kSampleChunk * pkv::kSampleMaxCand) return PKV_ERR_INVALID_ARGUMENT;
+    *bytes = pkv::sample_workspace_bytes(rows, vocab);
+    return PKV_OK;
+}
+
 extern "C" int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t rows, int32_t vocab,
                              int64_t ld, const float* temperature, const int32_t* top_k, const float* top_p,
-                             const float* u, void* stream) {
+                             const float* u, void* workspace, size_t workspace_bytes, void* stream) {
     if (rows < 0 || vocab < 1 || ld < vocab) return PKV_ERR_INVALID_ARGUMENT;
+    if (vocab > pkv::kSampleChunk * pkv::kSampleMaxCand) return PKV_ERR_INVALID_ARGUMENT;
+    if (static_cast<int64_t>(rows) * pkv::sample_chunks(vocab) > INT32_MAX) return PKV_ERR_INVALID_ARGUMENT;
     if (rows == 0) return PKV_OK;
-    if (!token || !logits || !temperature || !top_k || !top_p || !u) return PKV_ERR_NULL_POINTER;
-    pkv::SampleArgs a{logits, vocab, static_cast<size_t>(ld), temperature, top_k, top_p, u, token, kept};
+    if (!token || !logits || !temperature || !top_k || !top_p || !u || !workspace) return PKV_ERR_NULL_POINTER;
+    if (workspace_bytes < pkv::sample_workspace_bytes(rows, vocab)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0) return PKV_ERR_INVALID_ARGUMENT;
+    pkv::SampleArgs a{logits, vocab, static_cast<size_t>(ld), temperature, top_k, top_p, u, token, kept,
+                      static_cast<uint2*>(workspace), pkv::sample_chunks(vocab)};
     const hipError_t e = pkv::launch_sample(a, rows, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -58,7 +58,18 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
                                const int32_t* start_pos, const int32_t* new_start, int num_seqs, int total_new,
                                int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream);
 
-// Token sampling after the LM head (one workgroup per row of logits).
+// Token sampling after the LM head. Rows whose top-k set is small go
+// through a candidate pass (chunks of kSampleChunk logits, each keeping its
+// own top-k) and are finished from those candidates; the others by one
+// workgroup over the whole row.
+constexpr int kSampleChunk = 8192;      // logits per candidate-pass workgroup
+constexpr int kSampleMaxK = 256;        // largest top-k on the candidate path
+constexpr int kSampleMaxCand = 8192;    // candidates one finishing workgroup holds
+inline int sample_chunks(int vocab) { return (vocab + kSampleChunk - 1) / kSampleChunk; }
+// workspace: candidates [rows][chunks][kSampleMaxK] uint2
+inline size_t sample_workspace_bytes(int rows, int vocab) {
+    return static_cast<size_t>(rows) * sample_chunks(vocab) * kSampleMaxK * 8u;
+}
 struct SampleArgs {
     const float* logits;         // [rows][ld], the first vocab entries used
     int vocab;
@@ -69,6 +80,8 @@ struct SampleArgs {
     const float* u;              // [rows] uniform numbers in [0, 1)
     int32_t* token;              // [rows]
     int32_t* kept;               // [rows][2] tokens kept by top-k and by top-p, or nullptr
+    uint2* cand;                 // [rows][chunks][kSampleMaxK] (key, index) candidates
+    int chunks;                  // sample_chunks(vocab)
 };
 hipError_t launch_sample(const SampleArgs& a, int rows, hipStream_t stream);
 

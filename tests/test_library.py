@@ -177,3 +177,34 @@ def test_decode_argument_errors_come_before_any_launch():
     assert _call_decode(ws=256, ws_bytes=10) == -6    # workspace too small
     assert _call_decode(ws=300, ws_bytes=1 << 30) == -2   # workspace not 256-byte aligned
     assert _call_decode(S=0) == 0                     # nothing to do
+
+
+def _call_sample(**over):
+    lib = pkv.load_library()
+    a = dict(token=1, kept=None, logits=1, rows=4, vocab=20000, ld=20000, T=1, k=1, p=1, u=1, ws=1,
+             ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
+    return lib.sample_tokens(p(a["token"]), p(a["kept"]), p(a["logits"]), a["rows"], a["vocab"], a["ld"],
+                             p(a["T"]), p(a["k"]), p(a["p"]), p(a["u"]), p(a["ws"]), a["ws_bytes"],
+                             p(a["stream"]))
+
+
+def test_sampling_workspace_and_argument_errors():
+    # rows x ceil(vocab / 8192) chunks x 256 candidate slots x 8 bytes
+    assert pkv.sample_workspace_size(4, 20000) == 4 * 3 * 2048
+    assert pkv.sample_workspace_size(64, 128256) == 64 * 16 * 2048
+    assert pkv.sample_workspace_size(1, 8192) == 2048
+    with pytest.raises(pkv.PagedKVError):
+        pkv.sample_workspace_size(1, 0)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.sample_workspace_size(1, 8192 * 8192 + 1)
+    # every case fails host-side validation (the dummy pointers are never used)
+    assert _call_sample(vocab=0) == -2
+    assert _call_sample(ld=100) == -2
+    assert _call_sample(vocab=8192 * 8192 + 1, ld=8192 * 8192 + 1) == -2
+    assert _call_sample(u=0) == -1
+    assert _call_sample(ws=0) == -1
+    assert _call_sample(ws_bytes=4 * 3 * 2048 - 1) == -6
+    assert _call_sample(ws=260) == -2                 # workspace not 8-byte aligned
+    assert _call_sample(rows=0) == 0

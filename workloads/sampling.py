@@ -37,13 +37,13 @@ def build_sample_workload(rows, vocab, seed=7, temps=(0.0, 0.3, 0.8, 1.5), ks=(0
                           u=rng.random(rows).astype(np.float32))
 
 
-def lm_head_workload(seed=7) -> SampleWorkload:
-    """64 rows over a 128256-entry vocabulary: temperature 0.8, top-k 50,
-    top-p 0.9 (a common serving setting), logits ~ N(0, 4)."""
+def lm_head_workload(seed=7, top_k=50) -> SampleWorkload:
+    """64 rows over a 128256-entry vocabulary: temperature 0.8, top-k 50
+    (0 = off), top-p 0.9 (a common serving setting), logits ~ N(0, 4)."""
     rng = np.random.default_rng(seed)
     rows, vocab = 64, 128256
-    return SampleWorkload(name="sample-64rows-vocab128256-T0.8-k50-p0.9",
+    return SampleWorkload(name=f"sample-64rows-vocab128256-T0.8-k{top_k}-p0.9",
                           logits=(rng.standard_normal((rows, vocab)) * 2.0).astype(np.float32),
                           temperature=np.full(rows, 0.8, dtype=np.float32),
-                          top_k=np.full(rows, 50, dtype=np.int32), top_p=np.full(rows, 0.9, dtype=np.float32),
+                          top_k=np.full(rows, top_k, dtype=np.int32), top_p=np.full(rows, 0.9, dtype=np.float32),
                           u=rng.random(rows).astype(np.float32))
