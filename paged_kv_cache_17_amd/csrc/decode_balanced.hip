@@ -79,8 +79,9 @@ struct Bf16Kv {
 // scales this lane's scores and weights need.
 template <int G>
 struct Int8Kv {
-    // a tile is half the bytes of a bf16 one: keep two in flight
-    static constexpr int kDepth = 3;
+    // a tile is half the bytes of a bf16 one: keep two in flight (one with
+    // two query heads per kv head, whose registers would otherwise spill)
+    static constexpr int kDepth = G == 2 ? 2 : 3;
     static constexpr int kScales = G == 4 ? 1 : 4;
     struct Regs {
         u32x2 k[4], v[4];
@@ -123,9 +124,11 @@ struct Int8Kv {
 };
 
 // At least two waves per SIMD (at most 256 registers per lane): fewer
-// waves would halve the bytes the chip keeps in flight.
+// waves would halve the bytes the chip keeps in flight. Eight query heads
+// per kv head need more registers than that (state, query and two tiles):
+// one wave per SIMD, with the grid sized to match.
 template <int G, class Kv>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(G == 8 ? 1 : 2)))
 void decode_balanced_kernel(AttnArgs a) {
     extern __shared__ int s_mem[];
     const int S = a.num_seqs;
@@ -211,7 +214,7 @@ void decode_balanced_kernel(AttnArgs a) {
     int cur_seg = -1;
     bool cur_bad = false;
 
-    auto flush = [&]() {
+    auto flush = [&]() __attribute__((always_inline)) {
         float fm[G], fl[G];
         if constexpr (G == 4) {
             st.finish(lane, fm, fl);
