@@ -65,8 +65,8 @@ def parse():
 # that kernel's sources matches the one it records.
 COUNTERS = {
     "decode": (os.path.join(ROOT, "profiles", "decode_split_c2_counters.txt"),
-               ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_tile.h",
-                "paged_kv_cache_17_amd/csrc/device_common.h"]),
+               ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_mfma.h",
+                "paged_kv_cache_17_amd/csrc/decode_tile.h", "paged_kv_cache_17_amd/csrc/device_common.h"]),
     "chunk": (os.path.join(ROOT, "profiles", "chunk_mfma_c5_counters.txt"),
               ["paged_kv_cache_17_amd/csrc/chunk_mfma.hip", "paged_kv_cache_17_amd/csrc/device_common.h"]),
 }

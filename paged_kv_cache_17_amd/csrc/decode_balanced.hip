@@ -23,39 +23,82 @@
 //    always suffice;
 //  * the next tile's loads are issued before the current tile is computed,
 //    so every wave always has a tile in flight;
-//  * with four query heads per kv head the per-tile math is the
-//    reduce-scatter / one-exponential-per-lane form (DecodeStateG4);
+//  * with four query heads per kv head both per-tile products run on the
+//    matrix cores (decode_mfma.h); other group sizes use the vector-ALU
+//    tile math of decode_tile.h;
 //  * the K/V format is a template parameter: bf16 tiles, or 8-bit codes
 //    with one fp32 scale per (token, kv head) (half the bytes; the scales
-//    are folded into the scores and the weights, see decode_tile.h).
+//    are folded into the scores and the weights).
 //
 // Per-sequence block counts (ceil(L / 16), 0 for an invalid length) and
 // their prefix sums are built by every wave in LDS from seq_lens; wave 0
 // also stores the prefix for the merge pass. A tile whose table entry is
 // outside the pool is not used and its segment's partial is NaN.
+#include "decode_mfma.h"
 #include "decode_tile.h"
 #include "kernels.h"
 
 namespace pkv {
 namespace {
 
-// Dynamic LDS of one workgroup: prefix [S+1], lengths [S], then a 64-float
-// slot (16-byte aligned) for handing weights between lanes.
+// Dynamic LDS of one workgroup: prefix [S+1], then lengths [S].
 __host__ __device__ inline size_t balanced_lds_ints(int num_seqs) {
-    return (2 * static_cast<size_t>(num_seqs) + 1 + 3) / 4 * 4;
+    return 2 * static_cast<size_t>(num_seqs) + 1;
 }
 __host__ inline size_t balanced_lds_bytes(int num_seqs) {
-    return sizeof(int) * (balanced_lds_ints(num_seqs) + kWave);
+    return sizeof(int) * balanced_lds_ints(num_seqs);
 }
 
+
+// Query load and partial write of the vector-ALU tile math (decode_tile.h
+// layout: lane (r, c) works on dims 8c .. 8c+7; rows r = 0 hold the state
+// after the merge).
 template <int G>
-struct BalancedState { using T = DecodeState<G>; };
-template <>
-struct BalancedState<4> { using T = DecodeStateG4; };
+struct ValuRows {
+    using State = DecodeState<G>;
+    static constexpr int kQ = G;
+    static constexpr int kWaves = G == 8 ? 1 : 2;   // waves per SIMD the registers allow
+    __device__ __forceinline__ static void load_q(u32x4 (&qv)[kQ], const uint16_t* q_sg, int lane) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(q_sg + h * kTileD + (lane & 15) * 8);
+    }
+    __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, bool bad, int lane) {
+        const int c = lane & 15;
+        st.merge_rows();
+        if ((lane >> 4) == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float4* o = reinterpret_cast<float4*>(a.ws_o + (p * G + h) * kTileD + c * 8);
+                o[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+                o[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+                if (c == 0) a.ws_ml[p * G + h] = bad ? PartialML{NAN, NAN} : PartialML{st.m[h], st.l[h]};
+            }
+        }
+    }
+};
+
+// Query load and partial write of the matrix-core tile math (decode_mfma.h
+// layout: lane (q, n) holds head n's query at dims 32b + 8q .. +7, zero for
+// n >= 4).
+struct MfmaRows {
+    using State = MfmaStateG4;
+    static constexpr int kQ = 4;
+    static constexpr int kWaves = 2;
+    __device__ __forceinline__ static void load_q(u32x4 (&qv)[kQ], const uint16_t* q_sg, int lane) {
+        const int n = lane & 15;
+        const int q = lane >> 4;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            qv[b] = n < 4 ? *reinterpret_cast<const u32x4*>(q_sg + n * kTileD + 32 * b + 8 * q) : u32x4{0, 0, 0, 0};
+    }
+    __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, bool bad, int lane) {
+        st.write_partial(a.ws_o, a.ws_ml, p, bad, lane);
+    }
+};
 
 // bf16 K/V: per tile, eight 16-byte loads per lane (decode_tile.h layout).
 template <int G>
-struct Bf16Kv {
+struct Bf16Kv : ValuRows<G> {
     static constexpr int kDepth = 2;   // tiles in flight + 1
     struct Regs {
         u32x4 k[4], v[4];
@@ -68,24 +111,22 @@ struct Bf16Kv {
         const size_t off = static_cast<size_t>(tile) * kTileElems;
         load_tile(kc + off, vc + off, t.k, t.v);
     }
-    __device__ __forceinline__ void compute(typename BalancedState<G>::T& st, const Regs& t, const u32x4 (&qv)[G],
-                                            int lane, int ntok, float sl2, float* s_p) const {
-        if constexpr (G == 4) st.tile(t.k, t.v, qv, lane, ntok, sl2, s_p);
-        else st.tile(t.k, t.v, qv, lane >> 4, ntok, sl2);
+    __device__ __forceinline__ void compute(DecodeState<G>& st, const Regs& t, const u32x4 (&qv)[G],
+                                            int lane, int ntok, float sl2) const {
+        st.tile(t.k, t.v, qv, lane >> 4, ntok, sl2);
     }
 };
 
 // 8-bit codes + fp32 scales: per tile, eight 8-byte code loads and the
 // scales this lane's scores and weights need.
 template <int G>
-struct Int8Kv {
+struct Int8Kv : ValuRows<G> {
     // a tile is half the bytes of a bf16 one: keep two in flight (one with
     // two query heads per kv head, whose registers would otherwise spill)
     static constexpr int kDepth = G == 2 ? 2 : 3;
-    static constexpr int kScales = G == 4 ? 1 : 4;
     struct Regs {
         u32x2 k[4], v[4];
-        float sk[kScales], sv[kScales];
+        float sk[4], sv[4];   // tokens 4i + r
     };
     const int8_t* kc;
     const int8_t* vc;
@@ -104,22 +145,98 @@ struct Int8Kv {
         for (int i = 0; i < 4; ++i) t.v[i] = __builtin_nontemporal_load(vp + i * 64);
         const size_t so = static_cast<size_t>(tile) * kTileB;
         const int r = lane >> 4;
-        if constexpr (G == 4) {
-            const int tok = 4 * (lane & 3) + r;        // token of this lane's score
-            t.sk[0] = ks[so + tok];
-            t.sv[0] = vs[so + tok];
-        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                t.sk[i] = ks[so + 4 * i + r];
-                t.sv[i] = vs[so + 4 * i + r];
-            }
+        for (int i = 0; i < 4; ++i) {
+            t.sk[i] = ks[so + 4 * i + r];
+            t.sv[i] = vs[so + 4 * i + r];
         }
     }
-    __device__ __forceinline__ void compute(typename BalancedState<G>::T& st, const Regs& t, const u32x4 (&qv)[G],
-                                            int lane, int ntok, float sl2, float* s_p) const {
-        if constexpr (G == 4) st.tile_q8(t.k, t.v, t.sk[0], t.sv[0], qv, lane, ntok, sl2, s_p);
-        else st.tile_q8(t.k, t.v, t.sk, t.sv, qv, lane >> 4, ntok, sl2);
+    __device__ __forceinline__ void compute(DecodeState<G>& st, const Regs& t, const u32x4 (&qv)[G],
+                                            int lane, int ntok, float sl2) const {
+        st.tile_q8(t.k, t.v, t.sk, t.sv, qv, lane >> 4, ntok, sl2);
+    }
+};
+
+// Four query heads per kv head: both products on the matrix cores
+// (decode_mfma.h). Lane (q, n) loads token n's K at dims 32b + 8q .. +7
+// (b = 0..3) and tokens 4q .. 4q+3's V at dims 8n .. 8n+7: the same bytes per
+// tile as the vector-ALU layout, in the operand layouts of the two products.
+template <>
+struct Bf16Kv<4> : MfmaRows {
+    static constexpr int kDepth = 2;
+    struct Regs {
+        u32x4 k[4], v[4];
+    };
+    const uint16_t* kc;
+    const uint16_t* vc;
+    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane)
+        : kc(static_cast<const uint16_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
+          vc(static_cast<const uint16_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)) {}
+    __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
+        const size_t off = static_cast<size_t>(tile) * kTileElems;
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kc + off);
+        const u32x4* vp = reinterpret_cast<const u32x4*>(vc + off);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) t.k[b] = __builtin_nontemporal_load(kp + 4 * b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
+    }
+    __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
+                                            float sl2) const {
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[b]),
+                                                        __builtin_bit_cast(bf16x8, qv[b]), s, 0, 0, 0);
+        // rows past the sequence end may hold anything (NaN): zero them
+        u32x4 v[4];
+        const int q = lane >> 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = 4 * q + e < ntok ? t.v[e] : u32x4{0, 0, 0, 0};
+        const float none[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        st.update<false>(s, none, none, [&](int j) { return v_operand_bf16(v, j); }, lane, ntok, sl2);
+    }
+};
+
+template <>
+struct Int8Kv<4> : MfmaRows {
+    static constexpr int kDepth = 2;
+    struct Regs {
+        u32x2 k[4], v[4];
+        float4 sk, sv;
+    };
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* ks;
+    const float* vs;
+    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane)
+        : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
+          vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
+          ks(a.k_scale + 4 * (lane >> 4)),
+          vs(a.v_scale + 4 * (lane >> 4)) {}
+    __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
+        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
+        const u32x2* kp = reinterpret_cast<const u32x2*>(kc + off);
+        const u32x2* vp = reinterpret_cast<const u32x2*>(vc + off);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) t.k[b] = __builtin_nontemporal_load(kp + 4 * b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
+        const size_t so = static_cast<size_t>(tile) * kTileB;
+        t.sk = *reinterpret_cast<const float4*>(ks + so);
+        t.sv = *reinterpret_cast<const float4*>(vs + so);
+    }
+    __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
+                                            float sl2) const {
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(t.k[b])),
+                                                        __builtin_bit_cast(bf16x8, qv[b]), s, 0, 0, 0);
+        // codes are finite whatever the slot holds; weights past the end are 0
+        const float sk[4] = {t.sk.x, t.sk.y, t.sk.z, t.sk.w};
+        const float sv[4] = {t.sv.x, t.sv.y, t.sv.z, t.sv.w};
+        st.update<true>(s, sk, sv, [&](int j) { return v_operand_codes(t.v, j); }, lane, ntok, sl2);
     }
 };
 
@@ -128,13 +245,12 @@ struct Int8Kv {
 // per kv head need more registers than that (state, query and two tiles):
 // one wave per SIMD, with the grid sized to match.
 template <int G, class Kv>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(G == 8 ? 1 : 2)))
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(Kv::kWaves)))
 void decode_balanced_kernel(AttnArgs a) {
     extern __shared__ int s_mem[];
     const int S = a.num_seqs;
     int* P = s_mem;              // [S + 1] prefix sums of per-sequence block counts
     int* Ls = s_mem + S + 1;     // [S] lengths (0 when invalid)
-    float* s_p = reinterpret_cast<float*>(s_mem + balanced_lds_ints(S));
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
     const int table_tokens = a.table_stride * kTileB;
@@ -202,40 +318,18 @@ void decode_balanced_kernel(AttnArgs a) {
         }
     };
 
-    const int c = lane & 15;
-    const int r = lane >> 4;
     const Kv kv(a, lane);
-    const uint16_t* qc = static_cast<const uint16_t*>(a.q) + c * 8;
+    const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
     const float sl2 = a.scale_log2;
 
-    typename BalancedState<G>::T st;
+    typename Kv::State st;
     st.reset();
-    u32x4 qv[G];
+    u32x4 qv[Kv::kQ];
     int cur_seg = -1;
     bool cur_bad = false;
 
     auto flush = [&]() __attribute__((always_inline)) {
-        float fm[G], fl[G];
-        if constexpr (G == 4) {
-            st.finish(lane, fm, fl);
-        } else {
-            st.merge_rows();
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                fm[h] = st.m[h];
-                fl[h] = st.l[h];
-            }
-        }
-        const size_t p = static_cast<size_t>(w) + cur_seg;
-        if (r == 0) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float4* o = reinterpret_cast<float4*>(a.ws_o + (p * G + h) * kTileD + c * 8);
-                o[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
-                o[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
-                if (c == 0) a.ws_ml[p * G + h] = cur_bad ? PartialML{NAN, NAN} : PartialML{fm[h], fl[h]};
-            }
-        }
+        kv.flush(st, a, static_cast<size_t>(w) + cur_seg, cur_bad, lane);
     };
 
     // Tiles stream through Kv::kDepth buffers: tile j is issued kDepth - 1
@@ -265,9 +359,7 @@ void decode_balanced_kernel(AttnArgs a) {
             if (cur_seg >= 0) flush();
             const int s = seg / n_kv;
             const int g = seg - s * n_kv;
-            const uint16_t* qs = qc + (static_cast<size_t>(s) * n_kv * G + g * G) * kTileD;
-#pragma unroll
-            for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(qs + h * kTileD);
+            kv.load_q(qv, qbase + (static_cast<size_t>(s) * n_kv * G + g * G) * kTileD, lane);
             st.reset();
             cur_seg = seg;
             cur_bad = false;
@@ -275,7 +367,7 @@ void decode_balanced_kernel(AttnArgs a) {
         if (ntok < 0) {
             cur_bad = true;
         } else {
-            kv.compute(st, cur.t, qv, lane, ntok, sl2, s_p);
+            kv.compute(st, cur.t, qv, lane, ntok, sl2);
         }
     };
 

@@ -218,233 +218,3 @@ struct DecodeState {
 };
 
 }  // namespace pkv
-
-namespace pkv {
-
-// Reduce-scatter over the 16 lanes of a DPP row: on entry every lane holds
-// 16 partial values v[j]; on exit lane c of the row holds the row total of
-// v[c]. Four halving steps, each pairing lanes that differ in one more bit
-// of c (partners c^15, c^7, c^2, c^1 via row_mirror, row_half_mirror and
-// quad permutes): a lane keeps the half of its values whose index bit
-// matches its own and adds the partner's copy of that half.
-__device__ __forceinline__ float row16_reduce_scatter(const float (&v)[16], int c) {
-    const bool b3 = c & 8, b2 = c & 4, b1 = c & 2, b0 = c & 1;
-    float s1[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float keep = b3 ? v[k + 8] : v[k];
-        const float send = b3 ? v[k] : v[k + 8];
-        s1[k] = keep + __builtin_amdgcn_update_dpp(0.0f, send, 0x140, 0xF, 0xF, false);   // row_mirror
-    }
-    float s2[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float keep = b2 ? s1[k + 4] : s1[k];
-        const float send = b2 ? s1[k] : s1[k + 4];
-        s2[k] = keep + __builtin_amdgcn_update_dpp(0.0f, send, 0x141, 0xF, 0xF, false);   // row_half_mirror
-    }
-    float s3[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const float keep = b1 ? s2[k + 2] : s2[k];
-        const float send = b1 ? s2[k] : s2[k + 2];
-        s3[k] = keep + __builtin_amdgcn_update_dpp(0.0f, send, 0x4E, 0xF, 0xF, false);    // lane ^ 2
-    }
-    const float keep = b0 ? s3[1] : s3[0];
-    const float send = b0 ? s3[0] : s3[1];
-    return keep + __builtin_amdgcn_update_dpp(0.0f, send, 0xB1, 0xF, 0xF, false);         // lane ^ 1
-}
-
-// Online-softmax state for four query heads per kv head, with the tile's
-// 16 scores (4 tokens x 4 heads per row) spread one per lane: lane c of a
-// row owns head h = c / 4 and token slot i = c % 4 (token 4i + r of the
-// tile). Per tile each lane computes one exponential. The reference max
-// mref (per row and head) only moves when a new score exceeds it by more
-// than kLazy (log2 units), so p = 2^(s - mref) <= 2^kLazy and rescaling the
-// accumulators is rare; the partial state (mref, l, acc) is exact for any
-// reference value.
-struct DecodeStateG4 {
-    static constexpr int G = 4;
-    static constexpr float kLazy = 8.0f;
-    float mref;        // reference max of this lane's (row, head), log2 units
-    float mref_safe;   // mref, or 0 while it is still -inf
-    float l;           // sum of this lane's p
-    float acc[G][8];   // sum over the row's tokens of p * v, per head, this lane's 8 dims
-
-    __device__ __forceinline__ void reset() {
-        mref = -INFINITY;
-        mref_safe = 0.0f;
-        l = 0.0f;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) acc[h][k] = 0.0f;
-    }
-
-    // s_p: this wave's 64-float LDS slot used to hand the 16 weights of a row
-    // to every lane of the row.
-    __device__ __forceinline__ void tile(const u32x4 (&kr)[4], const u32x4 (&vr)[4], const u32x4 (&qv)[G],
-                                         int lane, int ntok, float sl2, float* s_p) {
-        const int c = lane & 15;
-        const int r = lane >> 4;
-        float part[16];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part[h * 4 + i] = dot8_bf16(kr[i], qv[h]);
-        const int i_own = c & 3;
-        const bool valid = 4 * i_own + r < ntok;
-        // The cross-lane reduction must run with every lane active, so it is
-        // computed before (not inside) the selection.
-        const float red = row16_reduce_scatter(part, c);
-        const float s = valid ? red * sl2 : -INFINITY;
-        // max over the 4 tokens of this (row, head): the lanes of one quad
-        float mx = fmaxf(s, __builtin_amdgcn_update_dpp(0.0f, s, 0xB1, 0xF, 0xF, false));
-        mx = fmaxf(mx, __builtin_amdgcn_update_dpp(0.0f, mx, 0x4E, 0xF, 0xF, false));
-        const bool need = mx > mref + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float nref = need ? mx : mref;
-            const float alpha = (nref == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
-            l *= alpha;
-            float al[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) al[h] = __shfl(alpha, (lane & 48) | (h << 2), kWave);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[h][k] *= al[h];
-            mref = nref;
-            mref_safe = (nref == -INFINITY) ? 0.0f : nref;
-        }
-        const float p = __builtin_amdgcn_exp2f(s - mref_safe);
-        l += p;
-        // hand the row's 16 weights to every lane of the row
-        s_p[lane] = p;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float pw[16];
-        const float4* row = reinterpret_cast<const float4*>(s_p + (lane & 48));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 t = row[q];
-            pw[4 * q + 0] = t.x; pw[4 * q + 1] = t.y; pw[4 * q + 2] = t.z; pw[4 * q + 3] = t.w;
-        }
-        __builtin_amdgcn_wave_barrier();   // all lanes read before the next tile overwrites
-        float vf[4][8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) widen8_bf16(vr[i], vf[i]);
-        if (ntok < kTileB) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = 4 * i + r < ntok;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) vf[i][k] = ok ? vf[i][k] : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float x = acc[h][k];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x = fmaf(pw[h * 4 + i], vf[i][k], x);
-                acc[h][k] = x;
-            }
-    }
-
-    // The same for a quantised tile. sk, sv: the K and V scales of the token
-    // this lane's score belongs to (4 (c % 4) + r). The score is the code dot
-    // product times sk; the weight handed to the row is p * sv, so the P.V
-    // products run on the codes; the normaliser keeps p.
-    __device__ __forceinline__ void tile_q8(const u32x2 (&kr)[4], const u32x2 (&vr)[4], float sk, float sv,
-                                            const u32x4 (&qv)[G], int lane, int ntok, float sl2, float* s_p) {
-        const int c = lane & 15;
-        const int r = lane >> 4;
-        float part[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 kb = codes8_to_bf16x8(kr[i]);
-#pragma unroll
-            for (int h = 0; h < G; ++h) part[h * 4 + i] = dot8_bf16(kb, qv[h]);
-        }
-        const int i_own = c & 3;
-        const bool valid = 4 * i_own + r < ntok;
-        const float red = row16_reduce_scatter(part, c);
-        const float s = valid ? red * sk * sl2 : -INFINITY;
-        float mx = fmaxf(s, __builtin_amdgcn_update_dpp(0.0f, s, 0xB1, 0xF, 0xF, false));
-        mx = fmaxf(mx, __builtin_amdgcn_update_dpp(0.0f, mx, 0x4E, 0xF, 0xF, false));
-        const bool need = mx > mref + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float nref = need ? mx : mref;
-            const float alpha = (nref == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
-            l *= alpha;
-            float al[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) al[h] = __shfl(alpha, (lane & 48) | (h << 2), kWave);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[h][k] *= al[h];
-            mref = nref;
-            mref_safe = (nref == -INFINITY) ? 0.0f : nref;
-        }
-        const float p = __builtin_amdgcn_exp2f(s - mref_safe);
-        l += p;
-        s_p[lane] = valid ? p * sv : 0.0f;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float pw[16];
-        const float4* row = reinterpret_cast<const float4*>(s_p + (lane & 48));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 t = row[q];
-            pw[4 * q + 0] = t.x; pw[4 * q + 1] = t.y; pw[4 * q + 2] = t.z; pw[4 * q + 3] = t.w;
-        }
-        __builtin_amdgcn_wave_barrier();   // all lanes read before the next tile overwrites
-        // token by token, so only one token's widened codes are live
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float vf[8];
-            widen8_codes(vr[i], vf);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(pw[h * 4 + i], vf[k], acc[h][k]);
-        }
-    }
-
-    // Per-head (m, l) of this row, in every lane of the row, then the
-    // cross-row merge; afterwards all lanes hold the wave's merged state.
-    __device__ __forceinline__ void finish(int lane, float (&m_out)[G], float (&l_out)[G]) {
-        float lq = l + __builtin_amdgcn_update_dpp(0.0f, l, 0xB1, 0xF, 0xF, false);
-        lq += __builtin_amdgcn_update_dpp(0.0f, lq, 0x4E, 0xF, 0xF, false);
-        float m[G], lh[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            m[h] = __shfl(mref, (lane & 48) | (h << 2), kWave);
-            lh[h] = __shfl(lq, (lane & 48) | (h << 2), kWave);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float M = fmaxf(m[h], __shfl_xor(m[h], 16, kWave));
-            M = fmaxf(M, __shfl_xor(M, 32, kWave));
-            const float w = __builtin_amdgcn_exp2f(m[h] - ((M == -INFINITY) ? 0.0f : M));
-            float lw = lh[h] * w;
-            lw += __shfl_xor(lw, 16, kWave);
-            lw += __shfl_xor(lw, 32, kWave);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float x = acc[h][k] * w;
-                x += __shfl_xor(x, 16, kWave);
-                x += __shfl_xor(x, 32, kWave);
-                acc[h][k] = x;
-            }
-            m_out[h] = M;
-            l_out[h] = lw;
-        }
-    }
-};
-
-}  // namespace pkv
