@@ -198,6 +198,32 @@ def test_chunk_matrix_core_path_shapes(n_q, n_kv):
     say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
 
 
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (64, 8)])
+def test_small_chunks_over_long_histories(n_q, n_kv):
+    """Verification-sized chunks (1 .. one query tile) over histories that end
+    just before, at and after multiples of 1024 keys; a sequence whose table
+    names a block outside the pool gives NaN rows only for itself."""
+    qt = 128 // (n_q // n_kv)
+    hist = [1018, 1019, 2043, 3000, 4090, 0, 1023, 1024, 700]
+    new = [5, 6, 5, qt, 5, min(17, qt), 1, 1, 3]
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist,
+                        new_lens=new, seed=21)
+    say("small chunks, long histories", n_q, n_kv)
+    _, _, err, lerr = _full_check(wl, "chunk", 0, check_pool=False)
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+    # one bad table entry (in the first range of sequence 3)
+    c = build_gpu_cache(wl)
+    ora = oracle.build_cache(wl)
+    c.table_dev[3, 2] = 10 ** 6
+    out, lse = run_chunk(c, wl)
+    got = out_f64(out, BF16)
+    ref, _ = oracle.paged_attention_all(ora)
+    lo, hi = int(wl.q_offsets[3]), int(wl.q_offsets[4])
+    assert np.isnan(got[lo:hi]).all() and np.isnan(lse[lo:hi].cpu().numpy()).all()
+    keep = [r for r in range(got.shape[0]) if not lo <= r < hi]
+    check_rows(got[keep], ref[keep], BF16, "rows next to a bad table")
+
+
 def test_lab_prompt_as_chunks_5_then_4():
     """The lab's 9-token prompt run as chunks [5, 4] equals one 9-token chunk."""
     one = build_workload(n_q=2, n_kv=2, head_dim=4, block_size=4, dtype=F32, hist_lens=[0], new_lens=[9],
