@@ -337,9 +337,11 @@ def bench_verify(args):
     512..4096 after the append, gamma = 4): append the 5 tokens of every
     sequence (the pending token and 4 drafts; re-appending the same tokens
     is idempotent) and verify them with one causal chunk of 5 queries per
-    sequence. Timed with the matrix-core chunk kernel (the library's choice)
-    and with the VALU split path (split_tokens 256) beside it. The chunk
-    reads each sequence's K/V once: the roofline is HBM."""
+    sequence. Timed with the library's choice (the balanced partition over
+    every (sequence, kv head, block) tile with the 20 (query, head) rows of a
+    kv head on the matrix cores, then the merge) and with the VALU split path
+    (split_tokens 256) beside it. The pass reads each sequence's K/V once:
+    the roofline is HBM; avg_launch_ms is the split pass alone."""
     import torch
     import paged_kv_cache_17_amd as pkv
     from gpu_harness import GpuSpec
@@ -404,7 +406,7 @@ def bench_verify(args):
         "config": {"workload": sw.name, "num_seqs": sw.num_seqs, "chunk": g1, "n_q": sw.n_q, "n_kv": sw.n_kv,
                    "head_dim": sw.head_dim, "block_size": sw.block_size, "context_tokens": int(lens.sum()),
                    "kv_bytes": kv_bytes, "cache_copies": len(gpus)},
-        "roofline": {"kernel": "chunk attention (matrix cores), 5-query chunks", "bound": "hbm",
+        "roofline": {"kernel": "balanced split pass (matrix cores), 5-query chunks", "bound": "hbm",
                      "achieved": kv_bytes / (kern_m * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": kv_bytes / (kern_m * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
                      "avg_launch_ms": kern_m, "algorithmic_bytes": kv_bytes, "algorithmic_flops": flops},
@@ -465,8 +467,12 @@ def main():
     def workspace(rows, max_len):
         n = pkv.paged_attn_workspace_size(rows, wl.n_q, wl.n_kv, wl.head_dim, wl.block_size, max_len, split)
         return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
-    ws = [(workspace(nd, max_dec) if nd else None, workspace(len(q_chk), max_chk) if nd < S else None)
-          for _ in caches]
+
+    def chunk_workspace():
+        n = pkv.paged_attn_chunk_workspace_size(S - nd, len(q_chk), max_c, wl.n_q, wl.n_kv, wl.head_dim,
+                                                wl.block_size, max_chk, split)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    ws = [(workspace(nd, max_dec) if nd else None, chunk_workspace() if nd < S else None) for _ in caches]
     stream = torch.cuda.current_stream()
 
     def step(i, ev_dec=None, ev_chk=None):

@@ -258,6 +258,14 @@ int paged_attn_split_tokens(int32_t num_q_rows, int32_t n_kv, int32_t block_size
 int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_t n_kv,
                               int32_t head_dim, int32_t block_size, int32_t max_seq_len,
                               int32_t split_tokens, size_t* bytes);
+/* Workspace for paged_attn_chunk on any of its paths: the larger of
+ * paged_attn_workspace_size(total_q, ...) and, when the chunk qualifies for
+ * the balanced path (see paged_attn_chunk), its partial slots. Needs the
+ * device (the balanced grid is sized from it). Errors: NULL_POINTER,
+ * INVALID_ARGUMENT, HIP. */
+int paged_attn_chunk_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t n_q,
+                                    int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                    int32_t max_seq_len, int32_t split_tokens, size_t* bytes);
 
 /* ======================================================================
  * paged_attn_decode - one query token per sequence.
@@ -303,7 +311,15 @@ int paged_attn_decode(void* out, float* lse, const void* q,
  *   [total_q][n_q][head_dim]; lse float [total_q][n_q] or NULL.
  * max_q_len: host bound on every C_s. seq_lens[s] >= C_s is required
  *   (else NaN rows). Other arguments as paged_attn_decode; the workspace
- *   is sized with num_q_rows = total_q.
+ *   is sized by paged_attn_chunk_workspace_size (or, for the chunk kernels
+ *   only, paged_attn_workspace_size with num_q_rows = total_q).
+ * Paths: bf16, head_dim 128, block_size 16, split_tokens 0 and
+ *   max_q_len * (n_q / n_kv) <= 32 (verification-sized chunks) with a
+ *   workspace of paged_attn_chunk_workspace_size bytes: the decode pass's
+ *   balanced partition over every (sequence, kv head, block) tile, all of a
+ *   kv head's (query, head) rows at once; otherwise one workgroup per
+ *   (query tile, kv head, sequence) on the matrix cores, or the generic
+ *   split path. All give the result defined above.
  * Errors: as paged_attn_decode. */
 int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_start,
                      const void* k_cache, const void* v_cache,

@@ -54,6 +54,8 @@ _SIGNATURES = {
     "kv_append": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p],
                   ctypes.c_int),
     "paged_attn_split_tokens": ([_i32, _i32, _i32, _i32, _i32, _pi32], ctypes.c_int),
+    "paged_attn_chunk_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.POINTER(_size_t)], ctypes.c_int),
     "paged_attn_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_size_t)],
                                   ctypes.c_int),
     "paged_attn_decode": ([_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -285,6 +287,16 @@ def paged_attn_split_tokens(num_q_rows, n_kv, block_size, max_seq_len, requested
     _check("paged_attn_split_tokens", load_library().paged_attn_split_tokens(
         int(num_q_rows), int(n_kv), int(block_size), int(max_seq_len), int(requested), ctypes.byref(out)))
     return out.value
+
+
+def paged_attn_chunk_workspace_size(num_seqs, total_q, max_q_len, n_q, n_kv, head_dim, block_size, max_seq_len,
+                                    split_tokens=0) -> int:
+    """Workspace bytes for paged_attn_chunk on any of its paths."""
+    n = _size_t(0)
+    _check("paged_attn_chunk_workspace_size", load_library().paged_attn_chunk_workspace_size(
+        int(num_seqs), int(total_q), int(max_q_len), int(n_q), int(n_kv), int(head_dim), int(block_size),
+        int(max_seq_len), int(split_tokens), ctypes.byref(n)))
+    return int(n.value)
 
 
 def paged_attn_workspace_size(num_q_rows, n_q, n_kv, head_dim, block_size, max_seq_len, split_tokens=0) -> int:

@@ -90,9 +90,13 @@ class PagedKVCache:
         B.kv_append(self.k_cache, self.v_cache, k_new, v_new, self.table_dev, start_pos, new_start,
                     stream=stream)
 
-    def workspace(self, num_q_rows: int, n_q: int, max_seq_len: int, split_tokens: int = 0):
-        need = B.paged_attn_workspace_size(num_q_rows, n_q, self.n_kv, self.head_dim, self.block_size,
-                                           max_seq_len, split_tokens)
+    def workspace(self, num_q_rows: int, n_q: int, max_seq_len: int, split_tokens: int = 0, chunk=None):
+        if chunk is None:
+            need = B.paged_attn_workspace_size(num_q_rows, n_q, self.n_kv, self.head_dim, self.block_size,
+                                               max_seq_len, split_tokens)
+        else:   # (num_seqs, max_q_len) of a chunk call
+            need = B.paged_attn_chunk_workspace_size(chunk[0], num_q_rows, chunk[1], n_q, self.n_kv, self.head_dim,
+                                                     self.block_size, max_seq_len, split_tokens)
         need = max(need, 256)
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
@@ -121,7 +125,8 @@ class PagedKVCache:
             out = torch.empty_like(q)
         if self.quantized:
             raise NotImplementedError("chunk attention over an 8-bit cache is not provided")
-        ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens)
+        ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
+                            chunk=(q_start.shape[0] - 1, max_q_len))
         B.paged_attn_chunk(out, lse, q, q_start, self.k_cache, self.v_cache, self.table_dev, seq_lens,
                            max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
         return out

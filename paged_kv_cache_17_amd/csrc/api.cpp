@@ -84,9 +84,10 @@ Layout ws_layout(int rows, int n_q, int head_dim, int max_splits) {
     return w;
 }
 
-// Balanced decode: W + S*n_kv partial slots of G heads, then the prefix.
-Layout ws_layout_balanced(int num_seqs, int n_q, int n_kv, int head_dim, int waves) {
-    const size_t parts = (static_cast<size_t>(waves) + static_cast<size_t>(num_seqs) * n_kv) * (n_q / n_kv);
+// Balanced pass: W + S*n_kv partial slots of `rows` rows (decode: the G
+// heads; small chunks: kChunkSlotRows (query, head) rows), then the prefix.
+Layout ws_layout_balanced(int num_seqs, int rows, int n_kv, int head_dim, int waves) {
+    const size_t parts = (static_cast<size_t>(waves) + static_cast<size_t>(num_seqs) * n_kv) * rows;
     Layout w;
     w.ml_bytes = parts * sizeof(pkv::PartialML);
     w.o_offset = align_up(w.ml_bytes);
@@ -96,15 +97,16 @@ Layout ws_layout_balanced(int num_seqs, int n_q, int n_kv, int head_dim, int wav
 }
 
 // Grid size of the balanced pass for the current device (cached for the
-// last shape asked about, per K/V format).
-int balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv = false) {
-    static thread_local int last_dev[2] = {-1, -1}, last_g[2] = {0, 0}, last_s[2] = {0, 0}, last_w[2] = {0, 0};
-    const int f = int8_kv ? 1 : 0;
+// last shape asked about, per pass: bf16 decode, 8-bit decode, small chunks).
+enum BalancedPass { kDecodeBf16 = 0, kDecodeInt8 = 1, kChunkBf16 = 2 };
+int balanced_waves(int n_q, int n_kv, int num_seqs, BalancedPass f = kDecodeBf16) {
+    static thread_local int last_dev[3] = {-1, -1, -1}, last_g[3] = {}, last_s[3] = {}, last_w[3] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     const int g = n_q / n_kv;
     if (dev != last_dev[f] || g != last_g[f] || num_seqs != last_s[f]) {
-        last_w[f] = pkv::decode_balanced_waves(n_q, n_kv, num_seqs, int8_kv);
+        last_w[f] = f == kChunkBf16 ? pkv::chunk_balanced_waves(n_q, n_kv, num_seqs)
+                                    : pkv::decode_balanced_waves(n_q, n_kv, num_seqs, f == kDecodeInt8);
         last_dev[f] = dev;
         last_g[f] = g;
         last_s[f] = num_seqs;
@@ -131,7 +133,7 @@ int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decod
     if (a.num_rows == 0) return PKV_OK;
     if (!workspace) return PKV_ERR_NULL_POINTER;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
-    const Layout w = balanced ? ws_layout_balanced(a.num_seqs, a.n_q, a.n_kv, a.head_dim, a.waves)
+    const Layout w = balanced ? ws_layout_balanced(a.num_seqs, a.n_q / a.n_kv, a.n_kv, a.head_dim, a.waves)
                               : ws_layout(a.num_rows, a.n_q, a.head_dim, a.max_splits);
     if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
     char* ws = static_cast<char*>(workspace);
@@ -264,14 +266,31 @@ extern "C" int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_
     const int max_splits = (max_seq_len + split - 1) / split;
     size_t need = ws_layout(num_q_rows, n_q, head_dim, max_splits).total;
     if (n_q % n_kv == 0 && balanced_eligible(PKV_BF16, split_tokens, num_q_rows, n_q, n_kv, head_dim, block_size)) {
-        for (bool int8_kv : {false, true}) {   // bf16 and 8-bit K/V (paged_attn_decode_q8)
-            const int waves = balanced_waves(n_q, n_kv, num_q_rows, int8_kv);
+        for (BalancedPass f : {kDecodeBf16, kDecodeInt8}) {   // bf16 and 8-bit K/V (paged_attn_decode_q8)
+            const int waves = balanced_waves(n_q, n_kv, num_q_rows, f);
             if (waves < 1) return PKV_ERR_HIP;
-            const size_t b = ws_layout_balanced(num_q_rows, n_q, n_kv, head_dim, waves).total;
+            const size_t b = ws_layout_balanced(num_q_rows, n_q / n_kv, n_kv, head_dim, waves).total;
             if (b > need) need = b;
         }
     }
     *bytes = need;
+    return PKV_OK;
+}
+
+extern "C" int paged_attn_chunk_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t n_q,
+                                               int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                               int32_t max_seq_len, int32_t split_tokens, size_t* bytes) {
+    if (!bytes) return PKV_ERR_NULL_POINTER;
+    if (num_seqs < 0 || max_q_len < 0) return PKV_ERR_INVALID_ARGUMENT;
+    int rc = paged_attn_workspace_size(total_q, n_q, n_kv, head_dim, block_size, max_seq_len, split_tokens, bytes);
+    if (rc != PKV_OK) return rc;
+    if (split_tokens == 0 && n_q % n_kv == 0 &&
+        pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len)) {
+        const int waves = balanced_waves(n_q, n_kv, num_seqs, kChunkBf16);
+        if (waves < 1) return PKV_ERR_HIP;
+        const size_t b = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, waves).total;
+        if (b > *bytes) *bytes = b;
+    }
     return PKV_OK;
 }
 
@@ -358,7 +377,7 @@ extern "C" int paged_attn_decode_q8(void* out, float* lse, const void* q, const 
         (reinterpret_cast<uintptr_t>(v_codes) & 7))
         return PKV_ERR_INVALID_ARGUMENT;
     pkv::AttnArgs a{};
-    a.waves = balanced_waves(n_q, n_kv, num_seqs, true);
+    a.waves = balanced_waves(n_q, n_kv, num_seqs, kDecodeInt8);
     if (a.waves < 1) return PKV_ERR_HIP;
     a.q = q;
     a.q_start = nullptr;
@@ -428,6 +447,27 @@ extern "C" int paged_attn_chunk(void* out, float* lse, const void* q, const int3
     a.split_tokens = split;
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
+    // Small chunks (every C_s <= 32 / G rows' worth): the balanced partition
+    // over all (sequence, kv head, block) tiles with both products on the
+    // matrix cores, as decode, when the workspace holds its partials
+    // (paged_attn_chunk_workspace_size); otherwise the chunk kernels below.
+    if (dtype == PKV_BF16 && split_tokens == 0 && workspace &&
+        reinterpret_cast<uintptr_t>(workspace) % kAlign == 0 && aligned16(q) && aligned16(k_cache) &&
+        aligned16(v_cache) && pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len)) {
+        const int waves = balanced_waves(n_q, n_kv, num_seqs, kChunkBf16);
+        const Layout w = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, waves);
+        if (waves >= 1 && workspace_bytes >= w.total) {
+            char* ws = static_cast<char*>(workspace);
+            a.waves = waves;
+            a.ws_ml = reinterpret_cast<pkv::PartialML*>(ws);
+            a.ws_o = reinterpret_cast<float*>(ws + w.o_offset);
+            a.prefix = reinterpret_cast<int*>(ws + w.prefix_offset);
+            hipStream_t st = static_cast<hipStream_t>(stream);
+            hipError_t e = pkv::launch_chunk_balanced(a, st, profile_events());
+            if (e == hipSuccess) e = pkv::launch_merge(a, out, lse, true, st);
+            return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+        }
+    }
     if (mfma) {
         const hipError_t e = pkv::launch_chunk_mfma(a, out, lse, static_cast<hipStream_t>(stream), profile_events());
         return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -94,24 +94,28 @@ __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a, T* __restrict__ 
     if (lse && threadIdx.x == 0) lse[static_cast<size_t>(row) * a.n_q + h] = kLn2 * (M + log2f(den));
 }
 
-// Balanced-decode merge: one workgroup of 256 threads per (sequence, kv
-// head) combines the G heads' partials in three rounds of independent
-// loads: (1) the sequence's length and prefix entries; (2) every partial's
-// (m, l) for the G heads, one partial per thread, staged in LDS, then per
-// head a wave reduces the maximum and the weighted sum; (3) the partial
-// outputs, four dims per thread, all partials' loads in flight together.
+// Balanced merge: one workgroup of 256 threads per (sequence, kv head)
+// combines the rows' partials in three rounds of independent loads: (1) the
+// sequence's length, query rows and prefix entries; (2) every partial's
+// (m, l) for the rows, one partial per thread, staged in LDS, then per row a
+// wave reduces the maximum and the weighted sum; (3) the partial outputs,
+// four dims per thread, all partials' loads in flight together. Rows are
+// (query i, head h) pairs, r = i * G + h, RS per partial slot: decode has
+// one query (RS = G), small chunks C_s <= RS / G queries (RS = 32), written
+// to row q_start[s] + i. A workgroup takes RB of the rows (rows RB * z ..,
+// z = blockIdx.z), so small chunks spread over several workgroups.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeMaxParts = 256;   // partials staged at once in LDS
 
-template <int G>
+template <int G, int RS, int RB>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs a, uint16_t* __restrict__ out,
                                                                        float* __restrict__ lse) {
     constexpr int D = 128;
-    __shared__ float s_m[kMergeMaxParts][G];     // m_j, then the weight 2^(m_j - M)
-    __shared__ float s_l[kMergeMaxParts][G];
-    __shared__ float s_M[G];
-    __shared__ float s_den[G];
-    __shared__ int s_info[3];                    // count, first slot, ok
+    __shared__ float s_m[kMergeMaxParts][RB];    // m_j, then the weight 2^(m_j - M)
+    __shared__ float s_l[kMergeMaxParts][RB];
+    __shared__ float s_M[RB];
+    __shared__ float s_den[RB];
+    __shared__ int s_info[5];                    // count, first slot, ok, first query row, rows used
     const int s = blockIdx.x;
     const int g = blockIdx.y;
     const int tid = threadIdx.x;
@@ -119,10 +123,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
     const int wave = tid / kWave;
     if (tid == 0) {
         const int L = a.seq_lens[s];
+        int row0 = s, C = 1;
+        if (a.q_start) {
+            row0 = a.q_start[s];
+            C = a.q_start[s + 1] - row0;
+        }
         const long long P = a.prefix[s];
         const long long nb = a.prefix[s + 1] - P;
         const long long Tt = static_cast<long long>(a.n_kv) * a.prefix[a.num_seqs];
-        bool ok = seq_len_ok(L, 1, a.max_seq_len, a.table_stride * a.block_size) &&
+        bool ok = C >= 1 && C * G <= RS && seq_len_ok(L, C, a.max_seq_len, a.table_stride * a.block_size) &&
                   nb == (L + a.block_size - 1) / a.block_size && Tt > 0;
         int count = 0;
         long long first = 0;
@@ -137,8 +146,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
         s_info[0] = count;
         s_info[1] = static_cast<int>(first);
         s_info[2] = ok;
+        s_info[3] = row0;
+        s_info[4] = C >= 1 ? min(C * G, RS) - RB * static_cast<int>(blockIdx.z) : 0;   // rows from here on
     }
-    if (tid < G) {
+    if (tid < RB) {
         s_M[tid] = -INFINITY;
         s_den[tid] = 0.0f;
     }
@@ -146,73 +157,80 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
     const int count = s_info[0];
     const size_t first = static_cast<size_t>(s_info[1]);
     const bool ok = s_info[2];
+    const int row0 = s_info[3];
+    const int used = min(s_info[4], RB);      // rows of this workgroup: rb .. rb + used - 1
+    const int rb = RB * static_cast<int>(blockIdx.z);
+    if (used <= 0) return;
 
-    // Per-head maximum over all partials; a NaN partial makes it NaN.
+    // Per-row maximum over all partials; a NaN partial makes it NaN.
     for (int j0 = 0; j0 < count; j0 += kMergeMaxParts) {
         const int n = min(count - j0, kMergeMaxParts);
         if (tid < n) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const PartialML p = a.ws_ml[(first + j0 + tid) * G + h];
-                s_m[tid][h] = p.m;
-                s_l[tid][h] = p.l;
+            for (int r = 0; r < used; ++r) {
+                const PartialML p = a.ws_ml[(first + j0 + tid) * RS + rb + r];
+                s_m[tid][r] = p.m;
+                s_l[tid][r] = p.l;
             }
         }
         __syncthreads();
-        for (int h = wave; h < G; h += kMergeThreads / kWave) {
+        for (int r = wave; r < used; r += kMergeThreads / kWave) {
             float M = -INFINITY;
             bool bad = false;
             for (int j = lane; j < n; j += kWave) {
-                bad |= isnan(s_m[j][h]);
-                M = fmaxf(M, s_m[j][h]);
+                bad |= isnan(s_m[j][r]);
+                M = fmaxf(M, s_m[j][r]);
             }
             M = wave_max(M);
             bad = __builtin_amdgcn_ballot_w64(bad) != 0;
-            if (lane == 0) s_M[h] = (bad || isnan(s_M[h])) ? NAN : fmaxf(s_M[h], M);
+            if (lane == 0) s_M[r] = (bad || isnan(s_M[r])) ? NAN : fmaxf(s_M[r], M);
         }
         __syncthreads();
     }
     // Weights and their sum (the staged block is still in LDS when
-    // count <= kMergeMaxParts; otherwise they are recomputed below).
+    // count <= kMergeMaxParts; otherwise they are recomputed below). A
+    // partial with m = -inf (a row that saw none of its range's keys) has
+    // weight 0.
     const bool staged = count <= kMergeMaxParts;
-    for (int h = wave; h < G; h += kMergeThreads / kWave) {
-        const float M = s_M[h];
+    for (int r = wave; r < used; r += kMergeThreads / kWave) {
+        const float M = s_M[r];
         float den = 0.0f;
         for (int j = lane; j < count; j += kWave) {
             float m, l;
             if (staged) {
-                m = s_m[j][h];
-                l = s_l[j][h];
+                m = s_m[j][r];
+                l = s_l[j][r];
             } else {
-                const PartialML p = a.ws_ml[(first + j) * G + h];
+                const PartialML p = a.ws_ml[(first + j) * RS + rb + r];
                 m = p.m;
                 l = p.l;
             }
             const float w = exp2f(m - M);
-            if (staged) s_m[j][h] = w;
+            if (staged) s_m[j][r] = w;
             den = fmaf(w, l, den);
         }
         den = wave_sum(den);
-        if (lane == 0) s_den[h] = den;
+        if (lane == 0) s_den[r] = den;
     }
     __syncthreads();
 
-    // Outputs: thread -> (head, 4 dims); partials' loads issued in groups of 8.
-    uint16_t* obase = out + (static_cast<size_t>(s) * a.n_q + g * G) * D;
-    for (int e = tid; e < G * D / 4; e += kMergeThreads) {
-        const int h = e / (D / 4);
-        const int k = 4 * (e - h * (D / 4));
-        const float M = s_M[h];
+    // Outputs: thread -> (row, 4 dims); partials' loads issued in groups of 8.
+    for (int e = tid; e < used * (D / 4); e += kMergeThreads) {
+        const int r = e / (D / 4);
+        const int k = 4 * (e - r * (D / 4));
+        const int qi = (rb + r) / G;
+        const int h = rb + r - qi * G;
+        const float M = s_M[r];
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        const float* ob = a.ws_o + (first * G + h) * D + k;
+        const float* ob = a.ws_o + (first * RS + rb + r) * D + k;
         int j = 0;
         for (; j + 8 <= count; j += 8) {
             float4 v[8];
             float wv[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(j + u) * G * D);
+            for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(j + u) * RS * D);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) wv[u] = staged ? s_m[j + u][h] : exp2f(a.ws_ml[(first + j + u) * G + h].m - M);
+            for (int u = 0; u < 8; ++u)
+                wv[u] = staged ? s_m[j + u][r] : exp2f(a.ws_ml[(first + j + u) * RS + rb + r].m - M);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 acc.x = fmaf(wv[u], v[u].x, acc.x);
@@ -222,22 +240,37 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
             }
         }
         for (; j < count; ++j) {
-            const float4 v = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(j) * G * D);
-            const float wj = staged ? s_m[j][h] : exp2f(a.ws_ml[(first + j) * G + h].m - M);
+            const float4 v = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(j) * RS * D);
+            const float wj = staged ? s_m[j][r] : exp2f(a.ws_ml[(first + j) * RS + rb + r].m - M);
             acc.x = fmaf(wj, v.x, acc.x);
             acc.y = fmaf(wj, v.y, acc.y);
             acc.z = fmaf(wj, v.z, acc.z);
             acc.w = fmaf(wj, v.w, acc.w);
         }
-        const float inv = (ok && !isnan(M)) ? 1.0f / s_den[h] : NAN;
+        const float inv = (ok && !isnan(M)) ? 1.0f / s_den[r] : NAN;
         uint2 w2;
         w2.x = pack2_bf16(acc.x * inv, acc.y * inv);
         w2.y = pack2_bf16(acc.z * inv, acc.w * inv);
-        *reinterpret_cast<uint2*>(obase + h * D + k) = w2;
+        *reinterpret_cast<uint2*>(out + ((static_cast<size_t>(row0) + qi) * a.n_q + g * G + h) * D + k) = w2;
     }
-    if (lse && tid < G) {
+    if (lse && tid < used) {
+        const int qi = (rb + tid) / G;
         const float M = s_M[tid];
-        lse[static_cast<size_t>(s) * a.n_q + g * G + tid] = (ok && !isnan(M)) ? kLn2 * (M + log2f(s_den[tid])) : NAN;
+        lse[(static_cast<size_t>(row0) + qi) * a.n_q + g * G + (rb + tid - qi * G)] =
+            (ok && !isnan(M)) ? kLn2 * (M + log2f(s_den[tid])) : NAN;
+    }
+}
+
+constexpr int kChunkMergeRows = 8;   // rows per merge workgroup for small chunks
+
+template <int G>
+void launch_merge_balanced(const AttnArgs& a, dim3 grid, uint16_t* out, float* lse, bool chunk, hipStream_t stream) {
+    if (chunk) {
+        grid.z = (min(a.max_q_len * G, kChunkSlotRows) + kChunkMergeRows - 1) / kChunkMergeRows;
+        hipLaunchKernelGGL((merge_balanced_kernel<G, kChunkSlotRows, kChunkMergeRows>), grid, dim3(kMergeThreads), 0,
+                           stream, a, out, lse);
+    } else {
+        hipLaunchKernelGGL((merge_balanced_kernel<G, G, G>), grid, dim3(kMergeThreads), 0, stream, a, out, lse);
     }
 }
 
@@ -247,11 +280,12 @@ hipError_t launch_merge(const AttnArgs& a, void* out, float* lse, bool bf16, hip
     if (a.waves > 0 && bf16 && a.head_dim == 128) {
         const dim3 grid(a.num_seqs, a.n_kv);
         auto out16 = static_cast<uint16_t*>(out);
+        const bool chunk = a.q_start != nullptr;   // small chunks: kChunkSlotRows rows per slot
         switch (a.n_q / a.n_kv) {
-            case 1: hipLaunchKernelGGL(merge_balanced_kernel<1>, grid, dim3(256), 0, stream, a, out16, lse); break;
-            case 2: hipLaunchKernelGGL(merge_balanced_kernel<2>, grid, dim3(256), 0, stream, a, out16, lse); break;
-            case 4: hipLaunchKernelGGL(merge_balanced_kernel<4>, grid, dim3(256), 0, stream, a, out16, lse); break;
-            case 8: hipLaunchKernelGGL(merge_balanced_kernel<8>, grid, dim3(256), 0, stream, a, out16, lse); break;
+            case 1: launch_merge_balanced<1>(a, grid, out16, lse, chunk, stream); break;
+            case 2: launch_merge_balanced<2>(a, grid, out16, lse, chunk, stream); break;
+            case 4: launch_merge_balanced<4>(a, grid, out16, lse, chunk, stream); break;
+            case 8: launch_merge_balanced<8>(a, grid, out16, lse, chunk, stream); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();

@@ -57,12 +57,18 @@ template <int G>
 struct ValuRows {
     using State = DecodeState<G>;
     static constexpr int kQ = G;
+    static constexpr int kSlotRows = G;              // partial rows per slot
     static constexpr int kWaves = G == 8 ? 1 : 2;   // waves per SIMD the registers allow
-    __device__ __forceinline__ static void load_q(u32x4 (&qv)[kQ], const uint16_t* q_sg, int lane) {
+    // One query per sequence: the G heads of kv head g. Returns the rows used.
+    __device__ __forceinline__ static int load_q(State&, u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g,
+                                                 int lane) {
+        const uint16_t* q_sg = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(s) * a.n_q + g * G) * kTileD;
 #pragma unroll
         for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(q_sg + h * kTileD + (lane & 15) * 8);
+        return G;
     }
-    __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, bool bad, int lane) {
+    __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, int /*used*/, bool bad,
+                                                 int lane) {
         const int c = lane & 15;
         st.merge_rows();
         if ((lane >> 4) == 0) {
@@ -77,22 +83,44 @@ struct ValuRows {
     }
 };
 
-// Query load and partial write of the matrix-core tile math (decode_mfma.h
-// layout: lane (q, n) holds head n's query at dims 32b + 8q .. +7, zero for
-// n >= 4).
+// Query load and partial write of the matrix-core tile math (decode_mfma.h):
+// rows r = i * G + h of (query i, head h) in NB blocks of 16; lane (q, n)
+// holds row 16b + n's query at dims 32c + 8q .. +7 (c = 0..3), zero for rows
+// past the C * G the sequence has. Decode: one query (q_start null), NB = 1,
+// G rows per partial slot; small chunks: C <= 32 / G queries, NB = 2, 32.
+template <int G, int NB>
 struct MfmaRows {
-    using State = MfmaStateG4;
-    static constexpr int kQ = 4;
+    using State = MfmaState<NB>;
+    static constexpr int kQ = 4 * NB;
+    static constexpr int kSlotRows = NB == 1 ? G : 16 * NB;
     static constexpr int kWaves = 2;
-    __device__ __forceinline__ static void load_q(u32x4 (&qv)[kQ], const uint16_t* q_sg, int lane) {
+    __device__ __forceinline__ static int load_q(State& st, u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g,
+                                                 int lane) {
         const int n = lane & 15;
         const int q = lane >> 4;
+        int row0 = s, C = 1;
+        if (a.q_start) {
+            row0 = a.q_start[s];
+            C = a.q_start[s + 1] - row0;
+        }
+        const int used = C * G;
+        const uint16_t* qb = static_cast<const uint16_t*>(a.q);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            qv[b] = n < 4 ? *reinterpret_cast<const u32x4*>(q_sg + n * kTileD + 32 * b + 8 * q) : u32x4{0, 0, 0, 0};
+        for (int b = 0; b < NB; ++b) {
+            const int r = 16 * b + n;
+            const int i = r / G;
+            st.ok[b] = r < used;
+            st.back[b] = C - 1 - i;
+            const uint16_t* qr = qb + ((static_cast<size_t>(row0) + i) * a.n_q + g * G + (r - i * G)) * kTileD + 8 * q;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                qv[4 * b + c] = st.ok[b] ? *reinterpret_cast<const u32x4*>(qr + 32 * c) : u32x4{0, 0, 0, 0};
+        }
+        return used;
     }
-    __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, bool bad, int lane) {
-        st.write_partial(a.ws_o, a.ws_ml, p, bad, lane);
+    __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, int used, bool bad,
+                                                 int lane) {
+        st.write_partial(a.ws_o, a.ws_ml, p, kSlotRows, used, bad, lane);
     }
 };
 
@@ -161,15 +189,17 @@ struct Int8Kv : ValuRows<G> {
 // (decode_mfma.h). Lane (q, n) loads token n's K at dims 32b + 8q .. +7
 // (b = 0..3) and tokens 4q .. 4q+3's V at dims 8n .. 8n+7: the same bytes per
 // tile as the vector-ALU layout, in the operand layouts of the two products.
-template <>
-struct Bf16Kv<4> : MfmaRows {
+template <int G, int NB>
+struct Bf16Mfma : MfmaRows<G, NB> {
+    using typename MfmaRows<G, NB>::State;
+    using MfmaRows<G, NB>::kQ;
     static constexpr int kDepth = 2;
     struct Regs {
         u32x4 k[4], v[4];
     };
     const uint16_t* kc;
     const uint16_t* vc;
-    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane)
+    __device__ __forceinline__ Bf16Mfma(const AttnArgs& a, int lane)
         : kc(static_cast<const uint16_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
           vc(static_cast<const uint16_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
@@ -183,23 +213,29 @@ struct Bf16Kv<4> : MfmaRows {
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
                                             float sl2) const {
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 s[NB];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[b]),
-                                                        __builtin_bit_cast(bf16x8, qv[b]), s, 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+            s[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[b]),
+                                                                __builtin_bit_cast(bf16x8, qv[4 * nb + b]), s[nb], 0, 0, 0);
+        }
         // rows past the sequence end may hold anything (NaN): zero them
         u32x4 v[4];
         const int q = lane >> 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = 4 * q + e < ntok ? t.v[e] : u32x4{0, 0, 0, 0};
         const float none[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        st.update<false>(s, none, none, [&](int j) { return v_operand_bf16(v, j); }, lane, ntok, sl2);
+        st.template update<false>(s, none, none, [&](int j) { return v_operand_bf16(v, j); }, lane, ntok, sl2);
     }
 };
 
-template <>
-struct Int8Kv<4> : MfmaRows {
+template <int G, int NB>
+struct Int8Mfma : MfmaRows<G, NB> {
+    using typename MfmaRows<G, NB>::State;
+    using MfmaRows<G, NB>::kQ;
     static constexpr int kDepth = 2;
     struct Regs {
         u32x2 k[4], v[4];
@@ -209,7 +245,7 @@ struct Int8Kv<4> : MfmaRows {
     const int8_t* vc;
     const float* ks;
     const float* vs;
-    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane)
+    __device__ __forceinline__ Int8Mfma(const AttnArgs& a, int lane)
         : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
           vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
           ks(a.k_scale + 4 * (lane >> 4)),
@@ -228,17 +264,38 @@ struct Int8Kv<4> : MfmaRows {
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
                                             float sl2) const {
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 s[NB];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(t.k[b])),
-                                                        __builtin_bit_cast(bf16x8, qv[b]), s, 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) s[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, codes8_to_bf16x8(t.k[b]));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, __builtin_bit_cast(bf16x8, qv[4 * nb + b]), s[nb],
+                                                                0, 0, 0);
+        }
         // codes are finite whatever the slot holds; weights past the end are 0
         const float sk[4] = {t.sk.x, t.sk.y, t.sk.z, t.sk.w};
         const float sv[4] = {t.sv.x, t.sv.y, t.sv.z, t.sv.w};
-        st.update<true>(s, sk, sv, [&](int j) { return v_operand_codes(t.v, j); }, lane, ntok, sl2);
+        st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(t.v, j); }, lane, ntok, sl2);
     }
 };
+
+// Decode with four query heads per kv head: one block of rows.
+template <>
+struct Bf16Kv<4> : Bf16Mfma<4, 1> {
+    using Bf16Mfma<4, 1>::Bf16Mfma;
+};
+template <>
+struct Int8Kv<4> : Int8Mfma<4, 1> {
+    using Int8Mfma<4, 1>::Int8Mfma;
+};
+
+// Small chunks: up to 32 (query, head) rows per kv head in two blocks.
+template <int G>
+using ChunkKv = Bf16Mfma<G, 2>;
+static_assert(ChunkKv<4>::kSlotRows == kChunkSlotRows, "chunk partial slots");
 
 // At least two waves per SIMD (at most 256 registers per lane): fewer
 // waves would halve the bytes the chip keeps in flight. Eight query heads
@@ -289,7 +346,9 @@ void decode_balanced_kernel(AttnArgs a) {
     const int n = t1 - t0;
 
     // Per-lane description of tile c0 + lane: segment, tile index
-    // (block * n_kv + g) and valid tokens (-1: bad table entry).
+    // (block * n_kv + g) and the sequence's keys from the tile's first one
+    // to its end (tokens below it are valid; more than 16 for all but the
+    // last block, which the chunk rows' masks rely on; -1: bad table entry).
     int i_seg = -1, i_tile = 0, i_ntok = 0;
     auto describe = [&](int c0) {
         const int t = c0 + lane;
@@ -311,7 +370,7 @@ void decode_balanced_kernel(AttnArgs a) {
                 blk = 0;
                 i_ntok = -1;
             } else {
-                i_ntok = min(kTileB, Ls[lo] - bi * kTileB);
+                i_ntok = Ls[lo] - bi * kTileB;
             }
             i_seg = lo * n_kv + g;
             i_tile = blk * n_kv + g;
@@ -319,7 +378,6 @@ void decode_balanced_kernel(AttnArgs a) {
     };
 
     const Kv kv(a, lane);
-    const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
     const float sl2 = a.scale_log2;
 
     typename Kv::State st;
@@ -328,8 +386,9 @@ void decode_balanced_kernel(AttnArgs a) {
     int cur_seg = -1;
     bool cur_bad = false;
 
+    int cur_used = 0;
     auto flush = [&]() __attribute__((always_inline)) {
-        kv.flush(st, a, static_cast<size_t>(w) + cur_seg, cur_bad, lane);
+        kv.flush(st, a, static_cast<size_t>(w) + cur_seg, cur_used, cur_bad, lane);
     };
 
     // Tiles stream through Kv::kDepth buffers: tile j is issued kDepth - 1
@@ -359,8 +418,8 @@ void decode_balanced_kernel(AttnArgs a) {
             if (cur_seg >= 0) flush();
             const int s = seg / n_kv;
             const int g = seg - s * n_kv;
-            kv.load_q(qv, qbase + (static_cast<size_t>(s) * n_kv * G + g * G) * kTileD, lane);
             st.reset();
+            cur_used = kv.load_q(st, qv, a, s, g, lane);
             cur_seg = seg;
             cur_bad = false;
         }
@@ -459,6 +518,17 @@ int decode_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv) {
 
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     return a.k_scale ? launch_kv<Int8Kv>(a, stream, ev) : launch_kv<Bf16Kv>(a, stream, ev);
+}
+
+bool chunk_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs, int max_q_len) {
+    return decode_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs) && max_q_len >= 1 &&
+           max_q_len * (n_q / n_kv) <= kChunkSlotRows;
+}
+
+int chunk_balanced_waves(int n_q, int n_kv, int num_seqs) { return waves_for<ChunkKv>(n_q, n_kv, num_seqs); }
+
+hipError_t launch_chunk_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
+    return launch_kv<ChunkKv>(a, stream, ev);
 }
 
 }  // namespace pkv

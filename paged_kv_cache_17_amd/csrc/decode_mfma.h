@@ -57,83 +57,113 @@ __device__ __forceinline__ i16x4 v_operand_codes(const u32x2 (&v)[4], int j) {
     return __builtin_bit_cast(i16x4, u32x2{lo, hi});
 }
 
-struct MfmaStateG4 {
+// Rows of the products: (query i, head h) pairs of one kv head, row r =
+// i * G + h, in NB blocks of 16 (decode: the G heads of one query, NB = 1;
+// small chunks: up to 32 rows, NB = 2). Lane (q, n) owns row 16b + n of
+// block b for the softmax and rows 16b + 4q + e of the output. `ok` marks
+// rows that exist; `back` = C - 1 - i, the number of the chunk's last keys
+// row r may not see (0 for decode). With ntok = the sequence's keys from
+// the tile's first key to its end (not capped at the tile), row r sees the
+// tile's tokens below ntok - back (chapter 5 section 4.1 and the lab's
+// causal chunk mask: query i at position L - C + i sees keys up to it).
+template <int NB>
+struct MfmaState {
     static constexpr float kLazy = 8.0f;
-    float mref;        // reference max of head n (log2 units), shared by its 16 lanes
-    float mref_safe;   // mref, or 0 while it is still -inf
-    float l;           // sum of this lane's weights (head n, tokens 4q .. 4q+3)
-    f32x4 acc[8];      // block j: O[4q + e][8n + j]; rows 0..3 (lanes q = 0) are the heads
+    float mref[NB];       // reference max of row 16b + n (log2 units), shared by its lanes
+    float mref_safe[NB];  // mref, or 0 while it is still -inf
+    float l[NB];          // sum of this lane's weights (row 16b + n, tokens 4q .. 4q+3)
+    f32x4 acc[NB][8];     // block b, dim block j: O[row 16b + 4q + e][8n + j]
+    bool ok[NB];          // row 16b + n exists
+    int back[NB];         // keys at the end of the chunk row 16b + n may not see
 
     __device__ __forceinline__ void reset() {
-        mref = -INFINITY;
-        mref_safe = 0.0f;
-        l = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int b = 0; b < NB; ++b) {
+            mref[b] = -INFINITY;
+            mref_safe[b] = 0.0f;
+            l[b] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[b][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
     }
 
-    // Raw scores s (head n, tokens 4q + e) -> weights -> O += P V. ks / vs:
-    // the K and V scales of tokens 4q + e (8-bit tiles; unused for bf16);
-    // vb(j): the V operand of block j.
+    // Raw scores s[b] (row 16b + n, tokens 4q + e) -> weights -> O += P V.
+    // ks / vs: the K and V scales of tokens 4q + e (8-bit tiles; unused for
+    // bf16); vb(j): the V operand of dim block j.
     template <bool kScaled, class VOperand>
-    __device__ __forceinline__ void update(const f32x4 s, const float (&ks)[4], const float (&vs)[4],
+    __device__ __forceinline__ void update(const f32x4 (&s)[NB], const float (&ks)[4], const float (&vs)[4],
                                            VOperand&& vb, int lane, int ntok, float sl2) {
-        const int n = lane & 15;
         const int q = lane >> 4;
-        float x[4];
+        i16x4 pa[NB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float raw = kScaled ? s[e] * ks[e] : s[e];
-            x[e] = 4 * q + e < ntok ? raw * sl2 : -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mx = xor16_max(mx);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const bool need = n < 4 && mx > mref + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float nref = need ? mx : mref;
-            const float alpha = (nref == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - nref);
-            l *= alpha;
-            // output rows are heads: head e's factor sits in lane e
-            float al[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) al[e] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alpha), e));
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[j][e] *= al[e];
-            mref = nref;
-            mref_safe = (nref == -INFINITY) ? 0.0f : nref;
-        }
-        float p[4], w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            p[e] = n < 4 ? __builtin_amdgcn_exp2f(x[e] - mref_safe) : 0.0f;
-            // past the sequence end the V scale may be unset: weight 0, no product
-            w[e] = kScaled ? (4 * q + e < ntok ? p[e] * vs[e] : 0.0f) : p[e];
-        }
-        l += (p[0] + p[1]) + (p[2] + p[3]);
-        const i16x4 pa = __builtin_bit_cast(i16x4, u32x2{pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3])});
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb(j), acc[j], 0, 0, 0);
-    }
-
-    // This wave's partial for the segment: lanes q = 0 hold the four heads'
-    // outputs at dims 8n .. 8n+7; head n's (m, l) goes from lane n.
-    __device__ __forceinline__ void write_partial(float* ws_o, PartialML* ws_ml, size_t slot, bool bad,
-                                                  int lane) const {
-        const int n = lane & 15;
-        const int q = lane >> 4;
-        float lt = l + __shfl_xor(l, 16, kWave);
-        lt += __shfl_xor(lt, 32, kWave);
-        if (q == 0) {
+        for (int b = 0; b < NB; ++b) {
+            const int lim = ntok - back[b];   // tokens 4q + e < lim are seen by this row
+            float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float4* o = reinterpret_cast<float4*>(ws_o + (slot * 4 + e) * kTileD + 8 * n);
-                o[0] = make_float4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
-                o[1] = make_float4(acc[4][e], acc[5][e], acc[6][e], acc[7][e]);
+                const float raw = kScaled ? s[b][e] * ks[e] : s[b][e];
+                x[e] = 4 * q + e < lim ? raw * sl2 : -INFINITY;
             }
-            if (n < 4) ws_ml[slot * 4 + n] = bad ? PartialML{NAN, NAN} : PartialML{mref_safe, lt};
+            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            mx = xor16_max(mx);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            const bool need = ok[b] && mx > mref[b] + kLazy;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float nref = need ? mx : mref[b];
+                const float alpha = (nref == mref[b]) ? 1.0f : __builtin_amdgcn_exp2f(mref[b] - nref);
+                l[b] *= alpha;
+                // output row 4q + e of the block takes the factor of lane 4q + e
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float al = __shfl(alpha, 4 * q + e, kWave);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[b][j][e] *= al;
+                }
+                mref[b] = nref;
+                mref_safe[b] = (nref == -INFINITY) ? 0.0f : nref;
+            }
+            float p[4], w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = ok[b] ? __builtin_amdgcn_exp2f(x[e] - mref_safe[b]) : 0.0f;
+                // past the sequence end the V scale may be unset: weight 0, no product
+                w[e] = kScaled ? (4 * q + e < lim ? p[e] * vs[e] : 0.0f) : p[e];
+            }
+            l[b] += (p[0] + p[1]) + (p[2] + p[3]);
+            pa[b] = __builtin_bit_cast(i16x4, u32x2{pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3])});
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const i16x4 v = vb(j);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[b], v, acc[b][j], 0, 0, 0);
+        }
+    }
+
+    // This wave's partial for the segment, `rows` rows per slot (rows <
+    // `used` exist): lane (q, n) stores rows 16b + 4q + e at dims 8n .. 8n+7,
+    // and the (m, l) of row 16b + n (m = -inf for a row that saw no key).
+    __device__ __forceinline__ void write_partial(float* ws_o, PartialML* ws_ml, size_t slot, int rows, int used,
+                                                  bool bad, int lane) const {
+        const int n = lane & 15;
+        const int q = lane >> 4;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float lt = l[b] + __shfl_xor(l[b], 16, kWave);
+            lt += __shfl_xor(lt, 32, kWave);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * b + 4 * q + e;
+                if (r < used) {
+                    float4* o = reinterpret_cast<float4*>(ws_o + (slot * rows + r) * kTileD + 8 * n);
+                    o[0] = make_float4(acc[b][0][e], acc[b][1][e], acc[b][2][e], acc[b][3][e]);
+                    o[1] = make_float4(acc[b][4][e], acc[b][5][e], acc[b][6][e], acc[b][7][e]);
+                }
+            }
+            const int r = 16 * b + n;
+            if (q == 0 && r < used)
+                ws_ml[slot * rows + r] = bad ? PartialML{NAN, NAN}
+                                             : PartialML{lt > 0.0f ? mref_safe[b] : -INFINITY, lt};
         }
     }
 };

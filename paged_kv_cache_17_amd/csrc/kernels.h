@@ -103,6 +103,15 @@ bool decode_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, 
 int decode_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv = false);
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
 
+// Small chunks through the same balanced partition (bf16, head_dim 128,
+// block_size 16): every (query, head) row of a kv head, at most
+// kChunkSlotRows of them (max_q_len * G), on the matrix cores; partial slots
+// of kChunkSlotRows rows, merged by launch_merge (a.q_start set).
+constexpr int kChunkSlotRows = 32;
+bool chunk_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs, int max_q_len);
+int chunk_balanced_waves(int n_q, int n_kv, int num_seqs);
+hipError_t launch_chunk_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
+
 // Chunk attention on MFMA (bf16, head_dim 128, block_size 16, sequences of
 // at most 32768 keys): writes out and lse directly, no workspace.
 bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size, int max_seq_len);

@@ -198,17 +198,20 @@ def test_chunk_matrix_core_path_shapes(n_q, n_kv):
     say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
 
 
-@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (64, 8)])
-def test_small_chunks_over_long_histories(n_q, n_kv):
-    """Verification-sized chunks (1 .. one query tile) over histories that end
-    just before, at and after multiples of 1024 keys; a sequence whose table
-    names a block outside the pool gives NaN rows only for itself."""
-    qt = 128 // (n_q // n_kv)
+@pytest.mark.parametrize("n_q,n_kv,rows", [(32, 8, 128), (64, 8, 128), (32, 8, 32), (64, 8, 32), (8, 8, 32)])
+def test_small_chunks_over_long_histories(n_q, n_kv, rows):
+    """Small chunks over histories that end just before, at and after
+    multiples of 1024 keys; a sequence whose table names a block outside the
+    pool gives NaN rows only for itself. rows = the most (query, head) rows
+    a chunk brings per kv head: 128 (up to one query tile: the per-tile
+    chunk kernel) or 32 (the balanced partition with both products on the
+    matrix cores)."""
+    qt = rows // (n_q // n_kv)
     hist = [1018, 1019, 2043, 3000, 4090, 0, 1023, 1024, 700]
-    new = [5, 6, 5, qt, 5, min(17, qt), 1, 1, 3]
+    new = [min(5, qt), min(6, qt), min(5, qt), qt, min(5, qt), min(17, qt), 1, 1, min(3, qt)]
     wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist,
                         new_lens=new, seed=21)
-    say("small chunks, long histories", n_q, n_kv)
+    say("small chunks, long histories", n_q, n_kv, rows)
     _, _, err, lerr = _full_check(wl, "chunk", 0, check_pool=False)
     say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
     # one bad table entry (in the first range of sequence 3)
