@@ -49,7 +49,7 @@ def parse():
                    help="time token sampling (temperature 0.8, top-k 50, top-p 0.9) over 64 rows of a "
                         "128256-entry vocabulary")
     p.add_argument("--sample-topk", type=int, default=50,
-                   help="top-k of the --sample workload (0 = off: every row takes the whole-row path)")
+                   help="top-k of the --sample workload (0 = off: every row takes the histogram path)")
     p.add_argument("--verify", action="store_true",
                    help="time a speculative verification step: gamma + 1 = 5 tokens per sequence of the "
                         "64-sequence batch appended and attended as one causal chunk")
@@ -291,9 +291,9 @@ def bench_bestof(args):
 def bench_sample(args):
     """Token sampling after the LM head: 64 rows x 128256 logits (fp32),
     temperature 0.8, top-k 50 (``--sample-topk``; 0 = off), top-p 0.9, one
-    uniform number per row. A step is one sample_tokens call (its candidate
-    kernel, finishing kernel and whole-row kernel, each doing nothing for the
-    rows of the other path); the algorithmic bytes are the logits read once."""
+    uniform number per row. A step is one sample_tokens call (its per-chunk
+    kernel and its finishing kernel); the algorithmic bytes are the logits
+    read once."""
     import torch
     import paged_kv_cache_17_amd as pkv
     from workloads import lm_head_workload
@@ -325,7 +325,7 @@ def bench_sample(args):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": sw.name, "rows": rows, "vocab": vocab, "logit_bytes": nbytes},
-        "roofline": {"kernel": "sample_tokens (all three kernels)", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+        "roofline": {"kernel": "sample_tokens (both kernels)", "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                      "traffic": None, "avg_launch_ms": ms, "algorithmic_bytes": nbytes},
     }

@@ -411,11 +411,14 @@ int paged_attn_decode_q8(void* out, float* lse, const void* q,
  *   kept: device int32 [rows][2] or NULL - tokens kept after top-k and
  *   after top-p. workspace: device memory of at least
  *   sample_workspace_size(rows, vocab) bytes, 8-byte aligned, owned by the
- *   caller, holding per-chunk candidates between the call's two kernels
+ *   caller, holding per-chunk results between the call's two kernels
  *   (contents on entry are ignored; calls sharing one workspace must not
  *   overlap). Rows with a top-k of at most 256 tokens (and greedy rows) are
- *   finished from those candidates, other rows by one workgroup over the
- *   whole row; both give the result defined above. Errors: NULL_POINTER,
+ *   finished from per-chunk candidates; rows with top-k off and a vocabulary
+ *   of at most 64 x 8192 from per-chunk maxima and fp64 mass histograms
+ *   (falling back to the next path when more than 12288 tokens share the
+ *   histogram bin of the top-p boundary); other rows by one workgroup over
+ *   the whole row. All paths give the result defined above. Errors: NULL_POINTER,
  *   INVALID_ARGUMENT (vocab < 1 or above 8192 x 8192, ld < vocab,
  *   rows x ceil(vocab / 8192) above INT32_MAX, workspace not 8-byte
  *   aligned), WORKSPACE_TOO_SMALL, HIP. */
@@ -424,7 +427,9 @@ int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t ro
                   const float* u, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace sample_tokens needs: rows x ceil(vocab / 8192) chunks,
- * each with 256 candidate slots of 8 bytes.
+ * each with 2048 fp64 histogram bins (which also hold the 256 candidate
+ * slots of 8 bytes) and a 16-byte header when there are at most 64 chunks,
+ * else with the 256 candidate slots only.
  * Errors: NULL_POINTER, INVALID_ARGUMENT (as for sample_tokens). */
 int sample_workspace_size(int32_t rows, int32_t vocab, size_t* bytes);
 

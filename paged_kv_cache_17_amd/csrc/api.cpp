@@ -242,7 +242,8 @@ extern "C" int sample_tokens(int32_t* token, int32_t* kept, const float* logits,
     if (workspace_bytes < pkv::sample_workspace_bytes(rows, vocab)) return PKV_ERR_WORKSPACE_TOO_SMALL;
     if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0) return PKV_ERR_INVALID_ARGUMENT;
     pkv::SampleArgs a{logits, vocab, static_cast<size_t>(ld), temperature, top_k, top_p, u, token, kept,
-                      static_cast<uint2*>(workspace), pkv::sample_chunks(vocab)};
+                      static_cast<unsigned char*>(workspace), rows, pkv::sample_chunks(vocab),
+                      pkv::sample_region_bytes(vocab)};
     const hipError_t e = pkv::launch_sample(a, rows, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -60,16 +60,32 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
 
 // Token sampling after the LM head. Rows whose top-k set is small go
 // through a candidate pass (chunks of kSampleChunk logits, each keeping its
-// own top-k) and are finished from those candidates; the others by one
-// workgroup over the whole row.
+// own top-k) and are finished from those candidates; rows with top-k off
+// (vocabularies of at most kSampleHistChunks chunks) through per-chunk mass
+// histograms; the others by one workgroup over the whole row.
 constexpr int kSampleChunk = 8192;      // logits per candidate-pass workgroup
 constexpr int kSampleMaxK = 256;        // largest top-k on the candidate path
 constexpr int kSampleMaxCand = 8192;    // candidates one finishing workgroup holds
+constexpr int kSampleHistBins = 2048;   // mass histogram bins per chunk (top 11 bits of the order key)
+constexpr int kSampleHistChunks = 64;   // widest row (in chunks) the histogram path merges
 inline int sample_chunks(int vocab) { return (vocab + kSampleChunk - 1) / kSampleChunk; }
-// workspace: candidates [rows][chunks][kSampleMaxK] uint2
-inline size_t sample_workspace_bytes(int rows, int vocab) {
-    return static_cast<size_t>(rows) * sample_chunks(vocab) * kSampleMaxK * 8u;
+// Per (row, chunk): a region of kSampleMaxK (key, index) candidates or, when
+// the row has at most kSampleHistChunks chunks, of kSampleHistBins fp64
+// masses (the candidates fit in it); then, for those rows, a 16-byte
+// header per (row, chunk) after all regions.
+inline size_t sample_region_bytes(int vocab) {
+    return sample_chunks(vocab) <= kSampleHistChunks ? static_cast<size_t>(kSampleHistBins) * 8u
+                                                     : static_cast<size_t>(kSampleMaxK) * 8u;
 }
+inline size_t sample_workspace_bytes(int rows, int vocab) {
+    const size_t per = sample_region_bytes(vocab) + (sample_chunks(vocab) <= kSampleHistChunks ? 16u : 0u);
+    return static_cast<size_t>(rows) * sample_chunks(vocab) * per;
+}
+struct SampleChunkHead {
+    float mc;          // largest z of the chunk
+    float pad;
+    double total;      // sum of exp(z - mc) over the chunk (written when top-p is off)
+};
 struct SampleArgs {
     const float* logits;         // [rows][ld], the first vocab entries used
     int vocab;
@@ -80,8 +96,10 @@ struct SampleArgs {
     const float* u;              // [rows] uniform numbers in [0, 1)
     int32_t* token;              // [rows]
     int32_t* kept;               // [rows][2] tokens kept by top-k and by top-p, or nullptr
-    uint2* cand;                 // [rows][chunks][kSampleMaxK] (key, index) candidates
+    unsigned char* ws;           // sample_workspace_bytes(rows, vocab), 8-byte aligned
+    int rows;
     int chunks;                  // sample_chunks(vocab)
+    size_t region;               // sample_region_bytes(vocab)
 };
 hipError_t launch_sample(const SampleArgs& a, int rows, hipStream_t stream);
 

@@ -15,7 +15,7 @@
 //    exceeds u times the kept total (u in [0, 1) is an input: the only
 //    random number the step uses).
 //
-// Two paths, chosen per row on the device:
+// Three paths, chosen per row on the device:
 //  * candidate path (greedy rows, and top-k sets of at most kSampleMaxK
 //    tokens): the row is cut into chunks of at most kSampleChunk logits,
 //    one 256-thread workgroup each, which reads its chunk once into
@@ -26,11 +26,22 @@
 //    those k-th keys (no other token can reach the row's top-k), orders
 //    them by counting (bitonic sort in LDS when many are tied), and runs
 //    top-p and the draw on the first k.
-//  * whole-row path (top-k off or large): one 1024-thread workgroup per row
-//    finds the k-th largest key and the top-p boundary by radix descents
-//    over the row (counts, and fp64 mass sums, per 8-bit digit in LDS);
-//    ties at a boundary are resolved in index order with wave ballots.
-// The second kernel runs both: each workgroup takes its row's path.
+//  * histogram path (top-k off, rows of at most kSampleHistChunks chunks):
+//    each chunk workgroup records its largest z and, with top-p on, the
+//    fp64 masses exp(z - chunk max) summed per bin of the key's top 11
+//    bits. One workgroup per row rescales and adds the chunks' histograms,
+//    finds the bin holding the top-p boundary, gathers that bin's tokens
+//    into LDS in one pass over the row and finishes the boundary there
+//    (two more key digits, then index digits among tied keys). The draw
+//    picks the chunk from per-chunk kept masses and walks that chunk only.
+//  * whole-row path (top-k between kSampleMaxK and the vocabulary, rows
+//    wider than kSampleHistChunks chunks, or a boundary bin of more than
+//    kBucketCap tokens): one 1024-thread workgroup per row finds the k-th
+//    largest key and the top-p boundary by radix descents over the row
+//    (counts, and fp64 mass sums, per 8-bit digit in LDS); ties at a
+//    boundary are resolved in index order with wave ballots.
+// The second kernel runs the finishing step: each workgroup takes its row's
+// path.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -46,6 +57,7 @@ constexpr int kWaves = kThreads / kWave;
 static_assert(kPerThread * kChunkThreads == kSampleChunk, "chunk split");
 static_assert(kSampleMaxK <= 4 * kWave, "one wave scans the top-k (4 per lane)");
 static_assert(kSampleMaxCand % kThreads == 0, "candidates per thread");
+static_assert(kChunkKeep + 2048 / 2 <= kSampleHistBins, "chunk pool: keep list and 2048 u32 digit bins");
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -96,6 +108,28 @@ __device__ __forceinline__ int kept_by_k(int k, int V) { return (k <= 0 || k >= 
 // whole-row path.
 __device__ __forceinline__ bool on_candidate_path(float T, int k_eff, int chunks) {
     return T == 0.0f || (k_eff <= kSampleMaxK && chunks * k_eff <= kSampleMaxCand);
+}
+
+// Rows with top-k off (T > 0) and at most kSampleHistChunks chunks; the
+// candidate path keeps precedence (a vocabulary of at most kSampleMaxK).
+__device__ __forceinline__ bool on_hist_path(float T, int k_eff, int V, int chunks) {
+    return T > 0.0f && k_eff >= V && chunks <= kSampleHistChunks;
+}
+
+// Workspace of (row, chunk): candidates, or the chunk's mass histogram; and
+// the chunk's header (histogram rows only).
+__device__ __forceinline__ unsigned char* chunk_region(const SampleArgs& a, int row, int s) {
+    return a.ws + (static_cast<size_t>(row) * a.chunks + s) * a.region;
+}
+__device__ __forceinline__ uint2* chunk_cands(const SampleArgs& a, int row, int s) {
+    return reinterpret_cast<uint2*>(chunk_region(a, row, s));
+}
+__device__ __forceinline__ double* chunk_hist(const SampleArgs& a, int row, int s) {
+    return reinterpret_cast<double*>(chunk_region(a, row, s));
+}
+__device__ __forceinline__ SampleChunkHead* chunk_head(const SampleArgs& a, int row, int s) {
+    return reinterpret_cast<SampleChunkHead*>(a.ws + static_cast<size_t>(a.rows) * a.chunks * a.region) +
+           static_cast<size_t>(row) * a.chunks + s;
 }
 
 __device__ __forceinline__ void write_result(const SampleArgs& a, int row, int token, int kk, int kp) {
@@ -173,9 +207,62 @@ __device__ __forceinline__ void chunk_digit(const uint32_t (&key)[kPerThread], i
     rem -= *s_above;
 }
 
-// One workgroup per (row, chunk), blockIdx.x = row * chunks + chunk. Writes
-// the chunk's min(k, chunk length) best (key, index) pairs to its candidate
-// slots, best first (decreasing key, ties by lower index).
+// Histogram path, pass 1: the chunk's largest z and, with top-p on, its
+// fp64 masses exp(z - chunk max) summed per bin of the key's top 11 bits
+// (the bins of every chunk line up, so the row adds them after rescaling);
+// with top-p off only the chunk's total mass. Keys of 0 lie past the
+// chunk's end.
+__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s,
+                                             const uint32_t (&key)[kPerThread], double* s_hm, uint32_t* s_tw) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const bool hist = a.top_p[row] < 1.0f;
+    uint32_t mk = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) mk = max(mk, key[i]);
+    mk = wave_max_u32(mk);
+    if (lane == 0) s_tw[wave] = mk;
+    if (hist)
+        for (int b = tid; b < kSampleHistBins; b += kChunkThreads) s_hm[b] = 0.0;
+    __syncthreads();
+    mk = s_tw[0];
+#pragma unroll
+    for (int w = 1; w < kChunkWaves; ++w) mk = max(mk, s_tw[w]);
+    const float mc = key_value(mk);
+    const double mcd = static_cast<double>(mc);
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        if (!key[i]) continue;
+        const double m = exp(static_cast<double>(key_value(key[i])) - mcd);
+        if (hist) atomicAdd(&s_hm[key[i] >> 21], m);
+        else tot += m;
+    }
+    SampleChunkHead* h = chunk_head(a, row, s);
+    if (hist) {
+        __syncthreads();
+        double* out = chunk_hist(a, row, s);
+        for (int b = tid; b < kSampleHistBins; b += kChunkThreads) out[b] = s_hm[b];
+        if (tid == 0) h->mc = mc;
+    } else {
+        tot = wave_sum_f64(tot);
+        if (lane == 0) s_hm[wave] = tot;
+        __syncthreads();
+        if (tid == 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int w = 0; w < kChunkWaves; ++w) t += s_hm[w];
+            h->mc = mc;
+            h->total = t;
+        }
+    }
+}
+
+// One workgroup per (row, chunk), blockIdx.x = row * chunks + chunk.
+// Candidate rows: writes the chunk's min(k, chunk length) best (key, index)
+// pairs to its candidate slots, best first (decreasing key, ties by lower
+// index). Histogram rows: chunk_masses.
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void sample_chunk_kernel(SampleArgs a) {
     const int S = a.chunks;
@@ -188,7 +275,8 @@ void sample_chunk_kernel(SampleArgs a) {
     const float T = a.temperature[row];
     if (!(T >= 0.0f)) return;
     const int k_eff = T > 0.0f ? kept_by_k(a.top_k[row], V) : 1;
-    if (!on_candidate_path(T, k_eff, S)) return;
+    const bool cand = on_candidate_path(T, k_eff, S);
+    if (!cand && !on_hist_path(T, k_eff, V, S)) return;
     const int C = (V + S - 1) / S;
     const int lo = s * C;
     const int hi = min(V, lo + C);
@@ -213,9 +301,14 @@ void sample_chunk_kernel(SampleArgs a) {
     for (int i = 0; i < kPerThread; ++i) key[i] = jb + i * kChunkThreads < hi ? order_key(__uint_as_float(key[i])) : 0u;
 
     __shared__ uint32_t s_tw[kChunkWaves];
-    __shared__ uint64_t s_keep[kChunkKeep];
-    __shared__ uint32_t s_hist[2048];
+    __shared__ uint64_t s_pool[kSampleHistBins];   // histogram rows: fp64 bins; candidate rows: keep list + digit bins
     __shared__ uint32_t s_tc[kPerThread * kChunkWaves];
+    if (!cand) {
+        chunk_masses(a, row, s, key, reinterpret_cast<double*>(s_pool), s_tw);
+        return;
+    }
+    uint64_t* s_keep = s_pool;
+    uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_pool + kChunkKeep);
     __shared__ int s_bin;
     __shared__ uint32_t s_above, s_n;
     const unsigned long long below = (1ull << lane) - 1ull;
@@ -309,7 +402,7 @@ void sample_chunk_kernel(SampleArgs a) {
     }
 
     // best first: the rank of each kept composite is its slot
-    uint2* out = a.cand + (static_cast<size_t>(row) * S + s) * kSampleMaxK;
+    uint2* out = chunk_cands(a, row, s);
     for (uint32_t e = tid; e < kept; e += kChunkThreads) {
         const uint64_t me = s_keep[e];
         uint32_t r = 0;
@@ -356,7 +449,9 @@ __device__ __forceinline__ bool cand_digit(const uint64_t (&c)[kCandPerThread], 
     return s_dig[2] != 0;
 }
 
-__device__ __forceinline__ void finish_from_candidates(const SampleArgs& a, int row, float T, int k_eff) {
+// pool: kernel-wide LDS of at least kMergeChunks * kSampleMaxK + 2 * kThreads words.
+__device__ __forceinline__ void finish_from_candidates(const SampleArgs& a, int row, float T, int k_eff,
+                                                       uint64_t* pool) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -364,7 +459,7 @@ __device__ __forceinline__ void finish_from_candidates(const SampleArgs& a, int 
     const int S = a.chunks;
     const int C = (V + S - 1) / S;
 
-    __shared__ uint32_t s_hist[2048];
+    uint32_t* s_hist = reinterpret_cast<uint32_t*>(pool + kMergeChunks * kSampleMaxK + kThreads);   // [2048]
     __shared__ int s_dig[3];                  // digit step: bin, count above it, bucket == rest
     __shared__ uint32_t s_cnt;
     __shared__ uint64_t s_sel[kSampleMaxK];   // the row's top-k, any order
@@ -375,19 +470,18 @@ __device__ __forceinline__ void finish_from_candidates(const SampleArgs& a, int 
     __shared__ int s_t;
 
     // the chunks' candidates as composites; 0 = empty (below every real one)
-    const uint2* cand = a.cand + static_cast<size_t>(row) * S * kSampleMaxK;
     const int n = S * k_eff;
     auto load = [&](int e) -> uint64_t {
         const int s = e / k_eff;
         const int t = e - s * k_eff;
         if (t >= min(V, s * C + C) - s * C) return 0;
-        const uint2 p = cand[static_cast<size_t>(s) * kSampleMaxK + t];
+        const uint2 p = chunk_cands(a, row, s)[t];
         return composite(p.x, p.y);
     };
 
     if (S <= kMergeChunks) {
-        __shared__ uint64_t s_c[kMergeChunks * kSampleMaxK];
-        __shared__ uint64_t s_sv[kThreads];
+        uint64_t* s_c = pool;                                  // [kMergeChunks * kSampleMaxK]
+        uint64_t* s_sv = pool + kMergeChunks * kSampleMaxK;    // [kThreads]
         __shared__ uint64_t s_tau;
         for (int e = tid; e < n; e += kThreads) s_c[e] = load(e);
         if (tid == 0) s_cnt = 0u;
@@ -854,8 +948,311 @@ __device__ __forceinline__ void sample_whole_row(const SampleArgs& a, int row, f
     if (tid == 0) write_result(a, row, s_i[0], kept_k, static_cast<int>(kept_p));
 }
 
-// ---- pass 2 of the candidate path, and the whole-row path -------------------------
+// ---- histogram path, pass 2 ----------------------------------------------------------
+constexpr int kBucketCap = 12288;   // tokens of the top-p boundary bin held in LDS
+constexpr int kPoolWords = 3 * kSampleHistBins / 2 + kBucketCap;   // fp64 bins, u32 counts, the bin's tokens
+static_assert(kSampleHistBins == 2 * kThreads, "two merged bins per thread");
+static_assert(kSampleHistChunks <= kWave, "one lane per chunk in the draw");
+static_assert(kSampleChunk == kWaves * 8 * kWave, "the walk covers a chunk with 8 loads per lane");
+static_assert(kSampleHistChunks * kSampleChunk <= (1 << 19), "indices fit the 19 bits of the tie digits");
+static_assert(kPoolWords >= kMergeChunks * kSampleMaxK + 2 * kThreads, "the pool holds the candidate finish");
+
+// One digit of the boundary search inside the gathered bin: fp64 masses and
+// counts of the tokens matching `prefix` under `pmask`, per NB bins of the
+// key bits at `shift`; then the bin, from the top, at which the mass
+// reaches `rest`. `above` grows by the mass of the bins above it. When
+// rounding leaves the gathered mass just short of `rest`, the boundary is
+// the lowest token: the lowest non-empty bin is taken.
+template <int NB>
+__device__ __forceinline__ void bucket_digit(const uint64_t* s_bk, uint32_t n1, int shift, double zmax, double rest,
+                                             double* s_bin, uint32_t* s_cnt, int* s_ri, double* s_rd,
+                                             uint32_t& prefix, uint32_t& pmask, double& above) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    for (int b = tid; b < NB; b += kThreads) {
+        s_bin[b] = 0.0;
+        s_cnt[b] = 0u;
+    }
+    __syncthreads();
+    for (uint32_t e = tid; e < n1; e += kThreads) {
+        const uint32_t key = comp_key(s_bk[e]);
+        if ((key & pmask) == prefix) {
+            const uint32_t b = (key >> shift) & (NB - 1);
+            atomicAdd(&s_bin[b], exp(static_cast<double>(key_value(key)) - zmax));
+            atomicAdd(&s_cnt[b], 1u);
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        double ab = 0.0;
+        int b = find_bin_from_top<NB>(s_bin, rest, &ab, lane);
+        if (lane == 0) {
+            if (b < 0) {
+                b = 0;
+                while (b < NB - 1 && s_cnt[b] == 0u) ++b;
+                ab = 0.0;
+                for (int i = NB - 1; i > b; --i) ab += s_bin[i];
+            }
+            s_ri[0] = b;
+            s_rd[0] = ab;
+        }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(s_ri[0]) << shift;
+    pmask |= static_cast<uint32_t>(NB - 1) << shift;
+    above += s_rd[0];
+}
+
+// One digit of the search for the rem-th smallest index among the gathered
+// tokens whose key is `key` (index bits at `shift`, NB bins, counted from
+// the top as NB - 1 - digit).
+template <int NB>
+__device__ __forceinline__ void tie_digit(const uint64_t* s_bk, uint32_t n1, uint32_t key, int shift,
+                                          uint32_t* s_cnt, int* s_ri, uint32_t& ip, uint32_t& imask, uint32_t& rem) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    for (int b = tid; b < NB; b += kThreads) s_cnt[b] = 0u;
+    __syncthreads();
+    for (uint32_t e = tid; e < n1; e += kThreads) {
+        const uint64_t c = s_bk[e];
+        const uint32_t idx = static_cast<uint32_t>(comp_index(c));
+        if (comp_key(c) == key && (idx & imask) == ip) atomicAdd(&s_cnt[NB - 1 - ((idx >> shift) & (NB - 1))], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        uint32_t ab = 0;
+        const int b = find_bin_from_top<NB>(s_cnt, rem, &ab, lane);   // rem never exceeds the tied tokens
+        if (lane == 0) {
+            s_ri[0] = b < 0 ? NB - 1 : b;
+            s_ri[1] = static_cast<int>(ab);
+        }
+    }
+    __syncthreads();
+    ip |= static_cast<uint32_t>(NB - 1 - s_ri[0]) << shift;
+    imask |= static_cast<uint32_t>(NB - 1) << shift;
+    rem -= static_cast<uint32_t>(s_ri[1]);
+}
+
+// Rows with top-k off, from the chunks' maxima and histograms. Returns
+// false, the same in every thread, when the top-p boundary's bin holds more
+// than kBucketCap tokens; the caller then takes the whole-row path.
+__device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int row, float T, uint64_t* pool) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int V = a.vocab;
+    const int S = a.chunks;
+    const int C = (V + S - 1) / S;
+    const Row r{a.logits + static_cast<size_t>(row) * a.ld, V, T};
+    double* s_bin = reinterpret_cast<double*>(pool);                          // [kSampleHistBins]
+    uint32_t* s_cnt = reinterpret_cast<uint32_t*>(pool + kSampleHistBins);    // [kSampleHistBins]
+    uint64_t* s_bk = pool + 3 * kSampleHistBins / 2;                          // [kBucketCap]
+    __shared__ double s_scale[kSampleHistChunks];   // exp(chunk max - row max)
+    __shared__ double s_kc[kSampleHistChunks];      // kept mass per chunk
+    __shared__ double s_wd[kWaves];
+    __shared__ uint32_t s_wu[kWaves];
+    __shared__ int s_ri[2];
+    __shared__ double s_rd[2];
+    __shared__ uint32_t s_n;
+
+    // ---- max z from the chunks' maxima ----------------------------------------------
+    if (tid < S) s_scale[tid] = static_cast<double>(chunk_head(a, row, tid)->mc);
+    __syncthreads();
+    double zmax = s_scale[0];
+    for (int c = 1; c < S; ++c) zmax = fmax(zmax, s_scale[c]);
+    __syncthreads();
+    if (tid < S) {
+        s_scale[tid] = exp(s_scale[tid] - zmax);
+        s_kc[tid] = 0.0;
+    }
+    if (tid == 0) s_n = 0u;
+    __syncthreads();
+
+    const float tp = a.top_p[row];
+    uint32_t pkey = 0;   // kept: key > pkey, or key == pkey and index <= pidx
+    int pidx = V;
+    uint32_t kept_p = static_cast<uint32_t>(V);
+    if (tp < 1.0f) {
+        // ---- the row's histogram: bins tid and tid + kThreads ----------------------
+        double m0 = 0.0, m1 = 0.0;
+#pragma unroll 4
+        for (int c = 0; c < S; ++c) {
+            const double* h = chunk_hist(a, row, c);
+            m0 += s_scale[c] * h[tid];
+            m1 += s_scale[c] * h[tid + kThreads];
+        }
+        s_bin[tid] = m0;
+        s_bin[tid + kThreads] = m1;
+        double tot = wave_sum_f64(m0 + m1);
+        if (lane == 0) s_wd[wave] = tot;
+        __syncthreads();
+        tot = 0.0;
+        for (int w = 0; w < kWaves; ++w) tot += s_wd[w];
+        const double need = static_cast<double>(tp) * tot;
+        if (wave == 0) {
+            double ab = 0.0;
+            int b = find_bin_from_top<kSampleHistBins>(s_bin, need, &ab, lane);
+            if (lane == 0) {
+                if (b < 0) {   // rounding: the lowest bin with mass holds the boundary
+                    b = 0;
+                    while (b < kSampleHistBins - 1 && !(s_bin[b] > 0.0)) ++b;
+                    ab = 0.0;
+                    for (int i = kSampleHistBins - 1; i > b; --i) ab += s_bin[i];
+                }
+                s_ri[0] = b;
+                s_rd[0] = ab;
+            }
+        }
+        __syncthreads();
+        const uint32_t b1 = static_cast<uint32_t>(s_ri[0]);
+        double above = s_rd[0];
+
+        // ---- gather the boundary bin's tokens; count the tokens above it ----------
+        uint32_t n_above = 0;
+        each_z(r, [&](int j, float zj) {
+            const uint32_t key = order_key(zj);
+            const uint32_t b = key >> 21;
+            n_above += b > b1;
+            if (b == b1) {
+                const uint32_t slot = atomicAdd(&s_n, 1u);
+                if (slot < kBucketCap) s_bk[slot] = composite(key, static_cast<uint32_t>(j));
+            }
+        });
+        n_above = wave_sum_u32(n_above);
+        if (lane == 0) s_wu[wave] = n_above;
+        __syncthreads();
+        const uint32_t n1 = s_n;
+        if (n1 > static_cast<uint32_t>(kBucketCap)) return false;
+        n_above = 0;
+        for (int w = 0; w < kWaves; ++w) n_above += s_wu[w];
+
+        // ---- the boundary key: two more digits over the gathered tokens ------------
+        uint32_t prefix = b1 << 21, pmask = 0xFFE00000u;
+        bucket_digit<2048>(s_bk, n1, 10, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
+        bucket_digit<1024>(s_bk, n1, 0, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
+        pkey = prefix;
+        const uint32_t ties = s_cnt[pkey & 1023u];
+        __syncthreads();   // the tie count is read before the counts are reused
+        // every tie has the same mass; keep the first `keep` of them in index order
+        const double pb = exp(static_cast<double>(key_value(pkey)) - zmax);
+        const double t = (need - above) / pb;
+        const uint32_t keep = t <= 1.0 ? 1u : static_cast<uint32_t>(fmin(ceil(t), static_cast<double>(ties)));
+        if (keep < ties) {
+            uint32_t ip = 0, imask = 0, rem = keep;
+            tie_digit<1024>(s_bk, n1, pkey, 9, s_cnt, s_ri, ip, imask, rem);
+            tie_digit<512>(s_bk, n1, pkey, 0, s_cnt, s_ri, ip, imask, rem);
+            pidx = static_cast<int>(ip);
+        }
+
+        // ---- kept mass per chunk: the gathered tokens kept, plus the bins above ----
+        uint32_t nk = 0;
+        for (uint32_t e = tid; e < n1; e += kThreads) {
+            const uint64_t c = s_bk[e];
+            const uint32_t key = comp_key(c);
+            const int j = comp_index(c);
+            if (key > pkey || (key == pkey && j <= pidx)) {
+                ++nk;
+                atomicAdd(&s_kc[j / C], exp(static_cast<double>(key_value(key)) - zmax));
+            }
+        }
+        nk = wave_sum_u32(nk);
+        if (lane == 0) s_wu[wave] = nk;
+        __syncthreads();
+        kept_p = n_above;
+        for (int w = 0; w < kWaves; ++w) kept_p += s_wu[w];
+        for (int c = wave; c < S; c += kWaves) {
+            const double* h = chunk_hist(a, row, c);
+            double acc = 0.0;
+#pragma unroll 4
+            for (int b = static_cast<int>(b1) + 1 + lane; b < kSampleHistBins; b += kWave) acc += h[b];
+            acc = wave_sum_f64(acc);
+            if (lane == 0) s_kc[c] += s_scale[c] * acc;
+        }
+        __syncthreads();
+    } else {
+        if (tid < S) s_kc[tid] = s_scale[tid] * chunk_head(a, row, tid)->total;
+        __syncthreads();
+    }
+
+    // ---- draw: the chunk, then the token, in vocabulary order ----------------------
+    if (wave == 0) {
+        const double kc = lane < S ? s_kc[lane] : 0.0;
+        const double incl = wave_incl_scan(kc, lane);
+        const double target = static_cast<double>(a.u[row]) * __shfl(incl, kWave - 1, kWave);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(kc > 0.0 && incl > target);
+        const unsigned long long any = __builtin_amdgcn_ballot_w64(kc > 0.0);
+        // rounding may put the target at the total: the last chunk with kept mass
+        const int c = hit ? __builtin_ctzll(hit) : (any ? 63 - __builtin_clzll(any) : 0);
+        const double before = __shfl(incl - kc, c, kWave);
+        if (lane == 0) {
+            s_ri[0] = c;
+            s_rd[0] = target;
+            s_rd[1] = before;
+        }
+    }
+    __syncthreads();
+    const double target = s_rd[0];
+    const int lo = s_ri[0] * C;
+    const int hi = min(V, lo + C);
+    const int base = lo + wave * (8 * kWave);   // this wave's 512 indices of the chunk
+    double mm[8];
+    uint32_t kbits = 0;
+    double wsum = 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int j = base + u * kWave + lane;
+        const float zj = r.x[min(j, hi - 1)] / T;
+        const uint32_t key = order_key(zj);
+        const bool kp = j < hi && (key > pkey || (key == pkey && j <= pidx));
+        mm[u] = kp ? exp(static_cast<double>(zj) - zmax) : 0.0;
+        kbits |= static_cast<uint32_t>(kp) << u;
+        wsum += mm[u];
+    }
+    wsum = wave_sum_f64(wsum);
+    const bool wany = __builtin_amdgcn_ballot_w64(kbits != 0u) != 0ull;
+    if (lane == 0) {
+        s_wd[wave] = wsum;
+        s_wu[wave] = wany;
+    }
+    __syncthreads();
+    double pre = s_rd[1], pre_last = pre;
+    int wh = -1, wl = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        if (!s_wu[w]) continue;
+        if (pre + s_wd[w] > target) {
+            wh = w;
+            break;
+        }
+        wl = w;
+        pre_last = pre;
+        pre += s_wd[w];
+    }
+    if (wh < 0) {   // rounding put the target at the chunk's total: its last kept token
+        wh = wl;
+        pre = pre_last;
+    }
+    if (wave == wh) {
+        double run = pre;
+        int found = -1, last = -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool kp = (kbits >> u) & 1u;
+            const double incl = wave_incl_scan(mm[u], lane);
+            const unsigned long long cross = __builtin_amdgcn_ballot_w64(kp && run + incl > target);
+            const unsigned long long any = __builtin_amdgcn_ballot_w64(kp);
+            const int j0 = base + u * kWave;
+            if (any) last = j0 + 63 - __builtin_clzll(any);
+            if (found < 0 && cross) found = j0 + __builtin_ctzll(cross);
+            run += __shfl(incl, kWave - 1, kWave);
+        }
+        if (lane == 0) write_result(a, row, found >= 0 ? found : last, V, static_cast<int>(kept_p));
+    }
+    return true;
+}
+
+// ---- the finishing kernel: one workgroup per row, on the row's path ---------------
 __global__ __launch_bounds__(kThreads) void sample_row_kernel(SampleArgs a) {
+    __shared__ uint64_t s_pool[kPoolWords];
     const int row = blockIdx.x;
     const float T = a.temperature[row];
     if (!(T >= 0.0f)) {   // negative or NaN temperature: no token
@@ -863,8 +1260,9 @@ __global__ __launch_bounds__(kThreads) void sample_row_kernel(SampleArgs a) {
         return;
     }
     const int k_eff = T > 0.0f ? kept_by_k(a.top_k[row], a.vocab) : 1;
-    if (on_candidate_path(T, k_eff, a.chunks)) finish_from_candidates(a, row, T, k_eff);
-    else sample_whole_row(a, row, T, k_eff);
+    if (on_candidate_path(T, k_eff, a.chunks)) finish_from_candidates(a, row, T, k_eff, s_pool);
+    else if (!on_hist_path(T, k_eff, a.vocab, a.chunks) || !finish_from_histograms(a, row, T, s_pool))
+        sample_whole_row(a, row, T, k_eff);
 }
 
 }  // namespace

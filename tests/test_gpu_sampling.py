@@ -9,9 +9,11 @@ the two may legitimately differ - the draw's u, or the top-p boundary
 share, within 1e-9 of a step - the GPU's answer is checked to be one of the
 valid neighbours; everywhere else tokens and kept counts are exact.
 
-Rows take one of two device paths (top-k of at most 256 tokens with
-chunks x k <= 8192: per-chunk candidates; otherwise one workgroup over the
-whole row); the cases below put rows on both sides of that line.
+Rows take one of three device paths (top-k of at most 256 tokens with
+chunks x k <= 8192: per-chunk candidates; top-k off on rows of at most 64
+chunks: per-chunk mass histograms, unless more than 12288 tokens share the
+top-p boundary's bin; otherwise one workgroup over the whole row); the
+cases below put rows on every side of those lines.
 """
 import numpy as np
 import pytest
@@ -105,6 +107,33 @@ def test_path_boundary_on_a_wide_vocabulary():
     assert exact >= 15
 
 
+def test_top_k_off_rows():
+    """Top-k off on a 128256-entry vocabulary (16 chunks): smooth rows of
+    several spreads, a row of identical logits (its boundary bin holds every
+    token, beyond what the histogram path gathers: whole-row path), rows on
+    coarse grids (large tied bins, ties at the boundary) and a row whose top
+    half is one tied value."""
+    sw = build_sample_workload(rows=24, vocab=128256, seed=21, ks=(0,), temps=(0.5, 1.0, 2.0),
+                               ps=(1.0, 0.99, 0.9, 0.5, 0.1), sigmas=(0.5, 2.0, 6.0))
+    sw.logits[0] = 0.5
+    sw.logits[1] = np.round(sw.logits[1] * 4.0) / 4.0
+    sw.logits[2] = np.round(sw.logits[2] * 64.0) / 64.0
+    sw.logits[3, ::2] = 3.0
+    sw.top_p[:4] = (0.5, 0.9, 0.9, 0.3)
+    exact = _check(sw)
+    assert exact >= 22
+
+
+def test_top_k_off_beyond_the_histogram_rows():
+    """65 chunks (one more than the histogram path merges) and 64 chunks
+    exactly, top-k off: the whole-row path and the widest histogram row."""
+    for vocab in (65 * 8192, 64 * 8192):
+        sw = build_sample_workload(rows=6, vocab=vocab, seed=vocab % 1000, ks=(0,), temps=(0.7, 1.3),
+                                   ps=(1.0, 0.9, 0.6))
+        exact = _check(sw)
+        assert exact >= 5, vocab
+
+
 def test_invalid_temperature_gives_no_token():
     import paged_kv_cache_17_amd as pkv
     x = torch.randn(3, 5000, device="cuda")
@@ -126,7 +155,7 @@ def test_workspace_is_checked():
     p = torch.ones(2, device="cuda")
     u = torch.full((2,), 0.5, device="cuda")
     need = pkv.sample_workspace_size(2, 20000)
-    assert need == 2 * 3 * 2048
+    assert need == 2 * 3 * (16384 + 16)
     small = torch.empty(need - 8, dtype=torch.uint8, device="cuda")
     with pytest.raises(pkv.PagedKVError):
         pkv.sample_tokens(x, T, k, p, u, workspace=small)
