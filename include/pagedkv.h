@@ -420,7 +420,7 @@ int paged_attn_decode_q8(void* out, float* lse, const void* q,
  *   histogram bin of the top-p boundary); other rows by one workgroup over
  *   the whole row. All paths give the result defined above. Errors: NULL_POINTER,
  *   INVALID_ARGUMENT (vocab < 1 or above 8192 x 8192, ld < vocab,
- *   rows x ceil(vocab / 8192) above INT32_MAX, workspace not 8-byte
+ *   rows x ceil(vocab / 8192) or rows x 4 above INT32_MAX, workspace not 8-byte
  *   aligned), WORKSPACE_TOO_SMALL, HIP. */
 int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t rows, int32_t vocab,
                   int64_t ld, const float* temperature, const int32_t* top_k, const float* top_p,
@@ -428,8 +428,9 @@ int sample_tokens(int32_t* token, int32_t* kept, const float* logits, int32_t ro
 
 /* Bytes of workspace sample_tokens needs: rows x ceil(vocab / 8192) chunks,
  * each with 2048 fp64 histogram bins (which also hold the 256 candidate
- * slots of 8 bytes) and a 16-byte header when there are at most 64 chunks,
- * else with the 256 candidate slots only.
+ * slots of 8 bytes) and a 16-byte header, plus per row 12288 8-byte slots
+ * and 64 bytes of counters, when there are at most 64 chunks; else the 256
+ * candidate slots per chunk only.
  * Errors: NULL_POINTER, INVALID_ARGUMENT (as for sample_tokens). */
 int sample_workspace_size(int32_t rows, int32_t vocab, size_t* bytes);
 

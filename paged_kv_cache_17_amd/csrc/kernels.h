@@ -77,9 +77,16 @@ inline size_t sample_region_bytes(int vocab) {
     return sample_chunks(vocab) <= kSampleHistChunks ? static_cast<size_t>(kSampleHistBins) * 8u
                                                      : static_cast<size_t>(kSampleMaxK) * 8u;
 }
+constexpr int kSampleBucketCap = 12288;  // tokens of a row's top-p boundary bin the histogram path holds
+constexpr int kSampleRowSplit = 4;       // workgroups per histogram row in the gathering pass
+// ... and per histogram row, after the headers: the boundary bin's tokens
+// (kSampleBucketCap 8-byte entries, a quarter per gathering workgroup) and
+// 64 bytes of counters.
 inline size_t sample_workspace_bytes(int rows, int vocab) {
-    const size_t per = sample_region_bytes(vocab) + (sample_chunks(vocab) <= kSampleHistChunks ? 16u : 0u);
-    return static_cast<size_t>(rows) * sample_chunks(vocab) * per;
+    const bool hist = sample_chunks(vocab) <= kSampleHistChunks;
+    const size_t per = sample_region_bytes(vocab) + (hist ? 16u : 0u);
+    const size_t row_extra = hist ? static_cast<size_t>(kSampleBucketCap) * 8u + 64u : 0u;
+    return static_cast<size_t>(rows) * (sample_chunks(vocab) * per + row_extra);
 }
 struct SampleChunkHead {
     float mc;          // largest z of the chunk

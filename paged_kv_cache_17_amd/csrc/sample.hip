@@ -132,6 +132,21 @@ __device__ __forceinline__ SampleChunkHead* chunk_head(const SampleArgs& a, int 
            static_cast<size_t>(row) * a.chunks + s;
 }
 
+// Histogram rows: the boundary bin's tokens gathered by the row's
+// workgroups (workgroup g writes the g-th quarter), and counters: [0]
+// workgroups done, [2 + 2g] and [3 + 2g] workgroup g's tokens (0xFFFFFFFF:
+// more than its quarter) and tokens above the bin; after the chunk headers.
+__device__ __forceinline__ unsigned char* row_extra(const SampleArgs& a, int row) {
+    return a.ws + static_cast<size_t>(a.rows) * a.chunks * (a.region + sizeof(SampleChunkHead)) +
+           static_cast<size_t>(row) * (static_cast<size_t>(kSampleBucketCap) * 8u + 64u);
+}
+__device__ __forceinline__ uint64_t* row_list(const SampleArgs& a, int row) {
+    return reinterpret_cast<uint64_t*>(row_extra(a, row));
+}
+__device__ __forceinline__ uint32_t* row_counters(const SampleArgs& a, int row) {
+    return reinterpret_cast<uint32_t*>(row_extra(a, row) + static_cast<size_t>(kSampleBucketCap) * 8u);
+}
+
 __device__ __forceinline__ void write_result(const SampleArgs& a, int row, int token, int kk, int kp) {
     a.token[row] = token;
     if (a.kept) {
@@ -207,17 +222,18 @@ __device__ __forceinline__ void chunk_digit(const uint32_t (&key)[kPerThread], i
     rem -= *s_above;
 }
 
-// Histogram path, pass 1: the chunk's largest z and, with top-p on, its
-// fp64 masses exp(z - chunk max) summed per bin of the key's top 11 bits
-// (the bins of every chunk line up, so the row adds them after rescaling);
-// with top-p off only the chunk's total mass. Keys of 0 lie past the
-// chunk's end.
+// Histogram path, pass 1: the chunk's largest z, its total mass and, with
+// top-p on, its fp64 masses exp(z - chunk max) per bin of the key's top 11
+// bits, stored as inclusive suffix sums (I[b] = mass of the bins b and
+// above; the bins of every chunk line up, so the row adds them after
+// rescaling). Keys of 0 lie past the chunk's end.
 __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s,
                                              const uint32_t (&key)[kPerThread], double* s_hm, uint32_t* s_tw) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const bool hist = a.top_p[row] < 1.0f;
+    __shared__ double s_wt[kChunkWaves];
     uint32_t mk = 0;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) mk = max(mk, key[i]);
@@ -242,17 +258,42 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
     SampleChunkHead* h = chunk_head(a, row, s);
     if (hist) {
         __syncthreads();
+        // suffix sums: thread t owns bins 8t .. 8t + 7; then the threads
+        // above it (a suffix scan over lanes, then over waves)
+        constexpr int kPer = kSampleHistBins / kChunkThreads;
+        double l[kPer];
+        double run = 0.0;
+#pragma unroll
+        for (int i = kPer - 1; i >= 0; --i) {
+            run += s_hm[kPer * tid + i];
+            l[i] = run;
+        }
+        double suf = run;   // inclusive over lanes lane .. 63 of this wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double y = __shfl_down(suf, o, kWave);
+            if (lane + o < kWave) suf += y;
+        }
+        if (lane == 0) s_wt[wave] = suf;
+        __syncthreads();
+        double above = __shfl_down(suf, 1, kWave);   // lanes above this one
+        if (lane == kWave - 1) above = 0.0;
+        for (int w = kChunkWaves - 1; w > wave; --w) above += s_wt[w];
         double* out = chunk_hist(a, row, s);
-        for (int b = tid; b < kSampleHistBins; b += kChunkThreads) out[b] = s_hm[b];
-        if (tid == 0) h->mc = mc;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) out[kPer * tid + i] = l[i] + above;
+        if (tid == 0) {
+            h->mc = mc;
+            h->total = l[0] + above;
+        }
     } else {
         tot = wave_sum_f64(tot);
-        if (lane == 0) s_hm[wave] = tot;
+        if (lane == 0) s_wt[wave] = tot;
         __syncthreads();
         if (tid == 0) {
             double t = 0.0;
 #pragma unroll
-            for (int w = 0; w < kChunkWaves; ++w) t += s_hm[w];
+            for (int w = 0; w < kChunkWaves; ++w) t += s_wt[w];
             h->mc = mc;
             h->total = t;
         }
@@ -304,6 +345,7 @@ void sample_chunk_kernel(SampleArgs a) {
     __shared__ uint64_t s_pool[kSampleHistBins];   // histogram rows: fp64 bins; candidate rows: keep list + digit bins
     __shared__ uint32_t s_tc[kPerThread * kChunkWaves];
     if (!cand) {
+        if (s == 0 && tid == 0) row_counters(a, row)[0] = 0u;   // counted up by the finishing kernel
         chunk_masses(a, row, s, key, reinterpret_cast<double*>(s_pool), s_tw);
         return;
     }
@@ -949,13 +991,14 @@ __device__ __forceinline__ void sample_whole_row(const SampleArgs& a, int row, f
 }
 
 // ---- histogram path, pass 2 ----------------------------------------------------------
-constexpr int kBucketCap = 12288;   // tokens of the top-p boundary bin held in LDS
+constexpr int kBucketCap = kSampleBucketCap;   // tokens of the top-p boundary bin held in LDS
 constexpr int kPoolWords = 3 * kSampleHistBins / 2 + kBucketCap;   // fp64 bins, u32 counts, the bin's tokens
 static_assert(kSampleHistBins == 2 * kThreads, "two merged bins per thread");
 static_assert(kSampleHistChunks <= kWave, "one lane per chunk in the draw");
 static_assert(kSampleChunk == kWaves * 8 * kWave, "the walk covers a chunk with 8 loads per lane");
 static_assert(kSampleHistChunks * kSampleChunk <= (1 << 19), "indices fit the 19 bits of the tie digits");
 static_assert(kPoolWords >= kMergeChunks * kSampleMaxK + 2 * kThreads, "the pool holds the candidate finish");
+static_assert(kBucketCap % (kWaves * kWave) == 0, "whole rows of the per-wave regions");
 
 // One digit of the boundary search inside the gathered bin: fp64 masses and
 // counts of the tokens matching `prefix` under `pmask`, per NB bins of the
@@ -1033,10 +1076,107 @@ __device__ __forceinline__ void tie_digit(const uint64_t* s_bk, uint32_t n1, uin
     rem -= static_cast<uint32_t>(s_ri[1]);
 }
 
+// The least order key kx of a logit x with key(fl(x / T)) >= target, or
+// 0xFFFFFFFF when no finite logit reaches it; called by a whole wave.
+// Correctly rounded division by T > 0 is monotone in x, and so is the key of
+// its result: a test of the scaled logit's key against `target` is a test of
+// kx against this value. Each step tests 64 evenly spaced keys of the range
+// left (those of -inf .. +inf at first; finite logits lie strictly inside).
+__device__ __forceinline__ uint32_t wave_key_threshold(uint32_t target, float T, int lane) {
+    auto reaches = [&](uint32_t kx) { return order_key(key_value(kx) / T) >= target; };
+    uint32_t lo = 0x007FFFFFu, hi = 0xFF800000u;   // reaches(hi); every key below lo fails
+    if (!reaches(hi)) return 0xFFFFFFFFu;
+    while (lo < hi) {
+        const uint32_t step = (hi - lo + kWave - 1) / kWave;
+        const uint32_t c = min(hi, lo + static_cast<uint32_t>(lane) * step);
+        const unsigned long long ok = __builtin_amdgcn_ballot_w64(reaches(c));
+        if (!ok) {
+            lo = __shfl(c, kWave - 1, kWave) + 1;
+        } else {
+            const int f = __builtin_ctzll(ok);
+            hi = __shfl(c, f, kWave);
+            if (f > 0) lo = __shfl(c, f - 1, kWave) + 1;
+            else lo = hi;
+        }
+    }
+    return lo;
+}
+
+constexpr int kGatherBatch = 8;                    // float4 loads per lane in flight in the gathering pass
+constexpr int kWaveCap = kBucketCap / kWaves;      // tokens of the bin one wave's slice may hold
+
+// The gathering pass's test of one element per lane (every lane of the wave
+// together): whether x lies in the bin (appended to the wave's region, at
+// most kWaveCap) and whether it lies above it (counted). kByKey compares
+// order keys (needed when a threshold is +0, which a float compare does not
+// tell from -0), else floats; kAll: every lane holds an element.
+template <bool kByKey, bool kAll>
+struct BinTest {
+    uint32_t k_lo, k_hi;
+    float f_lo, f_hi;
+    uint2* s_reg;
+    __device__ __forceinline__ void operator()(float xj, int j, bool in, uint32_t& n_w, uint32_t& above_w) const {
+        bool mem, abv;
+        if constexpr (kByKey) {
+            const uint32_t kx = order_key(xj);
+            mem = kx >= k_lo && kx < k_hi;
+            abv = kx >= k_hi;
+        } else {
+            mem = xj >= f_lo && xj < f_hi;
+            abv = xj >= f_hi;
+        }
+        if constexpr (!kAll) {
+            mem = mem && in;
+            abv = abv && in;
+        }
+        above_w += static_cast<uint32_t>(__builtin_popcountll(__builtin_amdgcn_ballot_w64(abv)));
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(mem);
+        if (m) {
+            const uint32_t slot =
+                n_w + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+            if (mem && slot < static_cast<uint32_t>(kWaveCap)) s_reg[slot] = make_uint2(__float_as_uint(xj), static_cast<uint32_t>(j));
+            n_w += static_cast<uint32_t>(__builtin_popcountll(m));
+        }
+    }
+};
+
+// One wave's float4 units [ubeg, uend) of the row (x4 = the row from its
+// first 16-byte boundary, element h0): kGatherBatch loads per lane at a time.
+template <bool kByKey>
+__device__ __forceinline__ void gather_units(const float4* x4, int h0, int ubeg, int uend, int lane,
+                                             const BinTest<kByKey, true>& full, const BinTest<kByKey, false>& part,
+                                             uint32_t& n_w, uint32_t& above_w) {
+    int u0 = ubeg;
+    for (; u0 + kGatherBatch * kWave <= uend; u0 += kGatherBatch * kWave) {
+        float4 v[kGatherBatch];
+#pragma unroll
+        for (int i = 0; i < kGatherBatch; ++i) v[i] = x4[u0 + i * kWave + lane];
+#pragma unroll
+        for (int i = 0; i < kGatherBatch; ++i) {
+            const int j = h0 + 4 * (u0 + i * kWave + lane);
+            full(v[i].x, j, true, n_w, above_w);
+            full(v[i].y, j + 1, true, n_w, above_w);
+            full(v[i].z, j + 2, true, n_w, above_w);
+            full(v[i].w, j + 3, true, n_w, above_w);
+        }
+    }
+    for (; u0 < uend; u0 += kWave) {
+        const int uu = u0 + lane;
+        const bool in = uu < uend;
+        const float4 v = x4[in ? uu : uend - 1];
+        const int j = h0 + 4 * uu;
+        part(v.x, j, in, n_w, above_w);
+        part(v.y, j + 1, in, n_w, above_w);
+        part(v.z, j + 2, in, n_w, above_w);
+        part(v.w, j + 3, in, n_w, above_w);
+    }
+}
+
 // Rows with top-k off, from the chunks' maxima and histograms. Returns
 // false, the same in every thread, when the top-p boundary's bin holds more
 // than kBucketCap tokens; the caller then takes the whole-row path.
-__device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int row, float T, uint64_t* pool) {
+__device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int row, int g, float T, uint64_t* pool) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -1054,6 +1194,14 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
     __shared__ int s_ri[2];
     __shared__ double s_rd[2];
     __shared__ uint32_t s_n;
+    __shared__ uint32_t s_thr[2];
+    __shared__ uint32_t s_wn[kWaves];
+    __shared__ uint64_t s_small[kWave];
+    __shared__ double s_kcw[kWaves][kSampleHistChunks];   // per wave: kept mass of gathered tokens per chunk
+    __shared__ uint32_t s_base;
+
+    const float tp = a.top_p[row];
+    if (g != 0 && !(tp < 1.0f)) return true;   // only the gathering pass is shared out
 
     // ---- max z from the chunks' maxima ----------------------------------------------
     if (tid < S) s_scale[tid] = static_cast<double>(chunk_head(a, row, tid)->mc);
@@ -1068,39 +1216,52 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
     if (tid == 0) s_n = 0u;
     __syncthreads();
 
-    const float tp = a.top_p[row];
     uint32_t pkey = 0;   // kept: key > pkey, or key == pkey and index <= pidx
     int pidx = V;
     uint32_t kept_p = static_cast<uint32_t>(V);
     if (tp < 1.0f) {
-        // ---- the row's histogram: bins tid and tid + kThreads ----------------------
-        double m0 = 0.0, m1 = 0.0;
-#pragma unroll 4
-        for (int c = 0; c < S; ++c) {
-            const double* h = chunk_hist(a, row, c);
-            m0 += s_scale[c] * h[tid];
-            m1 += s_scale[c] * h[tid + kThreads];
-        }
-        s_bin[tid] = m0;
-        s_bin[tid + kThreads] = m1;
-        double tot = wave_sum_f64(m0 + m1);
-        if (lane == 0) s_wd[wave] = tot;
-        __syncthreads();
-        tot = 0.0;
-        for (int w = 0; w < kWaves; ++w) tot += s_wd[w];
-        const double need = static_cast<double>(tp) * tot;
+        // ---- the bin holding the boundary: the largest b with I[b] >= need, where
+        // I[b] = sum over chunks of scale x suffix mass (two levels: the 64
+        // group starts 32k, then the 33 bins from the group's start) --------
         if (wave == 0) {
-            double ab = 0.0;
-            int b = find_bin_from_top<kSampleHistBins>(s_bin, need, &ab, lane);
+            const double t = lane < S ? s_scale[lane] * chunk_head(a, row, lane)->total : 0.0;
+            const double tot = wave_sum_f64(t);
+            if (lane == 0) s_rd[0] = tot;
+        }
+        __syncthreads();
+        const double need = static_cast<double>(tp) * s_rd[0];
+        // I at bin b by the 16 lanes of a group (chunks cs, cs + 16, ...), the
+        // same order wherever it is evaluated
+        auto suffix_at = [&](int b) -> double {
+            double v = 0.0;
+            if (b < kSampleHistBins)
+                for (int c = tid & 15; c < S; c += 16) v += s_scale[c] * chunk_hist(a, row, c)[b];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
+            return v;
+        };
+        {
+            const double v = suffix_at(32 * (tid >> 4));
+            if ((tid & 15) == 0) s_bin[tid >> 4] = v;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const unsigned long long ok = __builtin_amdgcn_ballot_w64(s_bin[lane] >= need);
+            if (lane == 0) s_ri[0] = ok ? 63 - __builtin_clzll(ok) : 0;
+        }
+        __syncthreads();
+        const int kA = s_ri[0];
+        if (tid < 33 * 16) {
+            const double v = suffix_at(32 * kA + (tid >> 4));
+            if ((tid & 15) == 0) s_bin[64 + (tid >> 4)] = v;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const unsigned long long ok = __builtin_amdgcn_ballot_w64(lane < 32 && s_bin[64 + lane] >= need);
+            const int i = ok ? 63 - __builtin_clzll(ok) : 0;
             if (lane == 0) {
-                if (b < 0) {   // rounding: the lowest bin with mass holds the boundary
-                    b = 0;
-                    while (b < kSampleHistBins - 1 && !(s_bin[b] > 0.0)) ++b;
-                    ab = 0.0;
-                    for (int i = kSampleHistBins - 1; i > b; --i) ab += s_bin[i];
-                }
-                s_ri[0] = b;
-                s_rd[0] = ab;
+                s_ri[0] = 32 * kA + i;
+                s_rd[0] = s_bin[64 + i + 1];   // I[b1 + 1]: the mass above the bin
             }
         }
         __syncthreads();
@@ -1108,51 +1269,214 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
         double above = s_rd[0];
 
         // ---- gather the boundary bin's tokens; count the tokens above it ----------
-        uint32_t n_above = 0;
-        each_z(r, [&](int j, float zj) {
-            const uint32_t key = order_key(zj);
-            const uint32_t b = key >> 21;
-            n_above += b > b1;
-            if (b == b1) {
-                const uint32_t slot = atomicAdd(&s_n, 1u);
-                if (slot < kBucketCap) s_bk[slot] = composite(key, static_cast<uint32_t>(j));
-            }
-        });
-        n_above = wave_sum_u32(n_above);
-        if (lane == 0) s_wu[wave] = n_above;
+        // The bin test is a test of x itself against two thresholds: as
+        // floats, or as order keys when one of them is +0 (which a float
+        // compare does not tell from -0). Each wave appends to its own region
+        // of the list (no atomics); the regions are compacted afterwards.
+        if (wave < 2) {
+            const uint32_t hb = b1 + static_cast<uint32_t>(wave);
+            const uint32_t k = hb >= static_cast<uint32_t>(kSampleHistBins) ? 0xFFFFFFFFu
+                                                                             : wave_key_threshold(hb << 21, T, lane);
+            if (lane == 0) s_thr[wave] = k;
+        }
+        if (tid == 0) s_n = 0u;   // set when a wave's share overflows its region
         __syncthreads();
-        const uint32_t n1 = s_n;
-        if (n1 > static_cast<uint32_t>(kBucketCap)) return false;
-        n_above = 0;
-        for (int w = 0; w < kWaves; ++w) n_above += s_wu[w];
-
-        // ---- the boundary key: two more digits over the gathered tokens ------------
-        uint32_t prefix = b1 << 21, pmask = 0xFFE00000u;
-        bucket_digit<2048>(s_bk, n1, 10, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
-        bucket_digit<1024>(s_bk, n1, 0, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
-        pkey = prefix;
-        const uint32_t ties = s_cnt[pkey & 1023u];
-        __syncthreads();   // the tie count is read before the counts are reused
-        // every tie has the same mass; keep the first `keep` of them in index order
-        const double pb = exp(static_cast<double>(key_value(pkey)) - zmax);
-        const double t = (need - above) / pb;
-        const uint32_t keep = t <= 1.0 ? 1u : static_cast<uint32_t>(fmin(ceil(t), static_cast<double>(ties)));
-        if (keep < ties) {
-            uint32_t ip = 0, imask = 0, rem = keep;
-            tie_digit<1024>(s_bk, n1, pkey, 9, s_cnt, s_ri, ip, imask, rem);
-            tie_digit<512>(s_bk, n1, pkey, 0, s_cnt, s_ri, ip, imask, rem);
-            pidx = static_cast<int>(ip);
+        const uint32_t k_lo = s_thr[0], k_hi = s_thr[1];
+        const float f_lo = key_value(k_lo);                              // NaN when nothing reaches the bin
+        const float f_hi = k_hi == 0xFFFFFFFFu ? INFINITY : key_value(k_hi);
+        const bool by_key = k_lo == 0x80000000u || k_hi == 0x80000000u;
+        uint32_t n_w = 0;       // tokens of the bin in this wave's slice
+        uint32_t above_w = 0;   // tokens above the bin in this wave's slice
+        uint2* s_reg = reinterpret_cast<uint2*>(s_bk) + wave * kWaveCap;
+        // elements before the first 16-byte boundary and after the last: wave 0
+        const float* x = r.x;
+        const int h0 = min(V, static_cast<int>((4u - ((reinterpret_cast<uintptr_t>(x) >> 2) & 3u)) & 3u));
+        const int n4 = (V - h0) / 4;
+        const int t0 = h0 + 4 * n4;
+        const float4* x4 = reinterpret_cast<const float4*>(x + h0);
+        // this workgroup's share of the units, then this wave's
+        const int gbeg = static_cast<int>(static_cast<long long>(g) * n4 / kSampleRowSplit);
+        const int gend = static_cast<int>(static_cast<long long>(g + 1) * n4 / kSampleRowSplit);
+        const int ubeg = gbeg + static_cast<int>(static_cast<long long>(wave) * (gend - gbeg) / kWaves);
+        const int uend = gbeg + static_cast<int>(static_cast<long long>(wave + 1) * (gend - gbeg) / kWaves);
+        if (by_key) {
+            const BinTest<true, true> full{k_lo, k_hi, f_lo, f_hi, s_reg};
+            const BinTest<true, false> part{k_lo, k_hi, f_lo, f_hi, s_reg};
+            if (wave == 0 && g == 0) {
+                const bool in = lane < h0 + (V - t0);
+                const int j = lane < h0 ? lane : t0 + (lane - h0);
+                part(x[in ? j : 0], j, in, n_w, above_w);
+            }
+            gather_units<true>(x4, h0, ubeg, uend, lane, full, part, n_w, above_w);
+        } else {
+            const BinTest<false, true> full{k_lo, k_hi, f_lo, f_hi, s_reg};
+            const BinTest<false, false> part{k_lo, k_hi, f_lo, f_hi, s_reg};
+            if (wave == 0 && g == 0) {
+                const bool in = lane < h0 + (V - t0);
+                const int j = lane < h0 ? lane : t0 + (lane - h0);
+                part(x[in ? j : 0], j, in, n_w, above_w);
+            }
+            gather_units<false>(x4, h0, ubeg, uend, lane, full, part, n_w, above_w);
+        }
+        if (lane == 0) {
+            s_wn[wave] = n_w;
+            s_wu[wave] = above_w;
+            if (n_w > static_cast<uint32_t>(kWaveCap)) s_n = 1u;
+        }
+        __syncthreads();
+        constexpr uint32_t kShare = kBucketCap / kSampleRowSplit;   // list entries per workgroup
+        uint32_t n_g = 0, pre = 0, above_g = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            if (w == wave) pre = n_g;
+            n_g += s_wn[w];
+            above_g += s_wu[w];
+        }
+        const bool wg_over = s_n != 0u || n_g > kShare;
+        if (!wg_over) {   // compact the waves' regions, logit keys becoming keys of z = x / T
+            uint2 mine[kWaveCap / kWave];
+#pragma unroll
+            for (int i = 0; i < kWaveCap / kWave; ++i) {
+                const uint32_t e = static_cast<uint32_t>(i * kWave + lane);
+                mine[i] = e < n_w ? s_reg[e] : make_uint2(0u, 0u);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kWaveCap / kWave; ++i) {
+                const uint32_t e = static_cast<uint32_t>(i * kWave + lane);
+                if (e < n_w) s_bk[pre + e] = composite(order_key(__uint_as_float(mine[i].x) / T), mine[i].y);
+            }
+            __syncthreads();
         }
 
-        // ---- kept mass per chunk: the gathered tokens kept, plus the bins above ----
+        // ---- the row's workgroups pool their shares; the last one to finish goes on
+        uint32_t* rc = row_counters(a, row);
+        uint64_t* rl = row_list(a, row);
+        if (!wg_over)
+            for (uint32_t e = tid; e < n_g; e += kThreads) rl[g * kShare + e] = s_bk[e];
+        if (tid == 0) {
+            rc[2 + 2 * g] = wg_over ? 0xFFFFFFFFu : n_g;
+            rc[3 + 2 * g] = above_g;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            // release: the workgroup's entries (complete in L2 after the
+            // barrier) are written back before it reports; the last to
+            // report acquires them (one fence each way, not one per wave)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const uint32_t t = atomicAdd(&rc[0], 1u);
+            const bool last = t == static_cast<uint32_t>(kSampleRowSplit - 1);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_n = last ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!s_n) return true;
+        // every other workgroup of the row has published its share: append
+        // theirs after this one's own (already in LDS)
+        uint32_t cnt[kSampleRowSplit], start[kSampleRowSplit];
+        uint32_t n1 = n_g, n_above = 0;
+        bool over = wg_over;
+#pragma unroll
+        for (int h = 0; h < kSampleRowSplit; ++h) {
+            cnt[h] = h == g ? n_g : rc[2 + 2 * h];
+            over = over || cnt[h] == 0xFFFFFFFFu;
+            n_above += h == g ? above_g : rc[3 + 2 * h];
+        }
+        if (over) return false;
+#pragma unroll
+        for (int h = 0; h < kSampleRowSplit; ++h) {   // the other shares, in order, after this one's
+            start[h] = n1;
+            if (h != g) n1 += cnt[h];
+        }
+        for (uint32_t e = n_g + tid; e < n1; e += kThreads) {
+            int hh = 0;
+#pragma unroll
+            for (int h = 0; h < kSampleRowSplit; ++h)
+                if (h != g && e >= start[h]) hh = h;   // the last share starting at or below e
+            s_bk[e] = rl[hh * kShare + (e - start[hh])];
+        }
+        __syncthreads();
+
+        // ---- the boundary key: more digits over the gathered tokens ----------------
+        uint32_t prefix = b1 << 21, pmask = 0xFFE00000u;
+        bucket_digit<2048>(s_bk, n1, 10, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
+        const uint32_t m2 = s_cnt[(prefix >> 10) & 2047u];   // tokens sharing the 21-bit prefix
+        if (tid == 0) s_n = 0u;
+        __syncthreads();
+        if (m2 <= static_cast<uint32_t>(kWave)) {
+            // Few: one wave orders them (distinct composites: ranks by
+            // comparison) and scans their masses in that order.
+            for (uint32_t e = tid; e < n1; e += kThreads) {
+                const uint64_t c = s_bk[e];
+                if ((comp_key(c) & pmask) == prefix) s_small[atomicAdd(&s_n, 1u)] = c;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const uint64_t me = lane < static_cast<int>(m2) ? s_small[lane] : 0ull;
+                int rk = 0;
+                for (int i = 0; i < static_cast<int>(m2); ++i) rk += __shfl(me, i, kWave) > me ? 1 : 0;
+                // element of rank `lane`, best first
+                const uint32_t lo32 = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(4 * rk, static_cast<int>(me)));
+                const uint32_t hi32 = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(4 * rk, static_cast<int>(me >> 32)));
+                const uint64_t srt = (static_cast<uint64_t>(hi32) << 32) | lo32;
+                const bool real = lane < static_cast<int>(m2);
+                const double m = real ? exp(static_cast<double>(key_value(comp_key(srt))) - zmax) : 0.0;
+                const double incl = wave_incl_scan(m, lane);
+                const unsigned long long reach = __builtin_amdgcn_ballot_w64(real && above + incl >= need);
+                const int t = reach ? __builtin_ctzll(reach) : static_cast<int>(m2) - 1;   // rounding: the last
+                const uint64_t bnd = __shfl(srt, t, kWave);
+                if (lane == 0) {
+                    s_ri[0] = static_cast<int>(comp_key(bnd));
+                    s_ri[1] = comp_index(bnd);
+                }
+            }
+            __syncthreads();
+            pkey = static_cast<uint32_t>(s_ri[0]);
+            pidx = s_ri[1];
+        } else {
+            bucket_digit<1024>(s_bk, n1, 0, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
+            pkey = prefix;
+            const uint32_t ties = s_cnt[pkey & 1023u];
+            __syncthreads();   // the tie count is read before the counts are reused
+            // every tie has the same mass; keep the first `keep` of them in index order
+            const double pb = exp(static_cast<double>(key_value(pkey)) - zmax);
+            const double t = (need - above) / pb;
+            const uint32_t keep = t <= 1.0 ? 1u : static_cast<uint32_t>(fmin(ceil(t), static_cast<double>(ties)));
+            if (keep < ties) {
+                uint32_t ip = 0, imask = 0, rem = keep;
+                tie_digit<1024>(s_bk, n1, pkey, 9, s_cnt, s_ri, ip, imask, rem);
+                tie_digit<512>(s_bk, n1, pkey, 0, s_cnt, s_ri, ip, imask, rem);
+                pidx = static_cast<int>(ip);
+            }
+        }
+
+        // ---- kept mass per chunk: the bins above b1, plus the gathered tokens kept --
+        // Gathered tokens: each mass once; consecutive list entries mostly
+        // share a chunk, so a wave adds the entries of one chunk at a time
+        // into its own row of s_kcw.
+        for (int i = tid; i < kWaves * kSampleHistChunks; i += kThreads) (&s_kcw[0][0])[i] = 0.0;
+        __syncthreads();
         uint32_t nk = 0;
-        for (uint32_t e = tid; e < n1; e += kThreads) {
-            const uint64_t c = s_bk[e];
-            const uint32_t key = comp_key(c);
-            const int j = comp_index(c);
-            if (key > pkey || (key == pkey && j <= pidx)) {
-                ++nk;
-                atomicAdd(&s_kc[j / C], exp(static_cast<double>(key_value(key)) - zmax));
+        for (uint32_t e0 = static_cast<uint32_t>(wave) * kWave; e0 < n1; e0 += kThreads) {   // wave-uniform
+            const uint32_t e = e0 + lane;
+            int ch = -1;
+            double m = 0.0;
+            if (e < n1) {
+                const uint64_t cc = s_bk[e];
+                const uint32_t key = comp_key(cc);
+                const int j = comp_index(cc);
+                if (key > pkey || (key == pkey && j <= pidx)) {
+                    ch = j / C;
+                    m = exp(static_cast<double>(key_value(key)) - zmax);
+                    ++nk;
+                }
+            }
+            unsigned long long todo = __builtin_amdgcn_ballot_w64(ch >= 0);
+            while (todo) {
+                const int c0 = __shfl(ch, __builtin_ctzll(todo), kWave);
+                const bool mine = ch == c0;
+                const double sum = wave_sum_f64(mine ? m : 0.0);
+                if (lane == 0) s_kcw[wave][c0] += sum;
+                todo &= ~__builtin_amdgcn_ballot_w64(mine);
             }
         }
         nk = wave_sum_u32(nk);
@@ -1160,13 +1484,11 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
         __syncthreads();
         kept_p = n_above;
         for (int w = 0; w < kWaves; ++w) kept_p += s_wu[w];
-        for (int c = wave; c < S; c += kWaves) {
-            const double* h = chunk_hist(a, row, c);
-            double acc = 0.0;
-#pragma unroll 4
-            for (int b = static_cast<int>(b1) + 1 + lane; b < kSampleHistBins; b += kWave) acc += h[b];
-            acc = wave_sum_f64(acc);
-            if (lane == 0) s_kc[c] += s_scale[c] * acc;
+        if (tid < S) {
+            const double acc = b1 + 1 < static_cast<uint32_t>(kSampleHistBins) ? chunk_hist(a, row, tid)[b1 + 1] : 0.0;
+            double bsum = 0.0;
+            for (int w = 0; w < kWaves; ++w) bsum += s_kcw[w][tid];
+            s_kc[tid] = s_scale[tid] * acc + bsum;
         }
         __syncthreads();
     } else {
@@ -1251,25 +1573,32 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
 }
 
 // ---- the finishing kernel: one workgroup per row, on the row's path ---------------
+// blockIdx.x = row * kSampleRowSplit + g: histogram rows share the gathering
+// pass among their g workgroups; every other row is finished by g = 0 alone.
 __global__ __launch_bounds__(kThreads) void sample_row_kernel(SampleArgs a) {
     __shared__ uint64_t s_pool[kPoolWords];
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / kSampleRowSplit;
+    const int g = blockIdx.x - row * kSampleRowSplit;
     const float T = a.temperature[row];
     if (!(T >= 0.0f)) {   // negative or NaN temperature: no token
-        if (threadIdx.x == 0) write_result(a, row, -1, 0, 0);
+        if (g == 0 && threadIdx.x == 0) write_result(a, row, -1, 0, 0);
         return;
     }
     const int k_eff = T > 0.0f ? kept_by_k(a.top_k[row], a.vocab) : 1;
+    if (on_hist_path(T, k_eff, a.vocab, a.chunks) && !on_candidate_path(T, k_eff, a.chunks)) {
+        if (!finish_from_histograms(a, row, g, T, s_pool)) sample_whole_row(a, row, T, k_eff);
+        return;
+    }
+    if (g != 0) return;
     if (on_candidate_path(T, k_eff, a.chunks)) finish_from_candidates(a, row, T, k_eff, s_pool);
-    else if (!on_hist_path(T, k_eff, a.vocab, a.chunks) || !finish_from_histograms(a, row, T, s_pool))
-        sample_whole_row(a, row, T, k_eff);
+    else sample_whole_row(a, row, T, k_eff);
 }
 
 }  // namespace
 
 hipError_t launch_sample(const SampleArgs& a, int rows, hipStream_t stream) {
     hipLaunchKernelGGL(sample_chunk_kernel, dim3(rows * a.chunks), dim3(kChunkThreads), 0, stream, a);
-    hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(sample_row_kernel, dim3(rows * kSampleRowSplit), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

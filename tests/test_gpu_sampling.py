@@ -155,7 +155,7 @@ def test_workspace_is_checked():
     p = torch.ones(2, device="cuda")
     u = torch.full((2,), 0.5, device="cuda")
     need = pkv.sample_workspace_size(2, 20000)
-    assert need == 2 * 3 * (16384 + 16)
+    assert need == 2 * (3 * (16384 + 16) + 12288 * 8 + 64)
     small = torch.empty(need - 8, dtype=torch.uint8, device="cuda")
     with pytest.raises(pkv.PagedKVError):
         pkv.sample_tokens(x, T, k, p, u, workspace=small)

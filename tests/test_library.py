@@ -191,12 +191,14 @@ def _call_sample(**over):
 
 
 def test_sampling_workspace_and_argument_errors():
-    # rows x ceil(vocab / 8192) chunks x (2048 fp64 histogram bins + a 16-byte
-    # header) up to 64 chunks; wider rows: 256 candidate slots x 8 bytes
-    assert pkv.sample_workspace_size(4, 20000) == 4 * 3 * (16384 + 16)
-    assert pkv.sample_workspace_size(64, 128256) == 64 * 16 * (16384 + 16)
-    assert pkv.sample_workspace_size(1, 8192) == 16384 + 16
-    assert pkv.sample_workspace_size(1, 64 * 8192) == 64 * (16384 + 16)
+    # up to 64 chunks of 8192 per row: per chunk 2048 fp64 histogram bins and a
+    # 16-byte header, per row 12288 8-byte gathered tokens and 64 bytes of
+    # counters; wider rows: 256 candidate slots x 8 bytes per chunk
+    row = 12288 * 8 + 64
+    assert pkv.sample_workspace_size(4, 20000) == 4 * (3 * (16384 + 16) + row)
+    assert pkv.sample_workspace_size(64, 128256) == 64 * (16 * (16384 + 16) + row)
+    assert pkv.sample_workspace_size(1, 8192) == 16384 + 16 + row
+    assert pkv.sample_workspace_size(1, 64 * 8192) == 64 * (16384 + 16) + row
     assert pkv.sample_workspace_size(2, 64 * 8192 + 1) == 2 * 65 * 2048
     with pytest.raises(pkv.PagedKVError):
         pkv.sample_workspace_size(1, 0)
@@ -208,6 +210,6 @@ def test_sampling_workspace_and_argument_errors():
     assert _call_sample(vocab=8192 * 8192 + 1, ld=8192 * 8192 + 1) == -2
     assert _call_sample(u=0) == -1
     assert _call_sample(ws=0) == -1
-    assert _call_sample(ws_bytes=4 * 3 * (16384 + 16) - 1) == -6
+    assert _call_sample(ws_bytes=4 * (3 * (16384 + 16) + row) - 1) == -6
     assert _call_sample(ws=260) == -2                 # workspace not 8-byte aligned
     assert _call_sample(rows=0) == 0
