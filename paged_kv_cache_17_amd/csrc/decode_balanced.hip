@@ -59,6 +59,7 @@ struct ValuRows {
     static constexpr int kQ = G;
     static constexpr int kSlotRows = G;              // partial rows per slot
     static constexpr int kWaves = G == 8 ? 1 : 2;   // waves per SIMD the registers allow
+    static constexpr int kRingBytes = 0;            // LDS a wave stages tiles in (none)
     // One query per sequence: the G heads of kv head g. Returns the rows used.
     __device__ __forceinline__ static int load_q(State&, u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g,
                                                  int lane) {
@@ -94,6 +95,7 @@ struct MfmaRows {
     static constexpr int kQ = 4 * NB;
     static constexpr int kSlotRows = NB == 1 ? G : 16 * NB;
     static constexpr int kWaves = 2;
+    static constexpr int kRingBytes = 0;
     __device__ __forceinline__ static int load_q(State& st, u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g,
                                                  int lane) {
         const int n = lane & 15;
@@ -133,14 +135,14 @@ struct Bf16Kv : ValuRows<G> {
     };
     const uint16_t* kc;
     const uint16_t* vc;
-    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane)
+    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane, unsigned char* /*ring*/)
         : kc(static_cast<const uint16_t*>(a.k_cache) + lane * 8), vc(static_cast<const uint16_t*>(a.v_cache) + lane * 8) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
         const size_t off = static_cast<size_t>(tile) * kTileElems;
         load_tile(kc + off, vc + off, t.k, t.v);
     }
     __device__ __forceinline__ void compute(DecodeState<G>& st, const Regs& t, const u32x4 (&qv)[G],
-                                            int lane, int ntok, float sl2) const {
+                                            int lane, int ntok, float sl2, int /*newer*/) const {
         st.tile(t.k, t.v, qv, lane >> 4, ntok, sl2);
     }
 };
@@ -150,8 +152,9 @@ struct Bf16Kv : ValuRows<G> {
 template <int G>
 struct Int8Kv : ValuRows<G> {
     // a tile is half the bytes of a bf16 one: keep two in flight (one with
-    // two query heads per kv head, whose registers would otherwise spill)
-    static constexpr int kDepth = G == 2 ? 2 : 3;
+    // one or two query heads per kv head, whose registers would otherwise
+    // spill)
+    static constexpr int kDepth = G <= 2 ? 2 : 3;
     struct Regs {
         u32x2 k[4], v[4];
         float sk[4], sv[4];   // tokens 4i + r
@@ -160,7 +163,7 @@ struct Int8Kv : ValuRows<G> {
     const int8_t* vc;
     const float* ks;
     const float* vs;
-    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane)
+    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane, unsigned char* /*ring*/)
         : kc(static_cast<const int8_t*>(a.k_cache) + lane * 8), vc(static_cast<const int8_t*>(a.v_cache) + lane * 8),
           ks(a.k_scale), vs(a.v_scale) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int lane) const {
@@ -180,7 +183,7 @@ struct Int8Kv : ValuRows<G> {
         }
     }
     __device__ __forceinline__ void compute(DecodeState<G>& st, const Regs& t, const u32x4 (&qv)[G],
-                                            int lane, int ntok, float sl2) const {
+                                            int lane, int ntok, float sl2, int /*newer*/) const {
         st.tile_q8(t.k, t.v, t.sk, t.sv, qv, lane >> 4, ntok, sl2);
     }
 };
@@ -199,7 +202,7 @@ struct Bf16Mfma : MfmaRows<G, NB> {
     };
     const uint16_t* kc;
     const uint16_t* vc;
-    __device__ __forceinline__ Bf16Mfma(const AttnArgs& a, int lane)
+    __device__ __forceinline__ Bf16Mfma(const AttnArgs& a, int lane, unsigned char* /*ring*/)
         : kc(static_cast<const uint16_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
           vc(static_cast<const uint16_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
@@ -212,7 +215,7 @@ struct Bf16Mfma : MfmaRows<G, NB> {
         for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
-                                            float sl2) const {
+                                            float sl2, int /*newer*/) const {
         f32x4 s[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -245,7 +248,7 @@ struct Int8Mfma : MfmaRows<G, NB> {
     const int8_t* vc;
     const float* ks;
     const float* vs;
-    __device__ __forceinline__ Int8Mfma(const AttnArgs& a, int lane)
+    __device__ __forceinline__ Int8Mfma(const AttnArgs& a, int lane, unsigned char* /*ring*/)
         : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
           vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
           ks(a.k_scale + 4 * (lane >> 4)),
@@ -263,7 +266,7 @@ struct Int8Mfma : MfmaRows<G, NB> {
         t.sv = *reinterpret_cast<const float4*>(vs + so);
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
-                                            float sl2) const {
+                                            float sl2, int /*newer*/) const {
         f32x4 s[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -287,9 +290,93 @@ template <>
 struct Bf16Kv<4> : Bf16Mfma<4, 1> {
     using Bf16Mfma<4, 1>::Bf16Mfma;
 };
+// 8-bit K/V with four query heads per kv head, staged through LDS. A tile
+// is half the bytes of a bf16 one, so one tile in flight per wave (all the
+// registers allow) keeps too few bytes in flight: each wave instead streams
+// its tiles into a ring of kDepth LDS slots with direct global-to-LDS loads,
+// which hold no registers, kDepth - 1 tiles ahead of the one it computes.
+// Slot image: K codes, V codes (16 tokens x 128 dims each; the 16-byte chunk
+// d of token t at chunk t * 8 + (d ^ (t & 7)), so that the reads below hit
+// distinct banks), then the 16 K and the 16 V scales.
+struct Int8Ring : MfmaRows<4, 1> {
+    static constexpr int kDepth = 4;
+    static constexpr int kSlot = 2 * kTileElems + 2 * kTileB * 4;
+    static constexpr int kRingBytes = kDepth * kSlot;
+    static constexpr int kLoads = 5;   // vector memory operations issued per tile
+    struct Regs {
+        int slot;
+    };
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* sc;   // K scales for lanes 0..15, V scales for lanes 16..31
+    unsigned char* ring;
+    int koff, voff;    // this lane's K and V read offsets in a slot
+    __device__ __forceinline__ Int8Ring(const AttnArgs& a, int lane, unsigned char* r)
+        : kc(static_cast<const int8_t*>(a.k_cache) + chunk_src(lane)),
+          vc(static_cast<const int8_t*>(a.v_cache) + chunk_src(lane)),
+          sc(lane < 16 ? a.k_scale + lane : a.v_scale + (lane - 16)),
+          ring(r) {
+        const int n = lane & 15, q = lane >> 4;
+        koff = (n * 8 + ((q >> 1) ^ (n & 7))) * 16 + (q & 1) * 8;
+        voff = (n & 1) * 8;
+    }
+    typedef __attribute__((address_space(3))) void* LdsPtr;
+    __device__ __forceinline__ static LdsPtr lds_ptr(unsigned char* p) { return (LdsPtr)(p); }
+    // Lane l's source chunk for LDS chunk l (and 64 + l, 1024 bytes on).
+    __device__ __forceinline__ static int chunk_src(int l) { return (l >> 3) * 128 + (((l & 7) ^ (l >> 3)) * 16); }
+
+    __device__ __forceinline__ void load(Regs& t, int tile, int lane) const {
+        unsigned char* dst = ring + t.slot * kSlot;
+        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(kc + off + i * 1024, lds_ptr(dst + i * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(vc + off + i * 1024, lds_ptr(dst + kTileElems + i * 1024), 16, 0, 0);
+        if (lane < 32)
+            __builtin_amdgcn_global_load_lds(sc + static_cast<size_t>(tile) * kTileB,
+                                             lds_ptr(dst + 2 * kTileElems), 4, 0, 0);
+    }
+    // The tile's loads are done once at most `newer` tiles' loads (issued
+    // after it) are outstanding.
+    __device__ __forceinline__ static void wait_loads(int newer) {
+        static_assert(kDepth - 1 <= 3 && kLoads == 5, "wait counts below");
+        if (newer <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (newer == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else if (newer == 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    }
+    __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
+                                            float sl2, int newer) const {
+        wait_loads(newer);
+        const unsigned char* src = ring + t.slot * kSlot;
+        const int q = lane >> 4, n = lane & 15;
+        u32x2 kr[4], vr[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)   // token n, dims 32b + 8q .. +7: chunk 2b + q / 2, swizzled
+            kr[b] = *reinterpret_cast<const u32x2*>(src + (koff ^ ((2 * b) << 4)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {   // token 4q + e, dims 8n .. 8n + 7
+            const int tk = 4 * q + e;
+            vr[e] = *reinterpret_cast<const u32x2*>(src + kTileElems + (tk * 8 + ((n >> 1) ^ (tk & 7))) * 16 + voff);
+        }
+        const float4 skv = *reinterpret_cast<const float4*>(src + 2 * kTileElems + 16 * q);
+        const float4 svv = *reinterpret_cast<const float4*>(src + 2 * kTileElems + 64 + 16 * q);
+        f32x4 s[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(kr[b])),
+                                                           __builtin_bit_cast(bf16x8, qv[b]), s[0], 0, 0, 0);
+        // codes are finite whatever the slot holds; weights past the end are 0
+        const float sk[4] = {skv.x, skv.y, skv.z, skv.w};
+        const float sv[4] = {svv.x, svv.y, svv.z, svv.w};
+        st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(vr, j); }, lane, ntok, sl2);
+    }
+};
 template <>
-struct Int8Kv<4> : Int8Mfma<4, 1> {
-    using Int8Mfma<4, 1>::Int8Mfma;
+struct Int8Kv<4> : Int8Ring {
+    using Int8Ring::Int8Ring;
 };
 
 // Small chunks: up to 32 (query, head) rows per kv head in two blocks.
@@ -377,7 +464,8 @@ void decode_balanced_kernel(AttnArgs a) {
         }
     };
 
-    const Kv kv(a, lane);
+    __shared__ __attribute__((aligned(16))) unsigned char s_ring[Kv::kRingBytes > 0 ? Kv::kRingBytes : 16];
+    const Kv kv(a, lane, s_ring);
     const float sl2 = a.scale_log2;
 
     typename Kv::State st;
@@ -400,18 +488,24 @@ void decode_balanced_kernel(AttnArgs a) {
         typename Kv::Regs t;
         int seg, ntok;
     };
+    Buf b[D];
+    if constexpr (Kv::kRingBytes > 0) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) b[u].t.slot = u;
+    }
     describe(t0);
-    auto issue = [&](int j, Buf& b) {
+    auto issue = [&](int j, Buf& bj) {
         const int lj = j & (kWave - 1);
         if (lj == 0 && j > 0) describe(t0 + j);
-        b.seg = __builtin_amdgcn_readlane(i_seg, lj);
-        b.ntok = __builtin_amdgcn_readlane(i_ntok, lj);
-        kv.load(b.t, __builtin_amdgcn_readlane(i_tile, lj), lane);
+        bj.seg = __builtin_amdgcn_readlane(i_seg, lj);
+        bj.ntok = __builtin_amdgcn_readlane(i_ntok, lj);
+        kv.load(bj.t, __builtin_amdgcn_readlane(i_tile, lj), lane);
     };
 
     // One step: issue tile i + D - 1 into fut, then compute tile i (in cur).
     auto step = [&](int i, const Buf& cur, Buf& fut) {
         if (i + D - 1 < n) issue(i + D - 1, fut);
+        const int newer = min(D - 1, n - 1 - i);   // tiles issued after tile i
         const int seg = cur.seg;
         const int ntok = cur.ntok;
         if (seg != cur_seg) {
@@ -426,26 +520,17 @@ void decode_balanced_kernel(AttnArgs a) {
         if (ntok < 0) {
             cur_bad = true;
         } else {
-            kv.compute(st, cur.t, qv, lane, ntok, sl2);
+            kv.compute(st, cur.t, qv, lane, ntok, sl2, newer);
         }
     };
 
-    Buf b0, b1;
-    issue(0, b0);
-    if constexpr (D == 2) {
-        for (int i = 0; i < n; i += 2) {
-            step(i, b0, b1);
-            if (i + 1 < n) step(i + 1, b1, b0);
-        }
-    } else {
-        static_assert(D == 3, "pipeline depth 2 or 3");
-        Buf b2;
-        if (n > 1) issue(1, b1);
-        for (int i = 0; i < n; i += 3) {
-            step(i, b0, b2);
-            if (i + 1 < n) step(i + 1, b1, b0);
-            if (i + 2 < n) step(i + 2, b2, b1);
-        }
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j)
+        if (j < n) issue(j, b[j]);
+    for (int i = 0; i < n; i += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u)
+            if (i + u < n) step(i + u, b[u], b[(u + D - 1) % D]);
     }
     flush();
 }
