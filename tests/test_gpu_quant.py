@@ -101,6 +101,26 @@ def test_q8_invalid_rows_become_nan():
     check_rows(got[[0, 4]], ref[[0, 4]], BF16, "valid q8 rows next to invalid ones")
 
 
+def test_q8_many_short_sequences():
+    """700 sequences of 1..300 keys at four query heads per kv head (the pass
+    that stages tiles through LDS): segments change every few tiles, so each
+    wave reloads queries and writes partials between tiles whose copies are
+    still in flight. Every row within tolerance; a repeat is bit-identical."""
+    L = np.random.default_rng(23).integers(1, 301, size=700)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=23)
+    say("q8, 700 short sequences")
+    c = build_gpu_cache(wl, quantized=True)
+    ora = oracle.build_quant_cache(wl)
+    got, got_lse = _decode(c, wl)
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(got, ref, BF16, "q8 700 short")
+    check_lse(got_lse, ref_lse, BF16, "q8 700 short lse")
+    say(f"  worst row rel err {err:.2e}")
+    got2, _ = _decode(c, wl)
+    assert np.array_equal(got, got2), "repeat run not bit-identical"
+
+
 def test_q8_full_size_decode_batch_sampled():
     """The 64-sequence decode batch (lengths 512..4096) through the 8-bit
     path: whole pools bit-exact, sampled sequences' rows within tolerance."""
