@@ -9,7 +9,8 @@
 //  * all (sequence s, kv head g, block b) tiles of the batch are numbered in
 //    one sequence: s-major, then g, then b (a "segment" is the run of tiles
 //    of one (s, g));
-//  * the grid is W single-wave workgroups, W = what the chip holds at once;
+//  * the grid is W single-wave workgroups, W = the CUs times the waves per
+//    CU the tile math's policy asks for (at most what fits at once);
 //    with W' = min(W, T), wave w < W' streams tiles
 //    [floor(w T / W'), floor((w+1) T / W')) of the T tiles - every wave
 //    reads the same number of bytes to within one tile and none is empty
@@ -59,15 +60,16 @@ struct ValuRows {
     static constexpr int kQ = G;
     static constexpr int kSlotRows = G;              // partial rows per slot
     static constexpr int kWaves = G == 8 ? 1 : 2;   // waves per SIMD the registers allow
+    static constexpr int kWavesPerCU = 0;           // waves per CU launched (0: all that fit)
     static constexpr int kRingBytes = 0;            // LDS a wave stages tiles in (none)
-    // One query per sequence: the G heads of kv head g. Returns the rows used.
-    __device__ __forceinline__ static int load_q(State&, u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g,
-                                                 int lane) {
+    // One query per sequence: the G heads of kv head g.
+    __device__ __forceinline__ static void fetch_q(u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g, int lane) {
         const uint16_t* q_sg = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(s) * a.n_q + g * G) * kTileD;
 #pragma unroll
         for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(q_sg + h * kTileD + (lane & 15) * 8);
-        return G;
     }
+    // The segment's row bookkeeping; returns the rows used.
+    __device__ __forceinline__ static int begin(State&, const AttnArgs&, int /*s*/, int /*lane*/) { return G; }
     __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, int /*used*/, bool bad,
                                                  int lane) {
         const int c = lane & 15;
@@ -95,30 +97,43 @@ struct MfmaRows {
     static constexpr int kQ = 4 * NB;
     static constexpr int kSlotRows = NB == 1 ? G : 16 * NB;
     static constexpr int kWaves = 2;
+    static constexpr int kWavesPerCU = 0;
     static constexpr int kRingBytes = 0;
-    __device__ __forceinline__ static int load_q(State& st, u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g,
-                                                 int lane) {
+    // Segment (s, g)'s first query row and number of queries.
+    __device__ __forceinline__ static int queries(const AttnArgs& a, int s, int& row0) {
+        row0 = s;
+        if (!a.q_start) return 1;
+        row0 = a.q_start[s];
+        return a.q_start[s + 1] - row0;
+    }
+    __device__ __forceinline__ static void fetch_q(u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g, int lane) {
         const int n = lane & 15;
         const int q = lane >> 4;
-        int row0 = s, C = 1;
-        if (a.q_start) {
-            row0 = a.q_start[s];
-            C = a.q_start[s + 1] - row0;
-        }
-        const int used = C * G;
+        int row0;
+        const int used = queries(a, s, row0) * G;
         const uint16_t* qb = static_cast<const uint16_t*>(a.q);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int r = 16 * b + n;
             const int i = r / G;
-            st.ok[b] = r < used;
-            st.back[b] = C - 1 - i;
             const uint16_t* qr = qb + ((static_cast<size_t>(row0) + i) * a.n_q + g * G + (r - i * G)) * kTileD + 8 * q;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                qv[4 * b + c] = st.ok[b] ? *reinterpret_cast<const u32x4*>(qr + 32 * c) : u32x4{0, 0, 0, 0};
+                qv[4 * b + c] = r < used ? *reinterpret_cast<const u32x4*>(qr + 32 * c) : u32x4{0, 0, 0, 0};
         }
-        return used;
+    }
+    // Which rows exist and how many keys at the chunk's end each may not
+    // see; returns the rows used.
+    __device__ __forceinline__ static int begin(State& st, const AttnArgs& a, int s, int lane) {
+        int row0;
+        const int C = queries(a, s, row0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int r = 16 * b + (lane & 15);
+            st.ok[b] = r < C * G;
+            st.back[b] = C - 1 - r / G;
+        }
+        return C * G;
     }
     __device__ __forceinline__ static void flush(State& st, const AttnArgs& a, size_t p, int used, bool bad,
                                                  int lane) {
@@ -192,11 +207,24 @@ struct Int8Kv : ValuRows<G> {
 // (decode_mfma.h). Lane (q, n) loads token n's K at dims 32b + 8q .. +7
 // (b = 0..3) and tokens 4q .. 4q+3's V at dims 8n .. 8n+7: the same bytes per
 // tile as the vector-ALU layout, in the operand layouts of the two products.
+//
+// How many tile loads the chip holds in flight matters more here than
+// hiding each wave's own latency: scattered tile reads get slower overall
+// when waves keep more of them outstanding. Measured per pass (64-sequence
+// batch / 256-sequence batch / 8 x 32k keys; verification chunks):
+//  * decode: six waves per CU, each waiting for all its loads (the next
+//    tile's included) before a tile's products, 101.2 / 327.7 / 161.2 us,
+//    against 101.3 / 336.8 / 164.9 with the next tile's loads left in flight
+//    at four waves per CU and 103.3 / 331.9 / 166.6 at eight;
+//  * chunks: four waves per CU with the next tile in flight, 114.6 us,
+//    against 115.6 waiting at six and 118.1 at eight.
 template <int G, int NB>
 struct Bf16Mfma : MfmaRows<G, NB> {
     using typename MfmaRows<G, NB>::State;
     using MfmaRows<G, NB>::kQ;
     static constexpr int kDepth = 2;
+    static constexpr bool kDrain = NB == 1;
+    static constexpr int kWavesPerCU = kDrain ? 6 : 4;
     struct Regs {
         u32x4 k[4], v[4];
     };
@@ -216,6 +244,7 @@ struct Bf16Mfma : MfmaRows<G, NB> {
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
                                             float sl2, int /*newer*/) const {
+        if constexpr (kDrain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         f32x4 s[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -235,71 +264,23 @@ struct Bf16Mfma : MfmaRows<G, NB> {
     }
 };
 
-template <int G, int NB>
-struct Int8Mfma : MfmaRows<G, NB> {
-    using typename MfmaRows<G, NB>::State;
-    using MfmaRows<G, NB>::kQ;
-    static constexpr int kDepth = 2;
-    struct Regs {
-        u32x2 k[4], v[4];
-        float4 sk, sv;
-    };
-    const int8_t* kc;
-    const int8_t* vc;
-    const float* ks;
-    const float* vs;
-    __device__ __forceinline__ Int8Mfma(const AttnArgs& a, int lane, unsigned char* /*ring*/)
-        : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
-          vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
-          ks(a.k_scale + 4 * (lane >> 4)),
-          vs(a.v_scale + 4 * (lane >> 4)) {}
-    __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
-        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
-        const u32x2* kp = reinterpret_cast<const u32x2*>(kc + off);
-        const u32x2* vp = reinterpret_cast<const u32x2*>(vc + off);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) t.k[b] = __builtin_nontemporal_load(kp + 4 * b);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
-        const size_t so = static_cast<size_t>(tile) * kTileB;
-        t.sk = *reinterpret_cast<const float4*>(ks + so);
-        t.sv = *reinterpret_cast<const float4*>(vs + so);
-    }
-    __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
-                                            float sl2, int /*newer*/) const {
-        f32x4 s[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const bf16x8 kb = __builtin_bit_cast(bf16x8, codes8_to_bf16x8(t.k[b]));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, __builtin_bit_cast(bf16x8, qv[4 * nb + b]), s[nb],
-                                                                0, 0, 0);
-        }
-        // codes are finite whatever the slot holds; weights past the end are 0
-        const float sk[4] = {t.sk.x, t.sk.y, t.sk.z, t.sk.w};
-        const float sv[4] = {t.sv.x, t.sv.y, t.sv.z, t.sv.w};
-        st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(t.v, j); }, lane, ntok, sl2);
-    }
-};
-
 // Decode with four query heads per kv head: one block of rows.
 template <>
 struct Bf16Kv<4> : Bf16Mfma<4, 1> {
     using Bf16Mfma<4, 1>::Bf16Mfma;
 };
-// 8-bit K/V with four query heads per kv head, staged through LDS. A tile
-// is half the bytes of a bf16 one, so one tile in flight per wave (all the
-// registers allow) keeps too few bytes in flight: each wave instead streams
-// its tiles into a ring of kDepth LDS slots with direct global-to-LDS loads,
-// which hold no registers, kDepth - 1 tiles ahead of the one it computes.
+// 8-bit K/V with four query heads per kv head, staged through LDS: each
+// wave streams its tiles into a ring of kDepth LDS slots with direct
+// global-to-LDS loads, which hold no registers, kDepth - 1 tiles ahead of
+// the one it computes. Two slots at two waves per SIMD measured fastest on
+// the 64-sequence batch (66.3 us; one slot 69.4, three 68.0, four 68.7, and
+// two slots at one or three waves per SIMD 68.2-68.5).
 // Slot image: K codes, V codes (16 tokens x 128 dims each; the 16-byte chunk
 // d of token t at chunk t * 8 + (d ^ (t & 7)), so that the reads below hit
 // distinct banks), then the 16 K and the 16 V scales.
 struct Int8Ring : MfmaRows<4, 1> {
-    static constexpr int kDepth = 4;
+    static constexpr int kDepth = 2;
+    static constexpr int kWavesPerCU = 8;
     static constexpr int kSlot = 2 * kTileElems + 2 * kTileB * 4;
     static constexpr int kRingBytes = kDepth * kSlot;
     static constexpr int kLoads = 5;   // vector memory operations issued per tile
@@ -361,16 +342,21 @@ struct Int8Ring : MfmaRows<4, 1> {
             const int tk = 4 * q + e;
             vr[e] = *reinterpret_cast<const u32x2*>(src + kTileElems + (tk * 8 + ((n >> 1) ^ (tk & 7))) * 16 + voff);
         }
-        const float4 skv = *reinterpret_cast<const float4*>(src + 2 * kTileElems + 16 * q);
-        const float4 svv = *reinterpret_cast<const float4*>(src + 2 * kTileElems + 64 + 16 * q);
+        // read as integers: read as floats (the copies' source type), the
+        // compiler takes them to alias the copies still in flight and waits
+        // for all of them here; wait_loads above already covers this slot
+        const u32x4 skv = *reinterpret_cast<const u32x4*>(src + 2 * kTileElems + 16 * q);
+        const u32x4 svv = *reinterpret_cast<const u32x4*>(src + 2 * kTileElems + 64 + 16 * q);
         f32x4 s[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(kr[b])),
                                                            __builtin_bit_cast(bf16x8, qv[b]), s[0], 0, 0, 0);
         // codes are finite whatever the slot holds; weights past the end are 0
-        const float sk[4] = {skv.x, skv.y, skv.z, skv.w};
-        const float sv[4] = {svv.x, svv.y, svv.z, svv.w};
+        const float sk[4] = {__uint_as_float(skv[0]), __uint_as_float(skv[1]), __uint_as_float(skv[2]),
+                             __uint_as_float(skv[3])};
+        const float sv[4] = {__uint_as_float(svv[0]), __uint_as_float(svv[1]), __uint_as_float(svv[2]),
+                             __uint_as_float(svv[3])};
         st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(vr, j); }, lane, ntok, sl2);
     }
 };
@@ -384,10 +370,10 @@ template <int G>
 using ChunkKv = Bf16Mfma<G, 2>;
 static_assert(ChunkKv<4>::kSlotRows == kChunkSlotRows, "chunk partial slots");
 
-// At least two waves per SIMD (at most 256 registers per lane): fewer
-// waves would halve the bytes the chip keeps in flight. Eight query heads
-// per kv head need more registers than that (state, query and two tiles):
-// one wave per SIMD, with the grid sized to match.
+// Register budget: kWaves waves per SIMD (two: at most 256 registers per
+// lane; eight query heads per kv head need more than that for state, query
+// and two tiles, so one). How many waves per CU the grid holds is chosen
+// apart from this (kWavesPerCU, else all that fit).
 template <int G, class Kv>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(Kv::kWaves)))
 void decode_balanced_kernel(AttnArgs a) {
@@ -493,6 +479,7 @@ void decode_balanced_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < D; ++u) b[u].t.slot = u;
     }
+    static_assert(D >= 2, "the next tile is issued before the current one is computed");
     describe(t0);
     auto issue = [&](int j, Buf& bj) {
         const int lj = j & (kWave - 1);
@@ -502,10 +489,19 @@ void decode_balanced_kernel(AttnArgs a) {
         kv.load(bj.t, __builtin_amdgcn_readlane(i_tile, lj), lane);
     };
 
-    // One step: issue tile i + D - 1 into fut, then compute tile i (in cur).
-    auto step = [&](int i, const Buf& cur, Buf& fut) {
-        if (i + D - 1 < n) issue(i + D - 1, fut);
-        const int newer = min(D - 1, n - 1 - i);   // tiles issued after tile i
+    // One step: issue tile i + D - 1 into fut (unless `tail` says it may be
+    // past the end), then compute tile i (in cur).
+    //
+    // The compiler places its waits for loads without regard to branch
+    // conditions: a load that some path leaves in flight where paths join
+    // counts as in flight on all of them, and the product that reads it
+    // then waits for every load issued since, the tiles in flight
+    // included. So the paths through a step of the main loop below leave
+    // the same loads outstanding: a new segment's query is waited for
+    // inside its branch (the empty asm reads the registers), before the
+    // issue, and the last D - 1 steps, which issue nothing, run in a loop
+    // of their own.
+    auto step = [&](int i, const Buf& cur, Buf& fut, bool tail) {
         const int seg = cur.seg;
         const int ntok = cur.ntok;
         if (seg != cur_seg) {
@@ -513,10 +509,15 @@ void decode_balanced_kernel(AttnArgs a) {
             const int s = seg / n_kv;
             const int g = seg - s * n_kv;
             st.reset();
-            cur_used = kv.load_q(st, qv, a, s, g, lane);
+            kv.fetch_q(qv, a, s, g, lane);
+            cur_used = kv.begin(st, a, s, lane);
+#pragma unroll
+            for (int h = 0; h < Kv::kQ; ++h) asm volatile("" : "+v"(qv[h]));
             cur_seg = seg;
             cur_bad = false;
         }
+        if (!tail || i + D - 1 < n) issue(i + D - 1, fut);
+        const int newer = tail ? min(D - 1, n - 1 - i) : D - 1;   // tiles issued after tile i
         if (ntok < 0) {
             cur_bad = true;
         } else {
@@ -527,10 +528,16 @@ void decode_balanced_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < D - 1; ++j)
         if (j < n) issue(j, b[j]);
-    for (int i = 0; i < n; i += D) {
+    // tile j sits in b[j % D]; every step of an iteration here issues
+    int i = 0;
+    for (; i + 2 * D - 2 < n; i += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) step(i + u, b[u], b[(u + D - 1) % D], false);
+    }
+    for (; i < n; i += D) {   // at most two iterations
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            if (i + u < n) step(i + u, b[u], b[(u + D - 1) % D]);
+            if (i + u < n) step(i + u, b[u], b[(u + D - 1) % D], true);
     }
     flush();
 }
@@ -555,6 +562,13 @@ int occupancy(size_t lds) {
     return blocks;
 }
 
+// Waves per CU the grid holds: the policy's choice, at most what fits.
+template <int G, class Kv>
+int waves_per_cu(size_t lds) {
+    const int fit = occupancy<G, Kv>(lds);
+    return Kv::kWavesPerCU > 0 && fit > Kv::kWavesPerCU ? Kv::kWavesPerCU : fit;
+}
+
 template <template <int> class Kv>
 int waves_for(int n_q, int n_kv, int num_seqs) {
     int dev = 0, cus = 0;
@@ -563,10 +577,10 @@ int waves_for(int n_q, int n_kv, int num_seqs) {
     const size_t lds = balanced_lds_bytes(num_seqs);
     int per_cu = 0;
     switch (n_q / n_kv) {
-        case 1: per_cu = occupancy<1, Kv<1>>(lds); break;
-        case 2: per_cu = occupancy<2, Kv<2>>(lds); break;
-        case 4: per_cu = occupancy<4, Kv<4>>(lds); break;
-        case 8: per_cu = occupancy<8, Kv<8>>(lds); break;
+        case 1: per_cu = waves_per_cu<1, Kv<1>>(lds); break;
+        case 2: per_cu = waves_per_cu<2, Kv<2>>(lds); break;
+        case 4: per_cu = waves_per_cu<4, Kv<4>>(lds); break;
+        case 8: per_cu = waves_per_cu<8, Kv<8>>(lds); break;
         default: return 0;
     }
     if (per_cu < 1) per_cu = 1;
