@@ -162,6 +162,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
     const int rb = RB * static_cast<int>(blockIdx.z);
     if (used <= 0) return;
 
+    // Output task of this thread: row r_o, dims k_o .. k_o + 3 (one task per
+    // thread at most). Its first kPre partials' outputs are requested now,
+    // so that their round trip overlaps the (m, l) round below.
+    static_assert(RB * (D / 4) <= kMergeThreads, "one output task per thread");
+    constexpr int kPre = 8;
+    const bool has_out = tid < used * (D / 4);
+    const int r_o = tid / (D / 4);
+    const int k_o = 4 * (tid - r_o * (D / 4));
+    const float* ob = a.ws_o + (first * RS + rb + r_o) * D + k_o;
+    float4 pre[kPre];
+    if (has_out) {
+#pragma unroll
+        for (int u = 0; u < kPre; ++u)
+            pre[u] = u < count ? *reinterpret_cast<const float4*>(ob + static_cast<size_t>(u) * RS * D)
+                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+
     // Per-row maximum over all partials; a NaN partial makes it NaN.
     for (int j0 = 0; j0 < count; j0 += kMergeMaxParts) {
         const int n = min(count - j0, kMergeMaxParts);
@@ -213,16 +230,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
     }
     __syncthreads();
 
-    // Outputs: thread -> (row, 4 dims); partials' loads issued in groups of 8.
-    for (int e = tid; e < used * (D / 4); e += kMergeThreads) {
-        const int r = e / (D / 4);
-        const int k = 4 * (e - r * (D / 4));
+    // Outputs: the first kPre partials from the registers, the rest in
+    // groups of 8 loads.
+    if (has_out) {
+        const int r = r_o;
+        const int k = k_o;
         const int qi = (rb + r) / G;
         const int h = rb + r - qi * G;
         const float M = s_M[r];
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        const float* ob = a.ws_o + (first * RS + rb + r) * D + k;
-        int j = 0;
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            if (u < count) {
+                const float wj = staged ? s_m[u][r] : exp2f(a.ws_ml[(first + u) * RS + rb + r].m - M);
+                acc.x = fmaf(wj, pre[u].x, acc.x);
+                acc.y = fmaf(wj, pre[u].y, acc.y);
+                acc.z = fmaf(wj, pre[u].z, acc.z);
+                acc.w = fmaf(wj, pre[u].w, acc.w);
+            }
+        }
+        int j = kPre;
         for (; j + 8 <= count; j += 8) {
             float4 v[8];
             float wv[8];
