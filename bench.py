@@ -1,9 +1,11 @@
 """Benchmark: decode tokens/s and KV-read HBM bandwidth of one paged decode step.
 
 A step is the whole hot path for one batch: append each sequence's new
-token's K/V into the pool through its block table (kv_append), then paged
-decode attention over every cached key (paged_attn_decode: split pass +
-merge pass). The workload is 64 sequences, 32 query / 8 kv heads,
+token's K/V into the pool through its block table, then paged decode
+attention over every cached key (split pass + merge pass). For bf16 decode
+batches this is one call, paged_attn_decode_append, whose split pass writes
+each new row just before it reads that block; ``--separate`` times
+kv_append followed by paged_attn_decode instead. The workload is 64 sequences, 32 query / 8 kv heads,
 head_dim 128, block_size 16, bf16 K/V, context lengths uniform in
 [512, 4096], blocks drawn in a seeded random order from a pool of 1.25x the
 blocks needed (seed 7). Block allocation for the step happens before the
@@ -50,6 +52,9 @@ def parse():
                         "128256-entry vocabulary")
     p.add_argument("--sample-topk", type=int, default=50,
                    help="top-k of the --sample workload (0 = off: every row takes the histogram path)")
+    p.add_argument("--separate", action="store_true",
+                   help="time the decode step as kv_append + paged_attn_decode (two launches) instead of "
+                        "paged_attn_decode_append")
     p.add_argument("--verify", action="store_true",
                    help="time a speculative verification step: gamma + 1 = 5 tokens per sequence of the "
                         "64-sequence batch appended and attended as one causal chunk")
@@ -474,10 +479,20 @@ def main():
         return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
     ws = [(workspace(nd, max_dec) if nd else None, chunk_workspace() if nd < S else None) for _ in caches]
     stream = torch.cuda.current_stream()
+    # one call per step: bf16 decode rows only, the library's partition, the tuned shape
+    fused = (not quant and not args.separate and split == 0 and nd == S and wl.head_dim == 128
+             and wl.block_size == 16)
 
     def step(i, ev_dec=None, ev_chk=None):
         j = i % len(caches)
         c, out = caches[j], outs[j]
+        if fused:
+            if ev_dec is not None:
+                pkv.pkv_set_profile_events(*ev_dec)
+            pkv.paged_attn_decode_append(out, None, q, c.k_cache, c.v_cache, k_new, v_new, c.table_dev, seq_lens,
+                                         max_dec, wl.scale, ws[j][0], stream=stream)
+            pkv.pkv_set_profile_events(None, None)
+            return
         c.append(k_new, v_new, start_pos, new_start, stream=stream)
         if nd:
             if ev_dec is not None:
@@ -557,6 +572,8 @@ def main():
                    "context_tokens": int(wl.seq_lens.sum()),
                    "kv_bytes": int(wl.seq_lens.sum()) * key_bytes if quant else wl.ideal_kv_bytes(),
                    "cache_copies": len(caches),
+                   "step": ("paged_attn_decode_append (append folded into the split pass)" if fused
+                            else "kv_append + paged_attn_decode" if nd == S else "kv_append + decode + chunk"),
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
     }
     if nd:
@@ -564,7 +581,8 @@ def main():
         achieved = dec_bytes / (kern_avg * 1e-3) / 1e9
         line["step_kv_gbps"] = line["config"]["kv_bytes"] / (ms_step * 1e-3) / 1e9
         line["step_kv_frac_of_peak"] = line["step_kv_gbps"] / PEAK_HBM_GBPS
-        line["roofline"] = {"kernel": "decode split pass", "bound": "hbm", "achieved": achieved,
+        line["roofline"] = {"kernel": "decode split pass" + (" (with the append)" if fused else ""),
+                            "bound": "hbm", "achieved": achieved,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                             "traffic": None if quant else measured_traffic(CONFIG_NAMES[args.config]),
                             "avg_launch_ms": kern_avg,

@@ -298,6 +298,39 @@ int paged_attn_decode(void* out, float* lse, const void* q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * paged_attn_decode_append - the whole decode step in one pass: each
+ * sequence's new token is appended to the pool, then one query token per
+ * sequence attends over the cache including it.
+ *
+ * Source: chapter 5 section 2.1 (a decode step appends k_t, v_t to the
+ * cache, then attends q_t over every cached key and value); the append
+ * places the token as the lab page's KVPool.write does (position p to slot
+ * p % B of block table[p / B], every kv head). Same result as kv_append of
+ * one token per sequence at position seq_lens[s] - 1 followed by
+ * paged_attn_decode, without the separate append launch: the wave that
+ * reads a sequence's last block for a kv head writes the new row first.
+ *
+ * k_new, v_new: device, [num_seqs][n_kv][head_dim] bf16, 16-byte aligned.
+ * seq_lens: keys per sequence after the append (the new token is at
+ *   seq_lens[s] - 1); table rows must cover it (kvpool_ensure). A sequence
+ *   whose length is out of range gets NaN rows and no append, and a token
+ *   whose table entry is outside the pool is not written (its rows NaN),
+ *   as in kv_append and paged_attn_decode.
+ * k_cache, v_cache: written at the appended slots only. Other arguments
+ *   and the workspace as paged_attn_decode (split_tokens is 0).
+ * Supported: dtype PKV_BF16, head_dim 128, block_size 16, n_q / n_kv in
+ *   {1, 2, 4, 8}, at most 8192 sequences, 16-byte aligned tensors; other
+ *   shapes return UNSUPPORTED (call kv_append, then paged_attn_decode).
+ * Errors: NULL_POINTER, INVALID_ARGUMENT, UNSUPPORTED,
+ * WORKSPACE_TOO_SMALL, HIP. */
+int paged_attn_decode_append(void* out, float* lse, const void* q, void* k_cache, void* v_cache,
+                             const void* k_new, const void* v_new, const int32_t* block_table,
+                             int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
+                             int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * paged_attn_chunk - a chunk of C_s consecutive query tokens per sequence
  * (chunked prefill), causal.
  *

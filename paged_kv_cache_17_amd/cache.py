@@ -119,6 +119,17 @@ class PagedKVCache:
                             max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
         return out
 
+    def decode_step(self, q, k_new, v_new, seq_lens, max_seq_len: int, scale: float, out=None, lse=None,
+                    stream=None):
+        """Append one token per sequence (``k_new``/``v_new`` ``[S, n_kv, d]`` at position
+        ``seq_lens - 1``) and attend, in one call (bf16, d 128, block 16)."""
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, 0)
+        B.paged_attn_decode_append(out, lse, q, self.k_cache, self.v_cache, k_new, v_new, self.table_dev,
+                                   seq_lens, max_seq_len, scale, ws, stream=stream)
+        return out
+
     def chunk(self, q, q_start, seq_lens, max_q_len: int, max_seq_len: int, scale: float, out=None,
               lse=None, split_tokens: int = 0, stream=None):
         if out is None:

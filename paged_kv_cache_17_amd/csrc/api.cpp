@@ -342,6 +342,66 @@ extern "C" int paged_attn_decode(void* out, float* lse, const void* q,
                          static_cast<hipStream_t>(stream));
 }
 
+extern "C" int paged_attn_decode_append(void* out, float* lse, const void* q, void* k_cache, void* v_cache,
+                                        const void* k_new, const void* v_new, const int32_t* block_table,
+                                        int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                        int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
+                                        int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size,
+                         table_stride, dtype, scale);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !k_new || !v_new || !block_table || !seq_lens)
+        return PKV_ERR_NULL_POINTER;
+    if (!balanced_eligible(dtype, 0, num_seqs, n_q, n_kv, head_dim, block_size) || !aligned16(q) ||
+        !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new))
+        return PKV_ERR_UNSUPPORTED;
+    pkv::AttnArgs a{};
+    a.waves = balanced_waves(n_q, n_kv, num_seqs);
+    if (a.waves < 1) return PKV_ERR_HIP;
+    a.q = q;
+    a.q_start = nullptr;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    // The append rides in the split pass while the batch has no more
+    // (sequence, kv head) segments than the pass has waves; with more, each
+    // wave would append several rows, each a dependent round trip under
+    // full load, and a launch of its own is faster (measured: 64 x 8 and
+    // 8 x 8 segments folded, 256 x 8 on its own).
+    if (static_cast<long long>(num_seqs) * n_kv <= a.waves) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_app = k_cache;
+        a.v_app = v_cache;
+    } else {
+        const hipError_t e = pkv::launch_kv_append_last(k_cache, v_cache, k_new, v_new, block_table, table_stride,
+                                                        seq_lens, num_seqs, max_seq_len, num_blocks, n_kv,
+                                                        static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return PKV_ERR_HIP;
+    }
+    a.table = block_table;
+    a.seq_lens = seq_lens;
+    a.table_stride = table_stride;
+    a.num_seqs = num_seqs;
+    a.num_rows = num_seqs;
+    a.max_q_len = 1;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_blocks;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    int split = 0;
+    rc = resolve_split(num_seqs, n_kv, block_size, max_seq_len, 0, &split);
+    if (rc != PKV_OK) return rc;
+    a.split_tokens = split;
+    a.max_splits = (max_seq_len + split - 1) / split;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    return run_attention(a, out, lse, dtype, true, true, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
 extern "C" int kv_append_q8(void* k_codes, void* v_codes, float* k_scale, float* v_scale, const void* k_new,
                             const void* v_new, int32_t new_dtype, const int32_t* block_table, int32_t table_stride,
                             const int32_t* start_pos, const int32_t* new_start, int32_t num_seqs, int32_t total_new,

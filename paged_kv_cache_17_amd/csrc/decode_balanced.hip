@@ -374,7 +374,7 @@ static_assert(ChunkKv<4>::kSlotRows == kChunkSlotRows, "chunk partial slots");
 // lane; eight query heads per kv head need more than that for state, query
 // and two tiles, so one). How many waves per CU the grid holds is chosen
 // apart from this (kWavesPerCU, else all that fit).
-template <int G, class Kv>
+template <int G, class Kv, bool kAppend = false>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(Kv::kWaves)))
 void decode_balanced_kernel(AttnArgs a) {
     extern __shared__ int s_mem[];
@@ -481,12 +481,33 @@ void decode_balanced_kernel(AttnArgs a) {
     }
     static_assert(D >= 2, "the next tile is issued before the current one is computed");
     describe(t0);
+    // Folded append (decode step stage 1): the new token of segment seg
+    // (sequence seg / n_kv, kv head seg % n_kv) sits at row `slot` of the
+    // segment's last tile, which only this wave reads. Lanes 0..15 write
+    // its K row, 16..31 its V row, just before the tile's loads are issued:
+    // one wave's accesses to one address are performed in order, so those
+    // loads return the new row without waiting for the stores to complete.
+    auto append_row = [&](int tile, int seg, int slot) {
+        if (lane < 32) {
+            const bool isv = lane >= 16;
+            const int c = lane & 15;
+            const uint16_t* src = static_cast<const uint16_t*>(isv ? a.v_new : a.k_new);
+            uint16_t* dst = static_cast<uint16_t*>(isv ? a.v_app : a.k_app);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(seg) * kTileD + 8 * c);
+            *reinterpret_cast<u32x4*>(dst + (static_cast<size_t>(tile) * kTileB + slot) * kTileD + 8 * c) = x;
+        }
+    };
     auto issue = [&](int j, Buf& bj) {
         const int lj = j & (kWave - 1);
         if (lj == 0 && j > 0) describe(t0 + j);
         bj.seg = __builtin_amdgcn_readlane(i_seg, lj);
         bj.ntok = __builtin_amdgcn_readlane(i_ntok, lj);
-        kv.load(bj.t, __builtin_amdgcn_readlane(i_tile, lj), lane);
+        const int tile = __builtin_amdgcn_readlane(i_tile, lj);
+        if constexpr (kAppend) {
+            // the last tile of a segment holds 1..16 of its keys
+            if (bj.ntok > 0 && bj.ntok <= kTileB) append_row(tile, bj.seg, bj.ntok - 1);
+        }
+        kv.load(bj.t, tile, lane);
     };
 
     // One step: issue tile i + D - 1 into fut (unless `tail` says it may be
@@ -542,14 +563,14 @@ void decode_balanced_kernel(AttnArgs a) {
     flush();
 }
 
-template <int G, class Kv>
+template <int G, class Kv, bool kAppend = false>
 hipError_t launch_g(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     const size_t lds = balanced_lds_bytes(a.num_seqs);
     if (ev.on())
-        hipExtLaunchKernelGGL(decode_balanced_kernel<G, Kv>, dim3(a.waves), dim3(kWave), lds, stream, ev.start,
-                              ev.stop, 0, a);
+        hipExtLaunchKernelGGL((decode_balanced_kernel<G, Kv, kAppend>), dim3(a.waves), dim3(kWave), lds, stream,
+                              ev.start, ev.stop, 0, a);
     else
-        hipLaunchKernelGGL((decode_balanced_kernel<G, Kv>), dim3(a.waves), dim3(kWave), lds, stream, a);
+        hipLaunchKernelGGL((decode_balanced_kernel<G, Kv, kAppend>), dim3(a.waves), dim3(kWave), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -616,6 +637,16 @@ int decode_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv) {
 }
 
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
+    if (a.k_new) {   // bf16 with the append folded in
+        if (a.k_scale || !a.v_new || !a.k_app || !a.v_app) return hipErrorInvalidValue;
+        switch (a.n_q / a.n_kv) {
+            case 1: return launch_g<1, Bf16Kv<1>, true>(a, stream, ev);
+            case 2: return launch_g<2, Bf16Kv<2>, true>(a, stream, ev);
+            case 4: return launch_g<4, Bf16Kv<4>, true>(a, stream, ev);
+            case 8: return launch_g<8, Bf16Kv<8>, true>(a, stream, ev);
+            default: return hipErrorInvalidValue;
+        }
+    }
     return a.k_scale ? launch_kv<Int8Kv>(a, stream, ev) : launch_kv<Bf16Kv>(a, stream, ev);
 }
 

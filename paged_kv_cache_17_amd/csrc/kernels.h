@@ -37,6 +37,14 @@ struct AttnArgs {
     PartialML* ws_ml;            // same slots as ws_o, without the head_dim axis
     int waves;                   // balanced decode: grid size W (0 = fixed split)
     int* prefix;                 // balanced decode: [S+1] block-count prefix sums
+    // Balanced bf16 decode with the append folded in (else all null): the
+    // new token of each sequence ([num_seqs][n_kv][head_dim]) is written to
+    // position seq_lens[s] - 1 of k_app / v_app (the same pools as
+    // k_cache / v_cache) before that tile is read.
+    const void* k_new;
+    const void* v_new;
+    void* k_app;
+    void* v_app;
 };
 
 // Optional event pair recorded by the kernel's own dispatch (start and end
@@ -51,6 +59,12 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
                             const int32_t* table, int table_stride, const int32_t* start_pos,
                             const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
                             int n_kv, int row_bytes, int block_size, hipStream_t stream);
+
+// The decode step's append on its own: one token per sequence at position
+// seq_lens[s] - 1 (bf16, head_dim 128, block_size 16; 16-byte aligned).
+hipError_t launch_kv_append_last(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                 const int32_t* table, int table_stride, const int32_t* seq_lens, int num_seqs,
+                                 int max_seq_len, int num_blocks, int n_kv, hipStream_t stream);
 
 // Quantising append (8-bit codes + one fp32 scale per token and kv head).
 hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,

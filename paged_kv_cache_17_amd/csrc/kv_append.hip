@@ -113,6 +113,36 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(
     if (lane == 0) (is_v ? vs : ks)[slot] = scale;
 }
 
+// The decode step's append: one token per sequence, at position
+// seq_lens[s] - 1, rows of 16-byte units (bf16, head_dim 128, block_size 16:
+// 16 units of K and of V per (sequence, kv head)). A sequence whose length
+// the decode rejects, or whose table entry there is outside the pool, gets
+// no write - the same tokens the decode pass with the append folded in
+// writes.
+__global__ __launch_bounds__(256) void kv_append_last_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc,
+                                                             const uint4* __restrict__ kn,
+                                                             const uint4* __restrict__ vn,
+                                                             const int32_t* __restrict__ table, int table_stride,
+                                                             const int32_t* __restrict__ seq_lens, int num_seqs,
+                                                             int max_seq_len, int num_blocks, int n_kv) {
+    constexpr int kUnits = 16, kBS = 16;
+    const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= static_cast<long long>(num_seqs) * n_kv * kUnits) return;
+    const int u = static_cast<int>(idx % kUnits);
+    const long long th = idx / kUnits;
+    const int h = static_cast<int>(th % n_kv);
+    const int s = static_cast<int>(th / n_kv);
+    const int L = seq_lens[s];
+    if (!seq_len_ok(L, 1, max_seq_len, table_stride * kBS)) return;
+    const int pos = L - 1;
+    const int blk = table[static_cast<size_t>(s) * table_stride + pos / kBS];
+    if (blk < 0 || blk >= num_blocks) return;
+    const size_t dst = ((static_cast<size_t>(blk) * n_kv + h) * kBS + pos % kBS) * kUnits + u;
+    const size_t src = static_cast<size_t>(th) * kUnits + u;
+    kc[dst] = kn[src];
+    vc[dst] = vn[src];
+}
+
 }  // namespace
 
 hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,
@@ -149,6 +179,17 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
     if (row_bytes % 4 == 0 && align % 4 == 0) PKV_APPEND(4);
     PKV_APPEND(2);
 #undef PKV_APPEND
+}
+
+hipError_t launch_kv_append_last(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                 const int32_t* table, int table_stride, const int32_t* seq_lens, int num_seqs,
+                                 int max_seq_len, int num_blocks, int n_kv, hipStream_t stream) {
+    const long long work = static_cast<long long>(num_seqs) * n_kv * 16;
+    hipLaunchKernelGGL(kv_append_last_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), static_cast<const uint4*>(k_new),
+                       static_cast<const uint4*>(v_new), table, table_stride, seq_lens, num_seqs, max_seq_len,
+                       num_blocks, n_kv);
+    return hipGetLastError();
 }
 
 }  // namespace pkv

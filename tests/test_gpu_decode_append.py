@@ -1,0 +1,152 @@
+"""GPU parity of the one-call decode step (paged_attn_decode_append).
+
+The new token of each sequence must land in the pool exactly where and as
+kv_append writes it (pool bytes bit-exact against the oracle, NaN-poisoned
+slots nobody wrote included), the rows must meet the bf16 bar against the
+oracle (per (row, head) max_d |out - ref| <= 2e-2 * max_d |ref|; lse within
+1e-2), and they must be bit-identical to kv_append followed by
+paged_attn_decode on the same inputs, which run the same tile math.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import BF16, F32, build_workload
+
+from gpu_harness import (build_gpu_cache, check_lse, check_rows, i32, out_f64, raw_to_torch, run_decode,
+                         torch_to_raw)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_17_amd as pkv
+    pkv.load_library()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _history_only_cache(wl):
+    """The cache as it stands before the step: history appended, tables
+    already covering the new token (kvpool_ensure), new slots still NaN."""
+    import paged_kv_cache_17_amd as pkv
+    from gpu_harness import torch_dtype
+    c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size, torch_dtype(wl.dtype),
+                         wl.num_seqs, wl.table_stride, alloc_order=wl.alloc_order, fill_nan=True,
+                         poison_workspace=True)
+    for s in range(wl.num_seqs):
+        c.ensure(s, int(wl.hist_lens[s]))
+    c.upload_table()
+    kh, vh = wl.packed_hist_kv()
+    if len(kh):
+        hs = np.zeros(wl.num_seqs + 1, dtype=np.int64)
+        np.cumsum(wl.hist_lens, out=hs[1:])
+        c.append(raw_to_torch(kh, wl.dtype), raw_to_torch(vh, wl.dtype), i32(np.zeros(wl.num_seqs)), i32(hs))
+    for s in range(wl.num_seqs):
+        c.ensure(s, int(wl.seq_lens[s]))
+    c.upload_table()
+    torch.cuda.synchronize()
+    return c
+
+
+def _step(c, wl):
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.decode_step(q, raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype), i32(wl.seq_lens),
+                        wl.max_seq_len, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check_step(wl, where):
+    c = _history_only_cache(wl)
+    out, lse = _step(c, wl)
+    ora = oracle.build_cache(wl)
+    assert np.array_equal(c.table, ora.tables())
+    assert np.array_equal(torch_to_raw(c.k_cache, wl.dtype).view(np.uint8), ora.pool_k.view(np.uint8))
+    assert np.array_equal(torch_to_raw(c.v_cache, wl.dtype).view(np.uint8), ora.pool_v.view(np.uint8))
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(out_f64(out, wl.dtype), ref, wl.dtype, where)
+    lerr = check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, wl.dtype, where)
+    c2 = build_gpu_cache(wl)
+    out2, lse2 = run_decode(c2, wl)
+    assert torch.equal(out, out2), "not bit-identical to kv_append + paged_attn_decode"
+    assert torch.equal(lse, lse2)
+    return err, lerr
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 33, 255, 256, 257, 1000, 2047, 2049, 3000]
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 8), (64, 8)])
+def test_step_ragged_lengths(n_q, n_kv):
+    # lengths 1 (only the new token), 16 / 17 (the token fills or opens a block)
+    L = np.array(RAGGED)
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=31)
+    say("decode step", n_q, n_kv)
+    err, lerr = _check_step(wl, f"decode step {n_q}/{n_kv}")
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+
+
+def test_step_many_short_sequences():
+    """700 sequences of 1..300 keys: most segments end inside one wave's
+    range, many waves append several sequences' tokens."""
+    L = np.random.default_rng(41).integers(1, 301, size=700)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=41)
+    say("decode step, 700 short sequences")
+    err, lerr = _check_step(wl, "decode step 700")
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+
+
+def test_step_rejects_other_shapes():
+    import paged_kv_cache_17_amd as pkv
+    L = np.array([5, 9])
+    wl = build_workload(n_q=4, n_kv=2, head_dim=64, block_size=16, dtype=F32, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=2)
+    c = _history_only_cache(wl)
+    with pytest.raises(pkv.PagedKVError) as e:
+        _step(c, wl)
+    assert e.value.status == -3   # PKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("many", [False, True])
+def test_step_invalid_length_row_is_nan_others_unchanged(many):
+    """A length beyond max_seq_len: that sequence's rows are NaN (and it gets
+    no append); every other row still meets the bar against the oracle (the
+    rejected sequence's tiles leave the partition, so the others' rounding
+    may change). With 14 sequences the append is folded into the split
+    pass, with 700 it runs as its own launch."""
+    rng = np.random.default_rng(43)
+    L = rng.integers(1, 301, size=700) if many else np.array(RAGGED)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=43)
+    say("decode step, one invalid length, many =", many)
+    ora = oracle.build_cache(wl)
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    c = _history_only_cache(wl)
+    bad = 3
+    lens = wl.seq_lens.copy()
+    lens[bad] = wl.max_seq_len + 5
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    lse = torch.empty((wl.num_seqs, wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.decode_step(q, raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype), i32(lens), wl.max_seq_len,
+                        wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[bad].float()).all() and torch.isnan(lse[bad]).all()
+    keep = [s for s in range(wl.num_seqs) if s != bad]
+    check_rows(out_f64(out, wl.dtype)[keep], ref[keep], wl.dtype, "invalid-length step")
+    check_lse(lse.cpu().numpy().astype(np.float64)[keep], ref_lse[keep], wl.dtype, "invalid-length step")
+    # the rejected sequence's new slot was not written (still the NaN poison)
+    pos = int(wl.seq_lens[bad]) - 1
+    blk = int(c.table[bad, pos // 16])
+    assert torch.isnan(c.k_cache[blk, :, pos % 16].float()).all()
