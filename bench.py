@@ -2,10 +2,11 @@
 
 A step is the whole hot path for one batch: append each sequence's new
 token's K/V into the pool through its block table, then paged decode
-attention over every cached key (split pass + merge pass). For bf16 decode
-batches this is one call, paged_attn_decode_append, whose split pass writes
-each new row just before it reads that block; ``--separate`` times
-kv_append followed by paged_attn_decode instead. The workload is 64 sequences, 32 query / 8 kv heads,
+attention over every cached key (split pass + merge pass). For decode
+batches this is one call, paged_attn_decode_append (8-bit cache:
+paged_attn_decode_q8_append), whose split pass writes each new row just
+before it reads that block; ``--separate`` times the append and the decode
+as two calls instead. The workload is 64 sequences, 32 query / 8 kv heads,
 head_dim 128, block_size 16, bf16 K/V, context lengths uniform in
 [512, 4096], blocks drawn in a seeded random order from a pool of 1.25x the
 blocks needed (seed 7). Block allocation for the step happens before the
@@ -480,8 +481,7 @@ def main():
     ws = [(workspace(nd, max_dec) if nd else None, chunk_workspace() if nd < S else None) for _ in caches]
     stream = torch.cuda.current_stream()
     # one call per step: bf16 decode rows only, the library's partition, the tuned shape
-    fused = (not quant and not args.separate and split == 0 and nd == S and wl.head_dim == 128
-             and wl.block_size == 16)
+    fused = not args.separate and split == 0 and nd == S and wl.head_dim == 128 and wl.block_size == 16
 
     def step(i, ev_dec=None, ev_chk=None):
         j = i % len(caches)
@@ -489,8 +489,13 @@ def main():
         if fused:
             if ev_dec is not None:
                 pkv.pkv_set_profile_events(*ev_dec)
-            pkv.paged_attn_decode_append(out, None, q, c.k_cache, c.v_cache, k_new, v_new, c.table_dev, seq_lens,
-                                         max_dec, wl.scale, ws[j][0], stream=stream)
+            if quant:
+                pkv.paged_attn_decode_q8_append(out, None, q, c.k_cache, c.v_cache, c.k_scale, c.v_scale, k_new,
+                                                v_new, c.table_dev, seq_lens, max_dec, wl.scale, ws[j][0],
+                                                stream=stream)
+            else:
+                pkv.paged_attn_decode_append(out, None, q, c.k_cache, c.v_cache, k_new, v_new, c.table_dev,
+                                             seq_lens, max_dec, wl.scale, ws[j][0], stream=stream)
             pkv.pkv_set_profile_events(None, None)
             return
         c.append(k_new, v_new, start_pos, new_start, stream=stream)
@@ -572,7 +577,8 @@ def main():
                    "context_tokens": int(wl.seq_lens.sum()),
                    "kv_bytes": int(wl.seq_lens.sum()) * key_bytes if quant else wl.ideal_kv_bytes(),
                    "cache_copies": len(caches),
-                   "step": ("paged_attn_decode_append (append folded into the split pass)" if fused
+                   "step": (("paged_attn_decode_q8_append" if quant else "paged_attn_decode_append")
+                            + " (one call: append folded into the split pass, or launched first)" if fused
                             else "kv_append + paged_attn_decode" if nd == S else "kv_append + decode + chunk"),
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
     }

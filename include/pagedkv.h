@@ -308,7 +308,10 @@ int paged_attn_decode(void* out, float* lse, const void* q,
  * p % B of block table[p / B], every kv head). Same result as kv_append of
  * one token per sequence at position seq_lens[s] - 1 followed by
  * paged_attn_decode, without the separate append launch: the wave that
- * reads a sequence's last block for a kv head writes the new row first.
+ * reads a sequence's last block for a kv head writes the new row first
+ * (while the batch has at most half as many (sequence, kv head) pairs as
+ * the pass has waves; with more, the append is a small launch of its own
+ * inside the call).
  *
  * k_new, v_new: device, [num_seqs][n_kv][head_dim] bf16, 16-byte aligned.
  * seq_lens: keys per sequence after the append (the new token is at
@@ -416,6 +419,31 @@ int paged_attn_decode_q8(void* out, float* lse, const void* q,
                          int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks,
                          int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * paged_attn_decode_q8_append - the decode step in one call over an 8-bit
+ * pool: each sequence's new token (bf16) is quantised into the pool at
+ * position seq_lens[s] - 1, then paged_attn_decode_q8 runs over it.
+ *
+ * Source: chapter 5 section 2.1 (append k_t, v_t, then attend) and
+ * section 4 (absmax quantisation, as kv_append_q8). Same result as
+ * kv_append_q8 (bf16 input) of one token per sequence followed by
+ * paged_attn_decode_q8: codes and scales bit-identical, outputs
+ * bit-identical. The append rides in the split pass while the batch has at
+ * most half as many (sequence, kv head) pairs as the pass has waves, else
+ * it is a small launch of its own before it.
+ *
+ * k_new, v_new: device, [num_seqs][n_kv][head_dim] bf16, 16-byte aligned.
+ * k_codes, v_codes, k_scale, v_scale: as paged_attn_decode_q8, written at
+ *   the appended slots only. A sequence whose length is out of range gets
+ *   NaN rows and no append; a token whose table entry is outside the pool
+ *   is not written. Other arguments and errors as paged_attn_decode_q8. */
+int paged_attn_decode_q8_append(void* out, float* lse, const void* q, void* k_codes, void* v_codes,
+                                float* k_scale, float* v_scale, const void* k_new, const void* v_new,
+                                const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks, int32_t n_q,
+                                int32_t n_kv, int32_t head_dim, int32_t block_size, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
  * sample_tokens - pick the next token of each row of logits.

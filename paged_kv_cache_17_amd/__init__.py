@@ -18,7 +18,7 @@ from .binding import (  # noqa: F401
     paged_attn_chunk,
     paged_attn_chunk_workspace_size,
     paged_attn_decode,
-    paged_attn_decode_append, paged_attn_decode_q8,
+    paged_attn_decode_append, paged_attn_decode_q8_append, paged_attn_decode_q8,
     paged_attn_split_tokens,
     paged_attn_workspace_size,
     pkv_set_profile_events,

@@ -121,11 +121,16 @@ class PagedKVCache:
 
     def decode_step(self, q, k_new, v_new, seq_lens, max_seq_len: int, scale: float, out=None, lse=None,
                     stream=None):
-        """Append one token per sequence (``k_new``/``v_new`` ``[S, n_kv, d]`` at position
-        ``seq_lens - 1``) and attend, in one call (bf16, d 128, block 16)."""
+        """Append one token per sequence (``k_new``/``v_new`` ``[S, n_kv, d]`` bf16 at position
+        ``seq_lens - 1``; quantised for an 8-bit cache) and attend, in one call (d 128, block 16)."""
         if out is None:
             out = torch.empty_like(q)
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, 0)
+        if self.quantized:
+            B.paged_attn_decode_q8_append(out, lse, q, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
+                                          k_new, v_new, self.table_dev, seq_lens, max_seq_len, scale, ws,
+                                          stream=stream)
+            return out
         B.paged_attn_decode_append(out, lse, q, self.k_cache, self.v_cache, k_new, v_new, self.table_dev,
                                    seq_lens, max_seq_len, scale, ws, stream=stream)
         return out

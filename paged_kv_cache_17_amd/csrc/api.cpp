@@ -364,12 +364,12 @@ extern "C" int paged_attn_decode_append(void* out, float* lse, const void* q, vo
     a.q_start = nullptr;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
-    // The append rides in the split pass while the batch has no more
-    // (sequence, kv head) segments than the pass has waves; with more, each
-    // wave would append several rows, each a dependent round trip under
-    // full load, and a launch of its own is faster (measured: 64 x 8 and
-    // 8 x 8 segments folded, 256 x 8 on its own).
-    if (static_cast<long long>(num_seqs) * n_kv <= a.waves) {
+    // The append rides in the split pass while the batch has at most half
+    // as many (sequence, kv head) segments as the pass has waves; with
+    // more, many waves append rows, each a dependent round trip under full
+    // load, and a launch of its own is faster (measured, bf16 and 8-bit:
+    // 64 x 8 and 8 x 8 segments folded win, 256 x 8 folded loses).
+    if (2LL * num_seqs * n_kv <= a.waves) {
         a.k_new = k_new;
         a.v_new = v_new;
         a.k_app = k_cache;
@@ -441,6 +441,64 @@ extern "C" int paged_attn_decode_q8(void* out, float* lse, const void* q, const 
     pkv::AttnArgs a{};
     a.waves = balanced_waves(n_q, n_kv, num_seqs, kDecodeInt8);
     if (a.waves < 1) return PKV_ERR_HIP;
+    a.q = q;
+    a.q_start = nullptr;
+    a.k_cache = k_codes;
+    a.v_cache = v_codes;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.table = block_table;
+    a.seq_lens = seq_lens;
+    a.table_stride = table_stride;
+    a.num_seqs = num_seqs;
+    a.num_rows = num_seqs;
+    a.max_q_len = 1;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_blocks;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.split_tokens = block_size;
+    a.max_splits = 1;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    return run_attention(a, out, lse, PKV_BF16, true, true, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int paged_attn_decode_q8_append(void* out, float* lse, const void* q, void* k_codes, void* v_codes,
+                                           float* k_scale, float* v_scale, const void* k_new, const void* v_new,
+                                           const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,
+                                           int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks, int32_t n_q,
+                                           int32_t n_kv, int32_t head_dim, int32_t block_size, float scale,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size, table_stride, PKV_BF16,
+                         scale);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_codes || !v_codes || !k_scale || !v_scale || !k_new || !v_new || !block_table || !seq_lens)
+        return PKV_ERR_NULL_POINTER;
+    if (!pkv::decode_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs)) return PKV_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new) ||
+        (reinterpret_cast<uintptr_t>(k_codes) & 7) || (reinterpret_cast<uintptr_t>(v_codes) & 7))
+        return PKV_ERR_INVALID_ARGUMENT;
+    pkv::AttnArgs a{};
+    a.waves = balanced_waves(n_q, n_kv, num_seqs, kDecodeInt8);
+    if (a.waves < 1) return PKV_ERR_HIP;
+    // folded while segments <= waves / 2, as for bf16 (paged_attn_decode_append)
+    if (2LL * num_seqs * n_kv <= a.waves) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_app = k_codes;
+        a.v_app = v_codes;
+        a.ks_app = k_scale;
+        a.vs_app = v_scale;
+    } else {
+        const hipError_t e = pkv::launch_kv_append_q8_last(
+            static_cast<int8_t*>(k_codes), static_cast<int8_t*>(v_codes), k_scale, v_scale, k_new, v_new, block_table,
+            table_stride, seq_lens, num_seqs, max_seq_len, num_blocks, n_kv, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return PKV_ERR_HIP;
+    }
     a.q = q;
     a.q_start = nullptr;
     a.k_cache = k_codes;

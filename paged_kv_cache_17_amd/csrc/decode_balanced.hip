@@ -62,6 +62,7 @@ struct ValuRows {
     static constexpr int kWaves = G == 8 ? 1 : 2;   // waves per SIMD the registers allow
     static constexpr int kWavesPerCU = 0;           // waves per CU launched (0: all that fit)
     static constexpr int kRingBytes = 0;            // LDS a wave stages tiles in (none)
+    static constexpr bool kCodes = false;           // pool of 8-bit codes + scales
     // One query per sequence: the G heads of kv head g.
     __device__ __forceinline__ static void fetch_q(u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g, int lane) {
         const uint16_t* q_sg = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(s) * a.n_q + g * G) * kTileD;
@@ -99,6 +100,7 @@ struct MfmaRows {
     static constexpr int kWaves = 2;
     static constexpr int kWavesPerCU = 0;
     static constexpr int kRingBytes = 0;
+    static constexpr bool kCodes = false;
     // Segment (s, g)'s first query row and number of queries.
     __device__ __forceinline__ static int queries(const AttnArgs& a, int s, int& row0) {
         row0 = s;
@@ -170,6 +172,7 @@ struct Int8Kv : ValuRows<G> {
     // one or two query heads per kv head, whose registers would otherwise
     // spill)
     static constexpr int kDepth = G <= 2 ? 2 : 3;
+    static constexpr bool kCodes = true;
     struct Regs {
         u32x2 k[4], v[4];
         float sk[4], sv[4];   // tokens 4i + r
@@ -281,6 +284,7 @@ struct Bf16Kv<4> : Bf16Mfma<4, 1> {
 struct Int8Ring : MfmaRows<4, 1> {
     static constexpr int kDepth = 2;
     static constexpr int kWavesPerCU = 8;
+    static constexpr bool kCodes = true;
     static constexpr int kSlot = 2 * kTileElems + 2 * kTileB * 4;
     static constexpr int kRingBytes = kDepth * kSlot;
     static constexpr int kLoads = 5;   // vector memory operations issued per tile
@@ -484,17 +488,46 @@ void decode_balanced_kernel(AttnArgs a) {
     // Folded append (decode step stage 1): the new token of segment seg
     // (sequence seg / n_kv, kv head seg % n_kv) sits at row `slot` of the
     // segment's last tile, which only this wave reads. Lanes 0..15 write
-    // its K row, 16..31 its V row, just before the tile's loads are issued:
-    // one wave's accesses to one address are performed in order, so those
-    // loads return the new row without waiting for the stores to complete.
+    // its K row, 16..31 its V row (dims 8c .. 8c + 7, c = lane % 16), just
+    // before the tile's loads are issued: one wave's accesses to one
+    // address are performed in order, so those loads return the new row
+    // without waiting for the stores to complete. An 8-bit pool takes the
+    // row quantised as kv_append_q8 does (chapter 5 section 4: absmax over
+    // the row, s = max(absmax, 1e-8) / 127, code = clamp(rint(x / s),
+    // -127, 127), fp32, correctly rounded division).
     auto append_row = [&](int tile, int seg, int slot) {
         if (lane < 32) {
             const bool isv = lane >= 16;
             const int c = lane & 15;
             const uint16_t* src = static_cast<const uint16_t*>(isv ? a.v_new : a.k_new);
-            uint16_t* dst = static_cast<uint16_t*>(isv ? a.v_app : a.k_app);
             const u32x4 x = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(seg) * kTileD + 8 * c);
-            *reinterpret_cast<u32x4*>(dst + (static_cast<size_t>(tile) * kTileB + slot) * kTileD + 8 * c) = x;
+            const size_t row = static_cast<size_t>(tile) * kTileB + slot;
+            if constexpr (Kv::kCodes) {
+                float f[8];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    f[2 * w] = __uint_as_float(static_cast<uint32_t>(x[w]) << 16);
+                    f[2 * w + 1] = __uint_as_float(static_cast<uint32_t>(x[w]) & 0xffff0000u);
+                }
+                float amax = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+                const float sc = fmaxf(amax, 1e-8f) / 127.0f;
+                uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float q = fminf(fmaxf(rintf(f[e] / sc), -127.0f), 127.0f);
+                    packed[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xffu) << (8 * (e & 3));
+                }
+                int8_t* dst = static_cast<int8_t*>(isv ? a.v_app : a.k_app);
+                *reinterpret_cast<u32x2*>(dst + row * kTileD + 8 * c) = u32x2{packed[0], packed[1]};
+                if (c == 0) (isv ? a.vs_app : a.ks_app)[row] = sc;
+            } else {
+                uint16_t* dst = static_cast<uint16_t*>(isv ? a.v_app : a.k_app);
+                *reinterpret_cast<u32x4*>(dst + row * kTileD + 8 * c) = x;
+            }
         }
     };
     auto issue = [&](int j, Buf& bj) {
@@ -637,8 +670,18 @@ int decode_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv) {
 }
 
 hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
+    if (a.k_new && a.k_scale) {   // 8-bit pool with the append folded in
+        if (!a.v_new || !a.k_app || !a.v_app || !a.ks_app || !a.vs_app) return hipErrorInvalidValue;
+        switch (a.n_q / a.n_kv) {
+            case 1: return launch_g<1, Int8Kv<1>, true>(a, stream, ev);
+            case 2: return launch_g<2, Int8Kv<2>, true>(a, stream, ev);
+            case 4: return launch_g<4, Int8Kv<4>, true>(a, stream, ev);
+            case 8: return launch_g<8, Int8Kv<8>, true>(a, stream, ev);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (a.k_new) {   // bf16 with the append folded in
-        if (a.k_scale || !a.v_new || !a.k_app || !a.v_app) return hipErrorInvalidValue;
+        if (!a.v_new || !a.k_app || !a.v_app) return hipErrorInvalidValue;
         switch (a.n_q / a.n_kv) {
             case 1: return launch_g<1, Bf16Kv<1>, true>(a, stream, ev);
             case 2: return launch_g<2, Bf16Kv<2>, true>(a, stream, ev);

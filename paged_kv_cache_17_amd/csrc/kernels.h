@@ -37,14 +37,17 @@ struct AttnArgs {
     PartialML* ws_ml;            // same slots as ws_o, without the head_dim axis
     int waves;                   // balanced decode: grid size W (0 = fixed split)
     int* prefix;                 // balanced decode: [S+1] block-count prefix sums
-    // Balanced bf16 decode with the append folded in (else all null): the
-    // new token of each sequence ([num_seqs][n_kv][head_dim]) is written to
-    // position seq_lens[s] - 1 of k_app / v_app (the same pools as
-    // k_cache / v_cache) before that tile is read.
+    // Balanced decode with the append folded in (else all null): the new
+    // token of each sequence (bf16 [num_seqs][n_kv][head_dim]) is written
+    // to position seq_lens[s] - 1 of k_app / v_app (the same pools as
+    // k_cache / v_cache; 8-bit pools: quantised, scales to ks_app / vs_app)
+    // before that tile is read.
     const void* k_new;
     const void* v_new;
     void* k_app;
     void* v_app;
+    float* ks_app;               // 8-bit pools: where the appended rows' scales go (k_scale / v_scale)
+    float* vs_app;
 };
 
 // Optional event pair recorded by the kernel's own dispatch (start and end
@@ -65,6 +68,12 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, con
 hipError_t launch_kv_append_last(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                                  const int32_t* table, int table_stride, const int32_t* seq_lens, int num_seqs,
                                  int max_seq_len, int num_blocks, int n_kv, hipStream_t stream);
+
+// The same for an 8-bit pool (bf16 input, quantised as kv_append_q8 does).
+hipError_t launch_kv_append_q8_last(int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale,
+                                    const void* k_new, const void* v_new, const int32_t* table, int table_stride,
+                                    const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_blocks, int n_kv,
+                                    hipStream_t stream);
 
 // Quantising append (8-bit codes + one fp32 scale per token and kv head).
 hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,

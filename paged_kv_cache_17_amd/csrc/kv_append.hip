@@ -143,6 +143,44 @@ __global__ __launch_bounds__(256) void kv_append_last_kernel(uint4* __restrict__
     vc[dst] = vn[src];
 }
 
+// The decode step's append into an 8-bit pool: one wave per (sequence, kv
+// head) row of K or of V at position seq_lens[s] - 1, bf16 input, quantised
+// exactly as kv_append_q8_kernel does; the same tokens as the decode pass
+// with the append folded in (head_dim 128, block_size 16).
+__global__ __launch_bounds__(256) void kv_append_q8_last_kernel(int8_t* __restrict__ kc, int8_t* __restrict__ vc,
+                                                                float* __restrict__ ks, float* __restrict__ vs,
+                                                                const uint16_t* __restrict__ kn,
+                                                                const uint16_t* __restrict__ vn,
+                                                                const int32_t* __restrict__ table, int table_stride,
+                                                                const int32_t* __restrict__ seq_lens, int num_seqs,
+                                                                int max_seq_len, int num_blocks, int n_kv) {
+    constexpr int kD = 128, kBS = 16;
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long row = static_cast<long long>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (row >= 2LL * num_seqs * n_kv) return;                 // whole wave exits together
+    const bool is_v = row & 1;
+    const long long th = row >> 1;
+    const int h = static_cast<int>(th % n_kv);
+    const int s = static_cast<int>(th / n_kv);
+    const int L = seq_lens[s];
+    if (!seq_len_ok(L, 1, max_seq_len, table_stride * kBS)) return;
+    const int pos = L - 1;
+    const int blk = table[static_cast<size_t>(s) * table_stride + pos / kBS];
+    if (blk < 0 || blk >= num_blocks) return;
+    const uint16_t* src = (is_v ? vn : kn) + static_cast<size_t>(th) * kD;
+    float amax = 0.0f;
+    for (int e = lane; e < kD; e += kWave) amax = fmaxf(amax, fabsf(Elem<uint16_t>::load(src + e)));
+    amax = wave_max(amax);
+    const float scale = fmaxf(amax, 1e-8f) / 127.0f;
+    const size_t slot = (static_cast<size_t>(blk) * n_kv + h) * kBS + pos % kBS;
+    int8_t* dst = (is_v ? vc : kc) + slot * kD;
+    for (int e = lane; e < kD; e += kWave) {
+        const float c = fminf(fmaxf(rintf(Elem<uint16_t>::load(src + e) / scale), -127.0f), 127.0f);
+        dst[e] = static_cast<int8_t>(c);
+    }
+    if (lane == 0) (is_v ? vs : ks)[slot] = scale;
+}
+
 }  // namespace
 
 hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,
@@ -188,6 +226,18 @@ hipError_t launch_kv_append_last(void* k_cache, void* v_cache, const void* k_new
     hipLaunchKernelGGL(kv_append_last_kernel, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, stream,
                        static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), static_cast<const uint4*>(k_new),
                        static_cast<const uint4*>(v_new), table, table_stride, seq_lens, num_seqs, max_seq_len,
+                       num_blocks, n_kv);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append_q8_last(int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale,
+                                    const void* k_new, const void* v_new, const int32_t* table, int table_stride,
+                                    const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_blocks, int n_kv,
+                                    hipStream_t stream) {
+    const long long rows = 2LL * num_seqs * n_kv;            // one wave per row, 4 waves per workgroup
+    hipLaunchKernelGGL(kv_append_q8_last_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream,
+                       k_codes, v_codes, k_scale, v_scale, static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), table, table_stride, seq_lens, num_seqs, max_seq_len,
                        num_blocks, n_kv);
     return hipGetLastError();
 }

@@ -32,12 +32,14 @@ def say(*a):
     print(*a, flush=True)
 
 
-def _history_only_cache(wl):
+def _history_only_cache(wl, quantized=False):
     """The cache as it stands before the step: history appended, tables
-    already covering the new token (kvpool_ensure), new slots still NaN."""
+    already covering the new token (kvpool_ensure), new slots still NaN
+    (8-bit: poison codes and scales)."""
     import paged_kv_cache_17_amd as pkv
     from gpu_harness import torch_dtype
-    c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size, torch_dtype(wl.dtype),
+    c = pkv.PagedKVCache(wl.num_blocks, wl.n_kv, wl.head_dim, wl.block_size,
+                         torch.int8 if quantized else torch_dtype(wl.dtype),
                          wl.num_seqs, wl.table_stride, alloc_order=wl.alloc_order, fill_nan=True,
                          poison_workspace=True)
     for s in range(wl.num_seqs):
@@ -150,3 +152,41 @@ def test_step_invalid_length_row_is_nan_others_unchanged(many):
     pos = int(wl.seq_lens[bad]) - 1
     blk = int(c.table[bad, pos // 16])
     assert torch.isnan(c.k_cache[blk, :, pos % 16].float()).all()
+
+
+# --------------------------------------------------------------- 8-bit pool ---
+
+
+def _check_step_q8(wl, where):
+    """8-bit pool: codes and scales bit-identical to kv_append_q8 of the new
+    tokens (the oracle pins kv_append_q8's codes in test_gpu_quant), and the
+    rows bit-identical to paged_attn_decode_q8 after it."""
+    c = _history_only_cache(wl, quantized=True)
+    out, lse = _step(c, wl)
+    c2 = build_gpu_cache(wl, quantized=True)
+    out2, lse2 = run_decode(c2, wl)
+    assert np.array_equal(c.table, c2.table)
+    assert torch.equal(c.k_cache, c2.k_cache) and torch.equal(c.v_cache, c2.v_cache), "codes differ"
+    assert np.array_equal(c.k_scale.cpu().numpy().view(np.uint32), c2.k_scale.cpu().numpy().view(np.uint32))
+    assert np.array_equal(c.v_scale.cpu().numpy().view(np.uint32), c2.v_scale.cpu().numpy().view(np.uint32))
+    assert torch.equal(out, out2), "not bit-identical to kv_append_q8 + paged_attn_decode_q8"
+    assert torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (64, 8)])
+def test_step_q8_ragged_lengths(n_q, n_kv):
+    L = np.array(RAGGED)
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=33)
+    say("8-bit decode step", n_q, n_kv)
+    _check_step_q8(wl, f"8-bit decode step {n_q}/{n_kv}")
+
+
+def test_step_q8_many_short_sequences():
+    """5600 segments, more than the pass's waves: the append runs as its own
+    launch inside the call."""
+    L = np.random.default_rng(45).integers(1, 301, size=700)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=45)
+    say("8-bit decode step, 700 short sequences")
+    _check_step_q8(wl, "8-bit decode step 700")
