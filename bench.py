@@ -343,7 +343,8 @@ def bench_verify(args):
     512..4096 after the append, gamma = 4): append the 5 tokens of every
     sequence (the pending token and 4 drafts; re-appending the same tokens
     is idempotent) and verify them with one causal chunk of 5 queries per
-    sequence. Timed with the library's choice (the balanced partition over
+    sequence, in one paged_attn_chunk_append call (``--separate``: kv_append,
+    then paged_attn_chunk). Timed with the library's choice (the balanced partition over
     every (sequence, kv head, block) tile with the 20 (query, head) rows of a
     kv head on the matrix cores, then the merge) and with the VALU split path
     (split_tokens 256) beside it. The pass reads each sequence's K/V once:
@@ -370,10 +371,19 @@ def bench_verify(args):
         def step(i, ev=None):
             g = gpus[i % len(gpus)]
             k, v, _ = g.cyc[0]
-            g.c.append(k, v, i32_lens[i % len(gpus)], g.q_start, stream=stream)
             if ev is not None:
                 pkv.pkv_set_profile_events(*ev)
-            g.verify(0, split_tokens=split, stream=stream)
+            lens_d = i32_after[i % len(gpus)]   # device copies made once, outside the timed steps
+            if args.separate:
+                pkv.pkv_set_profile_events(None, None)
+                g.c.append(k, v, i32_lens[i % len(gpus)], g.q_start, stream=stream)
+                if ev is not None:
+                    pkv.pkv_set_profile_events(*ev)
+                g.c.chunk(g.cyc[0][2], g.q_start, lens_d, g1, max_after, sw.scale, split_tokens=split,
+                          stream=stream)
+            else:   # one call: the append, then the chunk pass
+                g.c.chunk_step(g.cyc[0][2], g.q_start, k, v, lens_d, g1, max_after, sw.scale,
+                               split_tokens=split, stream=stream)
             pkv.pkv_set_profile_events(None, None)
 
         for i in range(args.warmup):
@@ -402,6 +412,8 @@ def bench_verify(args):
 
     from gpu_harness import i32
     i32_lens = [i32(g.lens) for g in gpus]
+    i32_after = [i32(g.lens + g1) for g in gpus]
+    max_after = int(max((g.lens + g1).max() for g in gpus))
     ms_m, kern_m = run(0)
     ms_v, _ = run(256)
     tokens = sw.num_seqs * g1

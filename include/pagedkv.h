@@ -368,6 +368,32 @@ int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_star
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * paged_attn_chunk_append - a chunk step in one call: each sequence's C_s
+ * new tokens (rows q_start[s] .. q_start[s+1]-1 of k_new / v_new, the last
+ * C_s of its seq_lens[s] keys) are appended to the pool, then the chunk
+ * attends as paged_attn_chunk.
+ *
+ * Source: the lab page's prefill branch and forward on a prompt chunk at
+ * offset start (write the chunk's K/V, then attend causally over the cache
+ * including it); chapter 5 section 5 (a verification pass appends the
+ * drafts and attends them as one chunk). Same result as kv_append of the
+ * chunk at start_pos = seq_lens - C_s followed by paged_attn_chunk, without
+ * the caller building start_pos / new_start: the append is launched first
+ * inside the call, with positions taken from seq_lens and q_start.
+ *
+ * k_new, v_new: device, [total_q][n_kv][head_dim] of dtype. A sequence that
+ *   the chunk pass rejects (seq_lens[s] < C_s, out of range) gets no
+ *   append; a token whose table entry is outside the pool is not written.
+ * Other arguments, workspace and errors as paged_attn_chunk. */
+int paged_attn_chunk_append(void* out, float* lse, const void* q, const int32_t* q_start,
+                            void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                            int32_t num_blocks, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                            int32_t block_size, float scale, int32_t dtype, int32_t split_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * 8-bit K/V (quantised cache).
  *
  * Source: chapter 5 section 4 (post-training quantisation, symmetric

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     kv_copy_blocks,
     load_library,
     paged_attn_chunk,
+    paged_attn_chunk_append,
     paged_attn_chunk_workspace_size,
     paged_attn_decode,
     paged_attn_decode_append, paged_attn_decode_q8_append, paged_attn_decode_q8,

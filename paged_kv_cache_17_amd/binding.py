@@ -64,6 +64,9 @@ _SIGNATURES = {
                                   _i32, ctypes.c_float, _i32, _p, _size_t, _p], ctypes.c_int),
     "paged_attn_decode_q8_append": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, ctypes.c_float, _p, _size_t, _p], ctypes.c_int),
+    "paged_attn_chunk_append": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _p, _size_t, _p],
+                                ctypes.c_int),
     "paged_attn_chunk": ([_p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, ctypes.c_float, _i32, _i32, _p, _size_t, _p], ctypes.c_int),
     "pkv_set_profile_events": ([_p, _p], ctypes.c_int),
@@ -362,6 +365,23 @@ def paged_attn_chunk(out, lse, q, q_start, k_cache, v_cache, block_table, seq_le
         _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         int(block_table.shape[1]), _ptr(seq_lens), int(seq_lens.shape[0]), int(total_q), int(max_q_len),
         int(max_seq_len), int(num_blocks), int(n_q), int(n_kv), int(d), int(bs), float(scale),
+        _dtype_code(k_cache), int(split_tokens),
+        _ptr(workspace) if workspace is not None else None,
+        int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
+        _stream(stream)))
+
+
+def paged_attn_chunk_append(out, lse, q, q_start, k_cache, v_cache, k_new, v_new, block_table, seq_lens,
+                            max_q_len, max_seq_len, scale, workspace, split_tokens=0, stream=None):
+    """Chunk step in one call: append ``k_new``/``v_new`` ``[sum C, n_kv, d]`` as the last C_s keys of
+    each sequence, then chunk attention as :func:`paged_attn_chunk`."""
+    _dev(out, lse, q, q_start, k_cache, v_cache, k_new, v_new, block_table, seq_lens, workspace)
+    num_blocks, n_kv, bs, d = k_cache.shape
+    total_q, n_q, _ = q.shape
+    _check("paged_attn_chunk_append", load_library().paged_attn_chunk_append(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(seq_lens.shape[0]), int(total_q),
+        int(max_q_len), int(max_seq_len), int(num_blocks), int(n_q), int(n_kv), int(d), int(bs), float(scale),
         _dtype_code(k_cache), int(split_tokens),
         _ptr(workspace) if workspace is not None else None,
         int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,

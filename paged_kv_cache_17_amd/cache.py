@@ -146,3 +146,18 @@ class PagedKVCache:
         B.paged_attn_chunk(out, lse, q, q_start, self.k_cache, self.v_cache, self.table_dev, seq_lens,
                            max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
         return out
+
+    def chunk_step(self, q, q_start, k_new, v_new, seq_lens, max_q_len: int, max_seq_len: int, scale: float,
+                   out=None, lse=None, split_tokens: int = 0, stream=None):
+        """Append each sequence's chunk (``k_new``/``v_new`` ``[sum C, n_kv, d]``, the last C_s of
+        ``seq_lens``) and attend it, in one call."""
+        if out is None:
+            out = torch.empty_like(q)
+        if self.quantized:
+            raise NotImplementedError("chunk attention over an 8-bit cache is not provided")
+        ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
+                            chunk=(q_start.shape[0] - 1, max_q_len))
+        B.paged_attn_chunk_append(out, lse, q, q_start, self.k_cache, self.v_cache, k_new, v_new, self.table_dev,
+                                  seq_lens, max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens,
+                                  stream=stream)
+        return out

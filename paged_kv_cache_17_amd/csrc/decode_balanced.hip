@@ -701,6 +701,7 @@ bool chunk_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, i
 int chunk_balanced_waves(int n_q, int n_kv, int num_seqs) { return waves_for<ChunkKv>(n_q, n_kv, num_seqs); }
 
 hipError_t launch_chunk_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
+    if (a.k_new) return hipErrorInvalidValue;   // chunk appends are launched on their own
     return launch_kv<ChunkKv>(a, stream, ev);
 }
 

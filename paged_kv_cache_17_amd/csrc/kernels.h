@@ -58,10 +58,14 @@ struct KernelEvents {
     bool on() const { return start || stop; }
 };
 
+// start_pos null: a chunk step, whose sequence s's new tokens are the last
+// new_start[s+1] - new_start[s] of seq_lens[s] keys (sequences the chunk
+// pass rejects get no write).
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* table, int table_stride, const int32_t* start_pos,
                             const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
-                            int n_kv, int row_bytes, int block_size, hipStream_t stream);
+                            int n_kv, int row_bytes, int block_size, hipStream_t stream,
+                            const int32_t* seq_lens = nullptr, int max_seq_len = 0);
 
 // The decode step's append on its own: one token per sequence at position
 // seq_lens[s] - 1 (bf16, head_dim 128, block_size 16; 16-byte aligned).

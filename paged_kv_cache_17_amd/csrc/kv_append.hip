@@ -27,7 +27,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const char* __restrict__ kn, const char* __restrict__ vn,
     const int32_t* __restrict__ table, int table_stride,
     const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start,
-    int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs) {
+    int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs,
+    const int32_t* __restrict__ seq_lens, int max_seq_len) {
     using P = typename Piece<UNIT>::T;
     __shared__ int s_start[kStagedSeqs + 1];
     const bool staged = num_seqs <= kStagedSeqs;
@@ -43,7 +44,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int t = static_cast<int>(th / n_kv);
     const int32_t* starts = staged ? s_start : new_start;
     const int s = seq_of_row(starts, num_seqs, t);
-    const int pos = start_pos[s] + (t - starts[s]);
+    int first = 0;   // position of sequence s's first new token
+    if (start_pos) {
+        first = start_pos[s];
+    } else {         // chunk step: the chunk's C tokens are the last C of seq_lens[s]
+        const int C = starts[s + 1] - starts[s];
+        const int L = seq_lens[s];
+        if (!seq_len_ok(L, C, max_seq_len, table_stride * bs)) return;
+        first = L - C;
+    }
+    const int pos = first + (t - starts[s]);
     if (pos < 0 || pos / bs >= table_stride) return;
     const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
     if (blk < 0 || blk >= num_blocks) return;   // unmapped slot: nothing is written
@@ -58,14 +68,14 @@ template <int UNIT>
 hipError_t launch_unit(void* kc, void* vc, const void* kn, const void* vn, const int32_t* table,
                        int table_stride, const int32_t* start_pos, const int32_t* new_start,
                        int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs,
-                       hipStream_t stream) {
+                       hipStream_t stream, const int32_t* seq_lens = nullptr, int max_seq_len = 0) {
     const long long work = static_cast<long long>(total_new) * n_kv * (row_bytes / UNIT);
     const unsigned grid = static_cast<unsigned>((work + 255) / 256);
     hipLaunchKernelGGL(kv_append_kernel<UNIT>, dim3(grid), dim3(256), 0, stream,
                        static_cast<char*>(kc), static_cast<char*>(vc),
                        static_cast<const char*>(kn), static_cast<const char*>(vn), table,
                        table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
-                       row_bytes, bs);
+                       row_bytes, bs, seq_lens, max_seq_len);
     return hipGetLastError();
 }
 
@@ -205,13 +215,14 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
 hipError_t launch_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                             const int32_t* table, int table_stride, const int32_t* start_pos,
                             const int32_t* new_start, int num_seqs, int total_new, int num_blocks,
-                            int n_kv, int row_bytes, int block_size, hipStream_t stream) {
+                            int n_kv, int row_bytes, int block_size, hipStream_t stream,
+                            const int32_t* seq_lens, int max_seq_len) {
     const uintptr_t align = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
                             reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new);
 #define PKV_APPEND(U)                                                                          \
     return launch_unit<U>(k_cache, v_cache, k_new, v_new, table, table_stride, start_pos,      \
                           new_start, num_seqs, total_new, num_blocks, n_kv, row_bytes,         \
-                          block_size, stream)
+                          block_size, stream, seq_lens, max_seq_len)
     if (row_bytes % 16 == 0 && align % 16 == 0) PKV_APPEND(16);
     if (row_bytes % 8 == 0 && align % 8 == 0) PKV_APPEND(8);
     if (row_bytes % 4 == 0 && align % 4 == 0) PKV_APPEND(4);

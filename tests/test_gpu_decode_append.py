@@ -190,3 +190,63 @@ def test_step_q8_many_short_sequences():
                         new_lens=np.ones_like(L), seed=45)
     say("8-bit decode step, 700 short sequences")
     _check_step_q8(wl, "8-bit decode step 700")
+
+
+# ------------------------------------------------------------ chunk steps ---
+
+
+def _check_chunk_step(wl, where):
+    """paged_attn_chunk_append against kv_append + paged_attn_chunk: pool
+    bytes bit-exact against the oracle, rows within the bar and
+    bit-identical to the two-call path."""
+    from gpu_harness import run_chunk
+    c = _history_only_cache(wl)
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.chunk_step(q, i32(wl.q_offsets), raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype),
+                       i32(wl.seq_lens), wl.max_new, wl.max_seq_len, wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    ora = oracle.build_cache(wl)
+    assert np.array_equal(c.table, ora.tables())
+    assert np.array_equal(torch_to_raw(c.k_cache, wl.dtype).view(np.uint8), ora.pool_k.view(np.uint8))
+    assert np.array_equal(torch_to_raw(c.v_cache, wl.dtype).view(np.uint8), ora.pool_v.view(np.uint8))
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    check_rows(out_f64(out, wl.dtype), ref, wl.dtype, where)
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, wl.dtype, where)
+    c2 = build_gpu_cache(wl)
+    out2, lse2 = run_chunk(c2, wl)
+    assert torch.equal(out, out2), "not bit-identical to kv_append + paged_attn_chunk"
+    assert torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 8)])
+def test_chunk_step_verify_sized(n_q, n_kv):
+    """5 new tokens per sequence (a verification pass), lengths that put the
+    chunk across a block boundary or fill a block: the balanced small-chunk
+    pass after the call's own append."""
+    L = np.array([5, 6, 16, 17, 20, 21, 33, 300, 1000, 2051])
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 5,
+                        new_lens=np.full_like(L, 5), seed=51)
+    say("chunk step, 5 tokens", n_q, n_kv)
+    _check_chunk_step(wl, f"chunk step {n_q}/{n_kv}")
+
+
+def test_chunk_step_many_sequences():
+    """200 sequences x 8 kv heads on the balanced small-chunk pass."""
+    L = np.random.default_rng(53).integers(5, 400, size=200)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 5,
+                        new_lens=np.full_like(L, 5), seed=53)
+    say("chunk step, 200 sequences")
+    _check_chunk_step(wl, "chunk step 200")
+
+
+def test_chunk_step_large_chunks_and_decode_rows():
+    """Chunks of 40 (the matrix-core chunk kernel) beside 1-token rows: the
+    append launched first, then that kernel."""
+    L = np.array([40, 57, 300, 1, 90])
+    C = np.array([40, 40, 40, 1, 1])
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - C,
+                        new_lens=C, seed=55)
+    say("chunk step, chunks of 40")
+    _check_chunk_step(wl, "chunk step 40")
