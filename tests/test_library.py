@@ -213,3 +213,41 @@ def test_sampling_workspace_and_argument_errors():
     assert _call_sample(ws_bytes=4 * (3 * (16384 + 16) + row) - 1) == -6
     assert _call_sample(ws=260) == -2                 # workspace not 8-byte aligned
     assert _call_sample(rows=0) == 0
+
+
+def test_one_call_steps_reject_bad_arguments_before_any_launch():
+    """paged_attn_decode_append / paged_attn_decode_q8_append /
+    paged_attn_chunk_append: shape, null-pointer, support and alignment
+    errors come back before any device call (the dummy pointers are never
+    used)."""
+    lib = pkv.load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
+
+    def dec(out=16, q=16, kn=16, vn=16, n_q=32, n_kv=8, d=128, bs=16, dtype=1, S=2):
+        return lib.paged_attn_decode_append(p(out), None, p(q), p(16), p(16), p(kn), p(vn), p(16), 4, p(16), S, 64,
+                                            8, n_q, n_kv, d, bs, 0.25, dtype, p(256), 1 << 20, None)
+
+    assert dec(n_q=3, n_kv=2) == -2                   # n_q not a multiple of n_kv
+    assert dec(dtype=7) == -2
+    assert dec(out=0) == -1 and dec(kn=0) == -1 and dec(vn=0) == -1
+    assert dec(dtype=0, d=16) == -3                   # fp32 / other shapes: kv_append + paged_attn_decode
+    assert dec(bs=8) == -3
+    assert dec(q=1) == -3                             # not 16-byte aligned
+    assert dec(S=0) == 0
+
+    def q8(q=16, kn=16, kc=16, d=128):
+        return lib.paged_attn_decode_q8_append(None if q == 0 else p(16), None, p(q), p(kc), p(16), p(16), p(16),
+                                               p(kn), p(16), p(16), 4, p(16), 2, 64, 8, 32, 8, d, 16, 0.25, p(256),
+                                               1 << 20, None)
+
+    assert q8(kn=0) == -1
+    assert q8(d=64) == -3
+    assert q8(q=1) == -2                              # q not 16-byte aligned
+    assert q8(kc=20) == -2                            # codes not 8-byte aligned
+
+    def chunk(kn=16, total_q=5, S=1):
+        return lib.paged_attn_chunk_append(p(16), None, p(16), p(16), p(16), p(16), p(kn), p(16), p(16), 4, p(16),
+                                           S, total_q, 5, 64, 8, 32, 8, 128, 16, 0.25, 1, 0, p(256), 1 << 20, None)
+
+    assert chunk(kn=0) == -1
+    assert chunk(total_q=0) == 0
