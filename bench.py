@@ -30,7 +30,6 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "decode tokens/s and achieved KV-read HBM GB/s (% of peak), paged attention, 1 GPU"
 PEAK_HBM_GBPS = 8000.0
@@ -192,7 +191,7 @@ def bench_bestof(args):
     last-level cache at the next."""
     import torch
     import paged_kv_cache_17_amd as pkv
-    from gpu_harness import build_gpu_fork_cache, i32, raw_to_torch
+    from paged_kv_cache_17_amd.replay import build_gpu_fork_cache, i32, raw_to_torch
     from workloads import best_of_n_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -351,7 +350,7 @@ def bench_verify(args):
     the roofline is HBM; avg_launch_ms is the split pass alone."""
     import torch
     import paged_kv_cache_17_amd as pkv
-    from gpu_harness import GpuSpec
+    from paged_kv_cache_17_amd.replay import GpuSpec
     from workloads import verify_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -410,7 +409,7 @@ def bench_verify(args):
             kern = float(np.mean([b.elapsed_time(a) for b, a in evs]))
         return ms, kern
 
-    from gpu_harness import i32
+    from paged_kv_cache_17_amd.replay import i32
     i32_lens = [i32(g.lens) for g in gpus]
     i32_after = [i32(g.lens + g1) for g in gpus]
     max_after = int(max((g.lens + g1).max() for g in gpus))
@@ -456,7 +455,7 @@ def main():
 
     import torch
     import paged_kv_cache_17_amd as pkv
-    from gpu_harness import build_gpu_cache, i32, raw_to_torch
+    from paged_kv_cache_17_amd.replay import build_gpu_cache, i32, raw_to_torch
     from workloads import CONFIG_NAMES, config_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"

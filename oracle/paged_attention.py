@@ -266,29 +266,33 @@ def block_alloc_slots(lengths, block_size: int):
 # --------------------------------------------------------------------------
 
 
+def token_slots(blocks, positions, block_size: int):
+    """(block id, slot) of each position through a table row: position ``p``
+    lives in slot ``p % B`` of block ``blocks[p // B]`` (lab page, the
+    ``KVPool`` class: the rule its write and gather both follow)."""
+    positions = np.asarray(positions, dtype=np.int64)
+    row = np.asarray(blocks, dtype=np.int64)
+    return row[positions // block_size], positions % block_size
+
+
 def append(pool_k, pool_v, blocks, start: int, k_new, v_new, block_size: int) -> None:
     """Write tokens ``start .. start+T-1`` into the pool through a table row.
 
     ``pool_*`` are ``[num_blocks, n_kv, B, d]`` raw arrays; ``k_new``/``v_new``
-    are ``[T, n_kv, d]``. Token at position ``p`` lands in block
-    ``blocks[p // B]``, slot ``p % B``, for every kv head (lab page,
-    ``KVPool.write``). Nothing else in the pool changes.
+    are ``[T, n_kv, d]``. Every kv head of a token goes to the token's slot
+    (``token_slots``). Nothing else in the pool changes.
     """
-    for i in range(len(k_new)):
-        p = start + i
-        blk = blocks[p // block_size]
-        pool_k[blk, :, p % block_size, :] = k_new[i]
-        pool_v[blk, :, p % block_size, :] = v_new[i]
+    blk, slot = token_slots(blocks, start + np.arange(len(k_new)), block_size)
+    pool_k[blk, :, slot, :] = k_new
+    pool_v[blk, :, slot, :] = v_new
 
 
 def gather(pool, blocks, length: int, block_size: int) -> np.ndarray:
-    """A sequence's cache as ``[n_kv, L, d]``: its blocks concatenated along
-    the token axis, truncated to ``L`` (lab page, ``KVPool.gather``)."""
-    n_kv, d = pool.shape[1], pool.shape[3]
-    if length == 0:
-        return np.zeros((n_kv, 0, d), dtype=pool.dtype)
-    nb = -(-length // block_size)
-    return np.concatenate([pool[blocks[i]] for i in range(nb)], axis=1)[:, :length]
+    """A sequence's cache as ``[n_kv, L, d]``: for each position 0..L-1 the
+    row held in its slot (lab page, ``KVPool.gather``: the sequence's blocks
+    read in table order, cut to its length)."""
+    blk, slot = token_slots(blocks, np.arange(length), block_size)
+    return pool[blk, :, slot, :].transpose(1, 0, 2)
 
 
 # --------------------------------------------------------------------------
@@ -318,17 +322,18 @@ def attention(q, K, V, scale: float, q_pos):
     if n_q % n_kv:
         raise ValueError("n_q must be a multiple of n_kv")
     group = n_q // n_kv
-    kv_of_head = np.arange(n_q) // group
-    Kh = K[kv_of_head]                                  # [n_q, L, d]
-    Vh = V[kv_of_head]
-    scores = np.einsum("thd,hjd->htj", q, Kh) * scale   # [n_q, T, L]
-    allow = np.arange(L)[None, :] <= np.asarray(q_pos)[:, None]   # [T, L]
+    # heads g*group .. g*group + group - 1 read kv head g: one product per kv head
+    qg = q.reshape(T, n_kv, group, d).transpose(1, 2, 0, 3)          # [n_kv, group, T, d]
+    scores = np.matmul(qg, K.transpose(0, 2, 1)[:, None]) * scale     # [n_kv, group, T, L]
+    scores = scores.reshape(n_q, T, L)
+    allow = np.arange(L)[None, :] <= np.asarray(q_pos)[:, None]       # [T, L]
     scores = np.where(allow[None], scores, -np.inf)
     m = scores.max(axis=-1, keepdims=True)
     e = np.exp(scores - m)
     z = e.sum(axis=-1, keepdims=True)
     p = e / z
-    out = np.einsum("htj,hjd->thd", p, Vh)
+    out = np.matmul(p.reshape(n_kv, group, T, L), V[:, None])         # [n_kv, group, T, d]
+    out = out.reshape(n_q, T, d).transpose(1, 0, 2)
     lse = (m[..., 0] + np.log(z[..., 0])).T             # [T, n_q]
     return out, lse, p
 
@@ -537,14 +542,11 @@ class QuantOracleCache(OracleCache):
         B = self.wl.block_size
         ck, sk = quantize_absmax(widen(k, self.wl.dtype))
         cv, sv = quantize_absmax(widen(v, self.wl.dtype))
-        blocks = self.seqs[s].blocks
-        for i in range(len(k)):
-            p = start + i
-            blk = blocks[p // B]
-            self.pool_k[blk, :, p % B, :] = ck[i]
-            self.pool_v[blk, :, p % B, :] = cv[i]
-            self.scale_k[blk, :, p % B] = sk[i]
-            self.scale_v[blk, :, p % B] = sv[i]
+        blk, slot = token_slots(self.seqs[s].blocks, start + np.arange(len(k)), B)
+        self.pool_k[blk, :, slot, :] = ck
+        self.pool_v[blk, :, slot, :] = cv
+        self.scale_k[blk, :, slot] = sk
+        self.scale_v[blk, :, slot] = sv
 
     def fill_history(self):
         wl = self.wl
@@ -567,9 +569,9 @@ class QuantOracleCache(OracleCache):
         blocks = self.seqs[s].blocks
         K = gather(self.pool_k, blocks, L, B)
         V = gather(self.pool_v, blocks, L, B)
-        nb = -(-L // B)
-        sk = np.concatenate([self.scale_k[blocks[i]] for i in range(nb)], axis=1)[:, :L]
-        sv = np.concatenate([self.scale_v[blocks[i]] for i in range(nb)], axis=1)[:, :L]
+        blk, slot = token_slots(blocks, np.arange(L), B)
+        sk = self.scale_k[blk, :, slot].T
+        sv = self.scale_v[blk, :, slot].T
         return dequantize(K, sk), dequantize(V, sv)
 
 

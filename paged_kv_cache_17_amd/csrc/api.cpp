@@ -128,14 +128,25 @@ int check_shape(int num_seqs, int max_seq_len, int num_blocks, int n_q, int n_kv
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decode, bool balanced,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (a.num_rows == 0) return PKV_OK;
+// The workspace checks of run_attention, on their own, so that entry points
+// that launch an append first can reject a bad workspace before it.
+int check_workspace(const pkv::AttnArgs& a, bool balanced, const void* workspace, size_t workspace_bytes,
+                    Layout* layout) {
     if (!workspace) return PKV_ERR_NULL_POINTER;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
     const Layout w = balanced ? ws_layout_balanced(a.num_seqs, a.n_q / a.n_kv, a.n_kv, a.head_dim, a.waves)
                               : ws_layout(a.num_rows, a.n_q, a.head_dim, a.max_splits);
     if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    if (layout) *layout = w;
+    return PKV_OK;
+}
+
+int run_attention(pkv::AttnArgs& a, void* out, float* lse, int dtype, bool decode, bool balanced,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (a.num_rows == 0) return PKV_OK;
+    Layout w;
+    const int rc = check_workspace(a, balanced, workspace, workspace_bytes, &w);
+    if (rc != PKV_OK) return rc;
     char* ws = static_cast<char*>(workspace);
     a.ws_ml = reinterpret_cast<pkv::PartialML*>(ws);
     a.ws_o = reinterpret_cast<float*>(ws + w.o_offset);
@@ -364,22 +375,6 @@ extern "C" int paged_attn_decode_append(void* out, float* lse, const void* q, vo
     a.q_start = nullptr;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
-    // The append rides in the split pass while the batch has at most half
-    // as many (sequence, kv head) segments as the pass has waves; with
-    // more, many waves append rows, each a dependent round trip under full
-    // load, and a launch of its own is faster (measured, bf16 and 8-bit:
-    // 64 x 8 and 8 x 8 segments folded win, 256 x 8 folded loses).
-    if (2LL * num_seqs * n_kv <= a.waves) {
-        a.k_new = k_new;
-        a.v_new = v_new;
-        a.k_app = k_cache;
-        a.v_app = v_cache;
-    } else {
-        const hipError_t e = pkv::launch_kv_append_last(k_cache, v_cache, k_new, v_new, block_table, table_stride,
-                                                        seq_lens, num_seqs, max_seq_len, num_blocks, n_kv,
-                                                        static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return PKV_ERR_HIP;
-    }
     a.table = block_table;
     a.seq_lens = seq_lens;
     a.table_stride = table_stride;
@@ -398,6 +393,25 @@ extern "C" int paged_attn_decode_append(void* out, float* lse, const void* q, vo
     a.split_tokens = split;
     a.max_splits = (max_seq_len + split - 1) / split;
     a.scale_log2 = scale * 1.44269504088896340736f;
+    // the workspace is checked before the append can write the pool
+    rc = check_workspace(a, true, workspace, workspace_bytes, nullptr);
+    if (rc != PKV_OK) return rc;
+    // The append rides in the split pass while the batch has at most half
+    // as many (sequence, kv head) segments as the pass has waves; with
+    // more, many waves append rows, each a dependent round trip under full
+    // load, and a launch of its own is faster (measured, bf16 and 8-bit:
+    // 64 x 8 and 8 x 8 segments folded win, 256 x 8 folded loses).
+    if (2LL * num_seqs * n_kv <= a.waves) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_app = k_cache;
+        a.v_app = v_cache;
+    } else {
+        const hipError_t e = pkv::launch_kv_append_last(k_cache, v_cache, k_new, v_new, block_table, table_stride,
+                                                        seq_lens, num_seqs, max_seq_len, num_blocks, n_kv,
+                                                        static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return PKV_ERR_HIP;
+    }
     return run_attention(a, out, lse, dtype, true, true, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }
@@ -485,20 +499,6 @@ extern "C" int paged_attn_decode_q8_append(void* out, float* lse, const void* q,
     pkv::AttnArgs a{};
     a.waves = balanced_waves(n_q, n_kv, num_seqs, kDecodeInt8);
     if (a.waves < 1) return PKV_ERR_HIP;
-    // folded while segments <= waves / 2, as for bf16 (paged_attn_decode_append)
-    if (2LL * num_seqs * n_kv <= a.waves) {
-        a.k_new = k_new;
-        a.v_new = v_new;
-        a.k_app = k_codes;
-        a.v_app = v_codes;
-        a.ks_app = k_scale;
-        a.vs_app = v_scale;
-    } else {
-        const hipError_t e = pkv::launch_kv_append_q8_last(
-            static_cast<int8_t*>(k_codes), static_cast<int8_t*>(v_codes), k_scale, v_scale, k_new, v_new, block_table,
-            table_stride, seq_lens, num_seqs, max_seq_len, num_blocks, n_kv, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return PKV_ERR_HIP;
-    }
     a.q = q;
     a.q_start = nullptr;
     a.k_cache = k_codes;
@@ -520,6 +520,23 @@ extern "C" int paged_attn_decode_q8_append(void* out, float* lse, const void* q,
     a.split_tokens = block_size;
     a.max_splits = 1;
     a.scale_log2 = scale * 1.44269504088896340736f;
+    // the workspace is checked before the append can write the pool
+    rc = check_workspace(a, true, workspace, workspace_bytes, nullptr);
+    if (rc != PKV_OK) return rc;
+    // folded while segments <= waves / 2, as for bf16 (paged_attn_decode_append)
+    if (2LL * num_seqs * n_kv <= a.waves) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_app = k_codes;
+        a.v_app = v_codes;
+        a.ks_app = k_scale;
+        a.vs_app = v_scale;
+    } else {
+        const hipError_t e = pkv::launch_kv_append_q8_last(
+            static_cast<int8_t*>(k_codes), static_cast<int8_t*>(v_codes), k_scale, v_scale, k_new, v_new, block_table,
+            table_stride, seq_lens, num_seqs, max_seq_len, num_blocks, n_kv, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return PKV_ERR_HIP;
+    }
     return run_attention(a, out, lse, PKV_BF16, true, true, workspace, workspace_bytes,
                          static_cast<hipStream_t>(stream));
 }
@@ -604,6 +621,11 @@ int chunk_impl(void* out, float* lse, const void* q, const int32_t* q_start, voi
             if (e == hipSuccess) e = pkv::launch_merge(a, out, lse, true, st);
             return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
         }
+    }
+    // the split path's workspace is checked before the append can write the pool
+    if (!mfma) {
+        rc = check_workspace(a, false, workspace, workspace_bytes, nullptr);
+        if (rc != PKV_OK) return rc;
     }
     rc = append_first();
     if (rc != PKV_OK) return rc;

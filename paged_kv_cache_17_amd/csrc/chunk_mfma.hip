@@ -193,11 +193,18 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     }
 
     // This lane's query in the B-operand layout: dims 16t + 8h + e, t = 0..7.
+    // The kernel needs a scale factor >= 0 (it takes the maximum of the raw
+    // scores and masks with -inf before scaling): a negative scale is
+    // applied as a query with flipped sign bits (exact) times |scale|, and
+    // scale 0 as a zero query times 1 (every allowed key then weighs the same).
+    const float sl2_in = a.scale_log2;
+    const uint32_t q_and = sl2_in == 0.0f ? 0u : 0xFFFFFFFFu;
+    const uint32_t q_xor = sl2_in < 0.0f ? 0x80008000u : 0u;
     u32x4 qv[8];
     {
         const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + orow * kD + 8 * h);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qv[t] = active ? qp[2 * t] : u32x4{0, 0, 0, 0};
+        for (int t = 0; t < 8; ++t) qv[t] = active ? (qp[2 * t] & q_and) ^ q_xor : u32x4{0, 0, 0, 0};
     }
 
     // Copy of one tile: wave w fetches cache block 4kt + w (keys 16w..16w+15
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
     float mref = -INFINITY, mref_safe = 0.0f, lsum = 0.0f;
-    const float sl2 = a.scale_log2;
+    const float sl2 = sl2_in == 0.0f ? 1.0f : fabsf(sl2_in);
     const int ntiles = kmax / kKeys + 1;
     const int pmin = P + q0;                      // smallest position in the tile
     const int kt_diag = (pmin + 1) / kKeys;       // tiles before this one need no mask

@@ -250,3 +250,115 @@ def test_chunk_step_large_chunks_and_decode_rows():
                         new_lens=C, seed=55)
     say("chunk step, chunks of 40")
     _check_chunk_step(wl, "chunk step 40")
+
+
+# ------------------------------------------------ errors before any write ---
+
+
+def _slot_is_poison(c, wl, s, quantized=False):
+    pos = int(wl.seq_lens[s]) - 1
+    blk = int(c.table[s, pos // wl.block_size])
+    if quantized:
+        return bool((c.k_cache[blk, :, pos % wl.block_size] == -128).all()) and \
+            bool(torch.isnan(c.k_scale[blk, :, pos % wl.block_size]).all())
+    return bool(torch.isnan(c.k_cache[blk, :, pos % wl.block_size].float()).all())
+
+
+def _smallest_accepted(call, hi):
+    """Smallest workspace byte count a call accepts, by bisection. ``call(n)``
+    runs an entry point with n bytes of workspace and returns its status."""
+    lo = 0                      # rejected (a call with no room fails)
+    assert call(hi) == 0
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        st = call(mid)
+        assert st in (0, -6), st
+        lo, hi = (lo, mid) if st == 0 else (mid, hi)
+    return hi
+
+
+@pytest.mark.parametrize("quantized", [False, True])
+def test_step_too_small_workspace_writes_nothing(quantized):
+    """700 sequences (the append is a launch of its own inside the call): a
+    workspace one byte short of what the step's partition needs, or
+    misaligned, is rejected before the append, so every new slot still holds
+    the poison. The exact need is found with the decode call of the same
+    partition, which writes nothing into the pool."""
+    import paged_kv_cache_17_amd as pkv
+    from paged_kv_cache_17_amd import binding as B
+    L = np.random.default_rng(47).integers(1, 301, size=700)
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=47)
+    say("decode step, workspace too small, 8-bit =", quantized)
+    c = _history_only_cache(wl, quantized=quantized)
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    kn, vn = raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype)
+    need = B.paged_attn_workspace_size(wl.num_seqs, wl.n_q, wl.n_kv, 128, 16, wl.max_seq_len, 0)
+    big = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lens = i32(wl.seq_lens)
+
+    def decode(nbytes):
+        try:
+            if quantized:
+                pkv.paged_attn_decode_q8(out, None, q, c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.table_dev,
+                                         lens, wl.max_seq_len, wl.scale, big[:nbytes])
+            else:
+                pkv.paged_attn_decode(out, None, q, c.k_cache, c.v_cache, c.table_dev, lens, wl.max_seq_len,
+                                      wl.scale, big[:nbytes])
+            return 0
+        except pkv.PagedKVError as e:
+            return e.status
+
+    exact = _smallest_accepted(decode, need)
+    torch.cuda.synchronize()
+    say(f"  step needs {exact} of the {need} bytes paged_attn_workspace_size reports")
+    for ws, status in ((big[:exact - 1], -6), (big[1:exact + 1], -2)):
+        with pytest.raises(pkv.PagedKVError) as e:
+            if quantized:
+                pkv.paged_attn_decode_q8_append(out, None, q, c.k_cache, c.v_cache, c.k_scale, c.v_scale, kn, vn,
+                                                c.table_dev, lens, wl.max_seq_len, wl.scale, ws)
+            else:
+                pkv.paged_attn_decode_append(out, None, q, c.k_cache, c.v_cache, kn, vn, c.table_dev, lens,
+                                             wl.max_seq_len, wl.scale, ws)
+        assert e.value.status == status
+    torch.cuda.synchronize()
+    assert all(_slot_is_poison(c, wl, s, quantized) for s in range(wl.num_seqs))
+    # with exactly the bytes it needs the step runs and writes every new slot
+    if quantized:
+        pkv.paged_attn_decode_q8_append(out, None, q, c.k_cache, c.v_cache, c.k_scale, c.v_scale, kn, vn,
+                                        c.table_dev, lens, wl.max_seq_len, wl.scale, big[:exact])
+    else:
+        pkv.paged_attn_decode_append(out, None, q, c.k_cache, c.v_cache, kn, vn, c.table_dev, lens,
+                                     wl.max_seq_len, wl.scale, big[:exact])
+    torch.cuda.synchronize()
+    assert not any(_slot_is_poison(c, wl, s, quantized) for s in range(wl.num_seqs))
+
+
+def test_chunk_step_too_small_workspace_writes_nothing():
+    """A chunk step on the split path (split_tokens > 0) with a workspace one
+    byte short is rejected before its append."""
+    import paged_kv_cache_17_amd as pkv
+    from paged_kv_cache_17_amd import binding as B
+    L = np.array([40, 57, 300, 90])
+    C = np.array([40, 40, 40, 1])
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - C,
+                        new_lens=C, seed=57)
+    say("chunk step, workspace too small")
+    c = _history_only_cache(wl)
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    need = B.paged_attn_workspace_size(q.shape[0], wl.n_q, wl.n_kv, 128, 16, wl.max_seq_len, 64)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_attn_chunk_append(torch.empty_like(q), None, q, i32(wl.q_offsets), c.k_cache, c.v_cache,
+                                    raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype), c.table_dev,
+                                    i32(wl.seq_lens), wl.max_new, wl.max_seq_len, wl.scale, ws[:need - 1],
+                                    split_tokens=64)
+    assert e.value.status == -6
+    torch.cuda.synchronize()
+    for s in range(wl.num_seqs):
+        for p in range(int(wl.hist_lens[s]), int(wl.seq_lens[s])):
+            blk = int(c.table[s, p // 16])
+            assert torch.isnan(c.k_cache[blk, :, p % 16].float()).all()

@@ -279,64 +279,25 @@ def test_invalid_rows_become_nan_and_leave_others_alone(fast):
     check_rows(got[keep], ref[keep], BF16, "valid rows next to invalid ones")
 
 
-# ----------------------------------------------------- full-size configs ---
-
-
-def _sample_seqs(wl, k=6):
-    order = np.argsort(wl.seq_lens, kind="stable")
-    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
-    rng = np.random.default_rng(0)
-    pick |= set(rng.choice(wl.num_seqs, size=min(k, wl.num_seqs), replace=False).tolist())
-    return sorted(pick)
-
-
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_config_sampled(cfg):
-    wl = config_workload(cfg)
-    say(f"config {cfg}: {wl.num_seqs} seqs, {int(wl.seq_lens.sum())} keys, {wl.num_blocks} blocks")
-    c = build_gpu_cache(wl, fill_nan=True)
-    assert np.array_equal(c.table, oracle.build_tables(wl))
-    kpool = torch_to_raw(c.k_cache, wl.dtype)
-    vpool = torch_to_raw(c.v_cache, wl.dtype)
-    picks = _sample_seqs(wl)
-    for s in picks:
-        L = int(wl.seq_lens[s])
-        k, v = wl.rows(s, 0, L)
-        blocks = c.table[s, :c.held[s]]
-        assert np.array_equal(oracle.gather(kpool, blocks, L, wl.block_size).view(np.uint16),
-                              k.transpose(1, 0, 2).view(np.uint16))
-        assert np.array_equal(oracle.gather(vpool, blocks, L, wl.block_size).view(np.uint16),
-                              v.transpose(1, 0, 2).view(np.uint16))
-    del kpool, vpool
-    if cfg == 5:
-        dec = np.nonzero(wl.new_lens == 1)[0]
-        pre = np.nonzero(wl.new_lens > 1)[0]
-        assert dec.tolist() == list(range(len(dec)))      # decode rows come first
-        nd = len(dec)
-        q = raw_to_torch(wl.q, BF16)
-        lens = i32(wl.seq_lens)
-        lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
-        import paged_kv_cache_17_amd as pkv
-        ws = c.workspace(int(q.shape[0]), wl.n_q, wl.max_seq_len)
-        out = torch.empty_like(q)
-        pkv.paged_attn_decode(out[:nd], lse[:nd], q[:nd], c.k_cache, c.v_cache, c.table_dev[:nd], lens[:nd],
-                              int(wl.seq_lens[:nd].max()), wl.scale, ws)
-        qs = wl.q_offsets[nd:] - wl.q_offsets[nd]
-        ws2 = torch.empty_like(ws)
-        pkv.paged_attn_chunk(out[nd:], lse[nd:], q[nd:], i32(qs), c.k_cache, c.v_cache, c.table_dev[nd:],
-                             lens[nd:], int(wl.new_lens[nd:].max()), int(wl.seq_lens[nd:].max()), wl.scale, ws2)
-        torch.cuda.synchronize()
-    else:
-        out, lse = run_decode(c, wl)
-    got = out_f64(out, wl.dtype)
-    got_lse = lse.cpu().numpy().astype(np.float64)
-    worst = 0.0
-    for s in picks:
-        a, b = int(wl.q_offsets[s]), int(wl.q_offsets[s + 1])
-        rows = range(a, b) if b - a <= 8 else [a, a + 1, (a + b) // 2, b - 2, b - 1]
-        ref, ref_lse = oracle.contiguous_attend(wl, s)
-        for r in rows:
-            worst = max(worst, check_rows(got[r:r + 1], ref[r - a:r - a + 1], wl.dtype, f"cfg {cfg} seq {s}"))
-            check_lse(got_lse[r], ref_lse[r - a], wl.dtype, f"cfg {cfg} seq {s}")
-    assert np.isfinite(got).all()
-    say(f"  sampled {len(picks)} seqs, worst row rel err {worst:.2e}")
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.7])
+def test_any_scale_sign_on_every_path(scale):
+    """The scale multiplies q.k whatever its sign: a negative scale favours
+    the keys least aligned with the query, scale 0 weighs every allowed key
+    the same (the output is the mean of the allowed values). Checked on the
+    matrix-core chunk kernel (chunks of 40 and 300), the balanced small-chunk
+    pass (chunks of 5), the generic chunk path (split 64), and decode."""
+    hist = [0, 17, 300, 1000, 2000]
+    new = [40, 300, 40, 1, 5]
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist, new_lens=new,
+                        seed=61, scale=scale)
+    say("scale", scale)
+    _full_check(wl, "chunk", 0, check_pool=False)
+    _full_check(wl, "chunk", 64, check_pool=False)
+    small = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=[3, 700, 2047],
+                           new_lens=[5, 5, 5], seed=62, scale=scale)
+    _full_check(small, "chunk", 0, check_pool=False)
+    L = np.array([1, 33, 900, 3000])
+    dec = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                         new_lens=np.ones_like(L), seed=63, scale=scale)
+    _full_check(dec, "decode", 0, check_pool=False)
+    _full_check(dec, "decode", 256, check_pool=False)

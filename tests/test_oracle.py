@@ -410,3 +410,45 @@ def test_fp32_rounding_is_far_inside_the_fp32_tolerance():
     o32 = (e / e.sum()) @ V32[0]
     err = np.max(np.abs(o32 - out[0, 0]))
     assert err < 100 * printed < 1e-5
+
+
+def _lab_pool_replay(wl):
+    """The lab page's KVPool, token by token: a sequence takes the next free
+    block (lowest rank, here the pool's order) each time a position reaches
+    the end of the blocks it holds; history of every sequence first, then
+    the step's new tokens, sequences in index order. Nothing is released
+    during a step, so "take the next free" is a walk along the order."""
+    from collections import deque
+    free = deque(int(b) for b in wl.alloc_order)
+    rows = [[] for _ in range(wl.num_seqs)]
+    B = wl.block_size
+    for lo, hi in ((np.zeros_like(wl.hist_lens), wl.hist_lens), (wl.hist_lens, wl.seq_lens)):
+        for s in range(wl.num_seqs):
+            for p in range(int(lo[s]), int(hi[s])):
+                if p // B == len(rows[s]):
+                    rows[s].append(free.popleft())
+    return rows
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_build_tables_is_the_lab_pool_replayed_token_by_token(cfg):
+    """oracle.build_tables (ceil-division bulk allocation) against a literal
+    per-token replay of the lab's pool on every configuration, plus the
+    invariants a table must satisfy: ceil(L / B) blocks per sequence, no
+    block in two rows, padding -1, and the blocks in use are exactly the
+    first ones of the allocation order."""
+    wl = config_workload(cfg)
+    t = oracle.build_tables(wl)
+    rows = _lab_pool_replay(wl)
+    B = wl.block_size
+    used = []
+    for s in range(wl.num_seqs):
+        nb = -(-int(wl.seq_lens[s]) // B)
+        assert len(rows[s]) == nb
+        assert t[s, :nb].tolist() == rows[s]
+        assert (t[s, nb:] == -1).all()
+        used += rows[s]
+    assert len(set(used)) == len(used)
+    assert sorted(used) == sorted(wl.alloc_order[:len(used)].tolist())
+    if cfg in (1, 4):   # the cache replay (history, then the step) makes the same rows
+        assert np.array_equal(t, oracle.build_cache(wl).tables())

@@ -41,22 +41,41 @@ def test_rollback_releases_exactly_the_blocks_past_the_committed_length():
         assert a.num_free == 200 - len(other.blocks)
 
 
-def test_tokens_per_cycle_follow_the_acceptance_formula():
-    """With each draft accepted independently with probability alpha until the
-    first rejection, a cycle commits the accepted drafts plus one sampled
-    token: between 1 and gamma + 1 tokens, (1 - alpha^(g+1)) / (1 - alpha)
-    on average."""
+def test_rollback_cycles_follow_the_acceptance_formula():
+    """Speculative cycles on one oracle row: each cycle grows the row for
+    gamma + 1 tokens (SequenceBlocks.ensure), then rolls it back to the
+    committed length (SequenceBlocks.truncate), the accepted drafts plus one
+    sampled token, with drafts accepted independently with probability alpha
+    until the first rejection (chapter 5 section 5). After every cycle the
+    row holds exactly ceil(L / B) blocks and the pool the rest; over the
+    cycles the committed tokens per cycle lie in [1, gamma + 1] with mean
+    (1 - alpha^(gamma+1)) / (1 - alpha)."""
     rng = np.random.default_rng(9)
+    B, N = 16, 8192
     for alpha in (0.3, 0.6, 0.85):
         for gamma in (1, 4, 5):
-            n = 200_000
+            n = 3000
             accept = rng.random((n, gamma)) < alpha
             n_acc = np.where(accept.all(axis=1), gamma, np.argmin(accept, axis=1))
-            tokens = n_acc + 1
+            a = oracle.BlockAllocator(N)
+            row = oracle.SequenceBlocks(B)
+            L = 7
+            row.ensure(a, L)
+            committed = []
+            for c in range(n):
+                row.ensure(a, L + gamma + 1)
+                row.truncate(a, L + int(n_acc[c]) + 1)
+                committed.append(int(n_acc[c]) + 1)
+                L += int(n_acc[c]) + 1
+                assert len(row.blocks) == -(-L // B)
+                assert a.num_free == N - len(row.blocks)
+            tokens = np.array(committed)
             assert tokens.min() >= 1 and tokens.max() <= gamma + 1
             expect = (1 - alpha ** (gamma + 1)) / (1 - alpha)
             sd = tokens.std() / np.sqrt(n)
             assert abs(tokens.mean() - expect) < 5 * sd
+            row.release(a)
+            assert a.num_free == N and a.free_ids() == list(range(N))
 
 
 def test_verify_chunk_equals_one_query_at_a_time():
