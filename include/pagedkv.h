@@ -74,6 +74,7 @@ extern "C" {
 #define PKV_ERR_HIP                 -8  /* a HIP launch failed (hipGetLastError) */
 #define PKV_ERR_NO_MEMORY           -9  /* host allocation for the pool object failed */
 #define PKV_ERR_INVALID_BLOCK      -10  /* a block id to share or copy is out of range, not allocated, or repeated */
+#define PKV_ERR_SCRATCH_LIMIT      -11  /* the call needs more split-K workspace than the static scratch holds */
 
 /* ---- element types ----------------------------------------------------- */
 #define PKV_F32  0   /* IEEE binary32 */
@@ -332,6 +333,33 @@ int paged_attn_decode_append(void* out, float* lse, const void* q, void* k_cache
                              int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
                              int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * paged_attn_decode_append_noalloc - paged_attn_decode_append with its
+ * split-K workspace in a static device array of the library instead of a
+ * caller buffer: the call allocates nothing (no hipMalloc, no allocating
+ * library routine).
+ *
+ * For callers that cannot allocate device memory: code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The array holds PKV_NOALLOC_SCRATCH_BYTES (16 MiB); each GPU the library
+ * runs on keeps its own copy until the process ends. Its device address is
+ * looked up on the first call on each device. A batch whose partition needs
+ * more (about (waves + num_seqs * n_kv) * (n_q / n_kv) partials of
+ * 8 + 4 * head_dim bytes: up to ~800 sequences at 8 kv heads and group 4)
+ * returns PKV_ERR_SCRATCH_LIMIT before anything is launched; use
+ * paged_attn_decode_append with a workspace for those. Nothing in the array
+ * has to start at zero. All calls on one GPU share its array, so calls that
+ * overlap in time on one GPU (different streams, or threads) race: serialise
+ * them. Arguments, results and other errors as paged_attn_decode_append. */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int paged_attn_decode_append_noalloc(void* out, float* lse, const void* q, void* k_cache, void* v_cache,
+                                     const void* k_new, const void* v_new, const int32_t* block_table,
+                                     int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                     int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
+                                     int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                                     void* stream);
 
 /* ======================================================================
  * paged_attn_chunk - a chunk of C_s consecutive query tokens per sequence

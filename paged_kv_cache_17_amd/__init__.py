@@ -19,7 +19,7 @@ from .binding import (  # noqa: F401
     paged_attn_chunk_append,
     paged_attn_chunk_workspace_size,
     paged_attn_decode,
-    paged_attn_decode_append, paged_attn_decode_q8_append, paged_attn_decode_q8,
+    paged_attn_decode_append, paged_attn_decode_q8_append, paged_attn_decode_q8, paged_attn_decode_append_noalloc,
     paged_attn_split_tokens,
     paged_attn_workspace_size,
     pkv_set_profile_events,

@@ -62,6 +62,8 @@ _SIGNATURES = {
                            ctypes.c_float, _i32, _i32, _p, _size_t, _p], ctypes.c_int),
     "paged_attn_decode_append": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i32, ctypes.c_float, _i32, _p, _size_t, _p], ctypes.c_int),
+    "paged_attn_decode_append_noalloc": ([_p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, ctypes.c_float, _i32, _p], ctypes.c_int),
     "paged_attn_decode_q8_append": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _i32, ctypes.c_float, _p, _size_t, _p], ctypes.c_int),
     "paged_attn_chunk_append": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
@@ -339,6 +341,20 @@ def paged_attn_decode_append(out, lse, q, k_cache, v_cache, k_new, v_new, block_
         _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(S), int(max_seq_len),
         int(num_blocks), int(n_q), int(n_kv), int(d), int(bs), float(scale), _dtype_code(k_cache),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def paged_attn_decode_append_noalloc(out, lse, q, k_cache, v_cache, k_new, v_new, block_table, seq_lens,
+                                     max_seq_len, scale, stream=None):
+    """:func:`paged_attn_decode_append` with the split-K workspace in the library's
+    static device array (no workspace argument; nothing is allocated)."""
+    _dev(out, lse, q, k_cache, v_cache, k_new, v_new, block_table, seq_lens)
+    num_blocks, n_kv, bs, d = k_cache.shape
+    S, n_q, _ = q.shape
+    _check("paged_attn_decode_append_noalloc", load_library().paged_attn_decode_append_noalloc(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(S), int(max_seq_len),
+        int(num_blocks), int(n_q), int(n_kv), int(d), int(bs), float(scale), _dtype_code(k_cache),
+        _stream(stream)))
 
 
 def paged_attn_decode_q8_append(out, lse, q, k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_table,

@@ -190,6 +190,7 @@ extern "C" const char* pkv_strerror(int status) {
         case PKV_ERR_HIP: return "HIP launch error";
         case PKV_ERR_NO_MEMORY: return "out of host memory";
         case PKV_ERR_INVALID_BLOCK: return "invalid block (out of range, not allocated, or repeated)";
+        case PKV_ERR_SCRATCH_LIMIT: return "the batch needs more split-K workspace than the static scratch holds";
         default: return "unknown status";
     }
 }
