@@ -122,6 +122,63 @@ def copy_probe(mib):
                       "bytes_written_per_launch": n}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def stream_probe(caches, tiles, stream, reps=20):
+    """Read-only streaming rates on this GPU (the library's pkv_stream_read):
+
+    * scattered tiles: ``tiles`` (K tile, V tile) pairs of 4 KiB each, taken
+      in a seeded random order from the bf16 pools of the cache copies (used
+      in turn), each wave streaming its own run of the order - the decode
+      split pass's access pattern without its arithmetic; 4, 6 and 8 waves
+      per CU, the best kept;
+    * contiguous: all of one K pool, grid-stride.
+
+    Returns GB/s figures (median of ``reps`` launches each)."""
+    import torch
+    import paged_kv_cache_17_amd as pkv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pool_tiles = caches[0].k_cache.shape[0] * caches[0].k_cache.shape[1]
+    assert caches[0].k_cache.shape[2] * caches[0].k_cache.shape[3] * 2 == 4096 and tiles <= pool_tiles
+    order = np.random.default_rng(11).permutation(pool_tiles)[:tiles].astype(np.int32)
+    assert order.min() >= 0 and order.max() < pool_tiles
+    order_d = torch.from_numpy(order).cuda()
+    sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+
+    def timed(launch):
+        for i in range(4):
+            launch(i)
+        for i, (b, a) in enumerate(ev):
+            b.record(stream)
+            launch(i)
+            a.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([b.elapsed_time(a) for b, a in ev]))
+
+    best = None
+    for per_cu in (4, 6, 8):
+        ms = timed(lambda i: pkv.pkv_stream_read(caches[i % len(caches)].k_cache, caches[i % len(caches)].v_cache,
+                                                 order_d, cus * per_cu, sink, stream=stream))
+        gbps = tiles * 8192 / (ms * 1e-3) / 1e9
+        if best is None or gbps > best[1]:
+            best = (per_cu, gbps)
+    nbytes = caches[0].k_cache.numel() * 2
+    ms = timed(lambda i: pkv.pkv_stream_read(caches[i % len(caches)].k_cache, None, None, cus * 8, sink,
+                                             stream=stream))
+    return {"random_tile_gbps": best[1], "random_tile_waves_per_cu": best[0], "tiles": int(tiles),
+            "contiguous_gbps": nbytes / (ms * 1e-3) / 1e9, "contiguous_bytes": int(nbytes)}
+
+
 _ORACLE_CACHE = None     # the oracle's cache, shared with forked workers
 
 
@@ -171,7 +228,7 @@ def cpu_baseline(wl, budget_s=10.0, quant=False):
         pool.map(_attend_some, parts)               # warm the workers
         dtn, nn = repeat(lambda: pool.map(_attend_some, parts))
     kv = wl.ideal_kv_bytes()
-    return {"value": tokens / dtn, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": tokens / dtn, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"the whole decode step ({wl.num_seqs} sequences, {int(wl.seq_lens.sum())} keys): "
                       f"table gather, bf16->float64 widening and attention in NumPy float64; {cores} forked "
                       f"worker processes with one BLAS thread each, median of {nn} repeats",
@@ -526,6 +583,14 @@ def main():
                                  stream=stream)
         pkv.pkv_set_profile_events(None, None)
 
+    # Cold start: the first call of the step on this process (code-object
+    # load, first dispatch) timed on the host, reported apart from the
+    # warmed-up steps.
+    torch.cuda.synchronize()
+    t_cold = time.perf_counter()
+    step(0)
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - t_cold) * 1e3
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -593,6 +658,7 @@ def main():
                             else "kv_append + paged_attn_decode" if nd == S else "kv_append + decode + chunk"),
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
     }
+    line["cold_start_ms"] = cold_ms
     if nd:
         kern_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_dec]))
         achieved = dec_bytes / (kern_avg * 1e-3) / 1e9
@@ -604,6 +670,11 @@ def main():
                             "traffic": None if quant else measured_traffic(CONFIG_NAMES[args.config]),
                             "avg_launch_ms": kern_avg,
                             "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash("decode")}
+        if not quant:
+            tile_pairs = int(sum(-(-int(L) // wl.block_size) for L in wl.seq_lens[:nd])) * wl.n_kv
+            probe = stream_probe(caches, tile_pairs, stream)
+            probe["split_pass_frac_of_random_tile"] = achieved / probe["random_tile_gbps"]
+            line["stream_probe"] = probe
     if nd < S:
         chk_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_chk]))
         tflops = chk_flops / (chk_avg * 1e-3) / 1e12

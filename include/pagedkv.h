@@ -560,6 +560,24 @@ int sample_workspace_size(int32_t rows, int32_t vocab, size_t* bytes);
  * Process-wide; not thread-safe. */
 int pkv_set_profile_events(void* before, void* after);
 
+/* Read-only streaming probe (measurement only, not part of the
+ * computation): reads device memory and folds it into a checksum, to give
+ * the attention passes' HBM rates something to be compared with.
+ *  - order == NULL: reads `bytes` (a multiple of 16) contiguous bytes at `a`
+ *    with `workgroups` workgroups of 256 threads; sink holds
+ *    workgroups * 256 uint32.
+ *  - order != NULL: `workgroups` single-wave workgroups; tile t of order
+ *    (t < tiles) names 4 KiB tile order[t] of `a` and the same tile of `b`
+ *    (the K and V tile of one (block, kv head) of a bf16 pool with
+ *    head_dim 128 and block_size 16); wave w reads its own contiguous run of
+ *    the order, one tile in flight while the previous is folded (the
+ *    decode split pass's access pattern without its arithmetic). The
+ *    caller keeps every order[t] inside both buffers. sink holds
+ *    workgroups * 64 uint32.
+ * a and b 16-byte aligned. Errors: NULL_POINTER, INVALID_ARGUMENT, HIP. */
+int pkv_stream_read(const void* a, const void* b, size_t bytes, const int32_t* order, int32_t tiles,
+                    int32_t workgroups, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

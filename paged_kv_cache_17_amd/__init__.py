@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     paged_attn_split_tokens,
     paged_attn_workspace_size,
     pkv_set_profile_events,
+    pkv_stream_read,
     sample_tokens,
     sample_workspace_size,
     strerror,

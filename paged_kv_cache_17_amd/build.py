@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 SOURCES = ["kvpool.cpp", "api.cpp", "kv_append.hip", "kv_copy.hip", "attn_generic.hip", "attn_merge.hip",
            "decode_bf16.hip", "decode_balanced.hip",
-           "chunk_mfma.hip", "sample.hip", "noalloc.hip"]
+           "chunk_mfma.hip", "sample.hip", "noalloc.hip", "stream_probe.hip"]
 
 
 def hipcc() -> str:
