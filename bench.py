@@ -136,19 +136,24 @@ def cpu_model():
 def stream_probe(caches, tiles, stream, reps=20):
     """Read-only streaming rates on this GPU (the library's pkv_stream_read):
 
-    * scattered tiles: ``tiles`` (K tile, V tile) pairs of 4 KiB each, taken
-      in a seeded random order from the bf16 pools of the cache copies (used
-      in turn), each wave streaming its own run of the order - the decode
-      split pass's access pattern without its arithmetic; 4, 6 and 8 waves
-      per CU, the best kept;
+    * scattered tiles: ``tiles`` (K tile, V tile) pairs - 4 KiB each for a
+      bf16 pool, 2 KiB of codes each for an 8-bit pool - taken in a seeded
+      random order from the pools of the cache copies (used in turn), each
+      wave streaming its own run of the order: the decode split pass's
+      access pattern without its arithmetic (the 8-bit pass also reads a
+      64-byte scale run per tile, left out here); 4, 6 and 8 waves per CU,
+      the best kept;
     * contiguous: all of one K pool, grid-stride.
 
     Returns GB/s figures (median of ``reps`` launches each)."""
     import torch
     import paged_kv_cache_17_amd as pkv
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    pool_tiles = caches[0].k_cache.shape[0] * caches[0].k_cache.shape[1]
-    assert caches[0].k_cache.shape[2] * caches[0].k_cache.shape[3] * 2 == 4096 and tiles <= pool_tiles
+    k0 = caches[0].k_cache
+    tile_bytes = k0.shape[2] * k0.shape[3] * k0.element_size()
+    assert tile_bytes in (2048, 4096)
+    pool_tiles = k0.shape[0] * k0.shape[1]
+    assert tiles <= pool_tiles
     order = np.random.default_rng(11).permutation(pool_tiles)[:tiles].astype(np.int32)
     assert order.min() >= 0 and order.max() < pool_tiles
     order_d = torch.from_numpy(order).cuda()
@@ -168,15 +173,16 @@ def stream_probe(caches, tiles, stream, reps=20):
     best = None
     for per_cu in (4, 6, 8):
         ms = timed(lambda i: pkv.pkv_stream_read(caches[i % len(caches)].k_cache, caches[i % len(caches)].v_cache,
-                                                 order_d, cus * per_cu, sink, stream=stream))
-        gbps = tiles * 8192 / (ms * 1e-3) / 1e9
+                                                 order_d, cus * per_cu, sink, tile_bytes=tile_bytes, stream=stream))
+        gbps = tiles * 2 * tile_bytes / (ms * 1e-3) / 1e9
         if best is None or gbps > best[1]:
             best = (per_cu, gbps)
-    nbytes = caches[0].k_cache.numel() * 2
+    nbytes = k0.numel() * k0.element_size()
     ms = timed(lambda i: pkv.pkv_stream_read(caches[i % len(caches)].k_cache, None, None, cus * 8, sink,
                                              stream=stream))
     return {"random_tile_gbps": best[1], "random_tile_waves_per_cu": best[0], "tiles": int(tiles),
-            "contiguous_gbps": nbytes / (ms * 1e-3) / 1e9, "contiguous_bytes": int(nbytes)}
+            "tile_bytes": int(tile_bytes), "contiguous_gbps": nbytes / (ms * 1e-3) / 1e9,
+            "contiguous_bytes": int(nbytes)}
 
 
 _ORACLE_CACHE = None     # the oracle's cache, shared with forked workers
@@ -670,11 +676,10 @@ def main():
                             "traffic": None if quant else measured_traffic(CONFIG_NAMES[args.config]),
                             "avg_launch_ms": kern_avg,
                             "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash("decode")}
-        if not quant:
-            tile_pairs = int(sum(-(-int(L) // wl.block_size) for L in wl.seq_lens[:nd])) * wl.n_kv
-            probe = stream_probe(caches, tile_pairs, stream)
-            probe["split_pass_frac_of_random_tile"] = achieved / probe["random_tile_gbps"]
-            line["stream_probe"] = probe
+        tile_pairs = int(sum(-(-int(L) // wl.block_size) for L in wl.seq_lens[:nd])) * wl.n_kv
+        probe = stream_probe(caches, tile_pairs, stream)
+        probe["split_pass_frac_of_random_tile"] = achieved / probe["random_tile_gbps"]
+        line["stream_probe"] = probe
     if nd < S:
         chk_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_chk]))
         tflops = chk_flops / (chk_avg * 1e-3) / 1e12

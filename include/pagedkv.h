@@ -460,8 +460,8 @@ int kv_append_q8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
 /* paged_attn_decode_q8 - paged_attn_decode over an 8-bit cache: keys and
  * values are read as s * code; q and out are bf16; fp32 accumulation.
  * Supported: head_dim 128, block_size 16, n_q / n_kv in {1, 2, 4, 8},
- * 1..8192 sequences (else UNSUPPORTED); q and out 16-byte aligned, code
- * pools 8-byte aligned (else INVALID_ARGUMENT). The workspace is sized by
+ * 1..8192 sequences (else UNSUPPORTED); q, out, both code pools and both
+ * scale arrays 16-byte aligned (else INVALID_ARGUMENT). The workspace is sized by
  * paged_attn_workspace_size with split_tokens 0 (the size covers both the
  * bf16 and the 8-bit pass). Invalid lengths or table entries give NaN rows
  * as in paged_attn_decode. Other arguments as paged_attn_decode. */
@@ -567,16 +567,16 @@ int pkv_set_profile_events(void* before, void* after);
  *    with `workgroups` workgroups of 256 threads; sink holds
  *    workgroups * 256 uint32.
  *  - order != NULL: `workgroups` single-wave workgroups; tile t of order
- *    (t < tiles) names 4 KiB tile order[t] of `a` and the same tile of `b`
- *    (the K and V tile of one (block, kv head) of a bf16 pool with
- *    head_dim 128 and block_size 16); wave w reads its own contiguous run of
- *    the order, one tile in flight while the previous is folded (the
- *    decode split pass's access pattern without its arithmetic). The
- *    caller keeps every order[t] inside both buffers. sink holds
- *    workgroups * 64 uint32.
+ *    (t < tiles) names tile order[t] of tile_bytes (4096 or 2048) bytes in
+ *    `a` and the same tile of `b` (the K and V tile of one (block, kv head):
+ *    4 KiB for a bf16 pool, 2 KiB of codes for an 8-bit pool, at head_dim
+ *    128 and block_size 16); wave w reads its own contiguous run of the
+ *    order, one tile in flight while the previous is folded (the decode
+ *    split pass's access pattern without its arithmetic). The caller keeps
+ *    every order[t] inside both buffers. sink holds workgroups * 64 uint32.
  * a and b 16-byte aligned. Errors: NULL_POINTER, INVALID_ARGUMENT, HIP. */
 int pkv_stream_read(const void* a, const void* b, size_t bytes, const int32_t* order, int32_t tiles,
-                    int32_t workgroups, uint32_t* sink, void* stream);
+                    int32_t tile_bytes, int32_t workgroups, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -72,7 +72,7 @@ _SIGNATURES = {
     "paged_attn_chunk": ([_p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, ctypes.c_float, _i32, _i32, _p, _size_t, _p], ctypes.c_int),
     "pkv_set_profile_events": ([_p, _p], ctypes.c_int),
-    "pkv_stream_read": ([_p, _p, _size_t, _p, _i32, _i32, _p, _p], ctypes.c_int),
+    "pkv_stream_read": ([_p, _p, _size_t, _p, _i32, _i32, _i32, _p, _p], ctypes.c_int),
     "sample_workspace_size": ([_i32, _i32, ctypes.POINTER(_size_t)], ctypes.c_int),
     "sample_tokens": ([_p, _p, _p, _i32, _i32, ctypes.c_int64, _p, _p, _p, _p, _p, _size_t, _p], ctypes.c_int),
 }
@@ -440,14 +440,16 @@ def pkv_set_profile_events(before, after):
     _check("pkv_set_profile_events", load_library().pkv_set_profile_events(b, a))
 
 
-def pkv_stream_read(a, b, order, workgroups, sink, stream=None):
+def pkv_stream_read(a, b, order, workgroups, sink, tile_bytes=4096, stream=None):
     """Read-only streaming probe (measurement only): ``order`` None reads all of
-    ``a`` contiguously; otherwise the 4 KiB tiles ``order`` names in ``a`` and ``b``
-    in the decode pass's per-wave pattern. ``sink`` receives a checksum per lane."""
+    ``a`` contiguously; otherwise the tiles of ``tile_bytes`` (4096 or 2048) that
+    ``order`` names in ``a`` and ``b``, in the decode pass's per-wave pattern.
+    ``sink`` receives a checksum per lane."""
     _dev(a, sink)
     if order is not None:
         _dev(b, order)
     nbytes = a.numel() * a.element_size()
     _check("pkv_stream_read", load_library().pkv_stream_read(
         _ptr(a), _ptr(b) if b is not None else None, int(nbytes), _ptr(order) if order is not None else None,
-        int(order.numel()) if order is not None else 0, int(workgroups), _ptr(sink), _stream(stream)))
+        int(order.numel()) if order is not None else 0, int(tile_bytes), int(workgroups), _ptr(sink),
+        _stream(stream)))

@@ -450,8 +450,8 @@ extern "C" int paged_attn_decode_q8(void* out, float* lse, const void* q, const 
     if (!out || !q || !k_codes || !v_codes || !k_scale || !v_scale || !block_table || !seq_lens)
         return PKV_ERR_NULL_POINTER;
     if (!pkv::decode_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs)) return PKV_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(k_codes) & 7) ||
-        (reinterpret_cast<uintptr_t>(v_codes) & 7))
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scale) ||
+        !aligned16(v_scale))
         return PKV_ERR_INVALID_ARGUMENT;
     pkv::AttnArgs a{};
     a.waves = balanced_waves(n_q, n_kv, num_seqs, kDecodeInt8);
@@ -494,8 +494,8 @@ extern "C" int paged_attn_decode_q8_append(void* out, float* lse, const void* q,
     if (!out || !q || !k_codes || !v_codes || !k_scale || !v_scale || !k_new || !v_new || !block_table || !seq_lens)
         return PKV_ERR_NULL_POINTER;
     if (!pkv::decode_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs)) return PKV_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new) ||
-        (reinterpret_cast<uintptr_t>(k_codes) & 7) || (reinterpret_cast<uintptr_t>(v_codes) & 7))
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_codes) ||
+        !aligned16(v_codes) || !aligned16(k_scale) || !aligned16(v_scale))
         return PKV_ERR_INVALID_ARGUMENT;
     pkv::AttnArgs a{};
     a.waves = balanced_waves(n_q, n_kv, num_seqs, kDecodeInt8);

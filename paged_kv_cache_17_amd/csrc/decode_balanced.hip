@@ -364,9 +364,89 @@ struct Int8Ring : MfmaRows<4, 1> {
         st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(vr, j); }, lane, ntok, sl2);
     }
 };
+// 8-bit K/V with four query heads per kv head, tiles in registers, the
+// next tile's loads in flight while one is computed. Lane (q, n) loads:
+//  * token n's codes at bytes 16q .. 16q + 15 and 64 + 16q .. 64 + 16q + 15
+//    (two 16-byte loads, each instruction reading one contiguous half of
+//    every token's row) for the score product. Which dims a lane holds in
+//    that contraction is free as long as its query operand holds the same
+//    ones: product b takes dims 64(b / 2) + 16q + 8(b % 2) .. + 7 (fetch_q
+//    below loads the query that way);
+//  * tokens 4q .. 4q + 3's codes at dims 8n .. 8n + 7 (four 8-byte loads,
+//    each instruction reading four whole 128-byte rows) for the output
+//    product, in the layout of v_operand_codes;
+//  * the K and V scales of tokens 4q .. 4q + 3 (one 16-byte load each).
+// 24 registers per tile. The pool of codes and the scale arrays must be
+// 16-byte aligned.
+struct Int8Regs : MfmaRows<4, 1> {
+    static constexpr int kDepth = 2;
+    static constexpr int kWavesPerCU = 8;
+    static constexpr bool kCodes = true;
+    struct Regs {
+        u32x4 k[2];
+        u32x2 v[4];
+        u32x4 sk, sv;
+    };
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* ks;
+    const float* vs;
+    __device__ __forceinline__ Int8Regs(const AttnArgs& a, int lane, unsigned char* /*ring*/)
+        : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 16 * (lane >> 4)),
+          vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
+          ks(a.k_scale + 4 * (lane >> 4)),
+          vs(a.v_scale + 4 * (lane >> 4)) {}
+    // The G = 4 heads' query (decode: one row per sequence), lane (q, n) head
+    // n's dims 64(b / 2) + 16q + 8(b % 2) .. + 7 for product b, zero for n >= 4.
+    __device__ __forceinline__ static void fetch_q(u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g, int lane) {
+        const int n = lane & 15, q = lane >> 4;
+        const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(s) * a.n_q + g * 4 + n) * kTileD +
+                             16 * q;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            qv[b] = n < 4 ? *reinterpret_cast<const u32x4*>(qr + 64 * (b >> 1) + 8 * (b & 1)) : u32x4{0, 0, 0, 0};
+    }
+    __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
+        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kc + off);
+        t.k[0] = __builtin_nontemporal_load(kp);
+        t.k[1] = __builtin_nontemporal_load(kp + 4);
+        const u32x2* vp = reinterpret_cast<const u32x2*>(vc + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
+        const size_t so = static_cast<size_t>(tile) * kTileB;
+        t.sk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + so));
+        t.sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + so));
+    }
+    __device__ __forceinline__ void compute(State& st, const Regs& t0, const u32x4 (&qv)[kQ], int lane, int ntok,
+                                            float sl2, int /*newer*/) const {
+        // The tile's registers pass through an empty statement here, after
+        // the next tile's loads were issued: without it the compiler unpacks
+        // a tile's codes at the end of the step before, where the loads of
+        // the tile after it are not issued yet, and every step then waits
+        // for the tile just requested.
+        Regs t = t0;
+        asm volatile("" : "+v"(t.k[0]), "+v"(t.k[1]), "+v"(t.v[0]), "+v"(t.v[1]), "+v"(t.v[2]), "+v"(t.v[3]),
+                     "+v"(t.sk), "+v"(t.sv));
+        f32x4 s[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const u32x4 w = t.k[b >> 1];
+            const u32x2 kb = (b & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(kb)),
+                                                           __builtin_bit_cast(bf16x8, qv[b]), s[0], 0, 0, 0);
+        }
+        // codes are finite whatever a slot past the end holds; its weight is 0
+        const float sk[4] = {__uint_as_float(t.sk[0]), __uint_as_float(t.sk[1]), __uint_as_float(t.sk[2]),
+                             __uint_as_float(t.sk[3])};
+        const float sv[4] = {__uint_as_float(t.sv[0]), __uint_as_float(t.sv[1]), __uint_as_float(t.sv[2]),
+                             __uint_as_float(t.sv[3])};
+        st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(t.v, j); }, lane, ntok, sl2);
+    }
+};
 template <>
-struct Int8Kv<4> : Int8Ring {
-    using Int8Ring::Int8Ring;
+struct Int8Kv<4> : Int8Regs {
+    using Int8Regs::Int8Regs;
 };
 
 // Small chunks: up to 32 (query, head) rows per kv head in two blocks.

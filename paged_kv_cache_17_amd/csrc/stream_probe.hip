@@ -21,7 +21,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
-constexpr int kTile16 = 256;    // 16-byte granules per 4 KiB tile
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
 
@@ -41,6 +40,7 @@ __global__ __launch_bounds__(256) void stream_contig_kernel(const u32x4* __restr
     sink[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
 }
 
+template <int kTile16>
 __global__ __launch_bounds__(kWave) void stream_tiles_kernel(const u32x4* __restrict__ kp,
                                                              const u32x4* __restrict__ vp,
                                                              const int32_t* __restrict__ order, int tiles,
@@ -48,23 +48,24 @@ __global__ __launch_bounds__(kWave) void stream_tiles_kernel(const u32x4* __rest
     const int w = blockIdx.x, W = gridDim.x, lane = threadIdx.x;
     const int t0 = static_cast<int>(static_cast<long long>(w) * tiles / W);
     const int t1 = static_cast<int>(static_cast<long long>(w + 1) * tiles / W);
+    constexpr int kPer = kTile16 / kWave;   // loads per lane per tile and pool
     uint32_t acc = 0;
-    u32x4 buf[8];
+    u32x4 buf[2 * kPer];
     auto issue = [&](int t) {
         const size_t base = static_cast<size_t>(order[t]) * kTile16 + lane;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) buf[i] = __builtin_nontemporal_load(kp + base + i * kWave);
+        for (int i = 0; i < kPer; ++i) buf[i] = __builtin_nontemporal_load(kp + base + i * kWave);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) buf[4 + i] = __builtin_nontemporal_load(vp + base + i * kWave);
+        for (int i = 0; i < kPer; ++i) buf[kPer + i] = __builtin_nontemporal_load(vp + base + i * kWave);
     };
     if (t0 < t1) issue(t0);
     for (int t = t0; t < t1; ++t) {
-        u32x4 cur[8];
+        u32x4 cur[2 * kPer];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = buf[i];
+        for (int i = 0; i < 2 * kPer; ++i) cur[i] = buf[i];
         if (t + 1 < t1) issue(t + 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc ^= fold(cur[i]);
+        for (int i = 0; i < 2 * kPer; ++i) acc ^= fold(cur[i]);
     }
     sink[static_cast<size_t>(w) * kWave + lane] = acc;
 }
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kWave) void stream_tiles_kernel(const u32x4* __rest
 }  // namespace
 
 extern "C" int pkv_stream_read(const void* a, const void* b, size_t bytes, const int32_t* order, int32_t tiles,
-                               int32_t workgroups, uint32_t* sink, void* stream) {
+                               int32_t tile_bytes, int32_t workgroups, uint32_t* sink, void* stream) {
     if (!a || !sink) return PKV_ERR_NULL_POINTER;
     if (workgroups < 1) return PKV_ERR_INVALID_ARGUMENT;
     if ((reinterpret_cast<uintptr_t>(a) & 15) || (b && (reinterpret_cast<uintptr_t>(b) & 15)))
@@ -85,8 +86,14 @@ extern "C" int pkv_stream_read(const void* a, const void* b, size_t bytes, const
     } else {
         if (!b) return PKV_ERR_NULL_POINTER;
         if (tiles < 0) return PKV_ERR_INVALID_ARGUMENT;
-        hipLaunchKernelGGL(stream_tiles_kernel, dim3(workgroups), dim3(kWave), 0, st, static_cast<const u32x4*>(a),
-                           static_cast<const u32x4*>(b), order, tiles, sink);
+        if (tile_bytes == 4096)
+            hipLaunchKernelGGL(stream_tiles_kernel<256>, dim3(workgroups), dim3(kWave), 0, st,
+                               static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), order, tiles, sink);
+        else if (tile_bytes == 2048)
+            hipLaunchKernelGGL(stream_tiles_kernel<128>, dim3(workgroups), dim3(kWave), 0, st,
+                               static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), order, tiles, sink);
+        else
+            return PKV_ERR_INVALID_ARGUMENT;
     }
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -235,15 +235,16 @@ def test_one_call_steps_reject_bad_arguments_before_any_launch():
     assert dec(q=1) == -3                             # not 16-byte aligned
     assert dec(S=0) == 0
 
-    def q8(q=16, kn=16, kc=16, d=128):
-        return lib.paged_attn_decode_q8_append(None if q == 0 else p(16), None, p(q), p(kc), p(16), p(16), p(16),
+    def q8(q=16, kn=16, kc=16, ks=16, d=128):
+        return lib.paged_attn_decode_q8_append(None if q == 0 else p(16), None, p(q), p(kc), p(16), p(ks), p(16),
                                                p(kn), p(16), p(16), 4, p(16), 2, 64, 8, 32, 8, d, 16, 0.25, p(256),
                                                1 << 20, None)
 
     assert q8(kn=0) == -1
     assert q8(d=64) == -3
     assert q8(q=1) == -2                              # q not 16-byte aligned
-    assert q8(kc=20) == -2                            # codes not 8-byte aligned
+    assert q8(kc=24) == -2                            # codes not 16-byte aligned
+    assert q8(ks=20) == -2                            # scales not 16-byte aligned
 
     def chunk(kn=16, total_q=5, S=1):
         return lib.paged_attn_chunk_append(p(16), None, p(16), p(16), p(16), p(16), p(kn), p(16), p(16), 4, p(16),
