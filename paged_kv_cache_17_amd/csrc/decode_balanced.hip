@@ -61,7 +61,6 @@ struct ValuRows {
     static constexpr int kSlotRows = G;              // partial rows per slot
     static constexpr int kWaves = G == 8 ? 1 : 2;   // waves per SIMD the registers allow
     static constexpr int kWavesPerCU = 0;           // waves per CU launched (0: all that fit)
-    static constexpr int kRingBytes = 0;            // LDS a wave stages tiles in (none)
     static constexpr bool kCodes = false;           // pool of 8-bit codes + scales
     // One query per sequence: the G heads of kv head g.
     __device__ __forceinline__ static void fetch_q(u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g, int lane) {
@@ -99,7 +98,6 @@ struct MfmaRows {
     static constexpr int kSlotRows = NB == 1 ? G : 16 * NB;
     static constexpr int kWaves = 2;
     static constexpr int kWavesPerCU = 0;
-    static constexpr int kRingBytes = 0;
     static constexpr bool kCodes = false;
     // Segment (s, g)'s first query row and number of queries.
     __device__ __forceinline__ static int queries(const AttnArgs& a, int s, int& row0) {
@@ -152,14 +150,14 @@ struct Bf16Kv : ValuRows<G> {
     };
     const uint16_t* kc;
     const uint16_t* vc;
-    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane, unsigned char* /*ring*/)
+    __device__ __forceinline__ Bf16Kv(const AttnArgs& a, int lane)
         : kc(static_cast<const uint16_t*>(a.k_cache) + lane * 8), vc(static_cast<const uint16_t*>(a.v_cache) + lane * 8) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
         const size_t off = static_cast<size_t>(tile) * kTileElems;
         load_tile(kc + off, vc + off, t.k, t.v);
     }
     __device__ __forceinline__ void compute(DecodeState<G>& st, const Regs& t, const u32x4 (&qv)[G],
-                                            int lane, int ntok, float sl2, int /*newer*/) const {
+                                            int lane, int ntok, float sl2) const {
         st.tile(t.k, t.v, qv, lane >> 4, ntok, sl2);
     }
 };
@@ -181,7 +179,7 @@ struct Int8Kv : ValuRows<G> {
     const int8_t* vc;
     const float* ks;
     const float* vs;
-    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane, unsigned char* /*ring*/)
+    __device__ __forceinline__ Int8Kv(const AttnArgs& a, int lane)
         : kc(static_cast<const int8_t*>(a.k_cache) + lane * 8), vc(static_cast<const int8_t*>(a.v_cache) + lane * 8),
           ks(a.k_scale), vs(a.v_scale) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int lane) const {
@@ -201,7 +199,7 @@ struct Int8Kv : ValuRows<G> {
         }
     }
     __device__ __forceinline__ void compute(DecodeState<G>& st, const Regs& t, const u32x4 (&qv)[G],
-                                            int lane, int ntok, float sl2, int /*newer*/) const {
+                                            int lane, int ntok, float sl2) const {
         st.tile_q8(t.k, t.v, t.sk, t.sv, qv, lane >> 4, ntok, sl2);
     }
 };
@@ -233,7 +231,7 @@ struct Bf16Mfma : MfmaRows<G, NB> {
     };
     const uint16_t* kc;
     const uint16_t* vc;
-    __device__ __forceinline__ Bf16Mfma(const AttnArgs& a, int lane, unsigned char* /*ring*/)
+    __device__ __forceinline__ Bf16Mfma(const AttnArgs& a, int lane)
         : kc(static_cast<const uint16_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
           vc(static_cast<const uint16_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)) {}
     __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
@@ -246,7 +244,7 @@ struct Bf16Mfma : MfmaRows<G, NB> {
         for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
-                                            float sl2, int /*newer*/) const {
+                                            float sl2) const {
         if constexpr (kDrain) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         f32x4 s[NB];
 #pragma unroll
@@ -271,98 +269,6 @@ struct Bf16Mfma : MfmaRows<G, NB> {
 template <>
 struct Bf16Kv<4> : Bf16Mfma<4, 1> {
     using Bf16Mfma<4, 1>::Bf16Mfma;
-};
-// 8-bit K/V with four query heads per kv head, staged through LDS: each
-// wave streams its tiles into a ring of kDepth LDS slots with direct
-// global-to-LDS loads, which hold no registers, kDepth - 1 tiles ahead of
-// the one it computes. Two slots at two waves per SIMD measured fastest on
-// the 64-sequence batch (66.3 us; one slot 69.4, three 68.0, four 68.7, and
-// two slots at one or three waves per SIMD 68.2-68.5).
-// Slot image: K codes, V codes (16 tokens x 128 dims each; the 16-byte chunk
-// d of token t at chunk t * 8 + (d ^ (t & 7)), so that the reads below hit
-// distinct banks), then the 16 K and the 16 V scales.
-struct Int8Ring : MfmaRows<4, 1> {
-    static constexpr int kDepth = 2;
-    static constexpr int kWavesPerCU = 8;
-    static constexpr bool kCodes = true;
-    static constexpr int kSlot = 2 * kTileElems + 2 * kTileB * 4;
-    static constexpr int kRingBytes = kDepth * kSlot;
-    static constexpr int kLoads = 5;   // vector memory operations issued per tile
-    struct Regs {
-        int slot;
-    };
-    const int8_t* kc;
-    const int8_t* vc;
-    const float* sc;   // K scales for lanes 0..15, V scales for lanes 16..31
-    unsigned char* ring;
-    int koff, voff;    // this lane's K and V read offsets in a slot
-    __device__ __forceinline__ Int8Ring(const AttnArgs& a, int lane, unsigned char* r)
-        : kc(static_cast<const int8_t*>(a.k_cache) + chunk_src(lane)),
-          vc(static_cast<const int8_t*>(a.v_cache) + chunk_src(lane)),
-          sc(lane < 16 ? a.k_scale + lane : a.v_scale + (lane - 16)),
-          ring(r) {
-        const int n = lane & 15, q = lane >> 4;
-        koff = (n * 8 + ((q >> 1) ^ (n & 7))) * 16 + (q & 1) * 8;
-        voff = (n & 1) * 8;
-    }
-    typedef __attribute__((address_space(3))) void* LdsPtr;
-    __device__ __forceinline__ static LdsPtr lds_ptr(unsigned char* p) { return (LdsPtr)(p); }
-    // Lane l's source chunk for LDS chunk l (and 64 + l, 1024 bytes on).
-    __device__ __forceinline__ static int chunk_src(int l) { return (l >> 3) * 128 + (((l & 7) ^ (l >> 3)) * 16); }
-
-    __device__ __forceinline__ void load(Regs& t, int tile, int lane) const {
-        unsigned char* dst = ring + t.slot * kSlot;
-        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_global_load_lds(kc + off + i * 1024, lds_ptr(dst + i * 1024), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_global_load_lds(vc + off + i * 1024, lds_ptr(dst + kTileElems + i * 1024), 16, 0, 0);
-        if (lane < 32)
-            __builtin_amdgcn_global_load_lds(sc + static_cast<size_t>(tile) * kTileB,
-                                             lds_ptr(dst + 2 * kTileElems), 4, 0, 0);
-    }
-    // The tile's loads are done once at most `newer` tiles' loads (issued
-    // after it) are outstanding.
-    __device__ __forceinline__ static void wait_loads(int newer) {
-        static_assert(kDepth - 1 <= 3 && kLoads == 5, "wait counts below");
-        if (newer <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (newer == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else if (newer == 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
-    }
-    __device__ __forceinline__ void compute(State& st, const Regs& t, const u32x4 (&qv)[kQ], int lane, int ntok,
-                                            float sl2, int newer) const {
-        wait_loads(newer);
-        const unsigned char* src = ring + t.slot * kSlot;
-        const int q = lane >> 4, n = lane & 15;
-        u32x2 kr[4], vr[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)   // token n, dims 32b + 8q .. +7: chunk 2b + q / 2, swizzled
-            kr[b] = *reinterpret_cast<const u32x2*>(src + (koff ^ ((2 * b) << 4)));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {   // token 4q + e, dims 8n .. 8n + 7
-            const int tk = 4 * q + e;
-            vr[e] = *reinterpret_cast<const u32x2*>(src + kTileElems + (tk * 8 + ((n >> 1) ^ (tk & 7))) * 16 + voff);
-        }
-        // read as integers: read as floats (the copies' source type), the
-        // compiler takes them to alias the copies still in flight and waits
-        // for all of them here; wait_loads above already covers this slot
-        const u32x4 skv = *reinterpret_cast<const u32x4*>(src + 2 * kTileElems + 16 * q);
-        const u32x4 svv = *reinterpret_cast<const u32x4*>(src + 2 * kTileElems + 64 + 16 * q);
-        f32x4 s[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(kr[b])),
-                                                           __builtin_bit_cast(bf16x8, qv[b]), s[0], 0, 0, 0);
-        // codes are finite whatever the slot holds; weights past the end are 0
-        const float sk[4] = {__uint_as_float(skv[0]), __uint_as_float(skv[1]), __uint_as_float(skv[2]),
-                             __uint_as_float(skv[3])};
-        const float sv[4] = {__uint_as_float(svv[0]), __uint_as_float(svv[1]), __uint_as_float(svv[2]),
-                             __uint_as_float(svv[3])};
-        st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(vr, j); }, lane, ntok, sl2);
-    }
 };
 // 8-bit K/V with four query heads per kv head, tiles in registers, the
 // next tile's loads in flight while one is computed. Lane (q, n) loads:
@@ -391,7 +297,7 @@ struct Int8Regs : MfmaRows<4, 1> {
     const int8_t* vc;
     const float* ks;
     const float* vs;
-    __device__ __forceinline__ Int8Regs(const AttnArgs& a, int lane, unsigned char* /*ring*/)
+    __device__ __forceinline__ Int8Regs(const AttnArgs& a, int lane)
         : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 16 * (lane >> 4)),
           vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
           ks(a.k_scale + 4 * (lane >> 4)),
@@ -419,7 +325,7 @@ struct Int8Regs : MfmaRows<4, 1> {
         t.sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + so));
     }
     __device__ __forceinline__ void compute(State& st, const Regs& t0, const u32x4 (&qv)[kQ], int lane, int ntok,
-                                            float sl2, int /*newer*/) const {
+                                            float sl2) const {
         // The tile's registers pass through an empty statement here, after
         // the next tile's loads were issued: without it the compiler unpacks
         // a tile's codes at the end of the step before, where the loads of
@@ -534,8 +440,7 @@ void decode_balanced_kernel(AttnArgs a) {
         }
     };
 
-    __shared__ __attribute__((aligned(16))) unsigned char s_ring[Kv::kRingBytes > 0 ? Kv::kRingBytes : 16];
-    const Kv kv(a, lane, s_ring);
+    const Kv kv(a, lane);
     const float sl2 = a.scale_log2;
 
     typename Kv::State st;
@@ -559,10 +464,6 @@ void decode_balanced_kernel(AttnArgs a) {
         int seg, ntok;
     };
     Buf b[D];
-    if constexpr (Kv::kRingBytes > 0) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) b[u].t.slot = u;
-    }
     static_assert(D >= 2, "the next tile is issued before the current one is computed");
     describe(t0);
     // Folded append (decode step stage 1): the new token of segment seg
@@ -651,11 +552,10 @@ void decode_balanced_kernel(AttnArgs a) {
             cur_bad = false;
         }
         if (!tail || i + D - 1 < n) issue(i + D - 1, fut);
-        const int newer = tail ? min(D - 1, n - 1 - i) : D - 1;   // tiles issued after tile i
         if (ntok < 0) {
             cur_bad = true;
         } else {
-            kv.compute(st, cur.t, qv, lane, ntok, sl2, newer);
+            kv.compute(st, cur.t, qv, lane, ntok, sl2);
         }
     };
 
