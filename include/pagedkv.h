@@ -259,10 +259,11 @@ int paged_attn_split_tokens(int32_t num_q_rows, int32_t n_kv, int32_t block_size
 int paged_attn_workspace_size(int32_t num_q_rows, int32_t n_q, int32_t n_kv,
                               int32_t head_dim, int32_t block_size, int32_t max_seq_len,
                               int32_t split_tokens, size_t* bytes);
-/* Workspace for paged_attn_chunk on any of its paths: the larger of
- * paged_attn_workspace_size(total_q, ...) and, when the chunk qualifies for
- * the balanced path (see paged_attn_chunk), its partial slots. Needs the
- * device (the balanced grid is sized from it). Errors: NULL_POINTER,
+/* Workspace for paged_attn_chunk on any of its paths (and for
+ * paged_attn_chunk_q8): the larger of paged_attn_workspace_size(total_q,
+ * ...) and, when the chunk qualifies for the balanced path (see
+ * paged_attn_chunk), its partial slots for a bf16 or an 8-bit pool. Needs
+ * the device (the balanced grid is sized from it). Errors: NULL_POINTER,
  * INVALID_ARGUMENT, HIP. */
 int paged_attn_chunk_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t n_q,
                                     int32_t n_kv, int32_t head_dim, int32_t block_size,
@@ -498,6 +499,37 @@ int paged_attn_decode_q8_append(void* out, float* lse, const void* q, void* k_co
                                 int32_t num_seqs, int32_t max_seq_len, int32_t num_blocks, int32_t n_q,
                                 int32_t n_kv, int32_t head_dim, int32_t block_size, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_chunk_q8 - paged_attn_chunk over an 8-bit cache, for
+ * verification-sized chunks: keys and values read as s * code; q and out
+ * bf16; fp32 accumulation. Source: chapter 5 section 5 (a verification
+ * pass attends the drafted tokens as one causal chunk) over the cache of
+ * chapter 5 section 4 (absmax codes) - the serving tutorial's section 7
+ * treats KV quantisation as a design point that combines with the others.
+ * Query i of sequence s sits at position seq_lens[s] - C_s + i (as
+ * paged_attn_chunk). Supported: head_dim 128, block_size 16, n_q / n_kv in
+ * {1, 2, 4, 8}, max_q_len * (n_q / n_kv) <= 32 (else UNSUPPORTED): the
+ * balanced partition over every (sequence, kv head, block) tile. q, out,
+ * code pools and scale arrays 16-byte aligned (else INVALID_ARGUMENT).
+ * workspace: paged_attn_chunk_workspace_size bytes (split_tokens 0), 256-byte
+ * aligned. Append the chunk first with kv_append_q8 (positions
+ * seq_lens - C_s). Invalid lengths or table entries give NaN rows. Errors
+ * as paged_attn_chunk. */
+int paged_attn_chunk_q8(void* out, float* lse, const void* q, const int32_t* q_start,
+                        const void* k_codes, const void* v_codes, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,
+                        int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                        int32_t num_blocks, int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                        float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* kv_copy_blocks_q8 - kv_copy_blocks for an 8-bit cache: block src_ids[i]'s
+ * codes and scales (K and V) onto block dst_ids[i]. Source: serving tutorial
+ * section 4.2 (copy-on-write of a shared block) with the 8-bit layout above;
+ * pair it with kvpool_cow as for kv_copy_blocks. Same pair rules and errors
+ * as kv_copy_blocks. */
+int kv_copy_blocks_q8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                      const int32_t* src_ids, const int32_t* dst_ids, int32_t n, int32_t num_blocks,
+                      int32_t n_kv, int32_t head_dim, int32_t block_size, void* stream);
 
 /* ======================================================================
  * sample_tokens - pick the next token of each row of logits.

@@ -14,7 +14,9 @@ from .paged_attention import (  # noqa: F401
     OutOfBlocks,
     QuantOracleCache,
     SequenceBlocks,
+    QUANT_POISON_CODE,
     append,
+    append_quantized,
     attention,
     attention_split_merge,
     bf16_bits_to_f64,
@@ -29,6 +31,8 @@ from .paged_attention import (  # noqa: F401
     paged_attention_all,
     quant_bytes,
     quantize_absmax,
+    quantized_rows,
+    token_slots,
     widen,
 )
 from . import sampling  # noqa: F401,E402

@@ -521,6 +521,27 @@ def quant_bytes(n_elements: int, bits: int, groups: int, scale_bytes: int) -> in
     return n_elements * bits // 8 + groups * scale_bytes
 
 
+def append_quantized(codes_k, codes_v, scale_k, scale_v, blocks, start: int, k_new, v_new, block_size: int,
+                     dtype: str) -> None:
+    """Quantise tokens ``start .. start+T-1`` (raw ``[T, n_kv, d]`` rows of
+    ``dtype``) row by row with ``quantize_absmax`` and write codes and scales
+    into their slots through a table row (the append rule of ``append``)."""
+    ck, sk = quantize_absmax(widen(k_new, dtype))
+    cv, sv = quantize_absmax(widen(v_new, dtype))
+    blk, slot = token_slots(blocks, start + np.arange(len(k_new)), block_size)
+    codes_k[blk, :, slot, :] = ck
+    codes_v[blk, :, slot, :] = cv
+    scale_k[blk, :, slot] = sk
+    scale_v[blk, :, slot] = sv
+
+
+def quantized_rows(rows, dtype: str) -> np.ndarray:
+    """Raw ``[..., d]`` rows as the 8-bit cache reads them back: ``s * code``
+    of their absmax quantisation, float64."""
+    codes, scales = quantize_absmax(widen(rows, dtype))
+    return dequantize(codes, scales)
+
+
 class QuantOracleCache(OracleCache):
     """The oracle's 8-bit pool: codes ``[num_blocks, n_kv, B, d]`` and one
     float32 scale per (block, kv head, slot), for K and for V. Tokens are
@@ -539,14 +560,8 @@ class QuantOracleCache(OracleCache):
         self.seqs = [SequenceBlocks(wl.block_size) for _ in range(wl.num_seqs)]
 
     def _append(self, s, start, k, v):
-        B = self.wl.block_size
-        ck, sk = quantize_absmax(widen(k, self.wl.dtype))
-        cv, sv = quantize_absmax(widen(v, self.wl.dtype))
-        blk, slot = token_slots(self.seqs[s].blocks, start + np.arange(len(k)), B)
-        self.pool_k[blk, :, slot, :] = ck
-        self.pool_v[blk, :, slot, :] = cv
-        self.scale_k[blk, :, slot] = sk
-        self.scale_v[blk, :, slot] = sv
+        append_quantized(self.pool_k, self.pool_v, self.scale_k, self.scale_v, self.seqs[s].blocks, start, k, v,
+                         self.wl.block_size, self.wl.dtype)
 
     def fill_history(self):
         wl = self.wl

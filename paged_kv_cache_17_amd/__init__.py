@@ -14,9 +14,11 @@ from .binding import (  # noqa: F401
     kv_append,
     kv_append_q8,
     kv_copy_blocks,
+    kv_copy_blocks_q8,
     load_library,
     paged_attn_chunk,
     paged_attn_chunk_append,
+    paged_attn_chunk_q8,
     paged_attn_chunk_workspace_size,
     paged_attn_decode,
     paged_attn_decode_append, paged_attn_decode_q8_append, paged_attn_decode_q8, paged_attn_decode_append_noalloc,

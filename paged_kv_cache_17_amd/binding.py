@@ -46,6 +46,9 @@ _SIGNATURES = {
     "kvpool_refcount": ([_p, _i32, _pi32], ctypes.c_int),
     "kvpool_fork": ([_p, _pi32, _i32, _pi32, _pi32, _i32, _i32], ctypes.c_int),
     "kvpool_cow": ([_p, _pi32, _i32, _i32, _i32, _pi32, _pi32, _i32, _pi32], ctypes.c_int),
+    "kv_copy_blocks_q8": ([_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p], ctypes.c_int),
+    "paged_attn_chunk_q8": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                             _i32, _i32, ctypes.c_float, _p, _size_t, _p], ctypes.c_int),
     "kv_copy_blocks": ([_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p], ctypes.c_int),
     "kv_append_q8": ([_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p],
                      ctypes.c_int),
@@ -453,3 +456,26 @@ def pkv_stream_read(a, b, order, workgroups, sink, tile_bytes=4096, stream=None)
         _ptr(a), _ptr(b) if b is not None else None, int(nbytes), _ptr(order) if order is not None else None,
         int(order.numel()) if order is not None else 0, int(tile_bytes), int(workgroups), _ptr(sink),
         _stream(stream)))
+
+
+def kv_copy_blocks_q8(k_codes, v_codes, k_scale, v_scale, src_ids, dst_ids, stream=None):
+    """Copy whole blocks of an 8-bit pool (codes and scales): ``src_ids[i]`` onto ``dst_ids[i]``."""
+    _dev(k_codes, v_codes, k_scale, v_scale, src_ids, dst_ids)
+    num_blocks, n_kv, bs, d = k_codes.shape
+    _check("kv_copy_blocks_q8", load_library().kv_copy_blocks_q8(
+        _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale), _ptr(src_ids), _ptr(dst_ids),
+        int(src_ids.numel()), int(num_blocks), int(n_kv), int(d), int(bs), _stream(stream)))
+
+
+def paged_attn_chunk_q8(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, max_q_len,
+                        max_seq_len, scale, workspace, stream=None):
+    """Chunk attention (verification-sized chunks) over an 8-bit pool: ``q``/``out`` bf16
+    ``[total_q, n_q, d]``."""
+    _dev(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, workspace)
+    num_blocks, n_kv, bs, d = k_codes.shape
+    total_q, n_q, _ = q.shape
+    _check("paged_attn_chunk_q8", load_library().paged_attn_chunk_q8(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(seq_lens.shape[0]), int(total_q),
+        int(max_q_len), int(max_seq_len), int(num_blocks), int(n_q), int(n_kv), int(d), int(bs), float(scale),
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))

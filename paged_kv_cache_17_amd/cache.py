@@ -70,12 +70,14 @@ class PagedKVCache:
         shared blocks in that range are replaced by private copies (host table
         updated, contents copied on the device). Returns the number of copies;
         call ``upload_table`` before the next device call that reads the table."""
-        if self.quantized:
-            raise NotImplementedError("copy-on-write of an 8-bit cache (codes and scales) is not provided")
         src, dst = self.pool.kvpool_cow(self.table, self.held, s, start, count)
         if len(src):
-            B.kv_copy_blocks(self.k_cache, self.v_cache, torch.from_numpy(src).to(self.device),
-                             torch.from_numpy(dst).to(self.device), stream=stream)
+            src_d, dst_d = torch.from_numpy(src).to(self.device), torch.from_numpy(dst).to(self.device)
+            if self.quantized:
+                B.kv_copy_blocks_q8(self.k_cache, self.v_cache, self.k_scale, self.v_scale, src_d, dst_d,
+                                    stream=stream)
+            else:
+                B.kv_copy_blocks(self.k_cache, self.v_cache, src_d, dst_d, stream=stream)
         return len(src)
 
     def upload_table(self, stream=None) -> None:
@@ -139,10 +141,15 @@ class PagedKVCache:
               lse=None, split_tokens: int = 0, stream=None):
         if out is None:
             out = torch.empty_like(q)
-        if self.quantized:
-            raise NotImplementedError("chunk attention over an 8-bit cache is not provided")
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
                             chunk=(q_start.shape[0] - 1, max_q_len))
+        if self.quantized:
+            # verification-sized chunks (max_q_len * n_q / n_kv <= 32) only
+            if split_tokens:
+                raise ValueError("chunks over an 8-bit cache use the balanced partition only (split_tokens=0)")
+            B.paged_attn_chunk_q8(out, lse, q, q_start, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
+                                  self.table_dev, seq_lens, max_q_len, max_seq_len, scale, ws, stream=stream)
+            return out
         B.paged_attn_chunk(out, lse, q, q_start, self.k_cache, self.v_cache, self.table_dev, seq_lens,
                            max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens, stream=stream)
         return out
@@ -154,7 +161,8 @@ class PagedKVCache:
         if out is None:
             out = torch.empty_like(q)
         if self.quantized:
-            raise NotImplementedError("chunk attention over an 8-bit cache is not provided")
+            raise NotImplementedError("no one-call chunk step over an 8-bit cache: call append() (kv_append_q8), "
+                                      "then chunk() (paged_attn_chunk_q8)")
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
                             chunk=(q_start.shape[0] - 1, max_q_len))
         B.paged_attn_chunk_append(out, lse, q, q_start, self.k_cache, self.v_cache, k_new, v_new, self.table_dev,

@@ -98,14 +98,14 @@ Layout ws_layout_balanced(int num_seqs, int rows, int n_kv, int head_dim, int wa
 
 // Grid size of the balanced pass for the current device (cached for the
 // last shape asked about, per pass: bf16 decode, 8-bit decode, small chunks).
-enum BalancedPass { kDecodeBf16 = 0, kDecodeInt8 = 1, kChunkBf16 = 2 };
+enum BalancedPass { kDecodeBf16 = 0, kDecodeInt8 = 1, kChunkBf16 = 2, kChunkInt8 = 3 };
 int balanced_waves(int n_q, int n_kv, int num_seqs, BalancedPass f = kDecodeBf16) {
-    static thread_local int last_dev[3] = {-1, -1, -1}, last_g[3] = {}, last_s[3] = {}, last_w[3] = {};
+    static thread_local int last_dev[4] = {-1, -1, -1, -1}, last_g[4] = {}, last_s[4] = {}, last_w[4] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     const int g = n_q / n_kv;
     if (dev != last_dev[f] || g != last_g[f] || num_seqs != last_s[f]) {
-        last_w[f] = f == kChunkBf16 ? pkv::chunk_balanced_waves(n_q, n_kv, num_seqs)
+        last_w[f] = f >= kChunkBf16 ? pkv::chunk_balanced_waves(n_q, n_kv, num_seqs, f == kChunkInt8)
                                     : pkv::decode_balanced_waves(n_q, n_kv, num_seqs, f == kDecodeInt8);
         last_dev[f] = dev;
         last_g[f] = g;
@@ -236,6 +236,22 @@ extern "C" int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_i
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+extern "C" int kv_copy_blocks_q8(void* k_codes, void* v_codes, float* k_scale, float* v_scale, const int32_t* src_ids,
+                                 const int32_t* dst_ids, int32_t n, int32_t num_blocks, int32_t n_kv, int32_t head_dim,
+                                 int32_t block_size, void* stream) {
+    if (n < 0 || num_blocks < 1 || n_kv < 1 || head_dim < 1 || block_size < 1) return PKV_ERR_INVALID_ARGUMENT;
+    if (n == 0) return PKV_OK;
+    if (!k_codes || !v_codes || !k_scale || !v_scale || !src_ids || !dst_ids) return PKV_ERR_NULL_POINTER;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // codes: n_kv * B * head_dim bytes per block; scales: n_kv * B floats
+    hipError_t e = pkv::launch_copy_blocks(k_codes, v_codes, src_ids, dst_ids, n, num_blocks,
+                                           static_cast<size_t>(n_kv) * block_size * head_dim, st);
+    if (e == hipSuccess)
+        e = pkv::launch_copy_blocks(k_scale, v_scale, src_ids, dst_ids, n, num_blocks,
+                                    static_cast<size_t>(n_kv) * block_size * sizeof(float), st);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 extern "C" int sample_workspace_size(int32_t rows, int32_t vocab, size_t* bytes) {
     if (!bytes) return PKV_ERR_NULL_POINTER;
     if (rows < 0 || vocab < 1 || vocab > pkv::kSampleChunk * pkv::kSampleMaxCand) return PKV_ERR_INVALID_ARGUMENT;
@@ -300,10 +316,12 @@ extern "C" int paged_attn_chunk_workspace_size(int32_t num_seqs, int32_t total_q
     if (rc != PKV_OK) return rc;
     if (split_tokens == 0 && n_q % n_kv == 0 &&
         pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len)) {
-        const int waves = balanced_waves(n_q, n_kv, num_seqs, kChunkBf16);
-        if (waves < 1) return PKV_ERR_HIP;
-        const size_t b = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, waves).total;
-        if (b > *bytes) *bytes = b;
+        for (BalancedPass f : {kChunkBf16, kChunkInt8}) {   // bf16 and 8-bit K/V (paged_attn_chunk_q8)
+            const int waves = balanced_waves(n_q, n_kv, num_seqs, f);
+            if (waves < 1) return PKV_ERR_HIP;
+            const size_t b = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, waves).total;
+            if (b > *bytes) *bytes = b;
+        }
     }
     return PKV_OK;
 }
@@ -665,4 +683,61 @@ extern "C" int paged_attn_chunk_append(void* out, float* lse, const void* q, con
     return chunk_impl(out, lse, q, q_start, k_cache, v_cache, k_new, v_new, block_table, table_stride, seq_lens,
                       num_seqs, total_q, max_q_len, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size, scale,
                       dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attn_chunk_q8(void* out, float* lse, const void* q, const int32_t* q_start, const void* k_codes,
+                                   const void* v_codes, const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                                   int32_t num_blocks, int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                   float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size, table_stride, PKV_BF16,
+                         scale);
+    if (rc != PKV_OK) return rc;
+    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len) return PKV_ERR_INVALID_ARGUMENT;
+    if (total_q == 0) return PKV_OK;
+    if (num_seqs == 0 || max_q_len == 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (!out || !q || !q_start || !k_codes || !v_codes || !k_scale || !v_scale || !block_table || !seq_lens)
+        return PKV_ERR_NULL_POINTER;
+    if (!pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len))
+        return PKV_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scale) ||
+        !aligned16(v_scale))
+        return PKV_ERR_INVALID_ARGUMENT;
+    pkv::AttnArgs a{};
+    a.waves = balanced_waves(n_q, n_kv, num_seqs, kChunkInt8);
+    if (a.waves < 1) return PKV_ERR_HIP;
+    a.q = q;
+    a.q_start = q_start;
+    a.k_cache = k_codes;
+    a.v_cache = v_codes;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.table = block_table;
+    a.seq_lens = seq_lens;
+    a.table_stride = table_stride;
+    a.num_seqs = num_seqs;
+    a.num_rows = total_q;
+    a.max_q_len = max_q_len;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_blocks;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.split_tokens = block_size;
+    a.max_splits = 1;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    if (!workspace) return PKV_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
+    const Layout w = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, a.waves);
+    if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_ml = reinterpret_cast<pkv::PartialML*>(ws);
+    a.ws_o = reinterpret_cast<float*>(ws + w.o_offset);
+    a.prefix = reinterpret_cast<int*>(ws + w.prefix_offset);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = pkv::launch_chunk_balanced(a, st, profile_events());
+    if (e == hipSuccess) e = pkv::launch_merge(a, out, lse, true, st);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

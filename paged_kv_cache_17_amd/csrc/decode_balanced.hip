@@ -360,6 +360,70 @@ template <int G>
 using ChunkKv = Bf16Mfma<G, 2>;
 static_assert(ChunkKv<4>::kSlotRows == kChunkSlotRows, "chunk partial slots");
 
+// Small chunks over an 8-bit pool (verification passes over a quantised
+// cache): the rows of ChunkKv, tiles in registers with Bf16Mfma's operand
+// layouts. Lane (q, n) loads token n's codes at dims 32b + 8q .. + 7 (four
+// 8-byte loads), tokens 4q .. 4q + 3's codes at dims 8n .. 8n + 7 (four
+// 8-byte loads, whole rows per instruction) and those tokens' K and V scales
+// (one 16-byte load each); codes become bf16 exactly, the K scale multiplies
+// the scores and the V scale the weights (as Int8Regs).
+template <int G>
+struct Int8ChunkKv : MfmaRows<G, 2> {
+    using typename MfmaRows<G, 2>::State;
+    using MfmaRows<G, 2>::kQ;
+    static constexpr int kDepth = 2;
+    static constexpr int kWavesPerCU = 4;
+    static constexpr bool kCodes = true;
+    struct Regs {
+        u32x2 k[4];
+        u32x2 v[4];
+        u32x4 sk, sv;
+    };
+    const int8_t* kc;
+    const int8_t* vc;
+    const float* ks;
+    const float* vs;
+    __device__ __forceinline__ Int8ChunkKv(const AttnArgs& a, int lane)
+        : kc(static_cast<const int8_t*>(a.k_cache) + (lane & 15) * kTileD + 8 * (lane >> 4)),
+          vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
+          ks(a.k_scale + 4 * (lane >> 4)),
+          vs(a.v_scale + 4 * (lane >> 4)) {}
+    __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
+        const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
+        const u32x2* kp = reinterpret_cast<const u32x2*>(kc + off);
+        const u32x2* vp = reinterpret_cast<const u32x2*>(vc + off);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) t.k[b] = __builtin_nontemporal_load(kp + 4 * b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t.v[e] = __builtin_nontemporal_load(vp + e * (kTileD / 8));
+        const size_t so = static_cast<size_t>(tile) * kTileB;
+        t.sk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + so));
+        t.sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + so));
+    }
+    __device__ __forceinline__ void compute(State& st, const Regs& t0, const u32x4 (&qv)[kQ], int lane, int ntok,
+                                            float sl2) const {
+        Regs t = t0;   // pinned here, after the next tile's loads (see Int8Regs)
+        asm volatile("" : "+v"(t.k[0]), "+v"(t.k[1]), "+v"(t.k[2]), "+v"(t.k[3]), "+v"(t.v[0]), "+v"(t.v[1]),
+                     "+v"(t.v[2]), "+v"(t.v[3]), "+v"(t.sk), "+v"(t.sv));
+        f32x4 s[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            s[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, codes8_to_bf16x8(t.k[b])),
+                                                                __builtin_bit_cast(bf16x8, qv[4 * nb + b]), s[nb], 0,
+                                                                0, 0);
+        }
+        const float sk[4] = {__uint_as_float(t.sk[0]), __uint_as_float(t.sk[1]), __uint_as_float(t.sk[2]),
+                             __uint_as_float(t.sk[3])};
+        const float sv[4] = {__uint_as_float(t.sv[0]), __uint_as_float(t.sv[1]), __uint_as_float(t.sv[2]),
+                             __uint_as_float(t.sv[3])};
+        st.template update<true>(s, sk, sv, [&](int j) { return v_operand_codes(t.v, j); }, lane, ntok, sl2);
+    }
+};
+static_assert(Int8ChunkKv<4>::kSlotRows == kChunkSlotRows, "chunk partial slots");
+
 // Register budget: kWaves waves per SIMD (two: at most 256 registers per
 // lane; eight query heads per kv head need more than that for state, query
 // and two tiles, so one). How many waves per CU the grid holds is chosen
@@ -678,11 +742,13 @@ bool chunk_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, i
            max_q_len * (n_q / n_kv) <= kChunkSlotRows;
 }
 
-int chunk_balanced_waves(int n_q, int n_kv, int num_seqs) { return waves_for<ChunkKv>(n_q, n_kv, num_seqs); }
+int chunk_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv) {
+    return int8_kv ? waves_for<Int8ChunkKv>(n_q, n_kv, num_seqs) : waves_for<ChunkKv>(n_q, n_kv, num_seqs);
+}
 
 hipError_t launch_chunk_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev) {
     if (a.k_new) return hipErrorInvalidValue;   // chunk appends are launched on their own
-    return launch_kv<ChunkKv>(a, stream, ev);
+    return a.k_scale ? launch_kv<Int8ChunkKv>(a, stream, ev) : launch_kv<ChunkKv>(a, stream, ev);
 }
 
 }  // namespace pkv

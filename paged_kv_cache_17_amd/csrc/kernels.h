@@ -161,7 +161,7 @@ hipError_t launch_decode_balanced(const AttnArgs& a, hipStream_t stream, KernelE
 // of kChunkSlotRows rows, merged by launch_merge (a.q_start set).
 constexpr int kChunkSlotRows = 32;
 bool chunk_balanced_supported(int n_q, int n_kv, int head_dim, int block_size, int num_seqs, int max_q_len);
-int chunk_balanced_waves(int n_q, int n_kv, int num_seqs);
+int chunk_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv = false);
 hipError_t launch_chunk_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
 
 // Chunk attention on MFMA (bf16, head_dim 128, block_size 16, sequences of

@@ -19,7 +19,9 @@ constexpr int kCopyThreads = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool kWide>
+// kUnit: bytes per access - 16 when sizes and addresses allow, else 2, else
+// 1 (an 8-bit pool whose block is an odd number of bytes).
+template <int kUnit>
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* __restrict__ k_cache,
                                                                    char* __restrict__ v_cache,
                                                                    const int32_t* __restrict__ src_ids,
@@ -34,16 +36,18 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* __restr
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
     const char* s = pool + static_cast<size_t>(src) * block_bytes;
     char* d = pool + static_cast<size_t>(dst) * block_bytes;
-    if constexpr (kWide) {
+    if constexpr (kUnit == 16) {
         const size_t n = block_bytes / 16;
         const u32x4* s4 = reinterpret_cast<const u32x4*>(s);
         u32x4* d4 = reinterpret_cast<u32x4*>(d);
         for (size_t i = threadIdx.x; i < n; i += kCopyThreads) d4[i] = __builtin_nontemporal_load(s4 + i);
-    } else {
+    } else if constexpr (kUnit == 2) {
         const size_t n = block_bytes / 2;
         const uint16_t* s2 = reinterpret_cast<const uint16_t*>(s);
         uint16_t* d2 = reinterpret_cast<uint16_t*>(d);
         for (size_t i = threadIdx.x; i < n; i += kCopyThreads) d2[i] = s2[i];
+    } else {
+        for (size_t i = threadIdx.x; i < block_bytes; i += kCopyThreads) d[i] = s[i];
     }
 }
 
@@ -52,16 +56,18 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* __restr
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
                               int n, int num_blocks, size_t block_bytes, hipStream_t stream) {
     const dim3 grid(n, 2);
-    const bool wide = block_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(k_cache) & 15) == 0 &&
-                      (reinterpret_cast<uintptr_t>(v_cache) & 15) == 0;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache);
     char* k = static_cast<char*>(k_cache);
     char* v = static_cast<char*>(v_cache);
-    if (wide)
-        hipLaunchKernelGGL(copy_blocks_kernel<true>, grid, dim3(kCopyThreads), 0, stream, k, v, src_ids, dst_ids,
+    if (block_bytes % 16 == 0 && (addr & 15) == 0)
+        hipLaunchKernelGGL(copy_blocks_kernel<16>, grid, dim3(kCopyThreads), 0, stream, k, v, src_ids, dst_ids,
+                           num_blocks, block_bytes);
+    else if (block_bytes % 2 == 0 && (addr & 1) == 0)
+        hipLaunchKernelGGL(copy_blocks_kernel<2>, grid, dim3(kCopyThreads), 0, stream, k, v, src_ids, dst_ids,
                            num_blocks, block_bytes);
     else
-        hipLaunchKernelGGL(copy_blocks_kernel<false>, grid, dim3(kCopyThreads), 0, stream, k, v, src_ids,
-                           dst_ids, num_blocks, block_bytes);
+        hipLaunchKernelGGL(copy_blocks_kernel<1>, grid, dim3(kCopyThreads), 0, stream, k, v, src_ids, dst_ids,
+                           num_blocks, block_bytes);
     return hipGetLastError();
 }
 

@@ -72,16 +72,18 @@ def build_gpu_cache(wl, fill_nan=True, alloc_order=None, quantized=False, with_n
     return c
 
 
-def build_gpu_fork_cache(fw, fill_nan=True, share=True):
+def build_gpu_fork_cache(fw, fill_nan=True, share=True, quantized=False):
     """Forked sequences through the library: prompts written once (rows
     0..P-1), each forked into its branches (rows P..P+n*P-1), the prompt rows
     released, then for every branch copy-on-write of the shared tail block
     and its own tokens appended. Returns (cache, number of block copies).
     With share=False every branch row instead gets a private copy of its
-    prompt (the no-sharing baseline)."""
+    prompt (the no-sharing baseline). quantized: an 8-bit pool (codes and
+    scales written by kv_append_q8, copied by kv_copy_blocks_q8)."""
     NP, NB = fw.num_prompts, fw.num_branches
-    c = PagedKVCache(fw.num_blocks, fw.n_kv, fw.head_dim, fw.block_size, torch_dtype(fw.dtype), NP + NB,
-                     fw.table_stride, alloc_order=fw.alloc_order, fill_nan=fill_nan, poison_workspace=fill_nan)
+    c = PagedKVCache(fw.num_blocks, fw.n_kv, fw.head_dim, fw.block_size,
+                     torch.int8 if quantized else torch_dtype(fw.dtype), NP + NB, fw.table_stride,
+                     alloc_order=fw.alloc_order, fill_nan=fill_nan, poison_workspace=fill_nan)
     if not share:
         lens = fw.branch_lens()
         for b in range(NB):
@@ -125,16 +127,17 @@ def build_gpu_fork_cache(fw, fill_nan=True, share=True):
 
 class GpuSpec:
     """Speculative-decoding cycles through the library: history appended
-    once, then per cycle gamma + 1 tokens appended (kv_append), verified as
-    one causal chunk (paged_attn_chunk) and rolled back to the committed
-    length (kvpool_truncate)."""
+    once, then per cycle gamma + 1 tokens appended (kv_append; an 8-bit pool:
+    kv_append_q8), verified as one causal chunk (paged_attn_chunk /
+    paged_attn_chunk_q8) and rolled back to the committed length
+    (kvpool_truncate)."""
 
-    def __init__(self, sw, fill_nan=True):
+    def __init__(self, sw, fill_nan=True, quantized=False):
         self.sw = sw
         S = sw.num_seqs
-        self.c = PagedKVCache(sw.num_blocks, sw.n_kv, sw.head_dim, sw.block_size, torch_dtype(sw.dtype), S,
-                              sw.table_stride, alloc_order=sw.alloc_order, fill_nan=fill_nan,
-                              poison_workspace=fill_nan)
+        self.c = PagedKVCache(sw.num_blocks, sw.n_kv, sw.head_dim, sw.block_size,
+                              torch.int8 if quantized else torch_dtype(sw.dtype), S, sw.table_stride,
+                              alloc_order=sw.alloc_order, fill_nan=fill_nan, poison_workspace=fill_nan)
         self.lens = np.array(sw.hist_lens, dtype=np.int64)
         for s in range(S):
             self.c.ensure(s, int(self.lens[s]))

@@ -65,3 +65,46 @@ class OracleSpec:
         for s, r in enumerate(self.rows):
             t[s, :len(r.blocks)] = r.blocks
         return t
+
+
+class OracleSpecQ8(OracleSpec):
+    """The same cycles over an 8-bit pool: codes (unwritten: -128) and one
+    fp32 scale per (block, kv head, slot) (unwritten: NaN); verification
+    attends over s * code of the committed history plus the cycle's tokens."""
+
+    def __init__(self, sw):
+        self.sw = sw
+        B = sw.block_size
+        shape = (sw.num_blocks, sw.n_kv, B, sw.head_dim)
+        self.pool_k = np.full(shape, oracle.QUANT_POISON_CODE, dtype=np.int8)
+        self.pool_v = self.pool_k.copy()
+        self.scale_k = np.full(shape[:3], np.nan, dtype=np.float32)
+        self.scale_v = self.scale_k.copy()
+        self.alloc = oracle.BlockAllocator(sw.num_blocks, sw.alloc_order)
+        self.rows = [oracle.SequenceBlocks(B) for _ in range(sw.num_seqs)]
+        self.lens = np.array(sw.hist_lens, dtype=np.int64)
+        self.hist = [(sw.hist_k[s], sw.hist_v[s]) for s in range(sw.num_seqs)]
+        for s in range(sw.num_seqs):
+            self.rows[s].ensure(self.alloc, int(self.lens[s]))
+            oracle.append_quantized(self.pool_k, self.pool_v, self.scale_k, self.scale_v, self.rows[s].blocks, 0,
+                                    sw.hist_k[s], sw.hist_v[s], B, sw.dtype)
+
+    def append_cycle(self, c):
+        sw = self.sw
+        for s in range(sw.num_seqs):
+            self.rows[s].ensure(self.alloc, int(self.lens[s]) + sw.gamma + 1)
+            oracle.append_quantized(self.pool_k, self.pool_v, self.scale_k, self.scale_v, self.rows[s].blocks,
+                                    int(self.lens[s]), sw.cyc_k[c][s], sw.cyc_v[c][s], sw.block_size, sw.dtype)
+
+    def verify(self, c):
+        sw = self.sw
+        g1 = sw.gamma + 1
+        outs = []
+        for s in range(sw.num_seqs):
+            K = oracle.quantized_rows(np.concatenate([self.hist[s][0], sw.cyc_k[c][s]]), sw.dtype).transpose(1, 0, 2)
+            V = oracle.quantized_rows(np.concatenate([self.hist[s][1], sw.cyc_v[c][s]]), sw.dtype).transpose(1, 0, 2)
+            L = int(self.lens[s])
+            q = oracle.widen(sw.cyc_q[c][s * g1:(s + 1) * g1], sw.dtype)
+            o, _, _ = oracle.attention(q, K, V, sw.scale, np.arange(L, L + g1))
+            outs.append(o)
+        return np.concatenate(outs)

@@ -124,3 +124,25 @@ def test_full_size_chunked_prefill_mix_every_row():
     worst, lworst, rows = _check_every_row(wl, out, lse)
     say(f"  {rows} rows (48 decode + 8192 chunk) x {wl.n_q} heads: worst row rel err {worst:.2e}, "
         f"lse {lworst:.2e}")
+
+
+def test_row_error_budget_matrix_core_vs_vector_alu_c2():
+    """Configuration 2 through the two decode tile maths: the balanced pass
+    (four heads per kv head: both products on the matrix cores, the weights
+    rounded to bf16 for the output product) and the fixed-split pass
+    (split 256: vector ALU, fp32 weights). Both must meet the bf16 bar on
+    every row; the printed worst and mean row errors are the measured
+    budget of each."""
+    wl = config_workload(2)
+    c = build_gpu_cache(wl, fill_nan=False)
+    refs = [oracle.contiguous_attend(wl, s)[0] for s in range(wl.num_seqs)]
+    ref = np.concatenate(refs)
+    scale = np.abs(ref).max(axis=-1)
+    from gpu_harness import run_decode
+    for split, name in ((0, "matrix cores (bf16 weights)"), (256, "vector ALU (fp32 weights)")):
+        out, _ = run_decode(c, wl, split)
+        got = out_f64(out, BF16)
+        rel = np.abs(got - ref).max(axis=-1) / scale
+        check_rows(got, ref, BF16, f"config 2 split {split}")
+        say(f"  {name}: worst row rel err {rel.max():.3e}, mean {rel.mean():.3e}, "
+            f"99th pct {np.percentile(rel, 99):.3e}")

@@ -140,3 +140,81 @@ def test_forked_branches_match_the_oracle(case):
         c.release(NP + b)
         c.release(NP + b)
     assert c.pool.kvpool_num_free() == fw.num_blocks
+
+
+def oracle_replay_q8(fw):
+    """oracle_replay over an 8-bit pool: codes (unwritten -128) and scales
+    (unwritten NaN) written by the oracle's quantising append, both copied
+    block by block on copy-on-write."""
+    B = fw.block_size
+    a = oracle.BlockAllocator(fw.num_blocks, fw.alloc_order)
+    shape = (fw.num_blocks, fw.n_kv, B, fw.head_dim)
+    ck = np.full(shape, oracle.QUANT_POISON_CODE, dtype=np.int8)
+    cv = ck.copy()
+    sk = np.full(shape[:3], np.nan, dtype=np.float32)
+    sv = sk.copy()
+    prompts = [oracle.SequenceBlocks(B) for _ in range(fw.num_prompts)]
+    branches = [oracle.SequenceBlocks(B) for _ in range(fw.num_branches)]
+    for p, P in enumerate(fw.prompt_lens):
+        prompts[p].ensure(a, int(P))
+        oracle.append_quantized(ck, cv, sk, sv, prompts[p].blocks, 0, fw.prompt_k[p], fw.prompt_v[p], B, fw.dtype)
+    for b in range(fw.num_branches):
+        branches[b].fork(a, prompts[fw.prompt_of(b)], int(fw.prompt_lens[fw.prompt_of(b)]))
+    for p in range(fw.num_prompts):
+        prompts[p].release(a)
+    copies = 0
+    for b in range(fw.num_branches):
+        P, g = int(fw.prompt_lens[fw.prompt_of(b)]), int(fw.own_lens[b])
+        pairs = branches[b].cow(a, P, g)
+        copies += len(pairs)
+        oracle.copy_blocks(ck, cv, pairs)
+        oracle.copy_blocks(sk, sv, pairs)
+        branches[b].ensure(a, P + g)
+    for b in range(fw.num_branches):
+        P = int(fw.prompt_lens[fw.prompt_of(b)])
+        oracle.append_quantized(ck, cv, sk, sv, branches[b].blocks, P, fw.own_k[b], fw.own_v[b], B, fw.dtype)
+    return a, ck, cv, sk, sv, branches, copies
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8)])
+def test_forked_branches_over_an_8bit_pool(n_q, n_kv):
+    """Copy-on-write composes with the 8-bit cache: the shared tail block's
+    codes and scales are copied (kv_copy_blocks_q8) before a branch writes,
+    codes, scales and tables equal the oracle's bit for bit, and decode over
+    the aliased tables (paged_attn_decode_q8) meets the bar against attention
+    over s * code of each branch's contiguous history."""
+    prompt_lens = [100, 512, 16, 1]
+    fw = build_fork_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, prompt_lens=prompt_lens,
+                             branches=3, seed=34,
+                             own_lens=np.random.default_rng(34).integers(1, 40, size=len(prompt_lens) * 3))
+    say(f"8-bit forks {n_q}/{n_kv}: prompts {fw.prompt_lens.tolist()} x {fw.branches}")
+    a, ck, cv, sk, sv, branches, copies = oracle_replay_q8(fw)
+    c, gcopies = build_gpu_fork_cache(fw, quantized=True)
+    NP, NB = fw.num_prompts, fw.num_branches
+    assert copies == gcopies and copies > 0
+    for b in range(NB):
+        assert c.table[NP + b, :c.held[NP + b]].tolist() == branches[b].blocks
+    assert c.pool.kvpool_free_ids().tolist() == a.free_ids()
+    assert np.array_equal(c.k_cache.cpu().numpy(), ck) and np.array_equal(c.v_cache.cpu().numpy(), cv)
+    assert np.array_equal(c.k_scale.cpu().numpy().view(np.uint32), sk.view(np.uint32))
+    assert np.array_equal(c.v_scale.cpu().numpy().view(np.uint32), sv.view(np.uint32))
+    import paged_kv_cache_17_amd as pkv
+    lens = fw.branch_lens()
+    q = raw_to_torch(fw.q, fw.dtype)
+    out = torch.empty_like(q)
+    lse = torch.empty((NB, fw.n_q), dtype=torch.float32, device="cuda")
+    ws = c.workspace(NB, fw.n_q, int(lens.max()))
+    pkv.paged_attn_decode_q8(out, lse, q, c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.table_dev[NP:], i32(lens),
+                             int(lens.max()), fw.scale, ws)
+    torch.cuda.synchronize()
+    got = out_f64(out, fw.dtype)
+    for b in range(NB):
+        P = fw.prompt_of(b)
+        K = oracle.quantized_rows(np.concatenate([fw.prompt_k[P], fw.own_k[b]]), fw.dtype).transpose(1, 0, 2)
+        V = oracle.quantized_rows(np.concatenate([fw.prompt_v[P], fw.own_v[b]]), fw.dtype).transpose(1, 0, 2)
+        ref, ref_lse, _ = oracle.attention(oracle.widen(fw.q[b:b + 1], fw.dtype), K, V, fw.scale, [int(lens[b]) - 1])
+        check_rows(got[b:b + 1], ref, fw.dtype, f"8-bit fork branch {b}")
+        check_lse(lse[b].cpu().numpy().astype(np.float64), ref_lse[0], fw.dtype, f"8-bit fork branch {b}")
+    for b in range(NB):
+        c.release(NP + b)
+    assert c.pool.kvpool_num_free() == fw.num_blocks

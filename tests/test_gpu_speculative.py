@@ -65,3 +65,34 @@ def test_verify_and_rollback_cycles(case, split):
     for s in range(sw.num_seqs):
         gpu.c.release(s)
     assert gpu.c.pool.kvpool_num_free() == sw.num_blocks
+
+
+@pytest.mark.parametrize("case", ["bf16-gqa", "bf16-gamma7"])
+def test_verify_and_rollback_cycles_over_an_8bit_pool(case):
+    """The same cycles over an 8-bit pool: kv_append_q8 writes each cycle's
+    tokens, paged_attn_chunk_q8 verifies them as one causal chunk, and
+    kvpool_truncate rolls back. Codes, scales and tables bit-exact against
+    the oracle's quantised replay; outputs within the bar against attention
+    over s * code of the committed history plus the cycle's tokens."""
+    from spec_replay import OracleSpecQ8
+    sw = build_spec_workload(**CASES[case])
+    print(f"8-bit speculative {case}: lens {sw.hist_lens.tolist()}, accepted {sw.accepted.tolist()}", flush=True)
+    ora = OracleSpecQ8(sw)
+    gpu = GpuSpec(sw, quantized=True)
+    for c in range(sw.cycles):
+        ora.append_cycle(c)
+        gpu.append_cycle(c)
+        out = gpu.verify(c)
+        torch.cuda.synchronize()
+        assert np.array_equal(gpu.c.table, ora.tables())
+        assert np.array_equal(gpu.c.k_cache.cpu().numpy(), ora.pool_k)
+        assert np.array_equal(gpu.c.v_cache.cpu().numpy(), ora.pool_v)
+        assert np.array_equal(gpu.c.k_scale.cpu().numpy().view(np.uint32), ora.scale_k.view(np.uint32))
+        assert np.array_equal(gpu.c.v_scale.cpu().numpy().view(np.uint32), ora.scale_v.view(np.uint32))
+        check_rows(out_f64(out, sw.dtype), ora.verify(c), sw.dtype, f"8-bit {case} cycle {c}")
+        ora.rollback(c)
+        gpu.rollback(c)
+        assert np.array_equal(gpu.c.table, ora.tables())
+    for s in range(sw.num_seqs):
+        gpu.c.release(s)
+    assert gpu.c.pool.kvpool_num_free() == sw.num_blocks

@@ -252,3 +252,29 @@ def test_one_call_steps_reject_bad_arguments_before_any_launch():
 
     assert chunk(kn=0) == -1
     assert chunk(total_q=0) == 0
+
+
+def test_8bit_chunk_and_copy_reject_bad_arguments_before_any_launch():
+    """paged_attn_chunk_q8 and kv_copy_blocks_q8: shape, null-pointer,
+    support and alignment errors come back before any device call."""
+    lib = pkv.load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
+
+    def chunk(out=16, kc=16, ks=16, n_q=32, n_kv=8, d=128, max_q=5, total_q=5, S=1):
+        return lib.paged_attn_chunk_q8(p(out), None, p(16), p(16), p(kc), p(16), p(ks), p(16), p(16), 4, p(16), S,
+                                       total_q, max_q, 64, 8, n_q, n_kv, d, 16, 0.25, p(256), 1 << 20, None)
+
+    assert chunk(n_q=3, n_kv=2) == -2
+    assert chunk(out=0) == -1 and chunk(kc=0) == -1 and chunk(ks=0) == -1
+    assert chunk(d=64) == -3                          # head_dim 128 only
+    assert chunk(max_q=9) == -3                       # 9 queries x 4 heads > 32 rows per kv head
+    assert chunk(kc=24) == -2                         # codes not 16-byte aligned
+    assert chunk(ks=20) == -2                         # scales not 16-byte aligned
+    assert chunk(total_q=0) == 0
+
+    def copy(kc=16, n=2, nb=8):
+        return lib.kv_copy_blocks_q8(p(kc), p(16), p(16), p(16), p(16), p(16), n, nb, 8, 128, 16, None)
+
+    assert copy(kc=0) == -1
+    assert copy(nb=0) == -2 and copy(n=-1) == -2
+    assert copy(n=0) == 0
