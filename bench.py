@@ -410,7 +410,9 @@ def bench_verify(args):
     every (sequence, kv head, block) tile with the 20 (query, head) rows of a
     kv head on the matrix cores, then the merge) and with the VALU split path
     (split_tokens 256) beside it. The pass reads each sequence's K/V once:
-    the roofline is HBM; avg_launch_ms is the split pass alone."""
+    the roofline is HBM; avg_launch_ms is the split pass alone. With
+    ``--kv int8`` the pool holds 8-bit codes and scales: kv_append_q8, then
+    paged_attn_chunk_q8 (no split-path comparison)."""
     import torch
     import paged_kv_cache_17_amd as pkv
     from paged_kv_cache_17_amd.replay import GpuSpec
@@ -420,7 +422,8 @@ def bench_verify(args):
     pkv.load_library()
     sw = verify_workload()
     g1 = sw.gamma + 1
-    gpus = [GpuSpec(sw, fill_nan=False) for _ in range(args.copies)]
+    quant = args.kv == "int8"
+    gpus = [GpuSpec(sw, fill_nan=False, quantized=quant) for _ in range(args.copies)]
     for g in gpus:
         g.append_cycle(0)
     torch.cuda.synchronize()
@@ -436,7 +439,7 @@ def bench_verify(args):
             if ev is not None:
                 pkv.pkv_set_profile_events(*ev)
             lens_d = i32_after[i % len(gpus)]   # device copies made once, outside the timed steps
-            if args.separate:
+            if args.separate or quant:   # an 8-bit pool: kv_append_q8, then paged_attn_chunk_q8
                 pkv.pkv_set_profile_events(None, None)
                 g.c.append(k, v, i32_lens[i % len(gpus)], g.q_start, stream=stream)
                 if ev is not None:
@@ -477,20 +480,24 @@ def bench_verify(args):
     i32_after = [i32(g.lens + g1) for g in gpus]
     max_after = int(max((g.lens + g1).max() for g in gpus))
     ms_m, kern_m = run(0)
-    ms_v, _ = run(256)
+    ms_v = None if quant else run(256)[0]
     tokens = sw.num_seqs * g1
+    if quant:   # codes + one fp32 scale per token and kv head, K and V
+        kv_bytes = int(lens.sum()) * sw.n_kv * (sw.head_dim + 4) * 2
     line = {
         "metric": METRIC, "value": tokens / (ms_m * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_m, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": sw.name, "num_seqs": sw.num_seqs, "chunk": g1, "n_q": sw.n_q, "n_kv": sw.n_kv,
+        "vs_baseline": None, "dtype": "int8 K/V, bf16 q/out, fp32 accumulate" if quant else "bf16",
+        "data": "synthetic",
+        "config": {"workload": sw.name + ("-kv-int8" if quant else ""), "num_seqs": sw.num_seqs, "chunk": g1, "n_q": sw.n_q, "n_kv": sw.n_kv,
                    "head_dim": sw.head_dim, "block_size": sw.block_size, "context_tokens": int(lens.sum()),
                    "kv_bytes": kv_bytes, "cache_copies": len(gpus)},
         "roofline": {"kernel": "balanced split pass (matrix cores), 5-query chunks", "bound": "hbm",
                      "achieved": kv_bytes / (kern_m * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": kv_bytes / (kern_m * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
                      "avg_launch_ms": kern_m, "algorithmic_bytes": kv_bytes, "algorithmic_flops": flops},
-        "valu_split_path": {"value": tokens / (ms_v * 1e-3), "ms_per_step": ms_v, "split_tokens": 256},
+        "valu_split_path": None if quant else {"value": tokens / (ms_v * 1e-3), "ms_per_step": ms_v,
+                                               "split_tokens": 256},
     }
     print(json.dumps(line), flush=True)
 
