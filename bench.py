@@ -72,6 +72,9 @@ COUNTERS = {
     "decode": (os.path.join(ROOT, "profiles", "decode_split_c2_counters.txt"),
                ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_mfma.h",
                 "paged_kv_cache_17_amd/csrc/decode_tile.h", "paged_kv_cache_17_amd/csrc/device_common.h"]),
+    "decode_q8": (os.path.join(ROOT, "profiles", "decode_split_c2_int8_counters.txt"),
+                  ["paged_kv_cache_17_amd/csrc/decode_balanced.hip", "paged_kv_cache_17_amd/csrc/decode_mfma.h",
+                   "paged_kv_cache_17_amd/csrc/decode_tile.h", "paged_kv_cache_17_amd/csrc/device_common.h"]),
     "chunk": (os.path.join(ROOT, "profiles", "chunk_mfma_c5_counters.txt"),
               ["paged_kv_cache_17_amd/csrc/chunk_mfma.hip", "paged_kv_cache_17_amd/csrc/device_common.h"]),
 }
@@ -87,8 +90,9 @@ def kernel_source_hash(kind="decode"):
 
 
 def measured_traffic(config_name, kind="decode"):
-    """HBM bytes per launch of the decode split kernel (kind "decode") or the
-    chunk kernel (kind "chunk") from the committed rocprofv3 counter summary
+    """HBM bytes per launch of the decode split kernel (kind "decode"; 8-bit
+    pool "decode_q8") or the chunk kernel (kind "chunk") from the committed
+    rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a
     plain copy of known size), or None if absent, stale or for another
     workload."""
@@ -680,7 +684,8 @@ def main():
         line["roofline"] = {"kernel": "decode split pass" + (" (with the append)" if fused else ""),
                             "bound": "hbm", "achieved": achieved,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                            "traffic": None if quant else measured_traffic(CONFIG_NAMES[args.config]),
+                            "traffic": measured_traffic(CONFIG_NAMES[args.config] + ("-kv-int8" if quant else ""),
+                                                        "decode_q8" if quant else "decode"),
                             "avg_launch_ms": kern_avg,
                             "algorithmic_bytes": dec_bytes, "source_sha": kernel_source_hash("decode")}
         tile_pairs = int(sum(-(-int(L) // wl.block_size) for L in wl.seq_lens[:nd])) * wl.n_kv
