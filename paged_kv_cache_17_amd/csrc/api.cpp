@@ -265,7 +265,6 @@ extern "C" int sample_tokens(int32_t* token, int32_t* kept, const float* logits,
     if (rows < 0 || vocab < 1 || ld < vocab) return PKV_ERR_INVALID_ARGUMENT;
     if (vocab > pkv::kSampleChunk * pkv::kSampleMaxCand) return PKV_ERR_INVALID_ARGUMENT;
     if (static_cast<int64_t>(rows) * pkv::sample_chunks(vocab) > INT32_MAX) return PKV_ERR_INVALID_ARGUMENT;
-    if (static_cast<int64_t>(rows) * pkv::kSampleRowSplit > INT32_MAX) return PKV_ERR_INVALID_ARGUMENT;
     if (rows == 0) return PKV_OK;
     if (!token || !logits || !temperature || !top_k || !top_p || !u || !workspace) return PKV_ERR_NULL_POINTER;
     if (workspace_bytes < pkv::sample_workspace_bytes(rows, vocab)) return PKV_ERR_WORKSPACE_TOO_SMALL;

@@ -89,36 +89,42 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
 // through a candidate pass (chunks of kSampleChunk logits, each keeping its
 // own top-k) and are finished from those candidates; rows with top-k off
 // (vocabularies of at most kSampleHistChunks chunks) through per-chunk mass
-// histograms; the others by one workgroup over the whole row.
+// histograms and per-chunk lists of the tokens near each chunk's own top-p
+// boundary; the others by one workgroup over the whole row.
 constexpr int kSampleChunk = 8192;      // logits per candidate-pass workgroup
 constexpr int kSampleMaxK = 256;        // largest top-k on the candidate path
 constexpr int kSampleMaxCand = 8192;    // candidates one finishing workgroup holds
 constexpr int kSampleHistBins = 2048;   // mass histogram bins per chunk (top 11 bits of the order key)
 constexpr int kSampleHistChunks = 64;   // widest row (in chunks) the histogram path merges
+constexpr int kSampleListCap = 4096;    // tokens one chunk lists around its own top-p boundary
+constexpr int kSampleWinBins = 5;       // the bins of that list: the chunk's boundary bin and two on each side
+constexpr int kSampleBucketCap = 12288; // boundary-bin tokens of a row the finishing pass holds
 inline int sample_chunks(int vocab) { return (vocab + kSampleChunk - 1) / kSampleChunk; }
+inline bool sample_hist_rows(int vocab) { return sample_chunks(vocab) <= kSampleHistChunks; }
 // Per (row, chunk): a region of kSampleMaxK (key, index) candidates or, when
 // the row has at most kSampleHistChunks chunks, of kSampleHistBins fp64
-// masses (the candidates fit in it); then, for those rows, a 16-byte
-// header per (row, chunk) after all regions.
+// masses (the candidates fit in it). For such vocabularies the regions are
+// followed by, per (row, chunk), a 16-byte header, 64 fp64 sums (every 32nd
+// bin's), a list of kSampleListCap 8-byte entries and a SampleChunkTally.
 inline size_t sample_region_bytes(int vocab) {
-    return sample_chunks(vocab) <= kSampleHistChunks ? static_cast<size_t>(kSampleHistBins) * 8u
-                                                     : static_cast<size_t>(kSampleMaxK) * 8u;
+    return sample_hist_rows(vocab) ? static_cast<size_t>(kSampleHistBins) * 8u
+                                   : static_cast<size_t>(kSampleMaxK) * 8u;
 }
-constexpr int kSampleBucketCap = 12288;  // tokens of a row's top-p boundary bin the histogram path holds
-constexpr int kSampleRowSplit = 4;       // workgroups per histogram row in the gathering pass
-// ... and per histogram row, after the headers: the boundary bin's tokens
-// (kSampleBucketCap 8-byte entries, a quarter per gathering workgroup) and
-// 64 bytes of counters.
+struct SampleChunkTally {  // histogram rows with top-p on, per chunk, written by the chunk pass
+    uint32_t wlo, whi;     // the bins whose tokens the chunk listed (around its own top-p boundary)
+    uint32_t listed[4];    // tokens listed by each wave (0xFFFFFFFF: more than its share)
+    uint32_t up[4];        // tokens above the window, per wave
+    uint32_t inbin[4][kSampleWinBins];  // tokens per wave and window bin (wlo + i)
+};
 inline size_t sample_workspace_bytes(int rows, int vocab) {
-    const bool hist = sample_chunks(vocab) <= kSampleHistChunks;
-    const size_t per = sample_region_bytes(vocab) + (hist ? 16u : 0u);
-    const size_t row_extra = hist ? static_cast<size_t>(kSampleBucketCap) * 8u + 64u : 0u;
-    return static_cast<size_t>(rows) * (sample_chunks(vocab) * per + row_extra);
+    const bool hist = sample_hist_rows(vocab);
+    const size_t per = sample_region_bytes(vocab) + (hist ? 16u + 512u + kSampleListCap * 8u + sizeof(SampleChunkTally) : 0u);
+    return static_cast<size_t>(rows) * sample_chunks(vocab) * per;
 }
 struct SampleChunkHead {
     float mc;          // largest z of the chunk
     float pad;
-    double total;      // sum of exp(z - mc) over the chunk (written when top-p is off)
+    double total;      // sum of exp(z - mc) over the chunk
 };
 struct SampleArgs {
     const float* logits;         // [rows][ld], the first vocab entries used

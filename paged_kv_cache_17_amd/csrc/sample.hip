@@ -7,7 +7,8 @@
 //  * z = logit / T (fp32, correctly rounded), ordered by decreasing z with
 //    ties going to the lower index;
 //  * top-k (k > 0): keep the first k of that order;
-//  * masses p = exp(z - max z), evaluated in fp64;
+//  * masses p = exp(z - max z), evaluated in fp64 (exp_f64.h; the z of
+//    each logit by an fp64 product that rounds as the division would);
 //  * top-p (p < 1): keep the shortest prefix of the order whose cumulative
 //    mass reaches p times the kept total - the boundary token and the
 //    largest are always kept;
@@ -29,11 +30,15 @@
 //  * histogram path (top-k off, rows of at most kSampleHistChunks chunks):
 //    each chunk workgroup records its largest z and, with top-p on, the
 //    fp64 masses exp(z - chunk max) summed per bin of the key's top 11
-//    bits. One workgroup per row rescales and adds the chunks' histograms,
-//    finds the bin holding the top-p boundary, gathers that bin's tokens
-//    into LDS in one pass over the row and finishes the boundary there
-//    (two more key digits, then index digits among tied keys). The draw
-//    picks the chunk from per-chunk kept masses and walks that chunk only.
+//    bits (as suffix sums), and lists its tokens in a few bins around its
+//    own top-p boundary with a count per bin. One workgroup per row
+//    rescales and adds the chunks' sums to find the bin holding the row's
+//    boundary, takes that bin's tokens from the chunks' lists (a chunk
+//    whose window misses the bin is scanned again, unless its largest z
+//    lies below it) and finishes the boundary there (two more key digits,
+//    then index digits among tied keys). The draw picks the chunk from
+//    per-chunk kept masses and walks that chunk only (prefetched while
+//    the boundary is found, on a guess from the bin's masses).
 //  * whole-row path (top-k between kSampleMaxK and the vocabulary, rows
 //    wider than kSampleHistChunks chunks, or a boundary bin of more than
 //    kBucketCap tokens): one 1024-thread workgroup per row finds the k-th
@@ -43,6 +48,7 @@
 // The second kernel runs the finishing step: each workgroup takes its row's
 // path.
 #include "device_common.h"
+#include "exp_f64.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -52,12 +58,26 @@ constexpr int kChunkThreads = 256;
 constexpr int kPerThread = kSampleChunk / kChunkThreads;
 constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kChunkKeep = 512;              // keys at or above a chunk's bound kept in LDS
-constexpr int kThreads = 1024;               // second kernel: one row per workgroup
+constexpr int kThreads = 1024;               // finishing kernel: one row per workgroup
 constexpr int kWaves = kThreads / kWave;
 static_assert(kPerThread * kChunkThreads == kSampleChunk, "chunk split");
 static_assert(kSampleMaxK <= 4 * kWave, "one wave scans the top-k (4 per lane)");
 static_assert(kSampleMaxCand % kThreads == 0, "candidates per thread");
 static_assert(kChunkKeep + 2048 / 2 <= kSampleHistBins, "chunk pool: keep list and 2048 u32 digit bins");
+
+// 2^(j/32) for exp_tab, copied into LDS by each kernel that evaluates
+// masses (32 threads, before its first barrier). The entries are selected
+// from literals, not loaded: a load here would have to wait for every load
+// the thread has in flight.
+__shared__ double s_exp2[32];
+__device__ __forceinline__ void put_exp2_table() {
+    const int j = threadIdx.x & 31;
+    double t = kExp2Frac[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) t = j == i ? kExp2Frac[i] : t;
+    if (threadIdx.x < 32) s_exp2[threadIdx.x] = t;
+}
+__device__ __forceinline__ double mass_exp(double x) { return exp_nonpos(x, s_exp2); }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -91,6 +111,29 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// base[i] through a 32-bit byte offset from a wave-uniform base (indices
+// within a row stay below 2^26), so that each load needs one address
+// register rather than two.
+__device__ __forceinline__ float load_at(const float* base, int i) {
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + static_cast<uint32_t>(i) * 4u);
+}
+
+// z = x / T rounded to fp32 (T > 0 finite, inv = 1 / T rounded to fp64),
+// as the division itself would give it. The fp64 product x * inv is within
+// a relative 2^-52 of x / T. A quotient of two fp32 values never equals the
+// midpoint between two adjacent normal fp32 values (with x = X 2^a, T = M
+// 2^c and the midpoint m = N 2^b, X, M, N odd, N of 25 bits, x = m T would
+// need the odd integer N M of 25 or more bits to equal X), and the numerator
+// of x / T - m is a nonzero multiple of 2^min(a, b + c), which puts x / T
+// more than 2^-49 (relative) away from every such midpoint. So rounding the
+// product to fp32 gives the correctly rounded quotient whenever the result
+// lies above the smallest normal value; at or below it (the subnormals,
+// where exact midpoints do occur), and for NaN, the division is done.
+__device__ __forceinline__ float div_by_t(float x, float T, double inv) {
+    const float q = static_cast<float>(static_cast<double>(x) * inv);
+    return fabsf(q) > 0x1p-126f ? q : x / T;
 }
 // (key, index) as one 64-bit value whose descending order is decreasing z
 // with ties to the lower index; 0 is below every real candidate.
@@ -132,20 +175,27 @@ __device__ __forceinline__ SampleChunkHead* chunk_head(const SampleArgs& a, int 
            static_cast<size_t>(row) * a.chunks + s;
 }
 
-// Histogram rows: the boundary bin's tokens gathered by the row's
-// workgroups (workgroup g writes the g-th quarter), and counters: [0]
-// workgroups done, [2 + 2g] and [3 + 2g] workgroup g's tokens (0xFFFFFFFF:
-// more than its quarter) and tokens above the bin; after the chunk headers.
-__device__ __forceinline__ unsigned char* row_extra(const SampleArgs& a, int row) {
-    return a.ws + static_cast<size_t>(a.rows) * a.chunks * (a.region + sizeof(SampleChunkHead)) +
-           static_cast<size_t>(row) * (static_cast<size_t>(kSampleBucketCap) * 8u + 64u);
+// Histogram rows, after the chunk headers: per (row, chunk) the suffix sums
+// of every 32nd bin (I[32 g], g < 64, contiguous), then per (row, chunk)
+// the list of the chunk's tokens near its own top-p boundary (one region of
+// kWinWaveCap per wave), then per (row, chunk) its tally.
+constexpr int kGroups = kSampleHistBins / 32;
+__device__ __forceinline__ size_t hist_base(const SampleArgs& a) {
+    return static_cast<size_t>(a.rows) * a.chunks * (a.region + sizeof(SampleChunkHead));
 }
-__device__ __forceinline__ uint64_t* row_list(const SampleArgs& a, int row) {
-    return reinterpret_cast<uint64_t*>(row_extra(a, row));
+__device__ __forceinline__ double* chunk_coarse(const SampleArgs& a, int row, int s) {
+    return reinterpret_cast<double*>(a.ws + hist_base(a)) + (static_cast<size_t>(row) * a.chunks + s) * kGroups;
 }
-__device__ __forceinline__ uint32_t* row_counters(const SampleArgs& a, int row) {
-    return reinterpret_cast<uint32_t*>(row_extra(a, row) + static_cast<size_t>(kSampleBucketCap) * 8u);
+__device__ __forceinline__ uint64_t* chunk_list(const SampleArgs& a, int row, int s) {
+    return reinterpret_cast<uint64_t*>(a.ws + hist_base(a) + static_cast<size_t>(a.rows) * a.chunks * kGroups * 8u) +
+           (static_cast<size_t>(row) * a.chunks + s) * kSampleListCap;
 }
+__device__ __forceinline__ SampleChunkTally* chunk_tally(const SampleArgs& a, int row, int s) {
+    return reinterpret_cast<SampleChunkTally*>(a.ws + hist_base(a) +
+                                               static_cast<size_t>(a.rows) * a.chunks * (kGroups + kSampleListCap) * 8u) +
+           static_cast<size_t>(row) * a.chunks + s;
+}
+constexpr int kWinWaveCap = kSampleListCap / kChunkWaves;   // one chunk-pass wave's share of the list
 
 __device__ __forceinline__ void write_result(const SampleArgs& a, int row, int token, int kk, int kp) {
     a.token[row] = token;
@@ -226,8 +276,14 @@ __device__ __forceinline__ void chunk_digit(const uint32_t (&key)[kPerThread], i
 // top-p on, its fp64 masses exp(z - chunk max) per bin of the key's top 11
 // bits, stored as inclusive suffix sums (I[b] = mass of the bins b and
 // above; the bins of every chunk line up, so the row adds them after
-// rescaling). Keys of 0 lie past the chunk's end.
-__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s,
+// rescaling), and the list of its tokens in a window of bins around its own
+// top-p boundary b_c (the largest b with I[b] >= top-p x I[0]): the
+// kSampleWinBins bins from b_c - 2, as (key, index) composites. The row's boundary bin, found
+// by the finishing pass from all chunks, usually lies in every chunk's
+// window; a chunk whose window misses it is scanned again there. Keys of 0
+// lie past the chunk's end; element i of this thread has index jb + i *
+// kChunkThreads.
+__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s, int jb,
                                              const uint32_t (&key)[kPerThread], double* s_hm, uint32_t* s_tw) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -251,7 +307,7 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         if (!key[i]) continue;
-        const double m = exp(static_cast<double>(key_value(key[i])) - mcd);
+        const double m = mass_exp(static_cast<double>(key_value(key[i])) - mcd);
         if (hist) atomicAdd(&s_hm[key[i] >> 21], m);
         else tot += m;
     }
@@ -282,9 +338,68 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
         double* out = chunk_hist(a, row, s);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) out[kPer * tid + i] = l[i] + above;
+        static_assert(32 % kPer == 0, "group starts fall on a thread's first bin");
+        if ((kPer * tid) % 32 == 0) chunk_coarse(a, row, s)[kPer * tid / 32] = l[0] + above;
         if (tid == 0) {
             h->mc = mc;
             h->total = l[0] + above;
+        }
+        // the window: b_c from the suffix sums (non-increasing in b, so the bins
+        // reaching the need are those up to b_c)
+        double tot = 0.0;
+#pragma unroll
+        for (int w = 0; w < kChunkWaves; ++w) tot += s_wt[w];
+        const double need = static_cast<double>(a.top_p[row]) * tot;
+        uint32_t lb = 0;   // 1 + the largest bin of this thread reaching the need
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (l[i] + above >= need) lb = max(lb, static_cast<uint32_t>(kPer * tid + i + 1));
+        lb = wave_max_u32(lb);
+        __shared__ uint32_t s_lb[kChunkWaves];
+        if (lane == 0) s_lb[wave] = lb;
+        __syncthreads();
+        lb = s_lb[0];
+#pragma unroll
+        for (int w = 1; w < kChunkWaves; ++w) lb = max(lb, s_lb[w]);
+        const uint32_t bc = lb > 0u ? lb - 1u : 0u;   // I[0] reaches any need below the total
+        const uint32_t wlo = bc >= 2u ? bc - 2u : 0u;
+        const uint32_t whi = min(wlo + static_cast<uint32_t>(kSampleWinBins - 1), static_cast<uint32_t>(kSampleHistBins - 1));
+        // each wave lists its tokens in its share of the list; per-lane counts per
+        // window bin in the bytes of `per` (at most kPerThread each)
+        static_assert(kPerThread < 256 && kSampleWinBins <= 8, "byte counters");
+        uint64_t* list = chunk_list(a, row, s) + wave * kWinWaveCap;
+        uint32_t n = 0, up = 0;
+        uint64_t per = 0;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const uint32_t bn = key[i] >> 21;
+            const bool inw = key[i] != 0u && bn >= wlo && bn <= whi;
+            up += key[i] != 0u && bn > whi ? 1u : 0u;
+            per += inw ? 1ull << (8u * (bn - wlo)) : 0ull;
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(inw);
+            if (m) {
+                const uint32_t slot =
+                    n + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+                if (inw && slot < static_cast<uint32_t>(kWinWaveCap))
+                    list[slot] = composite(key[i], static_cast<uint32_t>(jb + i * kChunkThreads));
+                n += static_cast<uint32_t>(__builtin_popcountll(m));
+            }
+        }
+        up = wave_sum_u32(up);
+        uint32_t nb[kSampleWinBins];
+#pragma unroll
+        for (int q = 0; q < kSampleWinBins; ++q) nb[q] = wave_sum_u32(static_cast<uint32_t>(per >> (8 * q)) & 255u);
+        SampleChunkTally* tl = chunk_tally(a, row, s);
+        if (lane == 0) {
+            tl->listed[wave] = n > static_cast<uint32_t>(kWinWaveCap) ? 0xFFFFFFFFu : n;
+            tl->up[wave] = up;
+#pragma unroll
+            for (int q = 0; q < kSampleWinBins; ++q) tl->inbin[wave][q] = nb[q];
+        }
+        if (tid == 0) {
+            tl->wlo = wlo;
+            tl->whi = whi;
         }
     } else {
         tot = wave_sum_f64(tot);
@@ -300,43 +415,64 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
     }
 }
 
-// One workgroup per (row, chunk), blockIdx.x = row * chunks + chunk.
-// Candidate rows: writes the chunk's min(k, chunk length) best (key, index)
-// pairs to its candidate slots, best first (decreasing key, ties by lower
-// index). Histogram rows: chunk_masses.
-__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void sample_chunk_kernel(SampleArgs a) {
+// One (row, chunk) item of the chunk kernel: the row's parameters and the
+// chunk's bounds; live when the row takes the candidate or the histogram
+// path.
+struct ChunkItem {
+    int row, s, lo, hi, k_eff;
+    float T;
+    bool cand, live;
+};
+
+__device__ __forceinline__ ChunkItem chunk_item(const SampleArgs& a, int it) {
+    ChunkItem c{};
+    c.live = false;
+    if (it >= a.rows * a.chunks) return c;
     const int S = a.chunks;
-    const int row = blockIdx.x / S;
-    const int s = blockIdx.x - row * S;
+    c.row = it / S;
+    c.s = it - c.row * S;
+    c.T = a.temperature[c.row];
+    const int32_t tk = a.top_k[c.row];   // loaded together with T
+    if (!(c.T >= 0.0f)) return c;
+    c.k_eff = c.T > 0.0f ? kept_by_k(tk, a.vocab) : 1;
+    c.cand = on_candidate_path(c.T, c.k_eff, S);
+    if (!c.cand && !on_hist_path(c.T, c.k_eff, a.vocab, S)) return c;
+    const int C = (a.vocab + S - 1) / S;
+    c.lo = c.s * C;
+    c.hi = min(a.vocab, c.lo + C);
+    c.live = c.lo < c.hi;
+    return c;
+}
+
+// Element i of this thread: index lo + i * kChunkThreads + tid. The loads
+// are unconditional (clamped to the last element) so that all of them are
+// in flight together.
+__device__ __forceinline__ void load_item(const SampleArgs& a, const ChunkItem& c, uint32_t (&key)[kPerThread]) {
+    const float* x = a.logits + static_cast<size_t>(c.row) * a.ld;
+    const int jb = c.lo + static_cast<int>(threadIdx.x);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(load_at(x, min(jb + i * kChunkThreads, c.hi - 1)));
+}
+
+// Candidate items: writes the chunk's min(k, chunk length) best (key,
+// index) pairs to its candidate slots, best first (decreasing key, ties by
+// lower index). Histogram items: chunk_masses. `key` holds the loaded
+// logits and becomes their order keys; past the chunk's end the key is 0,
+// which no finite z has (it is a negative NaN's key): such slots land in
+// the lowest bin and are never taken.
+__device__ __forceinline__ void chunk_item_work(const SampleArgs& a, const ChunkItem& c, uint32_t (&key)[kPerThread]) {
+    const int row = c.row, s = c.s, lo = c.lo, hi = c.hi, k_eff = c.k_eff;
+    const float T = c.T;
+    const bool cand = c.cand;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int V = a.vocab;
-    const float T = a.temperature[row];
-    if (!(T >= 0.0f)) return;
-    const int k_eff = T > 0.0f ? kept_by_k(a.top_k[row], V) : 1;
-    const bool cand = on_candidate_path(T, k_eff, S);
-    if (!cand && !on_hist_path(T, k_eff, V, S)) return;
-    const int C = (V + S - 1) / S;
-    const int lo = s * C;
-    const int hi = min(V, lo + C);
-    if (lo >= hi) return;
     const uint32_t want = static_cast<uint32_t>(min(k_eff, hi - lo));
-    const float* x = a.logits + static_cast<size_t>(row) * a.ld;
-
-    // element i of this thread: index lo + i * kChunkThreads + tid. Past the
-    // chunk's end the key is 0, which no finite z has (it is a negative NaN's
-    // key): such slots land in the lowest bin and are never taken.
-    // The loads are unconditional (clamped to the last element) so that all
-    // of them are in flight together.
     const int jb = lo + tid;
-    uint32_t key[kPerThread];
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(x[min(jb + i * kChunkThreads, hi - 1)]);
     if (T > 0.0f) {
+        const double inv = 1.0 / static_cast<double>(T);
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(__uint_as_float(key[i]) / T);
+        for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(div_by_t(__uint_as_float(key[i]), T, inv));
     }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) key[i] = jb + i * kChunkThreads < hi ? order_key(__uint_as_float(key[i])) : 0u;
@@ -345,8 +481,7 @@ void sample_chunk_kernel(SampleArgs a) {
     __shared__ uint64_t s_pool[kSampleHistBins];   // histogram rows: fp64 bins; candidate rows: keep list + digit bins
     __shared__ uint32_t s_tc[kPerThread * kChunkWaves];
     if (!cand) {
-        if (s == 0 && tid == 0) row_counters(a, row)[0] = 0u;   // counted up by the finishing kernel
-        chunk_masses(a, row, s, key, reinterpret_cast<double*>(s_pool), s_tw);
+        chunk_masses(a, row, s, jb, key, reinterpret_cast<double*>(s_pool), s_tw);
         return;
     }
     uint64_t* s_keep = s_pool;
@@ -452,6 +587,17 @@ void sample_chunk_kernel(SampleArgs a) {
         for (uint32_t f = 0; f < kept; ++f) r += s_keep[f] > me;
         if (r < want) out[r] = make_uint2(comp_key(me), static_cast<uint32_t>(comp_index(me)));
     }
+}
+
+// One workgroup per (row, chunk) item, blockIdx.x = row * chunks + chunk.
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void sample_chunk_kernel(SampleArgs a) {
+    const ChunkItem c = chunk_item(a, static_cast<int>(blockIdx.x));
+    if (!c.live) return;
+    uint32_t key[kPerThread];
+    load_item(a, c, key);
+    put_exp2_table();   // read after the first barrier
+    chunk_item_work(a, c, key);
 }
 
 // ---- candidate path, pass 2: merge, top-k, top-p, draw ----------------------
@@ -990,7 +1136,7 @@ __device__ __forceinline__ void sample_whole_row(const SampleArgs& a, int row, f
     if (tid == 0) write_result(a, row, s_i[0], kept_k, static_cast<int>(kept_p));
 }
 
-// ---- histogram path, pass 2 ----------------------------------------------------------
+// ---- histogram path, passes 2 and 3 ---------------------------------------------------
 constexpr int kBucketCap = kSampleBucketCap;   // tokens of the top-p boundary bin held in LDS
 constexpr int kPoolWords = 3 * kSampleHistBins / 2 + kBucketCap;   // fp64 bins, u32 counts, the bin's tokens
 static_assert(kSampleHistBins == 2 * kThreads, "two merged bins per thread");
@@ -998,30 +1144,32 @@ static_assert(kSampleHistChunks <= kWave, "one lane per chunk in the draw");
 static_assert(kSampleChunk == kWaves * 8 * kWave, "the walk covers a chunk with 8 loads per lane");
 static_assert(kSampleHistChunks * kSampleChunk <= (1 << 19), "indices fit the 19 bits of the tie digits");
 static_assert(kPoolWords >= kMergeChunks * kSampleMaxK + 2 * kThreads, "the pool holds the candidate finish");
-static_assert(kBucketCap % (kWaves * kWave) == 0, "whole rows of the per-wave regions");
 
 // One digit of the boundary search inside the gathered bin: fp64 masses and
 // counts of the tokens matching `prefix` under `pmask`, per NB bins of the
 // key bits at `shift`; then the bin, from the top, at which the mass
 // reaches `rest`. `above` grows by the mass of the bins above it. When
 // rounding leaves the gathered mass just short of `rest`, the boundary is
-// the lowest token: the lowest non-empty bin is taken.
-template <int NB>
+// the lowest token: the lowest non-empty bin is taken. kZeroed: the caller
+// has cleared the bins (before a barrier).
+template <int NB, bool kZeroed = false>
 __device__ __forceinline__ void bucket_digit(const uint64_t* s_bk, uint32_t n1, int shift, double zmax, double rest,
                                              double* s_bin, uint32_t* s_cnt, int* s_ri, double* s_rd,
                                              uint32_t& prefix, uint32_t& pmask, double& above) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    for (int b = tid; b < NB; b += kThreads) {
-        s_bin[b] = 0.0;
-        s_cnt[b] = 0u;
+    if constexpr (!kZeroed) {
+        for (int b = tid; b < NB; b += kThreads) {
+            s_bin[b] = 0.0;
+            s_cnt[b] = 0u;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     for (uint32_t e = tid; e < n1; e += kThreads) {
         const uint32_t key = comp_key(s_bk[e]);
         if ((key & pmask) == prefix) {
             const uint32_t b = (key >> shift) & (NB - 1);
-            atomicAdd(&s_bin[b], exp(static_cast<double>(key_value(key)) - zmax));
+            atomicAdd(&s_bin[b], mass_exp(static_cast<double>(key_value(key)) - zmax));
             atomicAdd(&s_cnt[b], 1u);
         }
     }
@@ -1076,107 +1224,99 @@ __device__ __forceinline__ void tie_digit(const uint64_t* s_bk, uint32_t n1, uin
     rem -= static_cast<uint32_t>(s_ri[1]);
 }
 
-// The least order key kx of a logit x with key(fl(x / T)) >= target, or
-// 0xFFFFFFFF when no finite logit reaches it; called by a whole wave.
-// Correctly rounded division by T > 0 is monotone in x, and so is the key of
-// its result: a test of the scaled logit's key against `target` is a test of
-// kx against this value. Each step tests 64 evenly spaced keys of the range
-// left (those of -inf .. +inf at first; finite logits lie strictly inside).
-__device__ __forceinline__ uint32_t wave_key_threshold(uint32_t target, float T, int lane) {
-    auto reaches = [&](uint32_t kx) { return order_key(key_value(kx) / T) >= target; };
-    uint32_t lo = 0x007FFFFFu, hi = 0xFF800000u;   // reaches(hi); every key below lo fails
-    if (!reaches(hi)) return 0xFFFFFFFFu;
-    while (lo < hi) {
-        const uint32_t step = (hi - lo + kWave - 1) / kWave;
-        const uint32_t c = min(hi, lo + static_cast<uint32_t>(lane) * step);
-        const unsigned long long ok = __builtin_amdgcn_ballot_w64(reaches(c));
-        if (!ok) {
-            lo = __shfl(c, kWave - 1, kWave) + 1;
-        } else {
-            const int f = __builtin_ctzll(ok);
-            hi = __shfl(c, f, kWave);
-            if (f > 0) lo = __shfl(c, f - 1, kWave) + 1;
-            else lo = hi;
-        }
-    }
-    return lo;
+// ---- histogram rows, pass 2 (the finishing kernel) --------------------------------
+// The row's boundary bin is found from the chunks' histograms by one wave,
+// which loads first the chunks' headers and group sums.
+constexpr int kSumBatch = 16;   // chunk sums loaded together per lane
+
+// The boundary search's first loads: the headers of chunks lane and the
+// group sums at group `lane` of chunks 0 .. kSumBatch - 1.
+// Unconditional (chunk indices clamped, the extra values ignored), so that
+// they are issued together.
+struct SearchLoads {
+    float mc;
+    double total;
+    double h[kSumBatch];
+};
+__device__ __forceinline__ SearchLoads search_loads(const SampleArgs& a, int row, int lane) {
+    const int S = a.chunks;
+    SearchLoads L;
+    const SampleChunkHead* hd = chunk_head(a, row, min(lane, S - 1));
+    L.mc = hd->mc;
+    L.total = hd->total;
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u) L.h[u] = chunk_coarse(a, row, min(u, S - 1))[lane];
+    return L;
 }
 
-constexpr int kGatherBatch = 8;                    // float4 loads per lane in flight in the gathering pass
-constexpr int kWaveCap = kBucketCap / kWaves;      // tokens of the bin one wave's slice may hold
-
-// The gathering pass's test of one element per lane (every lane of the wave
-// together): whether x lies in the bin (appended to the wave's region, at
-// most kWaveCap) and whether it lies above it (counted). kByKey compares
-// order keys (needed when a threshold is +0, which a float compare does not
-// tell from -0), else floats; kAll: every lane holds an element.
-template <bool kByKey, bool kAll>
-struct BinTest {
-    uint32_t k_lo, k_hi;
-    float f_lo, f_hi;
-    uint2* s_reg;
-    __device__ __forceinline__ void operator()(float xj, int j, bool in, uint32_t& n_w, uint32_t& above_w) const {
-        bool mem, abv;
-        if constexpr (kByKey) {
-            const uint32_t kx = order_key(xj);
-            mem = kx >= k_lo && kx < k_hi;
-            abv = kx >= k_hi;
-        } else {
-            mem = xj >= f_lo && xj < f_hi;
-            abv = xj >= f_hi;
-        }
-        if constexpr (!kAll) {
-            mem = mem && in;
-            abv = abv && in;
-        }
-        above_w += static_cast<uint32_t>(__builtin_popcountll(__builtin_amdgcn_ballot_w64(abv)));
-        const unsigned long long m = __builtin_amdgcn_ballot_w64(mem);
-        if (m) {
-            const uint32_t slot =
-                n_w + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-            if (mem && slot < static_cast<uint32_t>(kWaveCap)) s_reg[slot] = make_uint2(__float_as_uint(xj), static_cast<uint32_t>(j));
-            n_w += static_cast<uint32_t>(__builtin_popcountll(m));
-        }
+// v + the sum over chunks c0 .. S - 1, in chunk order, of s_scale[c] *
+// *src(c) (nothing where !on; src must give a valid address for every
+// chunk either way), kSumBatch loads in flight at a time.
+template <class Src>
+__device__ __forceinline__ double scaled_sum(int c0, int S, const double* s_scale, bool on, Src&& src, double v) {
+    for (; c0 < S; c0 += kSumBatch) {
+        double h[kSumBatch];
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u) h[u] = *src(min(c0 + u, S - 1));   // all issued, then summed
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u)
+            if (on && c0 + u < S) v += s_scale[c0 + u] * h[u];
     }
+    return v;
+}
+
+// The row's top-p boundary: the bin, the mass of the bins above it, need =
+// top-p x the row's mass, and max z; all scaled to exp(z - max z).
+struct RowBoundary {
+    uint32_t bin;
+    double above, need, zmax;
 };
 
-// One wave's float4 units [ubeg, uend) of the row (x4 = the row from its
-// first 16-byte boundary, element h0): kGatherBatch loads per lane at a time.
-template <bool kByKey>
-__device__ __forceinline__ void gather_units(const float4* x4, int h0, int ubeg, int uend, int lane,
-                                             const BinTest<kByKey, true>& full, const BinTest<kByKey, false>& part,
-                                             uint32_t& n_w, uint32_t& above_w) {
-    int u0 = ubeg;
-    for (; u0 + kGatherBatch * kWave <= uend; u0 += kGatherBatch * kWave) {
-        float4 v[kGatherBatch];
+// The bin holding the top-p boundary, by one wave: max z and the chunks'
+// scales exp(chunk max - max z) (written to s_scale), need = top-p x the
+// scaled total, then the largest b with I[b] >= need, I[b] = the sum over
+// chunks of scale x the chunk's suffix mass at b, in two levels (the 64
+// group starts 32 g from the contiguous group sums, then the 33 bins from
+// the chosen group's start).
+__device__ __forceinline__ RowBoundary boundary_bin(const SampleArgs& a, int row, float tp, int lane,
+                                                    const SearchLoads& L, double* s_scale) {
+    const int S = a.chunks;
+    const double mc = lane < S ? static_cast<double>(L.mc) : -INFINITY;
+    double zmax = mc;
 #pragma unroll
-        for (int i = 0; i < kGatherBatch; ++i) v[i] = x4[u0 + i * kWave + lane];
+    for (int o = 1; o < kWave; o <<= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, kWave));
+    const double sc = lane < S ? mass_exp(mc - zmax) : 0.0;
+    if (lane < S) s_scale[lane] = sc;
+    const double need = static_cast<double>(tp) * wave_sum_f64(lane < S ? sc * L.total : 0.0);
+    double g = 0.0;
 #pragma unroll
-        for (int i = 0; i < kGatherBatch; ++i) {
-            const int j = h0 + 4 * (u0 + i * kWave + lane);
-            full(v[i].x, j, true, n_w, above_w);
-            full(v[i].y, j + 1, true, n_w, above_w);
-            full(v[i].z, j + 2, true, n_w, above_w);
-            full(v[i].w, j + 3, true, n_w, above_w);
-        }
-    }
-    for (; u0 < uend; u0 += kWave) {
-        const int uu = u0 + lane;
-        const bool in = uu < uend;
-        const float4 v = x4[in ? uu : uend - 1];
-        const int j = h0 + 4 * uu;
-        part(v.x, j, in, n_w, above_w);
-        part(v.y, j + 1, in, n_w, above_w);
-        part(v.z, j + 2, in, n_w, above_w);
-        part(v.w, j + 3, in, n_w, above_w);
-    }
+    for (int u = 0; u < kSumBatch; ++u)
+        if (u < S) g += s_scale[u] * L.h[u];
+    g = scaled_sum(kSumBatch, S, s_scale, true, [&](int c) { return chunk_coarse(a, row, c) + lane; }, g);
+    const unsigned long long ok = __builtin_amdgcn_ballot_w64(g >= need);
+    const int kA = ok ? 63 - __builtin_clzll(ok) : 0;
+    const int b = 32 * kA + lane;   // lanes 0 .. 32: the group's bins and the next group's start
+    const double v = scaled_sum(0, S, s_scale, lane <= 32 && b < kSampleHistBins,
+                                [&](int c) { return chunk_hist(a, row, c) + min(b, kSampleHistBins - 1); }, 0.0);
+    const unsigned long long ok2 = __builtin_amdgcn_ballot_w64(lane < 32 && v >= need);
+    const int i = ok2 ? 63 - __builtin_clzll(ok2) : 0;
+    RowBoundary rb;
+    rb.bin = static_cast<uint32_t>(32 * kA + i);
+    rb.above = __shfl(v, i + 1, kWave);
+    rb.need = need;
+    rb.zmax = zmax;
+    return rb;
 }
 
-// Rows with top-k off, from the chunks' maxima and histograms. Returns
-// false, the same in every thread, when the top-p boundary's bin holds more
-// than kBucketCap tokens; the caller then takes the whole-row path.
-__device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int row, int g, float T, uint64_t* pool) {
+// Rows with top-k off, pass 2: from the chunks' maxima and histograms and,
+// with top-p on, their lists and tallies. Returns false, the same in every
+// thread, when the boundary bin's tokens do not fit (more than kBucketCap
+// over the row, or a scanned chunk holding more than its bound); the caller
+// then takes the whole-row path.
+constexpr int kListBatch = 8;   // list entries per lane loaded together
+static_assert(kListBatch * kWave <= kWinWaveCap, "a batch stays inside a wave's region");
+static_assert(kThreads * 8 >= kSampleChunk, "a chunk scan covers the chunk in 8 loads per thread");
+__device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int row, float T, float tp, uint64_t* pool) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -1184,221 +1324,219 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
     const int S = a.chunks;
     const int C = (V + S - 1) / S;
     const Row r{a.logits + static_cast<size_t>(row) * a.ld, V, T};
+    const double inv = 1.0 / static_cast<double>(T);
+    const float ur = a.u[row];
     double* s_bin = reinterpret_cast<double*>(pool);                          // [kSampleHistBins]
     uint32_t* s_cnt = reinterpret_cast<uint32_t*>(pool + kSampleHistBins);    // [kSampleHistBins]
     uint64_t* s_bk = pool + 3 * kSampleHistBins / 2;                          // [kBucketCap]
     __shared__ double s_scale[kSampleHistChunks];   // exp(chunk max - row max)
     __shared__ double s_kc[kSampleHistChunks];      // kept mass per chunk
+    __shared__ double s_acc[kSampleHistChunks];     // the chunk's suffix mass above the boundary bin
+    __shared__ double s_from[kSampleHistChunks];    // ... from the boundary bin up
     __shared__ double s_wd[kWaves];
     __shared__ uint32_t s_wu[kWaves];
     __shared__ int s_ri[2];
-    __shared__ double s_rd[2];
+    __shared__ double s_rd[4];
     __shared__ uint32_t s_n;
-    __shared__ uint32_t s_thr[2];
-    __shared__ uint32_t s_wn[kWaves];
     __shared__ uint64_t s_small[kWave];
-    __shared__ double s_kcw[kWaves][kSampleHistChunks];   // per wave: kept mass of gathered tokens per chunk
-    __shared__ uint32_t s_base;
-
-    const float tp = a.top_p[row];
-    if (g != 0 && !(tp < 1.0f)) return true;   // only the gathering pass is shared out
-
-    // ---- max z from the chunks' maxima ----------------------------------------------
-    if (tid < S) s_scale[tid] = static_cast<double>(chunk_head(a, row, tid)->mc);
-    __syncthreads();
-    double zmax = s_scale[0];
-    for (int c = 1; c < S; ++c) zmax = fmax(zmax, s_scale[c]);
-    __syncthreads();
-    if (tid < S) {
-        s_scale[tid] = exp(s_scale[tid] - zmax);
-        s_kc[tid] = 0.0;
-    }
-    if (tid == 0) s_n = 0u;
-    __syncthreads();
+    __shared__ uint32_t s_wlo[kSampleHistChunks], s_whi[kSampleHistChunks], s_lst[kSampleHistChunks][kChunkWaves];
+    __shared__ uint32_t s_inb[kSampleHistChunks][kSampleWinBins];   // the chunk's tokens per window bin
+    __shared__ double s_mc[kSampleHistChunks];                       // the chunk's max z
+    __shared__ uint32_t s_start[kSampleHistChunks], s_cap[kSampleHistChunks], s_mem[kSampleHistChunks];
+    __shared__ uint32_t s_up[kSampleHistChunks];
+    __shared__ uint32_t s_tot[4];
 
     uint32_t pkey = 0;   // kept: key > pkey, or key == pkey and index <= pidx
     int pidx = V;
     uint32_t kept_p = static_cast<uint32_t>(V);
+    double zmax;
+    int pred = -1;   // the chunk whose logits the draw prefetched into xpre[]
+    float xpre[8];
     if (tp < 1.0f) {
-        // ---- the bin holding the boundary: the largest b with I[b] >= need, where
-        // I[b] = sum over chunks of scale x suffix mass (two levels: the 64
-        // group starts 32k, then the 33 bins from the group's start) --------
+        // ---- the boundary bin (wave 0) and the chunks' tallies (wave 1) ------------------
         if (wave == 0) {
-            const double t = lane < S ? s_scale[lane] * chunk_head(a, row, lane)->total : 0.0;
-            const double tot = wave_sum_f64(t);
-            if (lane == 0) s_rd[0] = tot;
-        }
-        __syncthreads();
-        const double need = static_cast<double>(tp) * s_rd[0];
-        // I at bin b by the 16 lanes of a group (chunks cs, cs + 16, ...), the
-        // same order wherever it is evaluated
-        auto suffix_at = [&](int b) -> double {
-            double v = 0.0;
-            if (b < kSampleHistBins)
-                for (int c = tid & 15; c < S; c += 16) v += s_scale[c] * chunk_hist(a, row, c)[b];
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
-            return v;
-        };
-        {
-            const double v = suffix_at(32 * (tid >> 4));
-            if ((tid & 15) == 0) s_bin[tid >> 4] = v;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const unsigned long long ok = __builtin_amdgcn_ballot_w64(s_bin[lane] >= need);
-            if (lane == 0) s_ri[0] = ok ? 63 - __builtin_clzll(ok) : 0;
-        }
-        __syncthreads();
-        const int kA = s_ri[0];
-        if (tid < 33 * 16) {
-            const double v = suffix_at(32 * kA + (tid >> 4));
-            if ((tid & 15) == 0) s_bin[64 + (tid >> 4)] = v;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const unsigned long long ok = __builtin_amdgcn_ballot_w64(lane < 32 && s_bin[64 + lane] >= need);
-            const int i = ok ? 63 - __builtin_clzll(ok) : 0;
+            const SearchLoads L = search_loads(a, row, lane);
+            put_exp2_table();
+            if (lane < S) s_mc[lane] = static_cast<double>(L.mc);
+            const RowBoundary rb = boundary_bin(a, row, tp, lane, L, s_scale);
+            if (lane < S) {
+                const double* hc = chunk_hist(a, row, lane);
+                s_acc[lane] = rb.bin + 1u < static_cast<uint32_t>(kSampleHistBins) ? hc[rb.bin + 1] : 0.0;
+                s_from[lane] = hc[rb.bin];
+                s_kc[lane] = 0.0;
+            }
             if (lane == 0) {
-                s_ri[0] = 32 * kA + i;
-                s_rd[0] = s_bin[64 + i + 1];   // I[b1 + 1]: the mass above the bin
+                s_tot[3] = rb.bin;
+                s_rd[0] = rb.need;
+                s_rd[1] = rb.above;
+                s_rd[2] = rb.zmax;
             }
-        }
-        __syncthreads();
-        const uint32_t b1 = static_cast<uint32_t>(s_ri[0]);
-        double above = s_rd[0];
-
-        // ---- gather the boundary bin's tokens; count the tokens above it ----------
-        // The bin test is a test of x itself against two thresholds: as
-        // floats, or as order keys when one of them is +0 (which a float
-        // compare does not tell from -0). Each wave appends to its own region
-        // of the list (no atomics); the regions are compacted afterwards.
-        if (wave < 2) {
-            const uint32_t hb = b1 + static_cast<uint32_t>(wave);
-            const uint32_t k = hb >= static_cast<uint32_t>(kSampleHistBins) ? 0xFFFFFFFFu
-                                                                             : wave_key_threshold(hb << 21, T, lane);
-            if (lane == 0) s_thr[wave] = k;
-        }
-        if (tid == 0) s_n = 0u;   // set when a wave's share overflows its region
-        __syncthreads();
-        const uint32_t k_lo = s_thr[0], k_hi = s_thr[1];
-        const float f_lo = key_value(k_lo);                              // NaN when nothing reaches the bin
-        const float f_hi = k_hi == 0xFFFFFFFFu ? INFINITY : key_value(k_hi);
-        const bool by_key = k_lo == 0x80000000u || k_hi == 0x80000000u;
-        uint32_t n_w = 0;       // tokens of the bin in this wave's slice
-        uint32_t above_w = 0;   // tokens above the bin in this wave's slice
-        uint2* s_reg = reinterpret_cast<uint2*>(s_bk) + wave * kWaveCap;
-        // elements before the first 16-byte boundary and after the last: wave 0
-        const float* x = r.x;
-        const int h0 = min(V, static_cast<int>((4u - ((reinterpret_cast<uintptr_t>(x) >> 2) & 3u)) & 3u));
-        const int n4 = (V - h0) / 4;
-        const int t0 = h0 + 4 * n4;
-        const float4* x4 = reinterpret_cast<const float4*>(x + h0);
-        // this workgroup's share of the units, then this wave's
-        const int gbeg = static_cast<int>(static_cast<long long>(g) * n4 / kSampleRowSplit);
-        const int gend = static_cast<int>(static_cast<long long>(g + 1) * n4 / kSampleRowSplit);
-        const int ubeg = gbeg + static_cast<int>(static_cast<long long>(wave) * (gend - gbeg) / kWaves);
-        const int uend = gbeg + static_cast<int>(static_cast<long long>(wave + 1) * (gend - gbeg) / kWaves);
-        if (by_key) {
-            const BinTest<true, true> full{k_lo, k_hi, f_lo, f_hi, s_reg};
-            const BinTest<true, false> part{k_lo, k_hi, f_lo, f_hi, s_reg};
-            if (wave == 0 && g == 0) {
-                const bool in = lane < h0 + (V - t0);
-                const int j = lane < h0 ? lane : t0 + (lane - h0);
-                part(x[in ? j : 0], j, in, n_w, above_w);
-            }
-            gather_units<true>(x4, h0, ubeg, uend, lane, full, part, n_w, above_w);
-        } else {
-            const BinTest<false, true> full{k_lo, k_hi, f_lo, f_hi, s_reg};
-            const BinTest<false, false> part{k_lo, k_hi, f_lo, f_hi, s_reg};
-            if (wave == 0 && g == 0) {
-                const bool in = lane < h0 + (V - t0);
-                const int j = lane < h0 ? lane : t0 + (lane - h0);
-                part(x[in ? j : 0], j, in, n_w, above_w);
-            }
-            gather_units<false>(x4, h0, ubeg, uend, lane, full, part, n_w, above_w);
-        }
-        if (lane == 0) {
-            s_wn[wave] = n_w;
-            s_wu[wave] = above_w;
-            if (n_w > static_cast<uint32_t>(kWaveCap)) s_n = 1u;
-        }
-        __syncthreads();
-        constexpr uint32_t kShare = kBucketCap / kSampleRowSplit;   // list entries per workgroup
-        uint32_t n_g = 0, pre = 0, above_g = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            if (w == wave) pre = n_g;
-            n_g += s_wn[w];
-            above_g += s_wu[w];
-        }
-        const bool wg_over = s_n != 0u || n_g > kShare;
-        if (!wg_over) {   // compact the waves' regions, logit keys becoming keys of z = x / T
-            uint2 mine[kWaveCap / kWave];
+        } else if (wave == 1 && lane < S) {
+            const SampleChunkTally* tl = chunk_tally(a, row, lane);
+            s_wlo[lane] = tl->wlo;
+            s_whi[lane] = tl->whi;
+            uint32_t up = 0;
+            uint32_t nb[kSampleWinBins] = {};
 #pragma unroll
-            for (int i = 0; i < kWaveCap / kWave; ++i) {
-                const uint32_t e = static_cast<uint32_t>(i * kWave + lane);
-                mine[i] = e < n_w ? s_reg[e] : make_uint2(0u, 0u);
-            }
-            __syncthreads();
+            for (int w = 0; w < kChunkWaves; ++w) {
+                s_lst[lane][w] = tl->listed[w];
+                up += tl->up[w];
 #pragma unroll
-            for (int i = 0; i < kWaveCap / kWave; ++i) {
-                const uint32_t e = static_cast<uint32_t>(i * kWave + lane);
-                if (e < n_w) s_bk[pre + e] = composite(order_key(__uint_as_float(mine[i].x) / T), mine[i].y);
+                for (int q = 0; q < kSampleWinBins; ++q) nb[q] += tl->inbin[w][q];
             }
-            __syncthreads();
+            s_up[lane] = up;
+#pragma unroll
+            for (int q = 0; q < kSampleWinBins; ++q) s_inb[lane][q] = nb[q];
         }
-
-        // ---- the row's workgroups pool their shares; the last one to finish goes on
-        uint32_t* rc = row_counters(a, row);
-        uint64_t* rl = row_list(a, row);
-        if (!wg_over)
-            for (uint32_t e = tid; e < n_g; e += kThreads) rl[g * kShare + e] = s_bk[e];
-        if (tid == 0) {
-            rc[2 + 2 * g] = wg_over ? 0xFFFFFFFFu : n_g;
-            rc[3 + 2 * g] = above_g;
+        for (int b = tid; b < kSampleHistBins; b += kThreads) {   // the first digit's bins
+            s_bin[b] = 0.0;
+            s_cnt[b] = 0u;
         }
         __syncthreads();
-        if (tid == 0) {
-            // release: the workgroup's entries (complete in L2 after the
-            // barrier) are written back before it reports; the last to
-            // report acquires them (one fence each way, not one per wave)
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            const uint32_t t = atomicAdd(&rc[0], 1u);
-            const bool last = t == static_cast<uint32_t>(kSampleRowSplit - 1);
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            s_n = last ? 1u : 0u;
+        const uint32_t b1 = s_tot[3];
+        const double need = s_rd[0];
+        double above = s_rd[1];
+        zmax = s_rd[2];
+        // ---- each chunk's range of s_bk: its listed tokens when its window holds b1
+        // (and no wave's share overflowed), else room for a scan of the chunk; and the
+        // draw's likely chunk (the kept mass of chunk c lies between sc x I_c[b1 + 1],
+        // none of the bin kept, and sc x I_c[b1], all of it: take the midpoints) -------
+        if (wave == 0) {
+            bool cover = lane < S && b1 >= s_wlo[lane] && b1 <= s_whi[lane];
+            uint32_t nm = 0, na = 0;   // the chunk's tokens in b1, and in the window above it
+            if (lane < S) {
+#pragma unroll
+                for (int w = 0; w < kChunkWaves; ++w) cover = cover && s_lst[lane][w] != 0xFFFFFFFFu;
+#pragma unroll
+                for (int q = 0; q < kSampleWinBins; ++q) {
+                    const uint32_t bq = s_wlo[lane] + static_cast<uint32_t>(q);
+                    if (bq == b1) nm = s_inb[lane][q];
+                    if (bq > b1 && bq <= s_whi[lane]) na += s_inb[lane][q];
+                }
+            }
+            // Room for a chunk that is scanned: none when its largest z lies below the
+            // bin (nothing of it reaches b1: not scanned either); else its mass in the
+            // bin, I_c[b1] - I_c[b1 + 1], over the least mass a token of the bin can
+            // have, exp(z_lo - chunk max), with slack for the rounding of the sums,
+            // and at most the chunk's length.
+            const float zlo = key_value(b1 << 21);
+            const bool below = lane < S && !cover && static_cast<double>(zlo) > s_mc[lane];
+            uint32_t room = 0;
+            if (lane < S && !cover && !below) {
+                const double mmin = mass_exp(static_cast<double>(zlo) - s_mc[lane]);
+                const double mb = s_from[lane] - s_acc[lane] + 1e-15 * s_from[lane];
+                const double bound = mmin > 0.0 ? mb / (mmin * (1.0 - 1e-15)) + 1.0 : static_cast<double>(C);
+                room = static_cast<uint32_t>(fmin(bound, static_cast<double>(C)));
+            }
+            if (below) {   // nothing to scan, nothing listed to take
+                cover = true;
+                nm = 0u;
+            }
+            const uint32_t cap = cover ? nm : room;
+            const uint32_t incl = wave_incl_scan(cap, lane);
+            const unsigned long long scan = __builtin_amdgcn_ballot_w64(lane < S && !cover);
+            const double sc = lane < S ? s_scale[lane] : 0.0;
+            const double mid = lane < S ? 0.5 * sc * (s_acc[lane] + s_from[lane]) : 0.0;
+            const double cm = wave_incl_scan(mid, lane);
+            const double tgt = static_cast<double>(ur) * __shfl(cm, kWave - 1, kWave);
+            const unsigned long long hit = __builtin_amdgcn_ballot_w64(mid > 0.0 && cm > tgt);
+            if (lane < S) {
+                s_start[lane] = incl - cap;
+                s_cap[lane] = cap;
+                s_mem[lane] = 0u;
+                s_up[lane] = below ? 0u : (cover ? s_up[lane] + na : 0u);   // else counted by the scan
+            }
+            const uint32_t n1 = __shfl(incl, kWave - 1, kWave);
+            if (lane == 0) {
+                s_tot[0] = n1 > static_cast<uint32_t>(kBucketCap) ? 0xFFFFFFFFu : n1;
+                s_tot[1] = static_cast<uint32_t>(scan);
+                s_tot[2] = static_cast<uint32_t>(scan >> 32);
+                s_ri[0] = hit ? __builtin_ctzll(hit) : 0;
+            }
         }
         __syncthreads();
-        if (!s_n) return true;
-        // every other workgroup of the row has published its share: append
-        // theirs after this one's own (already in LDS)
-        uint32_t cnt[kSampleRowSplit], start[kSampleRowSplit];
-        uint32_t n1 = n_g, n_above = 0;
-        bool over = wg_over;
+        if (s_tot[0] == 0xFFFFFFFFu) return false;
+        const uint32_t n1 = s_tot[0];
+        unsigned long long scan = (static_cast<unsigned long long>(s_tot[2]) << 32) | s_tot[1];
+        {   // prefetch the likely chunk for the draw; it arrives during the digits
+            pred = s_ri[0];
+            const int lo = pred * C;
+            const int hi = min(V, lo + C);
+            const int base = lo + wave * (8 * kWave);
 #pragma unroll
-        for (int h = 0; h < kSampleRowSplit; ++h) {
-            cnt[h] = h == g ? n_g : rc[2 + 2 * h];
-            over = over || cnt[h] == 0xFFFFFFFFu;
-            n_above += h == g ? above_g : rc[3 + 2 * h];
+            for (int u = 0; u < 8; ++u) xpre[u] = load_at(r.x, min(base + u * kWave + lane, hi - 1));
         }
+        const unsigned long long below = (1ull << lane) - 1ull;
+        // ---- the listed tokens of the covered chunks: the bin's tokens to the chunk's
+        // range (one wave per chunk; the counts came with the tallies) ----------------
+        for (int c = wave; c < S; c += kWaves) {   // wave-uniform
+            if (((scan >> c) & 1ull) || s_cap[c] == 0u) continue;   // scanned below, or nothing to take
+            const uint32_t st = s_start[c];
+            uint32_t m = 0;
+            for (int w = 0; w < kChunkWaves; ++w) {
+                const uint64_t* l = chunk_list(a, row, c) + w * kWinWaveCap;
+                const uint32_t n = min(s_lst[c][w], static_cast<uint32_t>(kWinWaveCap));   // listed in full (covered)
+                for (uint32_t e0 = 0; e0 < n; e0 += kListBatch * kWave) {
+                    uint64_t t[kListBatch];
+#pragma unroll
+                    for (int u = 0; u < kListBatch; ++u) t[u] = l[e0 + u * kWave + lane];   // inside the region
+#pragma unroll
+                    for (int u = 0; u < kListBatch; ++u) {
+                        const uint32_t e = e0 + u * kWave + lane;
+                        const bool mem = e < n && (comp_key(t[u]) >> 21) == b1;
+                        const unsigned long long mm = __builtin_amdgcn_ballot_w64(mem);
+                        const uint32_t slot = m + static_cast<uint32_t>(__builtin_popcountll(mm & below));
+                        if (mem && slot < s_cap[c]) s_bk[st + slot] = t[u];
+                        m += static_cast<uint32_t>(__builtin_popcountll(mm));
+                    }
+                }
+            }
+            if (lane == 0) s_mem[c] = m;
+        }
+        // ---- the chunks whose window misses b1: scanned by the whole workgroup, each
+        // into its room ----------------------------------------------------------------
+        while (scan) {   // workgroup-uniform
+            const int c = __builtin_ctzll(scan);
+            scan &= scan - 1ull;
+            const int lo = c * C;
+            const int hi = min(V, lo + C);
+            const uint32_t st = s_start[c], cap = s_cap[c];
+            uint32_t up = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = lo + u * kThreads + tid;
+                const bool in = j < hi;
+                const uint32_t key = order_key(div_by_t(load_at(r.x, min(j, hi - 1)), T, inv));
+                const uint32_t bn = key >> 21;
+                const bool mem = in && bn == b1;
+                up += in && bn > b1 ? 1u : 0u;
+                const unsigned long long mm = __builtin_amdgcn_ballot_w64(mem);
+                if (mm) {
+                    uint32_t base = 0;
+                    if (lane == 0) base = atomicAdd(&s_mem[c], static_cast<uint32_t>(__builtin_popcountll(mm)));
+                    base = __shfl(base, 0, kWave);
+                    const uint32_t slot = base + static_cast<uint32_t>(__builtin_popcountll(mm & below));
+                    if (mem && slot < cap) s_bk[st + slot] = composite(key, static_cast<uint32_t>(j));
+                }
+            }
+            up = wave_sum_u32(up);
+            if (lane == 0) atomicAdd(&s_up[c], up);
+        }
+        __syncthreads();
+        bool over = false;   // a scanned chunk with more of the bin's tokens than its room (rounding)
+        for (int c = 0; c < S; ++c) over = over || s_mem[c] > s_cap[c];
         if (over) return false;
-#pragma unroll
-        for (int h = 0; h < kSampleRowSplit; ++h) {   // the other shares, in order, after this one's
-            start[h] = n1;
-            if (h != g) n1 += cnt[h];
-        }
-        for (uint32_t e = n_g + tid; e < n1; e += kThreads) {
-            int hh = 0;
-#pragma unroll
-            for (int h = 0; h < kSampleRowSplit; ++h)
-                if (h != g && e >= start[h]) hh = h;   // the last share starting at or below e
-            s_bk[e] = rl[hh * kShare + (e - start[hh])];
-        }
+        // the rest of each range: a composite of another bin, which no digit takes
+        const uint64_t other = composite(((b1 + 1u) & (kSampleHistBins - 1u)) << 21, 0u);
+        for (int c = wave; c < S; c += kWaves)
+            for (uint32_t e = s_mem[c] + lane; e < s_cap[c]; e += kWave) s_bk[s_start[c] + e] = other;
+        uint32_t n_above = 0;
+        for (int c = 0; c < S; ++c) n_above += s_up[c];
         __syncthreads();
 
         // ---- the boundary key: more digits over the gathered tokens ----------------
         uint32_t prefix = b1 << 21, pmask = 0xFFE00000u;
-        bucket_digit<2048>(s_bk, n1, 10, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
+        bucket_digit<2048, true>(s_bk, n1, 10, zmax, need - above, s_bin, s_cnt, s_ri, s_rd, prefix, pmask, above);
         const uint32_t m2 = s_cnt[(prefix >> 10) & 2047u];   // tokens sharing the 21-bit prefix
         if (tid == 0) s_n = 0u;
         __syncthreads();
@@ -1419,7 +1557,7 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
                 const uint32_t hi32 = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(4 * rk, static_cast<int>(me >> 32)));
                 const uint64_t srt = (static_cast<uint64_t>(hi32) << 32) | lo32;
                 const bool real = lane < static_cast<int>(m2);
-                const double m = real ? exp(static_cast<double>(key_value(comp_key(srt))) - zmax) : 0.0;
+                const double m = real ? mass_exp(static_cast<double>(key_value(comp_key(srt))) - zmax) : 0.0;
                 const double incl = wave_incl_scan(m, lane);
                 const unsigned long long reach = __builtin_amdgcn_ballot_w64(real && above + incl >= need);
                 const int t = reach ? __builtin_ctzll(reach) : static_cast<int>(m2) - 1;   // rounding: the last
@@ -1438,7 +1576,7 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
             const uint32_t ties = s_cnt[pkey & 1023u];
             __syncthreads();   // the tie count is read before the counts are reused
             // every tie has the same mass; keep the first `keep` of them in index order
-            const double pb = exp(static_cast<double>(key_value(pkey)) - zmax);
+            const double pb = mass_exp(static_cast<double>(key_value(pkey)) - zmax);
             const double t = (need - above) / pb;
             const uint32_t keep = t <= 1.0 ? 1u : static_cast<uint32_t>(fmin(ceil(t), static_cast<double>(ties)));
             if (keep < ties) {
@@ -1449,58 +1587,50 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
             }
         }
 
-        // ---- kept mass per chunk: the bins above b1, plus the gathered tokens kept --
-        // Gathered tokens: each mass once; consecutive list entries mostly
-        // share a chunk, so a wave adds the entries of one chunk at a time
-        // into its own row of s_kcw.
-        for (int i = tid; i < kWaves * kSampleHistChunks; i += kThreads) (&s_kcw[0][0])[i] = 0.0;
-        __syncthreads();
+        // ---- kept mass per chunk: the bins above b1, plus the bin's tokens kept --------
         uint32_t nk = 0;
-        for (uint32_t e0 = static_cast<uint32_t>(wave) * kWave; e0 < n1; e0 += kThreads) {   // wave-uniform
-            const uint32_t e = e0 + lane;
-            int ch = -1;
+        for (int c = wave; c < S; c += kWaves) {   // wave-uniform
+            const uint32_t n = s_mem[c], st = s_start[c];
             double m = 0.0;
-            if (e < n1) {
-                const uint64_t cc = s_bk[e];
+            for (uint32_t e = lane; e < n; e += kWave) {
+                const uint64_t cc = s_bk[st + e];
                 const uint32_t key = comp_key(cc);
                 const int j = comp_index(cc);
                 if (key > pkey || (key == pkey && j <= pidx)) {
-                    ch = j / C;
-                    m = exp(static_cast<double>(key_value(key)) - zmax);
+                    m += mass_exp(static_cast<double>(key_value(key)) - zmax);
                     ++nk;
                 }
             }
-            unsigned long long todo = __builtin_amdgcn_ballot_w64(ch >= 0);
-            while (todo) {
-                const int c0 = __shfl(ch, __builtin_ctzll(todo), kWave);
-                const bool mine = ch == c0;
-                const double sum = wave_sum_f64(mine ? m : 0.0);
-                if (lane == 0) s_kcw[wave][c0] += sum;
-                todo &= ~__builtin_amdgcn_ballot_w64(mine);
-            }
+            m = wave_sum_f64(m);
+            if (lane == 0) s_kc[c] = s_scale[c] * s_acc[c] + m;
         }
         nk = wave_sum_u32(nk);
         if (lane == 0) s_wu[wave] = nk;
         __syncthreads();
         kept_p = n_above;
         for (int w = 0; w < kWaves; ++w) kept_p += s_wu[w];
-        if (tid < S) {
-            const double acc = b1 + 1 < static_cast<uint32_t>(kSampleHistBins) ? chunk_hist(a, row, tid)[b1 + 1] : 0.0;
-            double bsum = 0.0;
-            for (int w = 0; w < kWaves; ++w) bsum += s_kcw[w][tid];
-            s_kc[tid] = s_scale[tid] * acc + bsum;
+    } else {
+        // top-p off: every token is kept; the chunks' totals, rescaled
+        if (wave == 0) {
+            put_exp2_table();
+            const double mc = lane < S ? static_cast<double>(chunk_head(a, row, lane)->mc) : -INFINITY;
+            const double ct = lane < S ? chunk_head(a, row, lane)->total : 0.0;
+            double zm = mc;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) zm = fmax(zm, __shfl_xor(zm, o, kWave));
+            if (lane < S) s_kc[lane] = mass_exp(mc - zm) * ct;
+            if (lane == 0) s_rd[0] = zm;
         }
         __syncthreads();
-    } else {
-        if (tid < S) s_kc[tid] = s_scale[tid] * chunk_head(a, row, tid)->total;
-        __syncthreads();
+        zmax = s_rd[0];
+        __syncthreads();   // s_rd is reused below
     }
 
     // ---- draw: the chunk, then the token, in vocabulary order ----------------------
     if (wave == 0) {
         const double kc = lane < S ? s_kc[lane] : 0.0;
         const double incl = wave_incl_scan(kc, lane);
-        const double target = static_cast<double>(a.u[row]) * __shfl(incl, kWave - 1, kWave);
+        const double target = static_cast<double>(ur) * __shfl(incl, kWave - 1, kWave);
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(kc > 0.0 && incl > target);
         const unsigned long long any = __builtin_amdgcn_ballot_w64(kc > 0.0);
         // rounding may put the target at the total: the last chunk with kept mass
@@ -1517,16 +1647,24 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
     const int lo = s_ri[0] * C;
     const int hi = min(V, lo + C);
     const int base = lo + wave * (8 * kWave);   // this wave's 512 indices of the chunk
+    float xv[8];
+    if (s_ri[0] == pred) {   // workgroup-uniform
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xv[u] = xpre[u];
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xv[u] = load_at(r.x, min(base + u * kWave + lane, hi - 1));
+    }
     double mm[8];
     uint32_t kbits = 0;
     double wsum = 0.0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int j = base + u * kWave + lane;
-        const float zj = r.x[min(j, hi - 1)] / T;
+        const float zj = div_by_t(xv[u], T, inv);
         const uint32_t key = order_key(zj);
         const bool kp = j < hi && (key > pkey || (key == pkey && j <= pidx));
-        mm[u] = kp ? exp(static_cast<double>(zj) - zmax) : 0.0;
+        mm[u] = kp ? mass_exp(static_cast<double>(zj) - zmax) : 0.0;
         kbits |= static_cast<uint32_t>(kp) << u;
         wsum += mm[u];
     }
@@ -1573,23 +1711,21 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
 }
 
 // ---- the finishing kernel: one workgroup per row, on the row's path ---------------
-// blockIdx.x = row * kSampleRowSplit + g: histogram rows share the gathering
-// pass among their g workgroups; every other row is finished by g = 0 alone.
 __global__ __launch_bounds__(kThreads) void sample_row_kernel(SampleArgs a) {
     __shared__ uint64_t s_pool[kPoolWords];
-    const int row = blockIdx.x / kSampleRowSplit;
-    const int g = blockIdx.x - row * kSampleRowSplit;
+    const int row = blockIdx.x;
     const float T = a.temperature[row];
+    const int32_t tk = a.top_k[row];   // loaded together with T and top-p
+    const float tp = a.top_p[row];
     if (!(T >= 0.0f)) {   // negative or NaN temperature: no token
-        if (g == 0 && threadIdx.x == 0) write_result(a, row, -1, 0, 0);
+        if (threadIdx.x == 0) write_result(a, row, -1, 0, 0);
         return;
     }
-    const int k_eff = T > 0.0f ? kept_by_k(a.top_k[row], a.vocab) : 1;
+    const int k_eff = T > 0.0f ? kept_by_k(tk, a.vocab) : 1;
     if (on_hist_path(T, k_eff, a.vocab, a.chunks) && !on_candidate_path(T, k_eff, a.chunks)) {
-        if (!finish_from_histograms(a, row, g, T, s_pool)) sample_whole_row(a, row, T, k_eff);
+        if (!finish_from_histograms(a, row, T, tp, s_pool)) sample_whole_row(a, row, T, k_eff);
         return;
     }
-    if (g != 0) return;
     if (on_candidate_path(T, k_eff, a.chunks)) finish_from_candidates(a, row, T, k_eff, s_pool);
     else sample_whole_row(a, row, T, k_eff);
 }
@@ -1597,8 +1733,9 @@ __global__ __launch_bounds__(kThreads) void sample_row_kernel(SampleArgs a) {
 }  // namespace
 
 hipError_t launch_sample(const SampleArgs& a, int rows, hipStream_t stream) {
-    hipLaunchKernelGGL(sample_chunk_kernel, dim3(rows * a.chunks), dim3(kChunkThreads), 0, stream, a);
-    hipLaunchKernelGGL(sample_row_kernel, dim3(rows * kSampleRowSplit), dim3(kThreads), 0, stream, a);
+    const int items = rows * a.chunks;
+    hipLaunchKernelGGL(sample_chunk_kernel, dim3(items), dim3(kChunkThreads), 0, stream, a);
+    hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -11,9 +11,10 @@ valid neighbours; everywhere else tokens and kept counts are exact.
 
 Rows take one of three device paths (top-k of at most 256 tokens with
 chunks x k <= 8192: per-chunk candidates; top-k off on rows of at most 64
-chunks: per-chunk mass histograms, unless more than 12288 tokens share the
-top-p boundary's bin; otherwise one workgroup over the whole row); the
-cases below put rows on every side of those lines.
+chunks: per-chunk mass histograms and per-chunk lists around each chunk's
+own top-p boundary, unless more than 12288 tokens share the row's boundary
+bin; otherwise one workgroup over the whole row); the cases below put rows
+on every side of those lines.
 """
 import numpy as np
 import pytest
@@ -124,6 +125,31 @@ def test_top_k_off_rows():
     assert exact >= 22
 
 
+def test_top_k_off_chunk_windows():
+    """Rows built so that chunks fall on every side of the histogram path's
+    per-chunk lists (each chunk lists its tokens in a few bins around its own
+    top-p boundary, and the row's boundary bin is taken from those lists):
+    an outlier that holds nearly all the mass (its bin is the boundary, every
+    other chunk lies below it), outliers that move the row's boundary a few
+    bins above most chunks' own (their lists miss it: those chunks are
+    scanned again), a chunk with thousands of tied logits at the boundary
+    (its list overflows: scanned), and a chunk far below the rest."""
+    sw = build_sample_workload(rows=8, vocab=128256, seed=31, ks=(0,), temps=(0.8,), ps=(0.9,), sigmas=(2.0,))
+    c = (128256 + 15) // 16
+    sw.logits[0, 7 * c + 5] = 25.0
+    sw.logits[1, 7 * c + 5] = 10.0
+    sw.logits[2, 3 * c:3 * c + 3000] = 2.5
+    sw.logits[3, 5 * c:6 * c] = -50.0
+    sw.logits[4, 2 * c + 9] = 11.0
+    sw.logits[4, 12 * c + 9] = 11.0
+    sw.logits[5, 9 * c:9 * c + 6000] = 3.0
+    sw.top_p[6:] = (0.5, 0.99)
+    sw.logits[6, 1 * c + 1] = 10.5
+    sw.logits[7, 14 * c + 77] = 9.5
+    exact = _check(sw)
+    assert exact >= 7
+
+
 def test_top_k_off_beyond_the_histogram_rows():
     """65 chunks (one more than the histogram path merges) and 64 chunks
     exactly, top-k off: the whole-row path and the widest histogram row."""
@@ -155,7 +181,8 @@ def test_workspace_is_checked():
     p = torch.ones(2, device="cuda")
     u = torch.full((2,), 0.5, device="cuda")
     need = pkv.sample_workspace_size(2, 20000)
-    assert need == 2 * (3 * (16384 + 16) + 12288 * 8 + 64)
+    # per chunk: histogram, header, group sums, list of tokens near its boundary, tally
+    assert need == 2 * 3 * (16384 + 16 + 512 + 4096 * 8 + 120)
     small = torch.empty(need - 8, dtype=torch.uint8, device="cuda")
     with pytest.raises(pkv.PagedKVError):
         pkv.sample_tokens(x, T, k, p, u, workspace=small)

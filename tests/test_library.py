@@ -191,14 +191,15 @@ def _call_sample(**over):
 
 
 def test_sampling_workspace_and_argument_errors():
-    # up to 64 chunks of 8192 per row: per chunk 2048 fp64 histogram bins and a
-    # 16-byte header, per row 12288 8-byte gathered tokens and 64 bytes of
-    # counters; wider rows: 256 candidate slots x 8 bytes per chunk
-    row = 12288 * 8 + 64
-    assert pkv.sample_workspace_size(4, 20000) == 4 * (3 * (16384 + 16) + row)
-    assert pkv.sample_workspace_size(64, 128256) == 64 * (16 * (16384 + 16) + row)
-    assert pkv.sample_workspace_size(1, 8192) == 16384 + 16 + row
-    assert pkv.sample_workspace_size(1, 64 * 8192) == 64 * (16384 + 16) + row
+    # up to 64 chunks of 8192 per row: per chunk 2048 fp64 histogram bins, a
+    # 16-byte header, 64 fp64 group sums, a list of 4096 8-byte entries (the
+    # tokens near the chunk's own top-p boundary) and a 120-byte tally; wider
+    # rows: 256 candidate slots x 8 bytes per chunk
+    chunk = 16384 + 16 + 512 + 4096 * 8 + 120
+    assert pkv.sample_workspace_size(4, 20000) == 4 * 3 * chunk
+    assert pkv.sample_workspace_size(64, 128256) == 64 * 16 * chunk
+    assert pkv.sample_workspace_size(1, 8192) == chunk
+    assert pkv.sample_workspace_size(1, 64 * 8192) == 64 * chunk
     assert pkv.sample_workspace_size(2, 64 * 8192 + 1) == 2 * 65 * 2048
     with pytest.raises(pkv.PagedKVError):
         pkv.sample_workspace_size(1, 0)
@@ -210,7 +211,7 @@ def test_sampling_workspace_and_argument_errors():
     assert _call_sample(vocab=8192 * 8192 + 1, ld=8192 * 8192 + 1) == -2
     assert _call_sample(u=0) == -1
     assert _call_sample(ws=0) == -1
-    assert _call_sample(ws_bytes=4 * (3 * (16384 + 16) + row) - 1) == -6
+    assert _call_sample(ws_bytes=4 * 3 * chunk - 1) == -6
     assert _call_sample(ws=260) == -2                 # workspace not 8-byte aligned
     assert _call_sample(rows=0) == 0
 
