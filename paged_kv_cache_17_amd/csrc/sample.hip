@@ -79,29 +79,62 @@ __device__ __forceinline__ void put_exp2_table() {
 }
 __device__ __forceinline__ double mass_exp(double x) { return exp_nonpos(x, s_exp2); }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Wave-wide inclusive scans by DPP moves (row_shr 1, 2, 4, 8 inside each row
+// of 16 lanes, then row_bcast 15 into rows 1 and 3 and row_bcast 31 into
+// rows 2 and 3), a few cycles a step instead of an LDS permute's latency;
+// totals are lane 63's. Lanes reading past their row take the identity.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t identity) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(identity), static_cast<int>(v), kCtrl,
+                                                             kRowMask, 0xF, false));
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ double dpp_f64(double v, double identity) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint64_t id = static_cast<uint64_t>(__double_as_longlong(identity));
+    const uint32_t lo = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(b), static_cast<uint32_t>(id));
+    const uint32_t hi = dpp_u32<kCtrl, kRowMask>(static_cast<uint32_t>(b >> 32), static_cast<uint32_t>(id >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+template <typename C, class Op>
+__device__ __forceinline__ C dpp_scan(C v, C identity, Op op) {
+    auto mv = [&](auto ctrl_tag, auto mask_tag, C x) -> C {
+        constexpr int kC = decltype(ctrl_tag)::value, kM = decltype(mask_tag)::value;
+        if constexpr (sizeof(C) == 8) return dpp_f64<kC, kM>(x, identity);
+        else return dpp_u32<kC, kM>(x, identity);
+    };
+    using I = std::integral_constant<int, 0xF>;
+    v = op(v, mv(std::integral_constant<int, 0x111>{}, I{}, v));   // row_shr:1
+    v = op(v, mv(std::integral_constant<int, 0x112>{}, I{}, v));   // row_shr:2
+    v = op(v, mv(std::integral_constant<int, 0x114>{}, I{}, v));   // row_shr:4
+    v = op(v, mv(std::integral_constant<int, 0x118>{}, I{}, v));   // row_shr:8
+    v = op(v, mv(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{}, v));   // row_bcast:15
+    v = op(v, mv(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{}, v));   // row_bcast:31
     return v;
+}
+__device__ __forceinline__ double lane63_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), kWave - 1));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), kWave - 1));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    return lane63_f64(dpp_scan(v, 0.0, [](double x, double y) { return x + y; }));
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+    return lane63_f64(dpp_scan(v, -__builtin_inf(), [](double x, double y) { return fmax(x, y); }));
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    const uint32_t t = dpp_scan(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(t), kWave - 1));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, o, kWave)));
-    return v;
+    const uint32_t t = dpp_scan(v, 0u, [](uint32_t x, uint32_t y) { return max(x, y); });
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(t), kWave - 1));
 }
 template <typename C>
-__device__ __forceinline__ C wave_incl_scan(C v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const C y = __shfl_up(v, o, kWave);
-        if (lane >= o) v += y;
-    }
-    return v;
+__device__ __forceinline__ C wave_incl_scan(C v, int) {
+    return dpp_scan(v, C(0), [](C x, C y) { return x + y; });
 }
 
 // Larger float -> larger key (NaN excluded), and back.
@@ -213,7 +246,7 @@ __device__ __forceinline__ void write_result(const SampleArgs& a, int row, int t
 template <int NB, typename C>
 __device__ __forceinline__ int find_bin_from_top(const C* bins, C need, C* above, int lane) {
     constexpr int B = NB / kWave;
-    static_assert(B * kWave == NB && (B & (B - 1)) == 0, "bins per lane");
+    static_assert(B * kWave == NB && (B & (B - 1)) == 0 && B <= kWave, "bins per lane");
     const int top = NB - 1 - B * lane;
     C local = 0;
 #pragma unroll
@@ -221,24 +254,18 @@ __device__ __forceinline__ int find_bin_from_top(const C* bins, C need, C* above
     const C incl = wave_incl_scan(local, lane);
     const unsigned long long m = __builtin_amdgcn_ballot_w64(incl >= need);
     if (!m) return -1;
+    // inside the first group that reaches `need`: its B bins from the top, one
+    // per lane, scanned after the mass of the groups above it
     const int first = __builtin_ctzll(m);
-    int bin = -1;
-    C ab = 0;
-    if (lane == first) {
-        C run = incl - local;
-        for (int i = 0; i < B; ++i) {
-            const C v = bins[top - i];
-            if (run + v >= need) {
-                bin = top - i;
-                break;
-            }
-            run += v;
-        }
-        ab = run;
-    }
-    bin = __shfl(bin, first, kWave);
-    *above = __shfl(ab, first, kWave);
-    return bin;
+    const int gtop = NB - 1 - B * first;
+    const C before = __shfl(incl - local, first, kWave);
+    const C v = lane < B ? bins[gtop - lane] : C(0);
+    const C run = before + wave_incl_scan(v, lane);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && run >= need);
+    if (!hit) return -1;   // rounding left the group's bins just short
+    const int i = __builtin_ctzll(hit);
+    *above = __shfl(run - v, i, kWave);
+    return gtop - i;
 }
 
 // ---- candidate path, pass 1: each chunk's own top-k --------------------------
@@ -1282,9 +1309,7 @@ __device__ __forceinline__ RowBoundary boundary_bin(const SampleArgs& a, int row
                                                     const SearchLoads& L, double* s_scale) {
     const int S = a.chunks;
     const double mc = lane < S ? static_cast<double>(L.mc) : -INFINITY;
-    double zmax = mc;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) zmax = fmax(zmax, __shfl_xor(zmax, o, kWave));
+    const double zmax = wave_max_f64(mc);
     const double sc = lane < S ? mass_exp(mc - zmax) : 0.0;
     if (lane < S) s_scale[lane] = sc;
     const double need = static_cast<double>(tp) * wave_sum_f64(lane < S ? sc * L.total : 0.0);
@@ -1471,23 +1496,43 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
         // range (one wave per chunk; the counts came with the tallies) ----------------
         for (int c = wave; c < S; c += kWaves) {   // wave-uniform
             if (((scan >> c) & 1ull) || s_cap[c] == 0u) continue;   // scanned below, or nothing to take
-            const uint32_t st = s_start[c];
+            const uint32_t st = s_start[c], cap = s_cap[c];
             uint32_t m = 0;
-            for (int w = 0; w < kChunkWaves; ++w) {
-                const uint64_t* l = chunk_list(a, row, c) + w * kWinWaveCap;
-                const uint32_t n = min(s_lst[c][w], static_cast<uint32_t>(kWinWaveCap));   // listed in full (covered)
-                for (uint32_t e0 = 0; e0 < n; e0 += kListBatch * kWave) {
-                    uint64_t t[kListBatch];
+            // the bin's tokens of a batch of list entries to the chunk's range
+            auto take = [&](const uint64_t (&t)[kListBatch], uint32_t e0, uint32_t n) {
 #pragma unroll
-                    for (int u = 0; u < kListBatch; ++u) t[u] = l[e0 + u * kWave + lane];   // inside the region
+                for (int u = 0; u < kListBatch; ++u) {
+                    const uint32_t e = e0 + u * kWave + lane;
+                    const bool mem = e < n && (comp_key(t[u]) >> 21) == b1;
+                    const unsigned long long mm = __builtin_amdgcn_ballot_w64(mem);
+                    const uint32_t slot = m + static_cast<uint32_t>(__builtin_popcountll(mm & below));
+                    if (mem && slot < cap) s_bk[st + slot] = t[u];
+                    m += static_cast<uint32_t>(__builtin_popcountll(mm));
+                }
+            };
+            // the four waves' lists in pairs, the first batch of both loaded together
+            // (inside the regions whatever their lengths), then any further batches
+            for (int w = 0; w < kChunkWaves; w += 2) {
+                const uint64_t* l0 = chunk_list(a, row, c) + w * kWinWaveCap;
+                const uint64_t* l1 = l0 + kWinWaveCap;
+                const uint32_t n0 = min(s_lst[c][w], static_cast<uint32_t>(kWinWaveCap));   // listed in full (covered)
+                const uint32_t n1w = min(s_lst[c][w + 1], static_cast<uint32_t>(kWinWaveCap));
+                uint64_t t0[kListBatch], t1[kListBatch];
 #pragma unroll
-                    for (int u = 0; u < kListBatch; ++u) {
-                        const uint32_t e = e0 + u * kWave + lane;
-                        const bool mem = e < n && (comp_key(t[u]) >> 21) == b1;
-                        const unsigned long long mm = __builtin_amdgcn_ballot_w64(mem);
-                        const uint32_t slot = m + static_cast<uint32_t>(__builtin_popcountll(mm & below));
-                        if (mem && slot < s_cap[c]) s_bk[st + slot] = t[u];
-                        m += static_cast<uint32_t>(__builtin_popcountll(mm));
+                for (int u = 0; u < kListBatch; ++u) {
+                    t0[u] = l0[u * kWave + lane];
+                    t1[u] = l1[u * kWave + lane];
+                }
+                take(t0, 0u, n0);
+                take(t1, 0u, n1w);
+                for (int h = 0; h < 2; ++h) {
+                    const uint64_t* l = h ? l1 : l0;
+                    const uint32_t n = h ? n1w : n0;
+                    for (uint32_t e0 = kListBatch * kWave; e0 < n; e0 += kListBatch * kWave) {
+                        uint64_t t[kListBatch];
+#pragma unroll
+                        for (int u = 0; u < kListBatch; ++u) t[u] = l[e0 + u * kWave + lane];
+                        take(t, e0, n);
                     }
                 }
             }
@@ -1615,9 +1660,7 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
             put_exp2_table();
             const double mc = lane < S ? static_cast<double>(chunk_head(a, row, lane)->mc) : -INFINITY;
             const double ct = lane < S ? chunk_head(a, row, lane)->total : 0.0;
-            double zm = mc;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) zm = fmax(zm, __shfl_xor(zm, o, kWave));
+            const double zm = wave_max_f64(mc);
             if (lane < S) s_kc[lane] = mass_exp(mc - zm) * ct;
             if (lane == 0) s_rd[0] = zm;
         }
@@ -1675,22 +1718,15 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
         s_wu[wave] = wany;
     }
     __syncthreads();
-    double pre = s_rd[1], pre_last = pre;
-    int wh = -1, wl = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        if (!s_wu[w]) continue;
-        if (pre + s_wd[w] > target) {
-            wh = w;
-            break;
-        }
-        wl = w;
-        pre_last = pre;
-        pre += s_wd[w];
-    }
-    if (wh < 0) {   // rounding put the target at the chunk's total: its last kept token
-        wh = wl;
-        pre = pre_last;
-    }
+    // the wave holding the target (every wave finds it): a scan over the waves' sums
+    const bool wu = lane < kWaves && s_wu[lane] != 0u;
+    const double wd = wu ? s_wd[lane] : 0.0;
+    const double cw = s_rd[1] + wave_incl_scan(wd, lane);
+    const unsigned long long hitw = __builtin_amdgcn_ballot_w64(wu && cw > target);
+    const unsigned long long anyw = __builtin_amdgcn_ballot_w64(wu);
+    // rounding may put the target at the chunk's total: its last wave with kept tokens
+    const int wh = hitw ? __builtin_ctzll(hitw) : (anyw ? 63 - __builtin_clzll(anyw) : 0);
+    const double pre = __shfl(cw - wd, wh, kWave);
     if (wave == wh) {
         double run = pre;
         int found = -1, last = -1;
