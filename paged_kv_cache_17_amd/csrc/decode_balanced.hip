@@ -265,13 +265,29 @@ struct Bf16Mfma : MfmaRows<G, NB> {
     }
 };
 
-// Decode with four query heads per kv head: one block of rows.
+// Decode with 2, 4 or 8 query heads per kv head: one block of 16 rows on
+// the matrix cores, G of them used. On the 64-sequence batch (lengths
+// 512..4096, 8 kv heads) against the vector-ALU tile math, us per call:
+// G = 2 107.8 against 113.1, G = 8 115.7 against 202.5 (there the vector
+// ALU's 8 x 16 dot products per token are the bound); G = 1 106.7 against
+// 108.1, left on the vector ALU with its 8-bit counterpart.
+template <>
+struct Bf16Kv<2> : Bf16Mfma<2, 1> {
+    using Bf16Mfma<2, 1>::Bf16Mfma;
+};
 template <>
 struct Bf16Kv<4> : Bf16Mfma<4, 1> {
     using Bf16Mfma<4, 1>::Bf16Mfma;
 };
-// 8-bit K/V with four query heads per kv head, tiles in registers, the
-// next tile's loads in flight while one is computed. Lane (q, n) loads:
+template <>
+struct Bf16Kv<8> : Bf16Mfma<8, 1> {
+    using Bf16Mfma<8, 1>::Bf16Mfma;
+};
+// 8-bit K/V with G = 2, 4 or 8 query heads per kv head on the matrix cores,
+// tiles in registers, the next tile's loads in flight while one is
+// computed (us per call on the batch above: G = 2 67.5 against the vector
+// ALU's 81.7, G = 8 77.1 against 215.0; G = 1 stays on the vector ALU, 65.5
+// against 68.1). Lane (q, n) loads:
 //  * token n's codes at bytes 16q .. 16q + 15 and 64 + 16q .. 64 + 16q + 15
 //    (two 16-byte loads, each instruction reading one contiguous half of
 //    every token's row) for the score product. Which dims a lane holds in
@@ -284,7 +300,10 @@ struct Bf16Kv<4> : Bf16Mfma<4, 1> {
 //  * the K and V scales of tokens 4q .. 4q + 3 (one 16-byte load each).
 // 24 registers per tile. The pool of codes and the scale arrays must be
 // 16-byte aligned.
-struct Int8Regs : MfmaRows<4, 1> {
+template <int G>
+struct Int8Regs : MfmaRows<G, 1> {
+    using typename MfmaRows<G, 1>::State;
+    using MfmaRows<G, 1>::kQ;
     static constexpr int kDepth = 2;
     static constexpr int kWavesPerCU = 8;
     static constexpr bool kCodes = true;
@@ -302,15 +321,15 @@ struct Int8Regs : MfmaRows<4, 1> {
           vc(static_cast<const int8_t*>(a.v_cache) + 4 * (lane >> 4) * kTileD + 8 * (lane & 15)),
           ks(a.k_scale + 4 * (lane >> 4)),
           vs(a.v_scale + 4 * (lane >> 4)) {}
-    // The G = 4 heads' query (decode: one row per sequence), lane (q, n) head
-    // n's dims 64(b / 2) + 16q + 8(b % 2) .. + 7 for product b, zero for n >= 4.
+    // The G heads' query (decode: one row per sequence), lane (q, n) head n's
+    // dims 64(b / 2) + 16q + 8(b % 2) .. + 7 for product b, zero for n >= G.
     __device__ __forceinline__ static void fetch_q(u32x4 (&qv)[kQ], const AttnArgs& a, int s, int g, int lane) {
         const int n = lane & 15, q = lane >> 4;
-        const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (static_cast<size_t>(s) * a.n_q + g * 4 + n) * kTileD +
-                             16 * q;
+        const uint16_t* qr = static_cast<const uint16_t*>(a.q) +
+                             (static_cast<size_t>(s) * a.n_q + g * G + min(n, G - 1)) * kTileD + 16 * q;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-            qv[b] = n < 4 ? *reinterpret_cast<const u32x4*>(qr + 64 * (b >> 1) + 8 * (b & 1)) : u32x4{0, 0, 0, 0};
+            qv[b] = n < G ? *reinterpret_cast<const u32x4*>(qr + 64 * (b >> 1) + 8 * (b & 1)) : u32x4{0, 0, 0, 0};
     }
     __device__ __forceinline__ void load(Regs& t, int tile, int /*lane*/) const {
         const size_t off = static_cast<size_t>(tile) * kTileElems;   // one byte per element
@@ -351,8 +370,16 @@ struct Int8Regs : MfmaRows<4, 1> {
     }
 };
 template <>
-struct Int8Kv<4> : Int8Regs {
-    using Int8Regs::Int8Regs;
+struct Int8Kv<2> : Int8Regs<2> {
+    using Int8Regs<2>::Int8Regs;
+};
+template <>
+struct Int8Kv<4> : Int8Regs<4> {
+    using Int8Regs<4>::Int8Regs;
+};
+template <>
+struct Int8Kv<8> : Int8Regs<8> {
+    using Int8Regs<8>::Int8Regs;
 };
 
 // Small chunks: up to 32 (query, head) rows per kv head in two blocks.

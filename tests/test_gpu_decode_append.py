@@ -173,7 +173,7 @@ def _check_step_q8(wl, where):
     assert torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (64, 8)])
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 8), (64, 8)])
 def test_step_q8_ragged_lengths(n_q, n_kv):
     L = np.array(RAGGED)
     wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
