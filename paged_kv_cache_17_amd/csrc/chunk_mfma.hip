@@ -26,7 +26,9 @@
 //    LDS row n of a 32-key subtile holds key pi(n) = n with bits 2 and 3
 //    swapped; then the accumulator registers of S^T already hold, for each
 //    16-key step, the 8 consecutive keys the next product needs in its B
-//    operand;
+//    operand. All 16 K operand reads are issued at once and each pair of
+//    products waits only for its own two (LDS reads complete in order; the
+//    global-to-LDS copies count in vmcnt, not lgkmcnt);
 //  * each lane owns whole query rows (one column of S^T), so the online
 //    softmax is lane-local plus one exchange with the other half-wave; the
 //    reference max moves only when a score exceeds it by 2^8 (exact, rare
@@ -38,6 +40,8 @@
 //    bf16 from registers.
 // Keys past the last one a tile needs are loaded as copies of that key
 // (finite cache data) and get weight 0.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -63,7 +67,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -97,6 +100,23 @@ __device__ __forceinline__ void lds_pin(i16x4& a, i16x4& b, i16x4& c, i16x4& d,
     asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h));
 }
 
+// K operand reads of 16-dim step T for both 32-key subtiles: LDS byte
+// offsets koff[T] (base included) + BOFF and + BOFF + 32 rows. Inline
+// assembly like lds_read_tr16, so that kwait can wait for them one step at
+// a time (the compiler waits for every LDS read at once while copies are in
+// flight).
+template <int BOFF, int T>
+__device__ __forceinline__ void kread(u32x4 (&kop)[2][8], const int (&koff)[8]) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kop[0][T]) : "v"(koff[T]), "i"(BOFF));
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kop[1][T]) : "v"(koff[T]), "i"(BOFF + 32 * kRowBytes));
+}
+// Waits until at most N of this wave's LDS reads are outstanding; the two
+// operands pass through the statement so their products stay after it.
+template <int N>
+__device__ __forceinline__ void kwait(u32x4& a, u32x4& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
 // Maximum of a value over lanes l and l ^ 32.
 __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -126,10 +146,14 @@ template <int G>
 __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uint16_t* __restrict__ out,
                                                                  float* __restrict__ lse) {
     constexpr int QT = kRows / G;                 // queries per workgroup
-    __shared__ __align__(16) uint16_t s_k0[kKeys * kD];
-    __shared__ __align__(16) uint16_t s_k1[kKeys * kD];
-    __shared__ __align__(16) uint16_t s_v0[kKeys * kD];
-    __shared__ __align__(16) uint16_t s_v1[kKeys * kD];
+    // K buffers 0 and 1, then V buffers 0 and 1, at fixed offsets so that
+    // every operand read addresses its buffer by an immediate.
+    __shared__ __align__(16) uint16_t s_buf[4 * kKeys * kD];
+    uint16_t* const s_k0 = s_buf;
+    uint16_t* const s_k1 = s_buf + kKeys * kD;
+    uint16_t* const s_v0 = s_buf + 2 * kKeys * kD;
+    uint16_t* const s_v1 = s_buf + 3 * kKeys * kD;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)s_buf));
     __shared__ int s_bad;
     __shared__ int s_tbl[kTblCache];
 
@@ -175,6 +199,18 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int kmax = P + q_last;                  // largest key any row of this tile sees
     const int nblk = kmax / kBS + 1;
     const int32_t* trow = a.table + static_cast<size_t>(s) * a.table_stride;
+    // The lane's query row, requested before the table is staged so that the
+    // two round trips overlap. Rows past the chunk read its last row (the
+    // loads are unconditional, hence issued together) and are zeroed below.
+    u32x4 qraw[8];
+    {
+        const size_t crow = (static_cast<size_t>(qs) + (active ? qi : max(C - 1, 0))) * a.n_q + g * G + head_l;
+        const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + crow * kD + 8 * h);
+        if (C >= 1) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) qraw[t] = qp[2 * t];
+        }
+    }
     if (tid == 0) s_bad = 0;
     __syncthreads();
     if (ok && nblk <= kTblCache)
@@ -201,11 +237,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const uint32_t q_and = sl2_in == 0.0f ? 0u : 0xFFFFFFFFu;
     const uint32_t q_xor = sl2_in < 0.0f ? 0x80008000u : 0u;
     u32x4 qv[8];
-    {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + orow * kD + 8 * h);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qv[t] = active ? (qp[2 * t] & q_and) ^ q_xor : u32x4{0, 0, 0, 0};
-    }
+    for (int t = 0; t < 8; ++t) qv[t] = active ? (qraw[t] & q_and) ^ q_xor : u32x4{0, 0, 0, 0};
 
     // Copy of one tile: wave w fetches cache block 4kt + w (keys 16w..16w+15
     // of the tile) into LDS rows 16w..16w+15, four rows per instruction.
@@ -218,12 +251,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int lc = lane & 15;
     const int last_blk = kmax / kBS;
     // Source of the copies for tile kt: per-wave block base (K, V) and the
-    // row bound. Rows past key kmax are replaced by a row <= kmax of block bsrc.
-    auto tile_src = [&](int kt) {
+    // row bound. Rows past key kmax are replaced by a row <= kmax of block
+    // min(bi, last_blk), whose table entry tbl_of(kt) reads (a tile ahead of
+    // its use, so the LDS round trip is off the tile's path).
+    auto tbl_of = [&](int kt) { return s_tbl[min(4 * kt + wave, last_blk)]; };
+    auto tile_src = [&](int kt, int idv) {
         const int bi = 4 * kt + wave;
-        const int bsrc = min(bi, last_blk);
         const int cap = bi > last_blk ? (kmax & (kBS - 1)) : min(kmax - kBS * bi, kBS - 1);
-        const int id = __builtin_amdgcn_readfirstlane(s_tbl[bsrc]);
+        const int id = __builtin_amdgcn_readfirstlane(idv);
         const size_t off = static_cast<size_t>(id) * blk_bytes + head_bytes;
         return TileSrc{kc + off, vc + off, cap};
     };
@@ -232,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int i = 0; i < 4; ++i) {
             const int gran = lc ^ swz(4 * i + lr);                 // logical granule of this lane's slot
             const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), src.cap);  // key pi(4i + lr)
-            __builtin_amdgcn_global_load_lds(src.kb + rk * kRowBytes + gran * 16,
+            __builtin_amdgcn_global_load_lds(src.kb + static_cast<uint32_t>(rk * kRowBytes + gran * 16),
                                              (lds_void*)(sk + (16 * wave + 4 * i) * kD), 16, 0, 0);
         }
     };
@@ -241,16 +276,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int i = 0; i < 4; ++i) {
             const int gran = lc ^ swz(4 * i + lr);
             const int rv = min(4 * i + lr, src.cap);
-            __builtin_amdgcn_global_load_lds(src.vb + rv * kRowBytes + gran * 16,
+            __builtin_amdgcn_global_load_lds(src.vb + static_cast<uint32_t>(rv * kRowBytes + gran * 16),
                                              (lds_void*)(sv + (16 * wave + 4 * i) * kD), 16, 0, 0);
         }
     };
 
-    // K read offsets (bytes, within a subtile): row n, logical granule 2t + h.
+    // K read addresses (LDS bytes, K buffer 0, first subtile): row n,
+    // logical granule 2t + h.
     int koff[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) koff[t] = n * kRowBytes + (((2 * t + h) ^ swz(n)) * 16);
-    // V^T read offsets (within a 16-key step): lane (group gq = lane/16,
+    for (int t = 0; t < 8; ++t) koff[t] = lds0 + n * kRowBytes + (((2 * t + h) ^ swz(n)) * 16);
+    // V^T read addresses (LDS bytes from the start of s_buf, within a 16-key step): lane (group gq = lane/16,
     // j = lane%16) reads row 8(gq/2) + 4a + j/4, elements 4(j%4)..+3 of the
     // 16 dims 32dt + 16(gq%2)...
     int voff[4][2];
@@ -262,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
             for (int aa = 0; aa < 2; ++aa) {
                 const int r = 8 * (gq >> 1) + 4 * aa + (j >> 2);
                 const int gran = 4 * dt + 2 * (gq & 1) + ((j >> 1) & 1);
-                voff[dt][aa] = r * kRowBytes + ((gran ^ swz(r)) * 16) + (j & 1) * 8;
+                voff[dt][aa] = lds0 + r * kRowBytes + ((gran ^ swz(r)) * 16) + (j & 1) * 8;
             }
     }
 
@@ -277,41 +313,52 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
     {
-        const TileSrc src = tile_src(0);
+        const TileSrc src = tile_src(0, tbl_of(0));
         issue_k(src, s_k0);
         issue_v(src, s_v0);
     }
+    int nid = tbl_of(1);          // table entry of the tile after the current one
     __syncthreads();
-    // One tile: compute from (sk, sv) while the next tile is copied into
-    // (nk, nv). Called with fixed buffers on even and odd tiles so every LDS
-    // address is a per-lane register plus an immediate.
-    auto tile = [&](int kt, uint16_t* sk, uint16_t* sv, uint16_t* nk, uint16_t* nv) {
-        const lds_char* skb = (const lds_char*)sk;
-        const lds_char* svb = (const lds_char*)sv;
+    // One tile: compute from buffers BUF while the next tile is copied into
+    // (nk, nv), the other buffers. Called with fixed buffers on even and odd
+    // tiles so every LDS address is a per-lane register plus an immediate.
+    auto tile = [&](int kt, auto buf, uint16_t* nk, uint16_t* nv) {
+        constexpr int BUF = decltype(buf)::value;
         // copies of the next tile: in flight during the whole tile
         if (kt + 1 < ntiles) {
-            const TileSrc nsrc = tile_src(kt + 1);
+            const TileSrc nsrc = tile_src(kt + 1, nid);
             issue_k(nsrc, nk);
             issue_v(nsrc, nv);
         }
+        nid = tbl_of(kt + 2);
 
-        // S^T for the two 32-key subtiles; all K operands are requested
-        // before the first product so the LDS latency is paid once.
+        // S^T for the two 32-key subtiles: all K operands are requested at
+        // once (the LDS latency is paid once), and each 16-dim step's pair of
+        // products starts as soon as its two operands have arrived.
+        constexpr int KB = BUF * kKeys * kRowBytes;
         u32x4 kop[2][8];
+        kread<KB, 0>(kop, koff);
+        kread<KB, 1>(kop, koff);
+        kread<KB, 2>(kop, koff);
+        kread<KB, 3>(kop, koff);
+        kread<KB, 4>(kop, koff);
+        kread<KB, 5>(kop, koff);
+        kread<KB, 6>(kop, koff);
+        kread<KB, 7>(kop, koff);
+        kwait<14>(kop[0][0], kop[1][0]);
+        kwait<12>(kop[0][1], kop[1][1]);
+        kwait<10>(kop[0][2], kop[1][2]);
+        kwait<8>(kop[0][3], kop[1][3]);
+        kwait<6>(kop[0][4], kop[1][4]);
+        kwait<4>(kop[0][5], kop[1][5]);
+        kwait<2>(kop[0][6], kop[1][6]);
+        kwait<0>(kop[0][7], kop[1][7]);
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                kop[u][t] = *(const lds_u32x4*)(skb + koff[t] + 32 * u * kRowBytes);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 sacc[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            sacc[u] = f32x16{};
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
                 sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[u][t]), as_bf16x8(qv[t]), sacc[u], 0, 0, 0);
-        }
         // V^T operands for the second product, requested while the weights
         // are computed.
         i16x4 vop[4][4][2];
@@ -319,11 +366,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int aa = 0; aa < 2; ++aa) {
-                const uint32_t va = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(svb + voff[dt][aa]));
-                vop[0][dt][aa] = lds_read_tr16<0 * 16 * kRowBytes>(va);
-                vop[1][dt][aa] = lds_read_tr16<1 * 16 * kRowBytes>(va);
-                vop[2][dt][aa] = lds_read_tr16<2 * 16 * kRowBytes>(va);
-                vop[3][dt][aa] = lds_read_tr16<3 * 16 * kRowBytes>(va);
+                constexpr int VB = (2 + BUF) * kKeys * kRowBytes;   // V buffer BUF
+                const uint32_t va = voff[dt][aa];
+                vop[0][dt][aa] = lds_read_tr16<VB + 0 * 16 * kRowBytes>(va);
+                vop[1][dt][aa] = lds_read_tr16<VB + 1 * 16 * kRowBytes>(va);
+                vop[2][dt][aa] = lds_read_tr16<VB + 2 * 16 * kRowBytes>(va);
+                vop[3][dt][aa] = lds_read_tr16<VB + 3 * 16 * kRowBytes>(va);
             }
 
         // Causal mask (diagonal tiles only), max, lazy rescale, weights.
@@ -344,10 +392,16 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
                 for (int r = 0; r < 16; ++r)
                     sv2[u][r] = (32 * u + key_of_reg(r) <= lim) ? sv2[u][r] : -INFINITY;
         }
+        {
+            // two independent chains, one per subtile
+            float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv2[u][r]);
+            for (int r = 0; r < 16; ++r) {
+                m0 = fmaxf(m0, sv2[0][r]);
+                m1 = fmaxf(m1, sv2[1][r]);
+            }
+            mx = fmaxf(m0, m1);
+        }
         mx = max_halves(mx) * sl2;
         const bool need = mx > mref + kLazy;
         if (__builtin_amdgcn_ballot_w64(need)) {
@@ -393,13 +447,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                 as_bf16x8(pb[t]), o[dt], 0, 0, 0);
             }
-        // the next tile's copies have landed (the barrier waits for them) and
-        // every wave is done reading this tile's buffers
+        // the next tile's copies have landed and every wave is done reading
+        // this tile's buffers
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
     for (int kt = 0; kt < ntiles; kt += 2) {
-        tile(kt, s_k0, s_v0, s_k1, s_v1);
-        if (kt + 1 < ntiles) tile(kt + 1, s_k1, s_v1, s_k0, s_v0);
+        tile(kt, std::integral_constant<int, 0>{}, s_k1, s_v1);
+        if (kt + 1 < ntiles) tile(kt + 1, std::integral_constant<int, 1>{}, s_k0, s_v0);
     }
 
     // Epilogue: combine the half-waves' sums, normalise, store.
