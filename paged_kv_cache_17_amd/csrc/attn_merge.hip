@@ -122,17 +122,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     if (tid == 0) {
+        // every load of this round is unconditional, so they are in flight
+        // together (decode has no q_start: prefix stands in, unused)
+        const int32_t* qsp = a.q_start ? a.q_start : a.prefix;
         const int L = a.seq_lens[s];
-        int row0 = s, C = 1;
-        if (a.q_start) {
-            row0 = a.q_start[s];
-            C = a.q_start[s + 1] - row0;
-        }
-        const long long P = a.prefix[s];
-        const long long nb = a.prefix[s + 1] - P;
-        const long long Tt = static_cast<long long>(a.n_kv) * a.prefix[a.num_seqs];
-        bool ok = C >= 1 && C * G <= RS && seq_len_ok(L, C, a.max_seq_len, a.table_stride * a.block_size) &&
-                  nb == (L + a.block_size - 1) / a.block_size && Tt > 0;
+        const int q0 = qsp[s], q1 = qsp[s + 1];
+        const int p0 = a.prefix[s], p1 = a.prefix[s + 1], pS = a.prefix[a.num_seqs];
+        const int row0 = a.q_start ? q0 : s;
+        const int C = a.q_start ? q1 - q0 : 1;
+        const long long P = p0;
+        const long long nb = p1 - p0;
+        const long long Tt = static_cast<long long>(a.n_kv) * pS;
+        // (& rather than &&: the length's load then stays with the others)
+        bool ok = (C >= 1) & (C * G <= RS) & seq_len_ok(L, C, a.max_seq_len, a.table_stride * a.block_size) &
+                  (nb == (L + a.block_size - 1) / a.block_size) & (Tt > 0);
         int count = 0;
         long long first = 0;
         if (ok) {
@@ -171,23 +174,30 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(AttnArgs 
     const int r_o = tid / (D / 4);
     const int k_o = 4 * (tid - r_o * (D / 4));
     const float* ob = a.ws_o + (first * RS + rb + r_o) * D + k_o;
+    // Unconditional loads (partials past `count` re-read the last one, and
+    // slot 0 stands in when there is none), so that all are issued together.
     float4 pre[kPre];
     if (has_out) {
 #pragma unroll
         for (int u = 0; u < kPre; ++u)
-            pre[u] = u < count ? *reinterpret_cast<const float4*>(ob + static_cast<size_t>(u) * RS * D)
-                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            pre[u] = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(max(min(u, count - 1), 0)) * RS * D);
     }
 
     // Per-row maximum over all partials; a NaN partial makes it NaN.
     for (int j0 = 0; j0 < count; j0 += kMergeMaxParts) {
         const int n = min(count - j0, kMergeMaxParts);
         if (tid < n) {
-            for (int r = 0; r < used; ++r) {
-                const PartialML p = a.ws_ml[(first + j0 + tid) * RS + rb + r];
-                s_m[tid][r] = p.m;
-                s_l[tid][r] = p.l;
-            }
+            // all RB rows' loads in flight at once (rows past `used` re-read
+            // the last used row and are not stored)
+            PartialML p[RB];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) p[r] = a.ws_ml[(first + j0 + tid) * RS + rb + min(r, used - 1)];
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+                if (r < used) {
+                    s_m[tid][r] = p[r].m;
+                    s_l[tid][r] = p[r].l;
+                }
         }
         __syncthreads();
         for (int r = wave; r < used; r += kMergeThreads / kWave) {
