@@ -43,6 +43,15 @@ constexpr double kExpInvStep = 0x1.71547652b82fep+5;    // 32 / ln2
 constexpr double kExpStepHi = 0x1.62e42fefa39efp-6;     // ln2 / 32, rounded
 constexpr double kExpStepLo = 0x1.abc9e3b39803fp-61;    // ln2 / 32 - kExpStepHi
 
+// Three of the Taylor coefficients (1/120, 1/24, 1/6), the ones that enter
+// the polynomial as addends. A kernel evaluating many exponentials may pass
+// copies it keeps in registers, so that the compiler does not rebuild them
+// for every evaluation; the values are the same.
+struct ExpCoef {
+    double c5, c4, c3;
+};
+constexpr ExpCoef kExpCoef{1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0};
+
 // exp(x) with the table of 2^(j/32) at `tab` (kExp2Frac or a copy of it).
 // Branch-free (the argument is clamped and the special results selected at
 // the end), so that a caller's independent evaluations can interleave.
@@ -68,15 +77,15 @@ PKV_HOST_DEVICE inline double exp_tab(double x, const double* tab) {
 // such an argument. Nothing can overflow, and below -746 the scaled result
 // rounds to 0 by itself (2^(j/32) (1 + p) 2^m with m <= -1077 lies below
 // half the least subnormal), so only the lower clamp and NaN remain.
-PKV_HOST_DEVICE inline double exp_nonpos(double x, const double* tab) {
+PKV_HOST_DEVICE inline double exp_nonpos(double x, const double* tab, const ExpCoef& k = kExpCoef) {
     const double xc = __builtin_fmax(x, -746.0);   // NaN becomes -746; -inf as well
     const double n = __builtin_rint(xc * kExpInvStep);
     double r = __builtin_fma(-n, kExpStepHi, xc);
     r = __builtin_fma(-n, kExpStepLo, r);
     const int ni = static_cast<int>(n);
-    double q = __builtin_fma(r, 1.0 / 720.0, 1.0 / 120.0);
-    q = __builtin_fma(q, r, 1.0 / 24.0);
-    q = __builtin_fma(q, r, 1.0 / 6.0);
+    double q = __builtin_fma(r, 1.0 / 720.0, k.c5);
+    q = __builtin_fma(q, r, k.c4);
+    q = __builtin_fma(q, r, k.c3);
     q = __builtin_fma(q, r, 0.5);
     const double p = __builtin_fma(q, r * r, r);
     const double t = tab[ni & 31];

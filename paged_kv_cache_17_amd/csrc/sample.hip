@@ -78,6 +78,14 @@ __device__ __forceinline__ void put_exp2_table() {
     if (threadIdx.x < 32) s_exp2[threadIdx.x] = t;
 }
 __device__ __forceinline__ double mass_exp(double x) { return exp_nonpos(x, s_exp2); }
+// The polynomial's addends held in registers (opaque to the compiler, which
+// would otherwise rebuild each of them for every exponential of a loop).
+__device__ __forceinline__ ExpCoef held_coef() {
+    ExpCoef k = kExpCoef;
+    asm volatile("" : "+v"(k.c5), "+v"(k.c4), "+v"(k.c3));
+    return k;
+}
+__device__ __forceinline__ double mass_exp(double x, const ExpCoef& k) { return exp_nonpos(x, s_exp2, k); }
 
 // Wave-wide inclusive scans by DPP moves (row_shr 1, 2, 4, 8 inside each row
 // of 16 lanes, then row_bcast 15 into rows 1 and 3 and row_bcast 31 into
@@ -153,8 +161,8 @@ __device__ __forceinline__ float load_at(const float* base, int i) {
     return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + static_cast<uint32_t>(i) * 4u);
 }
 
-// z = x / T rounded to fp32 (T > 0 finite, inv = 1 / T rounded to fp64),
-// as the division itself would give it. The fp64 product x * inv is within
+// x[i] <- x[i] / T rounded to fp32 (T > 0 finite, inv = 1 / T rounded to
+// fp64), as the division itself would give it. The fp64 product x * inv is within
 // a relative 2^-52 of x / T. A quotient of two fp32 values never equals the
 // midpoint between two adjacent normal fp32 values (with x = X 2^a, T = M
 // 2^c and the midpoint m = N 2^b, X, M, N odd, N of 25 bits, x = m T would
@@ -163,11 +171,27 @@ __device__ __forceinline__ float load_at(const float* base, int i) {
 // more than 2^-49 (relative) away from every such midpoint. So rounding the
 // product to fp32 gives the correctly rounded quotient whenever the result
 // lies above the smallest normal value; at or below it (the subnormals,
-// where exact midpoints do occur), and for NaN, the division is done.
-__device__ __forceinline__ float div_by_t(float x, float T, double inv) {
-    const float q = static_cast<float>(static_cast<double>(x) * inv);
-    return fabsf(q) > 0x1p-126f ? q : x / T;
+// where exact midpoints do occur), and for NaN, the division is done: only
+// in a wave that has such a value (rare), so that the common path does not
+// compute the divisions.
+template <int N>
+__device__ __forceinline__ void div_by_t(float (&x)[N], float T, double inv) {
+    float q[N];
+    bool slow = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        q[i] = static_cast<float>(static_cast<double>(x[i]) * inv);
+        slow |= !(fabsf(q[i]) > 0x1p-126f);
+    }
+    if (__builtin_amdgcn_ballot_w64(slow)) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if (!(fabsf(q[i]) > 0x1p-126f)) q[i] = x[i] / T;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = q[i];
 }
+
 // (key, index) as one 64-bit value whose descending order is decreasing z
 // with ties to the lower index; 0 is below every real candidate.
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
@@ -310,12 +334,12 @@ __device__ __forceinline__ void chunk_digit(const uint32_t (&key)[kPerThread], i
 // window; a chunk whose window misses it is scanned again there. Keys of 0
 // lie past the chunk's end; element i of this thread has index jb + i *
 // kChunkThreads.
-__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s, int jb,
+__device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s, int jb, float top_p,
                                              const uint32_t (&key)[kPerThread], double* s_hm, uint32_t* s_tw) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const bool hist = a.top_p[row] < 1.0f;
+    const bool hist = top_p < 1.0f;
     __shared__ double s_wt[kChunkWaves];
     uint32_t mk = 0;
 #pragma unroll
@@ -330,13 +354,24 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
     for (int w = 1; w < kChunkWaves; ++w) mk = max(mk, s_tw[w]);
     const float mc = key_value(mk);
     const double mcd = static_cast<double>(mc);
+    // Branch-free over the elements: a slot past the chunk's end (key 0)
+    // gets mass 0 (added to bin 0, which changes nothing).
+    const ExpCoef kc = held_coef();
     double tot = 0.0;
+    if (hist) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        if (!key[i]) continue;
-        const double m = mass_exp(static_cast<double>(key_value(key[i])) - mcd);
-        if (hist) atomicAdd(&s_hm[key[i] >> 21], m);
-        else tot += m;
+        for (int i = 0; i < kPerThread; ++i) {
+            const bool real = key[i] != 0u;
+            const double m = mass_exp((real ? static_cast<double>(key_value(key[i])) : mcd) - mcd, kc);
+            atomicAdd(&s_hm[key[i] >> 21], real ? m : 0.0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const bool real = key[i] != 0u;
+            const double m = mass_exp((real ? static_cast<double>(key_value(key[i])) : mcd) - mcd, kc);
+            tot += real ? m : 0.0;
+        }
     }
     SampleChunkHead* h = chunk_head(a, row, s);
     if (hist) {
@@ -376,7 +411,7 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
         double tot = 0.0;
 #pragma unroll
         for (int w = 0; w < kChunkWaves; ++w) tot += s_wt[w];
-        const double need = static_cast<double>(a.top_p[row]) * tot;
+        const double need = static_cast<double>(top_p) * tot;
         uint32_t lb = 0;   // 1 + the largest bin of this thread reaching the need
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
@@ -447,21 +482,36 @@ __device__ __forceinline__ void chunk_masses(const SampleArgs& a, int row, int s
 // path.
 struct ChunkItem {
     int row, s, lo, hi, k_eff;
-    float T;
+    float T, top_p;
     bool cand, live;
 };
 
-__device__ __forceinline__ ChunkItem chunk_item(const SampleArgs& a, int it) {
+// The row's T and k, requested through vector loads (a lane offset of 0
+// the compiler cannot see through) ahead of the logits: as scalar loads
+// their wait also held back the logits' loads.
+struct RowParams {
+    float T;
+    int32_t k;
+    float top_p;
+};
+__device__ __forceinline__ RowParams row_params(const SampleArgs& a, int it) {
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const int row = it / a.chunks + zero;
+    return RowParams{a.temperature[row], a.top_k[row], a.top_p[row]};
+}
+
+__device__ __forceinline__ ChunkItem chunk_item(const SampleArgs& a, int it, RowParams p) {
     ChunkItem c{};
     c.live = false;
     if (it >= a.rows * a.chunks) return c;
     const int S = a.chunks;
     c.row = it / S;
     c.s = it - c.row * S;
-    c.T = a.temperature[c.row];
-    const int32_t tk = a.top_k[c.row];   // loaded together with T
+    c.T = p.T;
+    c.top_p = p.top_p;
     if (!(c.T >= 0.0f)) return c;
-    c.k_eff = c.T > 0.0f ? kept_by_k(tk, a.vocab) : 1;
+    c.k_eff = c.T > 0.0f ? kept_by_k(p.k, a.vocab) : 1;
     c.cand = on_candidate_path(c.T, c.k_eff, S);
     if (!c.cand && !on_hist_path(c.T, c.k_eff, a.vocab, S)) return c;
     const int C = (a.vocab + S - 1) / S;
@@ -471,14 +521,21 @@ __device__ __forceinline__ ChunkItem chunk_item(const SampleArgs& a, int it) {
     return c;
 }
 
-// Element i of this thread: index lo + i * kChunkThreads + tid. The loads
-// are unconditional (clamped to the last element) so that all of them are
-// in flight together.
-__device__ __forceinline__ void load_item(const SampleArgs& a, const ChunkItem& c, uint32_t (&key)[kPerThread]) {
-    const float* x = a.logits + static_cast<size_t>(c.row) * a.ld;
-    const int jb = c.lo + static_cast<int>(threadIdx.x);
+// Element i of this thread: index lo + i * kChunkThreads + tid of chunk s
+// of row `row` (bounds from the item index alone, so these loads need not
+// wait for the row's parameters). The loads are unconditional (clamped to
+// the chunk's last element, or to the row's last one for a chunk past the
+// vocabulary) so that all of them are in flight together.
+__device__ __forceinline__ void load_item(const SampleArgs& a, int it, uint32_t (&key)[kPerThread]) {
+    const int S = a.chunks;
+    const int row = it / S;
+    const int C = (a.vocab + S - 1) / S;
+    const int lo = (it - row * S) * C;
+    const int hi = min(a.vocab, lo + C);
+    const float* x = a.logits + static_cast<size_t>(row) * a.ld;
+    const int jb = lo + static_cast<int>(threadIdx.x);
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(load_at(x, min(jb + i * kChunkThreads, c.hi - 1)));
+    for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(load_at(x, min(jb + i * kChunkThreads, hi - 1)));
 }
 
 // Candidate items: writes the chunk's min(k, chunk length) best (key,
@@ -498,8 +555,12 @@ __device__ __forceinline__ void chunk_item_work(const SampleArgs& a, const Chunk
     const int jb = lo + tid;
     if (T > 0.0f) {
         const double inv = 1.0 / static_cast<double>(T);
+        float z[kPerThread];
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(div_by_t(__uint_as_float(key[i]), T, inv));
+        for (int i = 0; i < kPerThread; ++i) z[i] = __uint_as_float(key[i]);
+        div_by_t(z, T, inv);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) key[i] = __float_as_uint(z[i]);
     }
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) key[i] = jb + i * kChunkThreads < hi ? order_key(__uint_as_float(key[i])) : 0u;
@@ -508,7 +569,7 @@ __device__ __forceinline__ void chunk_item_work(const SampleArgs& a, const Chunk
     __shared__ uint64_t s_pool[kSampleHistBins];   // histogram rows: fp64 bins; candidate rows: keep list + digit bins
     __shared__ uint32_t s_tc[kPerThread * kChunkWaves];
     if (!cand) {
-        chunk_masses(a, row, s, jb, key, reinterpret_cast<double*>(s_pool), s_tw);
+        chunk_masses(a, row, s, jb, c.top_p, key, reinterpret_cast<double*>(s_pool), s_tw);
         return;
     }
     uint64_t* s_keep = s_pool;
@@ -539,17 +600,22 @@ __device__ __forceinline__ void chunk_item_work(const SampleArgs& a, const Chunk
     for (int w = 1; w < kChunkWaves; ++w) thr = min(thr, s_tw[w]);
     thr = max(thr, 1u);
 
-    // the keys at or above the bound, as (key, index) composites
+    // the keys at or above the bound, as (key, index) composites: each wave
+    // counts its keys first and claims all their slots with one atomic
+    {
+        uint32_t wn = 0;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        const bool keep = key[i] >= thr;
-        const unsigned long long km = __builtin_amdgcn_ballot_w64(keep);
-        if (km) {
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s_n, static_cast<uint32_t>(__builtin_popcountll(km)));
-            base = __shfl(base, 0, kWave);
+        for (int i = 0; i < kPerThread; ++i) wn += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[i] >= thr));
+        uint32_t base = 0;
+        if (lane == 0 && wn) base = atomicAdd(&s_n, wn);
+        base = __builtin_amdgcn_readlane(base, 0);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const bool keep = key[i] >= thr;
+            const unsigned long long km = __builtin_amdgcn_ballot_w64(keep);
             const uint32_t slot = base + __builtin_popcountll(km & below);
             if (keep && slot < kChunkKeep) s_keep[slot] = composite(key[i], static_cast<uint32_t>(jb + i * kChunkThreads));
+            base += __builtin_popcountll(km);
         }
     }
     __syncthreads();
@@ -619,11 +685,18 @@ __device__ __forceinline__ void chunk_item_work(const SampleArgs& a, const Chunk
 // One workgroup per (row, chunk) item, blockIdx.x = row * chunks + chunk.
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void sample_chunk_kernel(SampleArgs a) {
-    const ChunkItem c = chunk_item(a, static_cast<int>(blockIdx.x));
-    if (!c.live) return;
+    const int it = static_cast<int>(blockIdx.x);
+    if (it >= a.rows * a.chunks) return;
+    const RowParams p = row_params(a, it);
     uint32_t key[kPerThread];
-    load_item(a, c, key);
-    put_exp2_table();   // read after the first barrier
+    load_item(a, it, key);   // needs no parameter of the row
+    put_exp2_table();        // read after the barrier
+    // The barrier keeps the logits' loads ahead of the row's checks below
+    // (otherwise the compiler moves the exits first, and the loads wait for
+    // T and k).
+    __syncthreads();
+    const ChunkItem c = chunk_item(a, it, p);
+    if (!c.live) return;
     chunk_item_work(a, c, key);
 }
 
@@ -1547,11 +1620,15 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
             const int hi = min(V, lo + C);
             const uint32_t st = s_start[c], cap = s_cap[c];
             uint32_t up = 0;
+            float zs[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) zs[u] = load_at(r.x, min(lo + u * kThreads + tid, hi - 1));
+            div_by_t(zs, T, inv);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int j = lo + u * kThreads + tid;
                 const bool in = j < hi;
-                const uint32_t key = order_key(div_by_t(load_at(r.x, min(j, hi - 1)), T, inv));
+                const uint32_t key = order_key(zs[u]);
                 const uint32_t bn = key >> 21;
                 const bool mem = in && bn == b1;
                 up += in && bn > b1 ? 1u : 0u;
@@ -1701,10 +1778,11 @@ __device__ __forceinline__ bool finish_from_histograms(const SampleArgs& a, int 
     double mm[8];
     uint32_t kbits = 0;
     double wsum = 0.0;
+    div_by_t(xv, T, inv);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int j = base + u * kWave + lane;
-        const float zj = div_by_t(xv[u], T, inv);
+        const float zj = xv[u];
         const uint32_t key = order_key(zj);
         const bool kp = j < hi && (key > pkey || (key == pkey && j <= pidx));
         mm[u] = kp ? mass_exp(static_cast<double>(zj) - zmax) : 0.0;
