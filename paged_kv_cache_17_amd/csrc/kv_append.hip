@@ -10,9 +10,11 @@
 namespace pkv {
 namespace {
 
+typedef uint32_t piece_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t piece_u32x2 __attribute__((ext_vector_type(2)));
 template <int UNIT> struct Piece;
-template <> struct Piece<16> { using T = uint4; };
-template <> struct Piece<8> { using T = uint2; };
+template <> struct Piece<16> { using T = piece_u32x4; };
+template <> struct Piece<8> { using T = piece_u32x2; };
 template <> struct Piece<4> { using T = uint32_t; };
 template <> struct Piece<2> { using T = uint16_t; };
 
@@ -31,17 +33,25 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int32_t* __restrict__ seq_lens, int max_seq_len) {
     using P = typename Piece<UNIT>::T;
     __shared__ int s_start[kStagedSeqs + 1];
+    // The piece this thread moves is requested first: its address depends on
+    // the thread's index alone, so its round trip overlaps the staging and
+    // the sequence's lookups (a thread past the end reads the last piece).
+    const int units = row_bytes / UNIT;
+    const long long total = static_cast<long long>(total_new) * n_kv * units;
+    const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const long long ic = idx < total ? idx : total - 1;
+    const int u = static_cast<int>(ic % units);
+    const long long th = ic / units;
+    const int h = static_cast<int>(th % n_kv);
+    const int t = static_cast<int>(th / n_kv);
+    const size_t src = (static_cast<size_t>(t) * n_kv + h) * row_bytes + static_cast<size_t>(u) * UNIT;
+    const P kp = *reinterpret_cast<const P*>(kn + src);
+    const P vp = *reinterpret_cast<const P*>(vn + src);
     const bool staged = num_seqs <= kStagedSeqs;
     if (staged)
         for (int i = threadIdx.x; i <= num_seqs; i += blockDim.x) s_start[i] = new_start[i];
     __syncthreads();
-    const int units = row_bytes / UNIT;
-    const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= static_cast<long long>(total_new) * n_kv * units) return;
-    const int u = static_cast<int>(idx % units);
-    const long long th = idx / units;
-    const int h = static_cast<int>(th % n_kv);
-    const int t = static_cast<int>(th / n_kv);
+    if (idx >= total) return;
     const int32_t* starts = staged ? s_start : new_start;
     const int s = seq_of_row(starts, num_seqs, t);
     int first = 0;   // position of sequence s's first new token
@@ -59,9 +69,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     if (blk < 0 || blk >= num_blocks) return;   // unmapped slot: nothing is written
     const size_t dst = ((static_cast<size_t>(blk) * n_kv + h) * bs + pos % bs) * row_bytes +
                        static_cast<size_t>(u) * UNIT;
-    const size_t src = (static_cast<size_t>(t) * n_kv + h) * row_bytes + static_cast<size_t>(u) * UNIT;
-    *reinterpret_cast<P*>(kc + dst) = *reinterpret_cast<const P*>(kn + src);
-    *reinterpret_cast<P*>(vc + dst) = *reinterpret_cast<const P*>(vn + src);
+    *reinterpret_cast<P*>(kc + dst) = kp;
+    *reinterpret_cast<P*>(vc + dst) = vp;
 }
 
 template <int UNIT>
