@@ -486,9 +486,9 @@ struct ChunkItem {
     bool cand, live;
 };
 
-// The row's T and k, requested through vector loads (a lane offset of 0
-// the compiler cannot see through) ahead of the logits: as scalar loads
-// their wait also held back the logits' loads.
+// The row's T, k and top-p, requested through vector loads (a lane offset
+// of 0 the compiler cannot see through) ahead of the logits: as scalar
+// loads their wait also held back the logits' loads.
 struct RowParams {
     float T;
     int32_t k;
