@@ -27,8 +27,10 @@
 //    swapped; then the accumulator registers of S^T already hold, for each
 //    16-key step, the 8 consecutive keys the next product needs in its B
 //    operand. All 16 K operand reads are issued at once and each pair of
-//    products waits only for its own two (LDS reads complete in order; the
-//    global-to-LDS copies count in vmcnt, not lgkmcnt);
+//    products waits only for its own two (LDS reads complete in order, the
+//    global-to-LDS copies count in vmcnt, not lgkmcnt, and the tile loop
+//    issues no scalar memory load, whose out-of-order return would share
+//    lgkmcnt: checked in the generated code for G = 1, 2, 4, 8);
 //  * each lane owns whole query rows (one column of S^T), so the online
 //    softmax is lane-local plus one exchange with the other half-wave; the
 //    reference max moves only when a score exceeds it by 2^8 (exact, rare
