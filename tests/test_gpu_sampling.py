@@ -125,6 +125,28 @@ def test_top_k_off_rows():
     assert exact >= 22
 
 
+def test_quotients_below_the_normal_range():
+    """Logits whose quotients by T fall at or below the smallest normal fp32
+    value, where the fp64 product does not round like the division (exact
+    midpoints exist among subnormals), so the kernels divide for those
+    values; some rows are tiny throughout, others carry a few tiny values
+    among normal ones, so waves mix both cases. Candidate path (k = 5, 50),
+    histogram path (k off, top-p 0.9 and 1) and both vocabulary widths."""
+    for vocab, seed in ((1000, 41), (50257, 42)):
+        sw = build_sample_workload(rows=16, vocab=vocab, seed=seed, ks=(0, 5, 50), temps=(0.8, 1.5, 3.0),
+                                   ps=(1.0, 0.9))
+        rng = np.random.default_rng(seed + 100)
+        tiny = (rng.standard_normal((8, vocab)) * 2e-38).astype(np.float32)
+        sw.logits[:8] = tiny                               # every quotient near or below 2^-126
+        sw.top_k[:8] = (0, 5, 0, 50, 0, 5, 0, 50)          # both paths on the tiny rows
+        idx = rng.integers(0, vocab, size=(8, 64))
+        for r in range(8, 16):
+            sw.logits[r, idx[r - 8]] = tiny[r - 8, idx[r - 8]]   # a few tiny values in normal rows
+        assert np.any(np.abs(sw.logits[:8] / sw.temperature[:8, None]) < np.float32(2.0 ** -126))
+        exact = _check(sw)
+        assert exact >= 15, (vocab, exact)
+
+
 def test_top_k_off_chunk_windows():
     """Rows built so that chunks fall on every side of the histogram path's
     per-chunk lists (each chunk lists its tokens in a few bins around its own
