@@ -107,6 +107,29 @@ def test_balanced_many_short_sequences():
     say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
 
 
+@pytest.mark.parametrize("n_q,lens", [(8, [20000]), (4, [65536, 3])])
+def test_balanced_long_segment_many_partials(n_q, lens):
+    """One kv head and a long sequence: the sequence's single (or dominant)
+    segment spans hundreds to thousands of waves (20000 keys: fewer tiles
+    than waves, one tile and one partial per wave, 1250 partials; 65536
+    keys: ~1500 partials), beyond the 256 partials the merge stages in LDS
+    at once, so it merges in several batches and recomputes the weights
+    from the workspace; at four heads also with 5-token chunks."""
+    L = np.array(lens)
+    wl = build_workload(n_q=n_q, n_kv=1, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                        new_lens=np.ones_like(L), seed=23)
+    say("balanced, long segment", n_q, lens)
+    _, _, err, lerr = _full_check(wl, "decode", 0, check_pool=False)
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+    if n_q == 4:
+        # the same with 5-token chunks (20 rows per kv head: the small-chunk pass
+        # and its row-group merge)
+        wl = build_workload(n_q=n_q, n_kv=1, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
+                            new_lens=np.full_like(L, 5), seed=24)
+        _, _, err, lerr = _full_check(wl, "chunk", 0, check_pool=False)
+        say(f"  chunks of 5: worst row rel err {err:.2e} lse {lerr:.2e}")
+
+
 def test_balanced_workspace_reuse_and_stale_contents():
     """Workspace contents on entry are ignored: back-to-back calls on one
     workspace, and calls on a workspace holding arbitrary bytes or zeros,
