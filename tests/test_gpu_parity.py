@@ -221,6 +221,18 @@ def test_chunk_matrix_core_path_shapes(n_q, n_kv):
     say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
 
 
+def test_chunks_past_the_matrix_core_kernels_table_cache():
+    """Chunks over a history longer than the 32768 keys whose table the
+    matrix-core chunk kernel stages in LDS: the call takes the general
+    split pass and merge instead; every row against the oracle (a 64-query
+    chunk over 40000 cached keys and a short sequence beside it)."""
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=[40000, 100],
+                        new_lens=[64, 7], seed=25)
+    say("chunks over a 40000-key history")
+    _, _, err, lerr = _full_check(wl, "chunk", 0, check_pool=False)
+    say(f"  worst row rel err {err:.2e} lse {lerr:.2e}")
+
+
 @pytest.mark.parametrize("n_q,n_kv,rows", [(32, 8, 128), (64, 8, 128), (32, 8, 32), (64, 8, 32), (8, 8, 32)])
 def test_small_chunks_over_long_histories(n_q, n_kv, rows):
     """Small chunks over histories that end just before, at and after
