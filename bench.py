@@ -540,8 +540,8 @@ def main():
     S = wl.num_seqs
     nd = int(np.argmax(wl.new_lens != 1)) if (wl.new_lens != 1).any() else S   # decode rows come first
     assert (wl.new_lens[:nd] == 1).all() and (wl.new_lens[nd:] > 1).all()
-    if quant and (nd < S or args.split):
-        sys.exit("the 8-bit cache has decode rows only, with the balanced partition")
+    if quant and args.split:
+        sys.exit("the 8-bit cache takes the library's partition only (no --split)")
     q = raw_to_torch(wl.q, wl.dtype)
     kn, vn = wl.packed_new_kv()
     k_new, v_new = raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype)
@@ -560,8 +560,12 @@ def main():
         return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
 
     def chunk_workspace():
-        n = pkv.paged_attn_chunk_workspace_size(S - nd, len(q_chk), max_c, wl.n_q, wl.n_kv, wl.head_dim,
-                                                wl.block_size, max_chk, split)
+        if quant:   # large chunks over the 8-bit cache: room for the staged bf16 blocks
+            n = pkv.paged_attn_chunk_q8_workspace_size(S - nd, len(q_chk), max_c, wl.n_q, wl.n_kv, wl.head_dim,
+                                                       wl.block_size, max_chk)
+        else:
+            n = pkv.paged_attn_chunk_workspace_size(S - nd, len(q_chk), max_c, wl.n_q, wl.n_kv, wl.head_dim,
+                                                    wl.block_size, max_chk, split)
         return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
     ws = [(workspace(nd, max_dec) if nd else None, chunk_workspace() if nd < S else None) for _ in caches]
     stream = torch.cuda.current_stream()
@@ -595,9 +599,14 @@ def main():
                                       max_dec, wl.scale, ws[j][0], split_tokens=split, stream=stream)
         if nd < S:
             pkv.pkv_set_profile_events(*ev_chk) if ev_chk is not None else pkv.pkv_set_profile_events(None, None)
-            pkv.paged_attn_chunk(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, c.table_dev[nd:],
-                                 seq_lens[nd:], max_c, max_chk, wl.scale, ws[j][1], split_tokens=split,
-                                 stream=stream)
+            if quant:   # blocks staged as bf16 in the workspace, then the matrix-core chunk kernel
+                pkv.paged_attn_chunk_q8(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, c.k_scale,
+                                        c.v_scale, c.table_dev[nd:], seq_lens[nd:], max_c, max_chk, wl.scale,
+                                        ws[j][1], stream=stream)
+            else:
+                pkv.paged_attn_chunk(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, c.table_dev[nd:],
+                                     seq_lens[nd:], max_c, max_chk, wl.scale, ws[j][1], split_tokens=split,
+                                     stream=stream)
         pkv.pkv_set_profile_events(None, None)
 
     # Cold start: the first call of the step on this process (code-object
@@ -698,7 +707,7 @@ def main():
         line["chunk_roofline"] = {"kernel": "chunk attention (matrix cores)", "bound": "mfma",
                                   "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                   "frac": tflops / PEAK_BF16_TFLOPS,
-                                  "traffic": measured_traffic(CONFIG_NAMES[args.config], "chunk"),
+                                  "traffic": None if quant else measured_traffic(CONFIG_NAMES[args.config], "chunk"),
                                   "avg_launch_ms": chk_avg, "algorithmic_flops": chk_flops,
                                   "source_sha": kernel_source_hash("chunk")}
         if not nd:

@@ -500,21 +500,35 @@ int paged_attn_decode_q8_append(void* out, float* lse, const void* q, void* k_co
                                 int32_t n_kv, int32_t head_dim, int32_t block_size, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* paged_attn_chunk_q8 - paged_attn_chunk over an 8-bit cache, for
- * verification-sized chunks: keys and values read as s * code; q and out
- * bf16; fp32 accumulation. Source: chapter 5 section 5 (a verification
- * pass attends the drafted tokens as one causal chunk) over the cache of
+/* paged_attn_chunk_q8 - paged_attn_chunk over an 8-bit cache: keys and
+ * values read as s * code; q and out bf16; fp32 accumulation. Source:
+ * chapter 5 section 5 (a verification pass attends the drafted tokens as
+ * one causal chunk) and section 2.2 (chunked prefill) over the cache of
  * chapter 5 section 4 (absmax codes) - the serving tutorial's section 7
  * treats KV quantisation as a design point that combines with the others.
  * Query i of sequence s sits at position seq_lens[s] - C_s + i (as
  * paged_attn_chunk). Supported: head_dim 128, block_size 16, n_q / n_kv in
- * {1, 2, 4, 8}, max_q_len * (n_q / n_kv) <= 32 (else UNSUPPORTED): the
- * balanced partition over every (sequence, kv head, block) tile. q, out,
- * code pools and scale arrays 16-byte aligned (else INVALID_ARGUMENT).
- * workspace: paged_attn_chunk_workspace_size bytes (split_tokens 0), 256-byte
- * aligned. Append the chunk first with kv_append_q8 (positions
- * seq_lens - C_s). Invalid lengths or table entries give NaN rows. Errors
- * as paged_attn_chunk. */
+ * {1, 2, 4, 8}, and either
+ *  - max_q_len * (n_q / n_kv) <= 32 (verification-sized chunks): the
+ *    balanced partition over every (sequence, kv head, block) tile, codes
+ *    exact in bf16, the scales applied to scores and weights in fp32; or
+ *  - larger chunks with max_seq_len <= 32768: the blocks each sequence
+ *    holds are first written to the workspace as bf16 s * code (the fp32
+ *    product rounded to bf16: one more rounding than the path above), then
+ *    the matrix-core chunk kernel of paged_attn_chunk runs over them;
+ * else UNSUPPORTED. q, out, code pools and scale arrays 16-byte aligned
+ * (else INVALID_ARGUMENT). workspace: paged_attn_chunk_q8_workspace_size
+ * bytes, 256-byte aligned. Append the chunk first with kv_append_q8
+ * (positions seq_lens - C_s). Invalid lengths or table entries give NaN
+ * rows. Errors as paged_attn_chunk. */
+/* Workspace for paged_attn_chunk_q8 (either of its paths): the balanced
+ * partition's partial slots (needs the device: the grid is sized from it),
+ * or for larger chunks num_seqs * ceil(max_seq_len / block_size) staged
+ * bf16 blocks of K and of V plus their table. 0 for shapes it does not
+ * support. Errors: NULL_POINTER, INVALID_ARGUMENT, HIP. */
+int paged_attn_chunk_q8_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t n_q,
+                                       int32_t n_kv, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                       size_t* bytes);
 int paged_attn_chunk_q8(void* out, float* lse, const void* q, const int32_t* q_start,
                         const void* k_codes, const void* v_codes, const float* k_scale, const float* v_scale,
                         const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,

@@ -57,6 +57,8 @@ _SIGNATURES = {
     "kv_append": ([_p, _p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p],
                   ctypes.c_int),
     "paged_attn_split_tokens": ([_i32, _i32, _i32, _i32, _i32, _pi32], ctypes.c_int),
+    "paged_attn_chunk_q8_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_size_t)],
+                                           ctypes.c_int),
     "paged_attn_chunk_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                          ctypes.POINTER(_size_t)], ctypes.c_int),
     "paged_attn_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_size_t)],
@@ -312,6 +314,16 @@ def paged_attn_chunk_workspace_size(num_seqs, total_q, max_q_len, n_q, n_kv, hea
     return int(n.value)
 
 
+def paged_attn_chunk_q8_workspace_size(num_seqs, total_q, max_q_len, n_q, n_kv, head_dim, block_size,
+                                       max_seq_len) -> int:
+    """Workspace bytes for paged_attn_chunk_q8 on either of its paths."""
+    n = _size_t(0)
+    _check("paged_attn_chunk_q8_workspace_size", load_library().paged_attn_chunk_q8_workspace_size(
+        int(num_seqs), int(total_q), int(max_q_len), int(n_q), int(n_kv), int(head_dim), int(block_size),
+        int(max_seq_len), ctypes.byref(n)))
+    return int(n.value)
+
+
 def paged_attn_workspace_size(num_q_rows, n_q, n_kv, head_dim, block_size, max_seq_len, split_tokens=0) -> int:
     out = _size_t()
     _check("paged_attn_workspace_size", load_library().paged_attn_workspace_size(
@@ -469,8 +481,8 @@ def kv_copy_blocks_q8(k_codes, v_codes, k_scale, v_scale, src_ids, dst_ids, stre
 
 def paged_attn_chunk_q8(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, max_q_len,
                         max_seq_len, scale, workspace, stream=None):
-    """Chunk attention (verification-sized chunks) over an 8-bit pool: ``q``/``out`` bf16
-    ``[total_q, n_q, d]``."""
+    """Chunk attention over an 8-bit pool: ``q``/``out`` bf16 ``[total_q, n_q, d]``; ``workspace``
+    of paged_attn_chunk_q8_workspace_size bytes."""
     _dev(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, workspace)
     num_blocks, n_kv, bs, d = k_codes.shape
     total_q, n_q, _ = q.shape

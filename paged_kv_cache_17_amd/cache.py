@@ -96,6 +96,9 @@ class PagedKVCache:
         if chunk is None:
             need = B.paged_attn_workspace_size(num_q_rows, n_q, self.n_kv, self.head_dim, self.block_size,
                                                max_seq_len, split_tokens)
+        elif self.quantized:   # (num_seqs, max_q_len) of a chunk call over the 8-bit cache
+            need = B.paged_attn_chunk_q8_workspace_size(chunk[0], num_q_rows, chunk[1], n_q, self.n_kv,
+                                                        self.head_dim, self.block_size, max_seq_len)
         else:   # (num_seqs, max_q_len) of a chunk call
             need = B.paged_attn_chunk_workspace_size(chunk[0], num_q_rows, chunk[1], n_q, self.n_kv, self.head_dim,
                                                      self.block_size, max_seq_len, split_tokens)
@@ -144,7 +147,6 @@ class PagedKVCache:
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
                             chunk=(q_start.shape[0] - 1, max_q_len))
         if self.quantized:
-            # verification-sized chunks (max_q_len * n_q / n_kv <= 32) only
             if split_tokens:
                 raise ValueError("chunks over an 8-bit cache use the balanced partition only (split_tokens=0)")
             B.paged_attn_chunk_q8(out, lse, q, q_start, self.k_cache, self.v_cache, self.k_scale, self.v_scale,

@@ -74,6 +74,26 @@ struct Layout {
     size_t total;
 };
 
+// Large chunks over an 8-bit pool: bf16 staging copies of the sequences'
+// K and V blocks (maxb = ceil(max_seq_len / block_size) per sequence) and
+// their compact table.
+struct StagingLayout {
+    int maxb;
+    size_t v_offset;
+    size_t table_offset;
+    size_t total;
+};
+StagingLayout staging_layout(int num_seqs, int max_seq_len, int n_kv, int head_dim, int block_size) {
+    StagingLayout l{};
+    l.maxb = (max_seq_len + block_size - 1) / block_size;
+    const size_t blocks = static_cast<size_t>(num_seqs) * l.maxb;
+    const size_t pool = align_up(blocks * n_kv * block_size * head_dim * sizeof(uint16_t));
+    l.v_offset = pool;
+    l.table_offset = 2 * pool;
+    l.total = 2 * pool + align_up(blocks * sizeof(int32_t));
+    return l;
+}
+
 Layout ws_layout(int rows, int n_q, int head_dim, int max_splits) {
     const size_t parts = static_cast<size_t>(rows) * n_q * max_splits;
     Layout w;
@@ -684,6 +704,84 @@ extern "C" int paged_attn_chunk_append(void* out, float* lse, const void* q, con
                       dtype, split_tokens, workspace, workspace_bytes, stream);
 }
 
+namespace {
+
+// paged_attn_chunk_q8 past 32 rows per kv head: the sequences' blocks
+// dequantised to bf16 into the workspace, then the bf16 matrix-core chunk
+// kernel over them (arguments already checked, except the workspace).
+int chunk_q8_staged(void* out, float* lse, const void* q, const int32_t* q_start, const void* k_codes,
+                    const void* v_codes, const float* k_scale, const float* v_scale, const int32_t* block_table,
+                    int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                    int32_t max_q_len, int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
+                    int32_t head_dim, int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    if (!workspace) return PKV_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
+    const StagingLayout l = staging_layout(num_seqs, max_seq_len, n_kv, head_dim, block_size);
+    if (static_cast<size_t>(num_seqs) * l.maxb > static_cast<size_t>(INT32_MAX)) return PKV_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < l.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* k_st = reinterpret_cast<uint16_t*>(ws);
+    uint16_t* v_st = reinterpret_cast<uint16_t*>(ws + l.v_offset);
+    int32_t* t_st = reinterpret_cast<int32_t*>(ws + l.table_offset);
+    pkv::AttnArgs d{};   // the 8-bit pool, for the staging copy
+    d.k_cache = k_codes;
+    d.v_cache = v_codes;
+    d.k_scale = k_scale;
+    d.v_scale = v_scale;
+    d.table = block_table;
+    d.table_stride = table_stride;
+    d.seq_lens = seq_lens;
+    d.num_seqs = num_seqs;
+    d.max_seq_len = max_seq_len;
+    d.num_blocks = num_blocks;
+    d.n_kv = n_kv;
+    d.head_dim = head_dim;
+    d.block_size = block_size;
+    pkv::AttnArgs a{};   // the chunk over the staged bf16 blocks
+    a.q = q;
+    a.q_start = q_start;
+    a.k_cache = k_st;
+    a.v_cache = v_st;
+    a.table = t_st;
+    a.seq_lens = seq_lens;
+    a.table_stride = l.maxb;
+    a.num_seqs = num_seqs;
+    a.num_rows = total_q;
+    a.max_q_len = max_q_len;
+    a.max_seq_len = max_seq_len;
+    a.num_blocks = num_seqs * l.maxb;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = pkv::launch_dequant_blocks(d, k_st, v_st, t_st, l.maxb, st);
+    if (e == hipSuccess) e = pkv::launch_chunk_mfma(a, out, lse, st, profile_events());
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int paged_attn_chunk_q8_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t n_q,
+                                                  int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                                  int32_t max_seq_len, size_t* bytes) {
+    if (!bytes) return PKV_ERR_NULL_POINTER;
+    if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv || head_dim < 1 ||
+        block_size < 1 || max_seq_len < 1)
+        return PKV_ERR_INVALID_ARGUMENT;
+    *bytes = 0;
+    if (pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len)) {
+        const int waves = balanced_waves(n_q, n_kv, num_seqs, kChunkInt8);
+        if (waves < 1) return PKV_ERR_HIP;
+        *bytes = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, waves).total;
+    } else if (pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size, max_seq_len)) {
+        *bytes = staging_layout(num_seqs, max_seq_len, n_kv, head_dim, block_size).total;
+    }
+    return PKV_OK;
+}
+
 extern "C" int paged_attn_chunk_q8(void* out, float* lse, const void* q, const int32_t* q_start, const void* k_codes,
                                    const void* v_codes, const float* k_scale, const float* v_scale,
                                    const int32_t* block_table, int32_t table_stride, const int32_t* seq_lens,
@@ -698,11 +796,16 @@ extern "C" int paged_attn_chunk_q8(void* out, float* lse, const void* q, const i
     if (num_seqs == 0 || max_q_len == 0) return PKV_ERR_INVALID_ARGUMENT;
     if (!out || !q || !q_start || !k_codes || !v_codes || !k_scale || !v_scale || !block_table || !seq_lens)
         return PKV_ERR_NULL_POINTER;
-    if (!pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len))
+    const bool balanced = pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len);
+    if (!balanced && !pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size, max_seq_len))
         return PKV_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scale) ||
         !aligned16(v_scale))
         return PKV_ERR_INVALID_ARGUMENT;
+    if (!balanced) return chunk_q8_staged(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, block_table,
+                                          table_stride, seq_lens, num_seqs, total_q, max_q_len, max_seq_len,
+                                          num_blocks, n_q, n_kv, head_dim, block_size, scale, workspace,
+                                          workspace_bytes, stream);
     pkv::AttnArgs a{};
     a.waves = balanced_waves(n_q, n_kv, num_seqs, kChunkInt8);
     if (a.waves < 1) return PKV_ERR_HIP;

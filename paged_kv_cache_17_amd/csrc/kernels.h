@@ -148,6 +148,14 @@ hipError_t launch_sample(const SampleArgs& a, int rows, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
                               int n, int num_blocks, size_t block_bytes, hipStream_t stream);
 
+// Large chunks over an 8-bit pool (head_dim 128): every block the sequences
+// hold, as bf16 scale x code, into a staging pool (block i of sequence s at
+// s * maxb + i, maxb = ceil(max_seq_len / block_size)) with a compact table
+// [num_seqs][maxb] naming those blocks (-1: no block there); the bf16 chunk
+// kernel then runs over them. a: the 8-bit call's arguments.
+hipError_t launch_dequant_blocks(const AttnArgs& a, uint16_t* k_out, uint16_t* v_out, int32_t* table_out, int maxb,
+                                 hipStream_t stream);
+
 // Split pass for any shape/dtype (one wave per row, head and key range).
 hipError_t launch_split_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
 

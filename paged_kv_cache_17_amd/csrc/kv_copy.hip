@@ -51,6 +51,60 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* __restr
     }
 }
 
+// Large chunks over an 8-bit pool (dequant_blocks below): one workgroup per
+// (logical block i, sequence s). The block's n_kv * B rows of head_dim
+// codes (head_dim 128: 8 threads per row, 16 codes each) become bf16 values
+// scale x code (the row's scale, fp32 product rounded to bf16) at staging
+// block s * maxb + i, which the compact table names; -1 where the sequence
+// has no block i (past its length, or a length out of range) or its table
+// entry lies outside the pool.
+__global__ __launch_bounds__(kCopyThreads) void dequant_blocks_kernel(AttnArgs a, uint16_t* __restrict__ ko,
+                                                                      uint16_t* __restrict__ vo,
+                                                                      int32_t* __restrict__ to, int maxb) {
+    constexpr int kD = 128;
+    const int i = blockIdx.x;
+    const int s = blockIdx.y;
+    const int B = a.block_size;
+    const int L = a.seq_lens[s];
+    const int nb = seq_len_ok(L, 1, a.max_seq_len, a.table_stride * B) ? (L + B - 1) / B : 0;
+    const size_t cb = static_cast<size_t>(s) * maxb + i;
+    int id = -1;
+    if (i < nb) {
+        id = a.table[static_cast<size_t>(s) * a.table_stride + i];
+        if (id < 0 || id >= a.num_blocks) id = -1;
+    }
+    if (threadIdx.x == 0) to[cb] = id < 0 ? -1 : static_cast<int32_t>(cb);
+    if (id < 0) return;
+    const int rows = a.n_kv * B;
+    const int c = threadIdx.x & 7;
+    for (int r = threadIdx.x >> 3; r < rows; r += kCopyThreads / 8) {
+        const size_t src = static_cast<size_t>(id) * rows + r;
+        const size_t dst = cb * rows + r;
+        const u32x4 kc = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.k_cache) + src * kD + 16 * c);
+        const u32x4 vc = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.v_cache) + src * kD + 16 * c);
+        const float ks = a.k_scale[src], vs = a.v_scale[src];
+        u32x4 kb[2], vb[2];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int sh = 16 * e;
+                const float k0 = static_cast<float>(static_cast<int8_t>(kc[w] >> sh));
+                const float k1 = static_cast<float>(static_cast<int8_t>(kc[w] >> (sh + 8)));
+                const float v0 = static_cast<float>(static_cast<int8_t>(vc[w] >> sh));
+                const float v1 = static_cast<float>(static_cast<int8_t>(vc[w] >> (sh + 8)));
+                kb[w >> 1][2 * (w & 1) + e] = pack2_bf16(ks * k0, ks * k1);
+                vb[w >> 1][2 * (w & 1) + e] = pack2_bf16(vs * v0, vs * v1);
+            }
+        u32x4* kd = reinterpret_cast<u32x4*>(ko + dst * kD + 16 * c);
+        u32x4* vd = reinterpret_cast<u32x4*>(vo + dst * kD + 16 * c);
+        kd[0] = kb[0];
+        kd[1] = kb[1];
+        vd[0] = vb[0];
+        vd[1] = vb[1];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_ids, const int32_t* dst_ids,
@@ -68,6 +122,13 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_i
     else
         hipLaunchKernelGGL(copy_blocks_kernel<1>, grid, dim3(kCopyThreads), 0, stream, k, v, src_ids, dst_ids,
                            num_blocks, block_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_blocks(const AttnArgs& a, uint16_t* k_out, uint16_t* v_out, int32_t* table_out, int maxb,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(dequant_blocks_kernel, dim3(maxb, a.num_seqs), dim3(kCopyThreads), 0, stream, a, k_out, v_out,
+                       table_out, maxb);
     return hipGetLastError();
 }
 

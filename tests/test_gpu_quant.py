@@ -1,4 +1,5 @@
-"""GPU parity of the 8-bit K/V path (kv_append_q8, paged_attn_decode_q8).
+"""GPU parity of the 8-bit K/V path (kv_append_q8, paged_attn_decode_q8,
+paged_attn_chunk_q8 on large chunks).
 
 Bars: the pool's codes and scales bit-exact against the oracle's
 quantiser (both take the integer decision in fp32 with correctly rounded
@@ -13,7 +14,7 @@ import pytest
 import oracle
 from workloads import BF16, F32, build_workload, config_workload
 
-from gpu_harness import build_gpu_cache, check_lse, check_rows, i32, out_f64, raw_to_torch
+from gpu_harness import build_gpu_cache, check_lse, check_rows, i32, out_f64, raw_to_torch, run_chunk
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -79,6 +80,41 @@ def test_q8_append_any_shape_is_bit_exact(dtype, d, bs):
     say("q8 append", dtype, d, bs)
     c = build_gpu_cache(wl, quantized=True)
     _pools_match(c, oracle.build_quant_cache(wl))
+
+
+@pytest.mark.parametrize("n_q,n_kv,hist,new", [
+    (32, 8, [0, 300, 1000, 2049, 4000], [512, 64, 100, 37, 9]),   # G 4: 36..2048 rows per kv head
+    (8, 8, [0, 33, 1500], [40, 100, 33]),                          # G 1: 33..100 rows
+    (64, 8, [17, 2000], [5, 6]),                                   # G 8: 40, 48 rows
+])
+def test_q8_large_chunks_match_the_oracle(n_q, n_kv, hist, new):
+    """Chunks past 32 (query, head) rows per kv head over an 8-bit pool: the
+    sequences' blocks are staged as bf16 s * code and the matrix-core chunk
+    kernel runs over them. Every row within tolerance of the oracle's
+    attention over s * code; a sequence with a table entry outside the pool
+    gets NaN rows and leaves the others unchanged."""
+    hist, new = np.array(hist), np.array(new)
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist,
+                        new_lens=new, seed=47)
+    say("q8 large chunks", n_q, n_kv, hist.tolist(), new.tolist())
+    c = build_gpu_cache(wl, quantized=True)
+    ora = oracle.build_quant_cache(wl)
+    _pools_match(c, ora)
+    out, lse = run_chunk(c, wl)
+    got = out_f64(out, BF16)
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(got, ref, BF16, "q8 large chunks")
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, BF16, "q8 large chunks lse")
+    say(f"  worst row rel err {err:.2e}")
+    out2, _ = run_chunk(c, wl)
+    assert np.array_equal(got, out_f64(out2, BF16)), "repeat run not bit-identical"
+    # one bad table entry in the last sequence's first block
+    c.table_dev[wl.num_seqs - 1, 0] = 10 ** 6
+    out3, lse3 = run_chunk(c, wl)
+    got3 = out_f64(out3, BF16)
+    lo = int(wl.q_offsets[-2])
+    assert np.isnan(got3[lo:]).all() and np.isnan(lse3[lo:].cpu().numpy()).all()
+    assert np.array_equal(got3[:lo], got[:lo])
 
 
 def test_q8_invalid_rows_become_nan():

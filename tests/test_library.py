@@ -261,14 +261,22 @@ def test_8bit_chunk_and_copy_reject_bad_arguments_before_any_launch():
     lib = pkv.load_library()
     p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
 
-    def chunk(out=16, kc=16, ks=16, n_q=32, n_kv=8, d=128, max_q=5, total_q=5, S=1):
-        return lib.paged_attn_chunk_q8(p(out), None, p(16), p(16), p(kc), p(16), p(ks), p(16), p(16), 4, p(16), S,
-                                       total_q, max_q, 64, 8, n_q, n_kv, d, 16, 0.25, p(256), 1 << 20, None)
+    def chunk(out=16, kc=16, ks=16, n_q=32, n_kv=8, d=128, max_q=5, total_q=5, S=1, max_len=64, ws=1 << 20):
+        return lib.paged_attn_chunk_q8(p(out), None, p(16), p(16), p(kc), p(16), p(ks), p(16), p(16), 4096, p(16), S,
+                                       total_q, max_q, max_len, 8, n_q, n_kv, d, 16, 0.25, p(256), ws, None)
 
     assert chunk(n_q=3, n_kv=2) == -2
     assert chunk(out=0) == -1 and chunk(kc=0) == -1 and chunk(ks=0) == -1
     assert chunk(d=64) == -3                          # head_dim 128 only
-    assert chunk(max_q=9) == -3                       # 9 queries x 4 heads > 32 rows per kv head
+    # 9 queries x 4 heads > 32 rows per kv head: the staged path, which needs
+    # num_seqs x ceil(max_seq_len / 16) bf16 blocks of K and V in the workspace
+    need = ctypes.c_size_t(0)
+    assert lib.paged_attn_chunk_q8_workspace_size(1, 9, 9, 32, 8, 128, 16, 64, ctypes.byref(need)) == 0
+    assert need.value >= 2 * 4 * 8 * 16 * 128 * 2 + 4 * 4
+    assert chunk(max_q=9, total_q=9, ws=need.value - 1) == -6
+    assert chunk(max_q=9, total_q=9, max_len=40000, ws=1 << 30) == -3   # past the chunk kernel's 32768 keys
+    assert lib.paged_attn_chunk_q8_workspace_size(1, 9, 9, 32, 8, 128, 16, 40000, ctypes.byref(need)) == 0
+    assert need.value == 0
     assert chunk(kc=24) == -2                         # codes not 16-byte aligned
     assert chunk(ks=20) == -2                         # scales not 16-byte aligned
     assert chunk(total_q=0) == 0
