@@ -20,8 +20,13 @@ template <> struct Piece<2> { using T = uint16_t; };
 
 // Sequences whose prefix array fits this many entries have it staged in LDS
 // once per workgroup, so the per-thread search for a token's sequence does
-// not chain global loads.
+// not chain global loads. The staging array is dynamic LDS of exactly
+// num_seqs + 1 entries, so a small batch does not cap the workgroups a CU
+// holds (a fixed 16 KiB array allowed ten).
 constexpr int kStagedSeqs = 4096;
+__host__ __device__ constexpr size_t staged_bytes(int num_seqs) {
+    return num_seqs <= kStagedSeqs ? static_cast<size_t>(num_seqs + 1) * sizeof(int) : 0;
+}
 
 template <int UNIT>
 __global__ __launch_bounds__(256) void kv_append_kernel(
@@ -32,7 +37,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     int num_seqs, int total_new, int num_blocks, int n_kv, int row_bytes, int bs,
     const int32_t* __restrict__ seq_lens, int max_seq_len) {
     using P = typename Piece<UNIT>::T;
-    __shared__ int s_start[kStagedSeqs + 1];
+    extern __shared__ int s_start[];
     // The piece this thread moves is requested first: its address depends on
     // the thread's index alone, so its round trip overlaps the staging and
     // the sequence's lookups (a thread past the end reads the last piece).
@@ -80,7 +85,7 @@ hipError_t launch_unit(void* kc, void* vc, const void* kn, const void* vn, const
                        hipStream_t stream, const int32_t* seq_lens = nullptr, int max_seq_len = 0) {
     const long long work = static_cast<long long>(total_new) * n_kv * (row_bytes / UNIT);
     const unsigned grid = static_cast<unsigned>((work + 255) / 256);
-    hipLaunchKernelGGL(kv_append_kernel<UNIT>, dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(kv_append_kernel<UNIT>, dim3(grid), dim3(256), staged_bytes(num_seqs), stream,
                        static_cast<char*>(kc), static_cast<char*>(vc),
                        static_cast<const char*>(kn), static_cast<const char*>(vn), table,
                        table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(
     const TIn* __restrict__ kn, const TIn* __restrict__ vn, const int32_t* __restrict__ table, int table_stride,
     const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start, int num_seqs, int total_new,
     int num_blocks, int n_kv, int d, int bs) {
-    __shared__ int s_start[kStagedSeqs + 1];
+    extern __shared__ int s_start[];
     const bool staged = num_seqs <= kStagedSeqs;
     if (staged)
         for (int i = threadIdx.x; i <= num_seqs; i += blockDim.x) s_start[i] = new_start[i];
@@ -130,6 +135,73 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(
         dst[e] = static_cast<int8_t>(c);
     }
     if (lane == 0) (is_v ? vs : ks)[slot] = scale;
+}
+
+// The same quantising append for bf16 rows of 128 values: 16 lanes per
+// (new token, kv head), each holding 8 values of its K row and 8 of its V
+// row in registers, so the row is read once, the max is a 16-lane
+// reduction and the codes leave as one 8-byte store per lane. The row's
+// values are requested before the staging and the lookups (a lane past the
+// end reads the last row); the arithmetic is kv_append_q8_kernel's.
+__global__ __launch_bounds__(256) void kv_append_q8_d128_kernel(
+    int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, const int32_t* __restrict__ table,
+    int table_stride, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start, int num_seqs,
+    int total_new, int num_blocks, int n_kv, int bs) {
+    constexpr int kD = 128, kLanes = 16;
+    extern __shared__ int s_start[];
+    const int c = threadIdx.x & (kLanes - 1);
+    const long long total = static_cast<long long>(total_new) * n_kv;
+    const long long th = static_cast<long long>(blockIdx.x) * (blockDim.x / kLanes) + threadIdx.x / kLanes;
+    const long long tc = th < total ? th : total - 1;
+    const size_t src = static_cast<size_t>(tc) * kD + 8 * c;
+    const piece_u32x4 kx = *reinterpret_cast<const piece_u32x4*>(kn + src);
+    const piece_u32x4 vx = *reinterpret_cast<const piece_u32x4*>(vn + src);
+    const bool staged = num_seqs <= kStagedSeqs;
+    if (staged)
+        for (int i = threadIdx.x; i <= num_seqs; i += blockDim.x) s_start[i] = new_start[i];
+    __syncthreads();
+    if (th >= total) return;                                   // the 16 lanes of a row exit together
+    const int h = static_cast<int>(tc % n_kv);
+    const int t = static_cast<int>(tc / n_kv);
+    const int32_t* starts = staged ? s_start : new_start;
+    const int s = seq_of_row(starts, num_seqs, t);
+    const int pos = start_pos[s] + (t - starts[s]);
+    if (pos < 0 || pos / bs >= table_stride) return;
+    const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
+    if (blk < 0 || blk >= num_blocks) return;                 // unmapped slot: nothing is written
+    const size_t slot = (static_cast<size_t>(blk) * n_kv + h) * bs + pos % bs;
+    float f[2][8], amax[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        f[0][2 * w] = __uint_as_float(kx[w] << 16);
+        f[0][2 * w + 1] = __uint_as_float(kx[w] & 0xffff0000u);
+        f[1][2 * w] = __uint_as_float(vx[w] << 16);
+        f[1][2 * w + 1] = __uint_as_float(vx[w] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax[r] = fmaxf(amax[r], fabsf(f[r][e]));
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) {                      // K and V reductions interleaved
+        const float mk = __shfl_xor(amax[0], o, kWave);
+        const float mv = __shfl_xor(amax[1], o, kWave);
+        amax[0] = fmaxf(amax[0], mk);
+        amax[1] = fmaxf(amax[1], mv);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const float scale = fmaxf(amax[r], 1e-8f) / 127.0f;
+        piece_u32x2 packed = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q = fminf(fmaxf(rintf(f[r][e] / scale), -127.0f), 127.0f);
+            packed[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xffu) << (8 * (e & 3));
+        }
+        *reinterpret_cast<piece_u32x2*>((r ? vc : kc) + slot * kD + 8 * c) = packed;
+        if (c == 0) (r ? vs : ks)[slot] = scale;
+    }
 }
 
 // The decode step's append: one token per sequence, at position
@@ -208,13 +280,21 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
                                int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream) {
     const long long rows = 2LL * total_new * n_kv;
     const unsigned grid = static_cast<unsigned>((rows + 3) / 4);     // four waves per workgroup
-    if (bf16_in)
-        hipLaunchKernelGGL(kv_append_q8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, k_cache, v_cache,
+    const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const size_t lds = staged_bytes(num_seqs);
+    if (bf16_in && head_dim == 128 && a16(k_new) && a16(v_new) && a16(k_cache) && a16(v_cache)) {
+        const long long pairs = static_cast<long long>(total_new) * n_kv;   // 16 per workgroup
+        hipLaunchKernelGGL(kv_append_q8_d128_kernel, dim3(static_cast<unsigned>((pairs + 15) / 16)), dim3(256), lds,
+                           stream, k_cache, v_cache, k_scale, v_scale, static_cast<const uint16_t*>(k_new),
+                           static_cast<const uint16_t*>(v_new), table, table_stride, start_pos, new_start, num_seqs,
+                           total_new, num_blocks, n_kv, block_size);
+    } else if (bf16_in)
+        hipLaunchKernelGGL(kv_append_q8_kernel<uint16_t>, dim3(grid), dim3(256), lds, stream, k_cache, v_cache,
                            k_scale, v_scale, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                            table, table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
                            head_dim, block_size);
     else
-        hipLaunchKernelGGL(kv_append_q8_kernel<float>, dim3(grid), dim3(256), 0, stream, k_cache, v_cache, k_scale,
+        hipLaunchKernelGGL(kv_append_q8_kernel<float>, dim3(grid), dim3(256), lds, stream, k_cache, v_cache, k_scale,
                            v_scale, static_cast<const float*>(k_new), static_cast<const float*>(v_new), table,
                            table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv, head_dim,
                            block_size);

@@ -70,10 +70,12 @@ def test_q8_append_and_decode_match_the_oracle(n_q, n_kv):
     assert np.array_equal(got, got2), "repeat run not bit-identical"
 
 
-@pytest.mark.parametrize("dtype,d,bs", [(F32, 128, 16), (F32, 8, 4), (BF16, 64, 8), (BF16, 5, 3)])
+@pytest.mark.parametrize("dtype,d,bs", [(F32, 128, 16), (F32, 8, 4), (BF16, 64, 8), (BF16, 5, 3),
+                                         (BF16, 128, 16), (BF16, 128, 5)])
 def test_q8_append_any_shape_is_bit_exact(dtype, d, bs):
     """The quantising append takes any head_dim / block_size and fp32 or
-    bf16 inputs; codes and scales equal the oracle's bit for bit."""
+    bf16 inputs (bf16 rows of 128 take the 16-lanes-per-row kernel); codes
+    and scales equal the oracle's bit for bit."""
     L = np.array([1, bs, bs + 1, 3 * bs + 2, 70])
     wl = build_workload(n_q=4, n_kv=2, head_dim=d, block_size=bs, dtype=dtype, hist_lens=L - 1,
                         new_lens=np.ones_like(L), seed=42)
