@@ -347,20 +347,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
         kread<KB, 5>(kop, koff);
         kread<KB, 6>(kop, koff);
         kread<KB, 7>(kop, koff);
-        kwait<14>(kop[0][0], kop[1][0]);
-        kwait<12>(kop[0][1], kop[1][1]);
-        kwait<10>(kop[0][2], kop[1][2]);
-        kwait<8>(kop[0][3], kop[1][3]);
-        kwait<6>(kop[0][4], kop[1][4]);
-        kwait<4>(kop[0][5], kop[1][5]);
-        kwait<2>(kop[0][6], kop[1][6]);
-        kwait<0>(kop[0][7], kop[1][7]);
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
+        auto spair = [&](auto tc) {
+            constexpr int T = decltype(tc)::value;
+            kwait<14 - 2 * T>(kop[0][T], kop[1][T]);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[u][t]), as_bf16x8(qv[t]), sacc[u], 0, 0, 0);
+                sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop[u][T]), as_bf16x8(qv[T]), sacc[u], 0, 0, 0);
+            // keeps each wait next to its own pair of products (the
+            // scheduler would otherwise gather the waits at the top)
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        spair(std::integral_constant<int, 0>{});
+        spair(std::integral_constant<int, 1>{});
+        spair(std::integral_constant<int, 2>{});
+        spair(std::integral_constant<int, 3>{});
+        spair(std::integral_constant<int, 4>{});
+        spair(std::integral_constant<int, 5>{});
+        spair(std::integral_constant<int, 6>{});
+        spair(std::integral_constant<int, 7>{});
         // V^T operands for the second product, requested while the weights
         // are computed.
         i16x4 vop[4][4][2];
