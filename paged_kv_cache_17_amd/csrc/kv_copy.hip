@@ -77,31 +77,44 @@ __global__ __launch_bounds__(kCopyThreads) void dequant_blocks_kernel(AttnArgs a
     if (id < 0) return;
     const int rows = a.n_kv * B;
     const int c = threadIdx.x & 7;
-    for (int r = threadIdx.x >> 3; r < rows; r += kCopyThreads / 8) {
-        const size_t src = static_cast<size_t>(id) * rows + r;
-        const size_t dst = cb * rows + r;
-        const u32x4 kc = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.k_cache) + src * kD + 16 * c);
-        const u32x4 vc = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.v_cache) + src * kD + 16 * c);
-        const float ks = a.k_scale[src], vs = a.v_scale[src];
-        u32x4 kb[2], vb[2];
+    constexpr int kStride = kCopyThreads / 8;    // rows per pass of the workgroup
+    constexpr int kUnroll = 4;                   // passes whose loads are in flight together
+    for (int r0 = threadIdx.x >> 3; r0 < rows; r0 += kUnroll * kStride) {
+        // every load first; rows past the end re-read the last row and store
+        // it again, identical bytes (no branch, so the loads stay together)
+        u32x4 kc[kUnroll], vc[kUnroll];
+        float ks[kUnroll], vs[kUnroll];
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
+        for (int j = 0; j < kUnroll; ++j) {
+            const size_t src = static_cast<size_t>(id) * rows + min(r0 + j * kStride, rows - 1);
+            kc[j] = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.k_cache) + src * kD + 16 * c);
+            vc[j] = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.v_cache) + src * kD + 16 * c);
+            ks[j] = a.k_scale[src];
+            vs[j] = a.v_scale[src];
+        }
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int sh = 16 * e;
-                const float k0 = static_cast<float>(static_cast<int8_t>(kc[w] >> sh));
-                const float k1 = static_cast<float>(static_cast<int8_t>(kc[w] >> (sh + 8)));
-                const float v0 = static_cast<float>(static_cast<int8_t>(vc[w] >> sh));
-                const float v1 = static_cast<float>(static_cast<int8_t>(vc[w] >> (sh + 8)));
-                kb[w >> 1][2 * (w & 1) + e] = pack2_bf16(ks * k0, ks * k1);
-                vb[w >> 1][2 * (w & 1) + e] = pack2_bf16(vs * v0, vs * v1);
-            }
-        u32x4* kd = reinterpret_cast<u32x4*>(ko + dst * kD + 16 * c);
-        u32x4* vd = reinterpret_cast<u32x4*>(vo + dst * kD + 16 * c);
-        kd[0] = kb[0];
-        kd[1] = kb[1];
-        vd[0] = vb[0];
-        vd[1] = vb[1];
+        for (int j = 0; j < kUnroll; ++j) {
+            const size_t dst = cb * rows + min(r0 + j * kStride, rows - 1);
+            u32x4 kb[2], vb[2];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int sh = 16 * e;
+                    const float k0 = static_cast<float>(static_cast<int8_t>(kc[j][w] >> sh));
+                    const float k1 = static_cast<float>(static_cast<int8_t>(kc[j][w] >> (sh + 8)));
+                    const float v0 = static_cast<float>(static_cast<int8_t>(vc[j][w] >> sh));
+                    const float v1 = static_cast<float>(static_cast<int8_t>(vc[j][w] >> (sh + 8)));
+                    kb[w >> 1][2 * (w & 1) + e] = pack2_bf16(ks[j] * k0, ks[j] * k1);
+                    vb[w >> 1][2 * (w & 1) + e] = pack2_bf16(vs[j] * v0, vs[j] * v1);
+                }
+            u32x4* kd = reinterpret_cast<u32x4*>(ko + dst * kD + 16 * c);
+            u32x4* vd = reinterpret_cast<u32x4*>(vo + dst * kD + 16 * c);
+            kd[0] = kb[0];
+            kd[1] = kb[1];
+            vd[0] = vb[0];
+            vd[1] = vb[1];
+        }
     }
 }
 
