@@ -70,6 +70,18 @@ def test_append_that_opens_a_block():
     assert c.held.tolist() == [3, 2, 1, 1]
 
 
+def test_append_past_the_staged_sequence_prefix():
+    """More sequences than the append kernel stages in LDS (4096): each
+    thread then searches the prefix array in global memory for its token's
+    sequence. Pools bit-exact, every chunk row within the bar."""
+    rng = np.random.default_rng(31)
+    S = 4200
+    wl = build_workload(n_q=2, n_kv=1, head_dim=128, block_size=16, dtype=BF16,
+                        hist_lens=rng.integers(0, 40, size=S), new_lens=rng.integers(1, 4, size=S), seed=31)
+    say("append, 4200 sequences", int(wl.new_lens.sum()), "new tokens")
+    _full_check(wl, "chunk")
+
+
 RAGGED = [1, 2, 15, 16, 17, 31, 33, 255, 256, 257, 511, 512, 513, 1000, 1023, 1025, 2047, 2049, 3000]
 
 

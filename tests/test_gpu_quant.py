@@ -119,6 +119,20 @@ def test_q8_large_chunks_match_the_oracle(n_q, n_kv, hist, new):
     assert np.array_equal(got3[:lo], got[:lo])
 
 
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_q8_append_past_the_staged_sequence_prefix(dtype):
+    """More sequences than the quantising append stages in LDS (4096), bf16
+    rows of 128 (16 lanes per row) and fp32 rows (one wave per row): codes
+    and scales bit-exact."""
+    rng = np.random.default_rng(37)
+    S = 4200
+    wl = build_workload(n_q=2, n_kv=1, head_dim=128, block_size=16, dtype=dtype,
+                        hist_lens=rng.integers(0, 40, size=S), new_lens=rng.integers(1, 4, size=S), seed=37)
+    say("q8 append, 4200 sequences", dtype)
+    c = build_gpu_cache(wl, quantized=True)
+    _pools_match(c, oracle.build_quant_cache(wl))
+
+
 def test_q8_invalid_rows_become_nan():
     L = np.array([40, 50, 60, 70, 80])
     wl = build_workload(n_q=8, n_kv=2, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,
