@@ -90,3 +90,49 @@ def test_random_shape(seed):
     err = check_rows(out_f64(out, wl.dtype), ref, wl.dtype, name)
     check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, wl.dtype, name)
     print(f"  worst row error {err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", range(2000, 2060))
+def test_random_shape_one_call_step(seed):
+    """The one-call steps (append and attention in one call) from the
+    history-only state: the decode step where it exists (bf16 or 8-bit,
+    head_dim 128, block size 16; other shapes UNSUPPORTED) and the chunk step
+    on every bf16 / fp32 shape (there is none over an 8-bit pool). Pools
+    bit-exact after the call, every row within the bar."""
+    from paged_kv_cache_17_amd.binding import PagedKVError
+    wl, mode, quant, split = draw_case(seed)
+    if mode == "chunk" and quant:
+        pytest.skip("no one-call chunk step over an 8-bit pool")
+    name = (f"seed {seed}: {mode} step {'8-bit' if quant else wl.dtype} d{wl.head_dim} B{wl.block_size} "
+            f"n_kv{wl.n_kv} G{wl.n_q // wl.n_kv} S{wl.num_seqs} split {split}")
+    print(name, flush=True)
+    c = build_gpu_cache(wl, quantized=quant, with_new=False)
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    kn, vn = raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype)
+    lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
+    try:
+        if mode == "decode":
+            out = c.decode_step(q, kn, vn, i32(wl.seq_lens), wl.max_seq_len, wl.scale, lse=lse)
+        else:
+            out = c.chunk_step(q, i32(wl.q_offsets), kn, vn, i32(wl.seq_lens), wl.max_new, wl.max_seq_len,
+                               wl.scale, lse=lse, split_tokens=split)
+        torch.cuda.synchronize()
+    except PagedKVError as e:
+        assert mode == "decode" and e.status == UNSUPPORTED, name
+        assert (wl.head_dim, wl.block_size, wl.dtype) != (128, 16, BF16), name
+        return
+    if quant:
+        ora = oracle.build_quant_cache(wl)
+        assert np.array_equal(c.k_cache.cpu().numpy(), ora.pool_k)
+        assert np.array_equal(c.v_cache.cpu().numpy(), ora.pool_v)
+        assert np.array_equal(c.k_scale.cpu().numpy().view(np.uint32), ora.scale_k.view(np.uint32))
+        assert np.array_equal(c.v_scale.cpu().numpy().view(np.uint32), ora.scale_v.view(np.uint32))
+    else:
+        ora = oracle.build_cache(wl)
+        assert np.array_equal(torch_to_raw(c.k_cache, wl.dtype).view(np.uint8), ora.pool_k.view(np.uint8))
+        assert np.array_equal(torch_to_raw(c.v_cache, wl.dtype).view(np.uint8), ora.pool_v.view(np.uint8))
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(out_f64(out, wl.dtype), ref, wl.dtype, name)
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, wl.dtype, name)
+    print(f"  worst row error {err:.2e}", flush=True)
