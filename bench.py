@@ -571,6 +571,12 @@ def main():
     stream = torch.cuda.current_stream()
     # one call per step: bf16 decode rows only, the library's partition, the tuned shape
     fused = not args.separate and split == 0 and nd == S and wl.head_dim == 128 and wl.block_size == 16
+    # mixed batch, one call per kind of row: the decode rows' step with its
+    # append folded in, the chunks' step with its append fused into the
+    # matrix-core chunk kernel
+    mixed_fused = (not args.separate and split == 0 and 0 < nd < S and not quant and wl.head_dim == 128
+                   and wl.block_size == 16)
+    nd_new = int(wl.q_offsets[nd]) if nd < S else 0     # packed new rows of the decode sequences
 
     def step(i, ev_dec=None, ev_chk=None):
         j = i % len(caches)
@@ -585,6 +591,18 @@ def main():
             else:
                 pkv.paged_attn_decode_append(out, None, q, c.k_cache, c.v_cache, k_new, v_new, c.table_dev,
                                              seq_lens, max_dec, wl.scale, ws[j][0], stream=stream)
+            pkv.pkv_set_profile_events(None, None)
+            return
+        if mixed_fused:
+            if ev_dec is not None:
+                pkv.pkv_set_profile_events(*ev_dec)
+            pkv.paged_attn_decode_append(out[:qd], None, q_dec, c.k_cache, c.v_cache, k_new[:nd_new],
+                                         v_new[:nd_new], c.table_dev[:nd], seq_lens[:nd], max_dec, wl.scale,
+                                         ws[j][0], stream=stream)
+            pkv.pkv_set_profile_events(*ev_chk) if ev_chk is not None else pkv.pkv_set_profile_events(None, None)
+            pkv.paged_attn_chunk_append(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, k_new[nd_new:],
+                                        v_new[nd_new:], c.table_dev[nd:], seq_lens[nd:], max_c, max_chk, wl.scale,
+                                        ws[j][1], stream=stream)
             pkv.pkv_set_profile_events(None, None)
             return
         c.append(k_new, v_new, start_pos, new_start, stream=stream)
@@ -681,7 +699,10 @@ def main():
                    "cache_copies": len(caches),
                    "step": (("paged_attn_decode_q8_append" if quant else "paged_attn_decode_append")
                             + " (one call: append folded into the split pass, or launched first)" if fused
-                            else "kv_append + paged_attn_decode" if nd == S else "kv_append + decode + chunk"),
+                            else "kv_append + paged_attn_decode" if nd == S
+                            else "paged_attn_decode_append (decode rows) + paged_attn_chunk_append (chunks, the "
+                                 "append fused into the chunk kernel)" if mixed_fused
+                            else "kv_append + decode + chunk"),
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
     }
     line["cold_start_ms"] = cold_ms

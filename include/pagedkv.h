@@ -407,8 +407,12 @@ int paged_attn_chunk(void* out, float* lse, const void* q, const int32_t* q_star
  * including it); chapter 5 section 5 (a verification pass appends the
  * drafts and attends them as one chunk). Same result as kv_append of the
  * chunk at start_pos = seq_lens - C_s followed by paged_attn_chunk, without
- * the caller building start_pos / new_start: the append is launched first
- * inside the call, with positions taken from seq_lens and q_start.
+ * the caller building start_pos / new_start (positions come from seq_lens
+ * and q_start). On the matrix-core chunk kernel (bf16, head_dim 128,
+ * block_size 16, split_tokens 0, 16-byte aligned k_new / v_new) the append
+ * is fused into it: each workgroup writes its own query tile's tokens and
+ * reads the chunk's keys from k_new / v_new. Otherwise the append is
+ * launched first inside the call.
  *
  * k_new, v_new: device, [total_q][n_kv][head_dim] of dtype. A sequence that
  *   the chunk pass rejects (seq_lens[s] < C_s, out of range) gets no

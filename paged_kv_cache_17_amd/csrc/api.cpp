@@ -665,6 +665,15 @@ int chunk_impl(void* out, float* lse, const void* q, const int32_t* q_start, voi
         rc = check_workspace(a, false, workspace, workspace_bytes, nullptr);
         if (rc != PKV_OK) return rc;
     }
+    if (mfma && append && aligned16(k_new) && aligned16(v_new)) {
+        // the append fused into the matrix-core chunk kernel
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_app = k_cache;
+        a.v_app = v_cache;
+        const hipError_t e = pkv::launch_chunk_mfma(a, out, lse, st, profile_events());
+        return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    }
     rc = append_first();
     if (rc != PKV_OK) return rc;
     if (mfma) {

@@ -42,6 +42,14 @@
 //    bf16 from registers.
 // Keys past the last one a tile needs are loaded as copies of that key
 // (finite cache data) and get weight 0.
+//
+// Chunk step with the append fused in (a.k_new set): each workgroup first
+// writes its own query tile's tokens (K and V rows of its kv head) from the
+// new rows into their pool slots, and every tile reads the chunk's own keys
+// from the new rows rather than from the pool (blocks past the cached keys
+// whole, the block where the chunk starts split by row). No workgroup then
+// reads a slot that another writes, and the pool ends as after a separate
+// append.
 #include <type_traits>
 
 #include "device_common.h"
@@ -78,6 +86,13 @@ struct TileSrc {
     const char* kb;
     const char* vb;
     int cap;
+    // chunk step with the append fused in: rows 0 .. fr - 1 of the block are
+    // cached keys (read from the pool at kb / vb), rows fr .. are the chunk's
+    // own keys, read from its new rows at kn / vn (row fr there, n_kv rows
+    // apart); fr = 16: the whole block is cached.
+    int fr;
+    const char* kn;
+    const char* vn;
 };
 
 // Transposing LDS read, issued as inline assembly so the compiler does not
@@ -144,7 +159,7 @@ __device__ __forceinline__ constexpr int key_of_reg(int r) {
     return 16 * ((r >> 2) >> 1) + 4 * ((r >> 2) & 1) + (r & 3);
 }
 
-template <int G>
+template <int G, bool FUSED>
 __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uint16_t* __restrict__ out,
                                                                  float* __restrict__ lse) {
     constexpr int QT = kRows / G;                 // queries per workgroup
@@ -222,6 +237,49 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
             s_tbl[b] = id;
         }
     __syncthreads();
+    const size_t blk_bytes = static_cast<size_t>(n_kv) * kBS * kRowBytes;
+    const size_t head_bytes = static_cast<size_t>(g) * kBS * kRowBytes;
+    // The append of this workgroup's own query tile (chunk step with the
+    // append fused in): tokens P + q0 .. P + q_last of kv head g go from the
+    // new rows to their pool slots (each token whose table entry lies in the
+    // pool, as the separate append writes). The attention reads the chunk's
+    // keys from the new rows, so no workgroup reads a slot that another
+    // writes. (Issued before the first tile, which measured faster than at
+    // the end of the workgroup.)
+    auto append_tile = [&]() {
+        if constexpr (FUSED) {
+            if (!ok || nblk > kTblCache) return;
+            const int items = (q_last - q0 + 1) * 2 * (kRowBytes / 16);   // 16-byte granules of K and V rows
+            const char* kn = static_cast<const char*>(a.k_new);
+            const char* vn = static_cast<const char*>(a.v_new);
+            char* kw = static_cast<char*>(a.k_app);
+            char* vw = static_cast<char*>(a.v_app);
+            for (int b0 = tid; b0 < items; b0 += 4 * kThreads) {
+                // four granules per thread, loads first (past the end: the
+                // last granule again, the same bytes stored twice)
+                u32x4 val[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int it = min(b0 + j * kThreads, items - 1);
+                    const int tok = it >> 5, isv = (it >> 4) & 1, gr = it & 15;
+                    const char* src = (isv ? vn : kn) +
+                                      (static_cast<size_t>(qs + q0 + tok) * n_kv + g) * kRowBytes + gr * 16;
+                    val[j] = *reinterpret_cast<const u32x4*>(src);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int it = min(b0 + j * kThreads, items - 1);
+                    const int tok = it >> 5, isv = (it >> 4) & 1, gr = it & 15;
+                    const int p = P + q0 + tok;
+                    const int id = s_tbl[p / kBS];
+                    if (id >= 0 && id < a.num_blocks)
+                        *reinterpret_cast<u32x4*>((isv ? vw : kw) + static_cast<size_t>(id) * blk_bytes + head_bytes +
+                                                  (p % kBS) * kRowBytes + gr * 16) = val[j];
+                }
+            }
+        }
+    };
+    append_tile();
     if (!ok || nblk > kTblCache || s_bad) {
         if (active) {
             for (int e = h; e < kD; e += 2) Elem<uint16_t>::store(out + orow * kD + e, NAN);
@@ -247,8 +305,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     // Lane l writes granule l%16 of row 16w + 4i + l/16.
     const char* kc = static_cast<const char*>(a.k_cache);
     const char* vc = static_cast<const char*>(a.v_cache);
-    const size_t blk_bytes = static_cast<size_t>(n_kv) * kBS * kRowBytes;
-    const size_t head_bytes = static_cast<size_t>(g) * kBS * kRowBytes;
     const int lr = lane >> 4;
     const int lc = lane & 15;
     const int last_blk = kmax / kBS;
@@ -257,12 +313,24 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     // min(bi, last_blk), whose table entry tbl_of(kt) reads (a tile ahead of
     // its use, so the LDS round trip is off the tile's path).
     auto tbl_of = [&](int kt) { return s_tbl[min(4 * kt + wave, last_blk)]; };
+    const size_t new_stride = static_cast<size_t>(n_kv) * kRowBytes;   // between new rows of one kv head
     auto tile_src = [&](int kt, int idv) {
         const int bi = 4 * kt + wave;
         const int cap = bi > last_blk ? (kmax & (kBS - 1)) : min(kmax - kBS * bi, kBS - 1);
         const int id = __builtin_amdgcn_readfirstlane(idv);
         const size_t off = static_cast<size_t>(id) * blk_bytes + head_bytes;
-        return TileSrc{kc + off, vc + off, cap};
+        TileSrc src{kc + off, vc + off, cap, kBS, nullptr, nullptr};
+        if constexpr (FUSED) {
+            const int b0 = kBS * min(bi, last_blk);                       // first key of the block read
+            src.fr = min(max(P - b0, 0), kBS);
+            if (src.fr < kBS) {   // new row of key b0 + fr (>= P)
+                const size_t noff = (static_cast<size_t>(qs) + (b0 + src.fr - P)) * new_stride +
+                                    static_cast<size_t>(g) * kRowBytes;
+                src.kn = static_cast<const char*>(a.k_new) + noff;
+                src.vn = static_cast<const char*>(a.v_new) + noff;
+            }
+        }
+        return src;
     };
     auto issue_k = [&](const TileSrc& src, uint16_t* sk) {
 #pragma unroll
@@ -280,6 +348,49 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
             const int rv = min(4 * i + lr, src.cap);
             __builtin_amdgcn_global_load_lds(src.vb + static_cast<uint32_t>(rv * kRowBytes + gran * 16),
                                              (lds_void*)(sv + (16 * wave + 4 * i) * kD), 16, 0, 0);
+        }
+    };
+    // Fused append: a block holding some of the chunk's own keys. Rows fr ..
+    // come from the new rows (n_kv rows apart there), rows below fr from the
+    // pool; fr = 0 (the whole block new) keeps one source for the wave, and
+    // only the block where the chunk starts splits lanes between the two.
+    auto issue_fresh = [&](const TileSrc& src, uint16_t* sk, uint16_t* sv) {
+        const int ns = static_cast<int>(new_stride);
+        auto row = [&](const char* pool, const char* fresh, int r, int gran, uint16_t* dst) {
+            const uint32_t no = static_cast<uint32_t>((r - src.fr) * ns + gran * 16);
+            if (src.fr == 0) {
+                __builtin_amdgcn_global_load_lds(fresh + no, (lds_void*)dst, 16, 0, 0);
+                asm volatile("; new row");
+            } else {
+                const uint32_t po = static_cast<uint32_t>(r * kRowBytes + gran * 16);
+                __builtin_amdgcn_global_load_lds(r < src.fr ? pool + po : fresh + no, (lds_void*)dst, 16, 0, 0);
+                asm volatile("; cached or new row");
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gran = lc ^ swz(4 * i + lr);
+            const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), src.cap);
+            row(src.kb, src.kn, rk, gran, sk + (16 * wave + 4 * i) * kD);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gran = lc ^ swz(4 * i + lr);
+            const int rv = min(4 * i + lr, src.cap);
+            row(src.vb, src.vn, rv, gran, sv + (16 * wave + 4 * i) * kD);
+        }
+    };
+    // The copies of one tile into (k, v). (The empty statements, each
+    // different, keep the compiler from merging the two sides into one with
+    // per-lane addresses.)
+    auto issue = [&](const TileSrc& src, uint16_t* sk, uint16_t* sv) {
+        if (!FUSED || src.fr >= kBS) {
+            issue_k(src, sk);
+            issue_v(src, sv);
+            if constexpr (FUSED) asm volatile("; cached block");
+        } else {
+            issue_fresh(src, sk, sv);
+            asm volatile("; block with new keys");
         }
     };
 
@@ -314,11 +425,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const int kt_diag = (pmin + 1) / kKeys;       // tiles before this one need no mask
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-    {
-        const TileSrc src = tile_src(0, tbl_of(0));
-        issue_k(src, s_k0);
-        issue_v(src, s_v0);
-    }
+    issue(tile_src(0, tbl_of(0)), s_k0, s_v0);
     int nid = tbl_of(1);          // table entry of the tile after the current one
     __syncthreads();
     // One tile: compute from buffers BUF while the next tile is copied into
@@ -327,11 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     auto tile = [&](int kt, auto buf, uint16_t* nk, uint16_t* nv) {
         constexpr int BUF = decltype(buf)::value;
         // copies of the next tile: in flight during the whole tile
-        if (kt + 1 < ntiles) {
-            const TileSrc nsrc = tile_src(kt + 1, nid);
-            issue_k(nsrc, nk);
-            issue_v(nsrc, nv);
-        }
+        if (kt + 1 < ntiles) issue(tile_src(kt + 1, nid), nk, nv);
         nid = tbl_of(kt + 2);
 
         // S^T for the two 32-key subtiles: all K operands are requested at
@@ -482,8 +585,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     if (lse && h == 0) lse[orow] = kLn2 * (mref + log2f(ltot));
 }
 
-template <int G>
-hipError_t launch_g(const AttnArgs& a, void* out, float* lse, hipStream_t stream, KernelEvents ev) {
+template <int G, bool FUSED>
+hipError_t launch_gf(const AttnArgs& a, void* out, float* lse, hipStream_t stream, KernelEvents ev) {
     constexpr int QT = kRows / G;
     const int nq = (a.max_q_len + QT - 1) / QT;
     const int pairs = a.num_seqs * a.n_kv;
@@ -491,10 +594,15 @@ hipError_t launch_g(const AttnArgs& a, void* out, float* lse, hipStream_t stream
     const dim3 grid(per_xcd * nq * kXcds);
     uint16_t* o = static_cast<uint16_t*>(out);
     if (ev.on())
-        hipExtLaunchKernelGGL(chunk_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a, o, lse);
+        hipExtLaunchKernelGGL((chunk_mfma_kernel<G, FUSED>), grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a,
+                              o, lse);
     else
-        hipLaunchKernelGGL(chunk_mfma_kernel<G>, grid, dim3(kThreads), 0, stream, a, o, lse);
+        hipLaunchKernelGGL((chunk_mfma_kernel<G, FUSED>), grid, dim3(kThreads), 0, stream, a, o, lse);
     return hipGetLastError();
+}
+template <int G>
+hipError_t launch_g(const AttnArgs& a, void* out, float* lse, hipStream_t stream, KernelEvents ev) {
+    return a.k_new ? launch_gf<G, true>(a, out, lse, stream, ev) : launch_gf<G, false>(a, out, lse, stream, ev);
 }
 
 }  // namespace

@@ -179,7 +179,11 @@ int chunk_balanced_waves(int n_q, int n_kv, int num_seqs, bool int8_kv = false);
 hipError_t launch_chunk_balanced(const AttnArgs& a, hipStream_t stream, KernelEvents ev = {});
 
 // Chunk attention on MFMA (bf16, head_dim 128, block_size 16, sequences of
-// at most 32768 keys): writes out and lse directly, no workspace.
+// at most 32768 keys): writes out and lse directly, no workspace. With
+// a.k_new / a.v_new set (bf16 [total_q][n_kv][128], 16-byte aligned) it is
+// the chunk step: the chunk's rows are also written to a.k_app / a.v_app
+// (the pools) at positions seq_lens - C_s .. seq_lens - 1, and the chunk's
+// own keys are read from the new rows.
 bool chunk_mfma_supported(int n_q, int n_kv, int head_dim, int block_size, int max_seq_len);
 hipError_t launch_chunk_mfma(const AttnArgs& a, void* out, float* lse, hipStream_t stream,
                              KernelEvents ev = {});

@@ -94,28 +94,42 @@ def test_full_size_decode_step_every_row(cfg):
     say(f"  {rows} rows x {wl.n_q} heads: worst row rel err {worst:.2e}, lse {lworst:.2e}")
 
 
-def test_full_size_chunked_prefill_mix_every_row():
+@pytest.mark.parametrize("separate", [False, True])
+def test_full_size_chunked_prefill_mix_every_row(separate):
+    """Configuration 5 through the benchmark's step: the decode rows' one-call
+    step (append folded into the split pass) and the chunks' one-call step
+    (append fused into the matrix-core chunk kernel); with separate=True the
+    benchmark's --separate form, every new row appended first, then the
+    decode rows, then the chunks. Pools bit-exact, every row within the bar."""
     wl = config_workload(5)
     nd = int(np.argmax(wl.new_lens != 1))
     assert (wl.new_lens[:nd] == 1).all() and (wl.new_lens[nd:] == 512).all()
-    say(f"config 5: {nd} decode + {wl.num_seqs - nd} chunk seqs, {int(wl.seq_lens.sum())} keys")
+    say(f"config 5 ({'separate calls' if separate else 'one call per kind of row'}): {nd} decode + "
+        f"{wl.num_seqs - nd} chunk seqs, {int(wl.seq_lens.sum())} keys")
     c = build_gpu_cache(wl, fill_nan=True, with_new=False)
     import paged_kv_cache_17_amd as pkv
     q = raw_to_torch(wl.q, BF16)
     kn, vn = wl.packed_new_kv()
-    # the benchmark's step: append every new row, then the decode rows, then the chunks
-    c.append(raw_to_torch(kn, BF16), raw_to_torch(vn, BF16), i32(wl.hist_lens), i32(wl.q_offsets))
+    kn, vn = raw_to_torch(kn, BF16), raw_to_torch(vn, BF16)
     lens = i32(wl.seq_lens)
     qd = int(wl.q_offsets[nd])
     lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
     out = torch.empty_like(q)
     ws = c.workspace(qd, wl.n_q, int(wl.seq_lens[:nd].max())).clone()
-    pkv.paged_attn_decode(out[:qd], lse[:qd], q[:qd], c.k_cache, c.v_cache, c.table_dev[:nd], lens[:nd],
-                          int(wl.seq_lens[:nd].max()), wl.scale, ws)
     max_c, max_chk = int(wl.new_lens[nd:].max()), int(wl.seq_lens[nd:].max())
     ws2 = c.workspace(q.shape[0] - qd, wl.n_q, max_chk, chunk=(wl.num_seqs - nd, max_c)).clone()
-    pkv.paged_attn_chunk(out[qd:], lse[qd:], q[qd:], i32(wl.q_offsets[nd:] - qd), c.k_cache, c.v_cache,
-                         c.table_dev[nd:], lens[nd:], max_c, max_chk, wl.scale, ws2)
+    starts = i32(wl.q_offsets[nd:] - qd)
+    if separate:
+        c.append(kn, vn, i32(wl.hist_lens), i32(wl.q_offsets))
+        pkv.paged_attn_decode(out[:qd], lse[:qd], q[:qd], c.k_cache, c.v_cache, c.table_dev[:nd], lens[:nd],
+                              int(wl.seq_lens[:nd].max()), wl.scale, ws)
+        pkv.paged_attn_chunk(out[qd:], lse[qd:], q[qd:], starts, c.k_cache, c.v_cache, c.table_dev[nd:],
+                             lens[nd:], max_c, max_chk, wl.scale, ws2)
+    else:
+        pkv.paged_attn_decode_append(out[:qd], lse[:qd], q[:qd], c.k_cache, c.v_cache, kn[:qd], vn[:qd],
+                                     c.table_dev[:nd], lens[:nd], int(wl.seq_lens[:nd].max()), wl.scale, ws)
+        pkv.paged_attn_chunk_append(out[qd:], lse[qd:], q[qd:], starts, c.k_cache, c.v_cache, kn[qd:], vn[qd:],
+                                    c.table_dev[nd:], lens[nd:], max_c, max_chk, wl.scale, ws2)
     torch.cuda.synchronize()
     say("  step done; comparing pools")
     _check_pools(c, wl)
