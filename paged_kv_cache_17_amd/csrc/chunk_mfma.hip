@@ -244,8 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     // new rows to their pool slots (each token whose table entry lies in the
     // pool, as the separate append writes). The attention reads the chunk's
     // keys from the new rows, so no workgroup reads a slot that another
-    // writes. (Issued before the first tile, which measured faster than at
-    // the end of the workgroup.)
+    // writes. (Issued with the first tile's copies, which measured faster
+    // than at the end of the workgroup.)
     auto append_tile = [&]() {
         if constexpr (FUSED) {
             if (!ok || nblk > kTblCache) return;
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
             }
         }
     };
-    append_tile();
     if (!ok || nblk > kTblCache || s_bad) {
+        append_tile();
         if (active) {
             for (int e = h; e < kD; e += 2) Elem<uint16_t>::store(out + orow * kD + e, NAN);
             if (lse && h == 0) lse[orow] = NAN;
@@ -356,28 +356,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     // only the block where the chunk starts splits lanes between the two.
     auto issue_fresh = [&](const TileSrc& src, uint16_t* sk, uint16_t* sv) {
         const int ns = static_cast<int>(new_stride);
-        auto row = [&](const char* pool, const char* fresh, int r, int gran, uint16_t* dst) {
-            const uint32_t no = static_cast<uint32_t>((r - src.fr) * ns + gran * 16);
-            if (src.fr == 0) {
-                __builtin_amdgcn_global_load_lds(fresh + no, (lds_void*)dst, 16, 0, 0);
-                asm volatile("; new row");
-            } else {
-                const uint32_t po = static_cast<uint32_t>(r * kRowBytes + gran * 16);
-                __builtin_amdgcn_global_load_lds(r < src.fr ? pool + po : fresh + no, (lds_void*)dst, 16, 0, 0);
-                asm volatile("; cached or new row");
+        if (src.fr == 0) {        // the whole block new: one source, as the cached blocks
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int gran = lc ^ swz(4 * i + lr);
+                const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), src.cap);
+                __builtin_amdgcn_global_load_lds(src.kn + static_cast<uint32_t>(__mul24(rk, ns) + gran * 16),
+                                                 (lds_void*)(sk + (16 * wave + 4 * i) * kD), 16, 0, 0);
             }
-        };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int gran = lc ^ swz(4 * i + lr);
-            const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), src.cap);
-            row(src.kb, src.kn, rk, gran, sk + (16 * wave + 4 * i) * kD);
-        }
+            for (int i = 0; i < 4; ++i) {
+                const int gran = lc ^ swz(4 * i + lr);
+                const int rv = min(4 * i + lr, src.cap);
+                __builtin_amdgcn_global_load_lds(src.vn + static_cast<uint32_t>(__mul24(rv, ns) + gran * 16),
+                                                 (lds_void*)(sv + (16 * wave + 4 * i) * kD), 16, 0, 0);
+            }
+            asm volatile("; new block");
+        } else {                  // the block where the chunk starts: rows below fr cached
+            auto row = [&](const char* pool, const char* fresh, int r, int gran, uint16_t* dst) {
+                const uint32_t po = static_cast<uint32_t>(r * kRowBytes + gran * 16);
+                const uint32_t no = static_cast<uint32_t>((r - src.fr) * ns + gran * 16);
+                __builtin_amdgcn_global_load_lds(r < src.fr ? pool + po : fresh + no, (lds_void*)dst, 16, 0, 0);
+            };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int gran = lc ^ swz(4 * i + lr);
-            const int rv = min(4 * i + lr, src.cap);
-            row(src.vb, src.vn, rv, gran, sv + (16 * wave + 4 * i) * kD);
+            for (int i = 0; i < 4; ++i) {
+                const int gran = lc ^ swz(4 * i + lr);
+                const int rk = min(lr | ((i & 1) << 3) | ((i >> 1) << 2), src.cap);
+                row(src.kb, src.kn, rk, gran, sk + (16 * wave + 4 * i) * kD);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int gran = lc ^ swz(4 * i + lr);
+                const int rv = min(4 * i + lr, src.cap);
+                row(src.vb, src.vn, rv, gran, sv + (16 * wave + 4 * i) * kD);
+            }
+            asm volatile("; block split between cached and new keys");
         }
     };
     // The copies of one tile into (k, v). (The empty statements, each
@@ -426,6 +439,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(AttnArgs a, uin
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
     issue(tile_src(0, tbl_of(0)), s_k0, s_v0);
+    append_tile();                // its loads wait behind the first tile's copies, not before them
     int nid = tbl_of(1);          // table entry of the tile after the current one
     __syncthreads();
     // One tile: compute from buffers BUF while the next tile is copied into
