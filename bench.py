@@ -574,7 +574,7 @@ def main():
     # mixed batch, one call per kind of row: the decode rows' step with its
     # append folded in, the chunks' step with its append fused into the
     # matrix-core chunk kernel
-    mixed_fused = (not args.separate and split == 0 and 0 < nd < S and not quant and wl.head_dim == 128
+    mixed_fused = (not args.separate and split == 0 and 0 < nd < S and wl.head_dim == 128
                    and wl.block_size == 16)
     nd_new = int(wl.q_offsets[nd]) if nd < S else 0     # packed new rows of the decode sequences
 
@@ -596,13 +596,23 @@ def main():
         if mixed_fused:
             if ev_dec is not None:
                 pkv.pkv_set_profile_events(*ev_dec)
-            pkv.paged_attn_decode_append(out[:qd], None, q_dec, c.k_cache, c.v_cache, k_new[:nd_new],
-                                         v_new[:nd_new], c.table_dev[:nd], seq_lens[:nd], max_dec, wl.scale,
-                                         ws[j][0], stream=stream)
+            if quant:
+                pkv.paged_attn_decode_q8_append(out[:qd], None, q_dec, c.k_cache, c.v_cache, c.k_scale, c.v_scale,
+                                                k_new[:nd_new], v_new[:nd_new], c.table_dev[:nd], seq_lens[:nd],
+                                                max_dec, wl.scale, ws[j][0], stream=stream)
+            else:
+                pkv.paged_attn_decode_append(out[:qd], None, q_dec, c.k_cache, c.v_cache, k_new[:nd_new],
+                                             v_new[:nd_new], c.table_dev[:nd], seq_lens[:nd], max_dec, wl.scale,
+                                             ws[j][0], stream=stream)
             pkv.pkv_set_profile_events(*ev_chk) if ev_chk is not None else pkv.pkv_set_profile_events(None, None)
-            pkv.paged_attn_chunk_append(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, k_new[nd_new:],
-                                        v_new[nd_new:], c.table_dev[nd:], seq_lens[nd:], max_c, max_chk, wl.scale,
-                                        ws[j][1], stream=stream)
+            if quant:   # the chunks' quantising append fused into the expansion of their blocks to bf16
+                pkv.paged_attn_chunk_q8_append(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, c.k_scale,
+                                               c.v_scale, k_new[nd_new:], v_new[nd_new:], c.table_dev[nd:],
+                                               seq_lens[nd:], max_c, max_chk, wl.scale, ws[j][1], stream=stream)
+            else:
+                pkv.paged_attn_chunk_append(out[qd:], None, q_chk, chunk_start, c.k_cache, c.v_cache, k_new[nd_new:],
+                                            v_new[nd_new:], c.table_dev[nd:], seq_lens[nd:], max_c, max_chk,
+                                            wl.scale, ws[j][1], stream=stream)
             pkv.pkv_set_profile_events(None, None)
             return
         c.append(k_new, v_new, start_pos, new_start, stream=stream)
@@ -700,6 +710,9 @@ def main():
                    "step": (("paged_attn_decode_q8_append" if quant else "paged_attn_decode_append")
                             + " (one call: append folded into the split pass, or launched first)" if fused
                             else "kv_append + paged_attn_decode" if nd == S
+                            else "paged_attn_decode_q8_append (decode rows) + paged_attn_chunk_q8_append (chunks, "
+                                 "the quantising append fused into the expansion of their blocks)"
+                            if mixed_fused and quant
                             else "paged_attn_decode_append (decode rows) + paged_attn_chunk_append (chunks, the "
                                  "append fused into the chunk kernel)" if mixed_fused
                             else "kv_append + decode + chunk"),

@@ -523,7 +523,7 @@ int paged_attn_decode_q8_append(void* out, float* lse, const void* q, void* k_co
  * else UNSUPPORTED. q, out, code pools and scale arrays 16-byte aligned
  * (else INVALID_ARGUMENT). workspace: paged_attn_chunk_q8_workspace_size
  * bytes, 256-byte aligned. Append the chunk first with kv_append_q8
- * (positions seq_lens - C_s). Invalid lengths or table entries give NaN
+ * (positions seq_lens - C_s), or call paged_attn_chunk_q8_append. Invalid lengths or table entries give NaN
  * rows. Errors as paged_attn_chunk. */
 /* Workspace for paged_attn_chunk_q8 (either of its paths): the balanced
  * partition's partial slots (needs the device: the grid is sized from it),
@@ -539,6 +539,26 @@ int paged_attn_chunk_q8(void* out, float* lse, const void* q, const int32_t* q_s
                         int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
                         int32_t num_blocks, int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
                         float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_chunk_q8_append - the chunk step over an 8-bit cache in one
+ * call: each sequence's C_s new bf16 rows (rows q_start[s] ..
+ * q_start[s+1]-1 of k_new / v_new, [total_q][n_kv][head_dim]) quantised
+ * into the pool as kv_append_q8 does, at the last C_s of its seq_lens[s]
+ * positions, then paged_attn_chunk_q8. Source: as paged_attn_chunk_append
+ * (the lab page's prefill branch; chapter 5 section 5's verification pass)
+ * over the cache of chapter 5 section 4. Same result as kv_append_q8 at
+ * start_pos = seq_lens - C_s followed by paged_attn_chunk_q8; a sequence
+ * the chunk pass rejects gets no append, a token whose table entry is
+ * outside the pool is not written. Every argument and the workspace are
+ * checked before anything is written. Other arguments, support and errors
+ * as paged_attn_chunk_q8. */
+int paged_attn_chunk_q8_append(void* out, float* lse, const void* q, const int32_t* q_start,
+                               void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                               const void* k_new, const void* v_new, const int32_t* block_table,
+                               int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
+                               int32_t max_q_len, int32_t max_seq_len, int32_t num_blocks, int32_t n_q,
+                               int32_t n_kv, int32_t head_dim, int32_t block_size, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* kv_copy_blocks_q8 - kv_copy_blocks for an 8-bit cache: block src_ids[i]'s
  * codes and scales (K and V) onto block dst_ids[i]. Source: serving tutorial

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     paged_attn_chunk,
     paged_attn_chunk_append,
     paged_attn_chunk_q8,
+    paged_attn_chunk_q8_append,
     paged_attn_chunk_q8_workspace_size,
     paged_attn_chunk_workspace_size,
     paged_attn_decode,

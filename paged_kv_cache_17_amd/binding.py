@@ -49,6 +49,8 @@ _SIGNATURES = {
     "kv_copy_blocks_q8": ([_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p], ctypes.c_int),
     "paged_attn_chunk_q8": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                              _i32, _i32, ctypes.c_float, _p, _size_t, _p], ctypes.c_int),
+    "paged_attn_chunk_q8_append": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _size_t, _p], ctypes.c_int),
     "kv_copy_blocks": ([_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p], ctypes.c_int),
     "kv_append_q8": ([_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p],
                      ctypes.c_int),
@@ -491,3 +493,18 @@ def paged_attn_chunk_q8(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale
         _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens), int(seq_lens.shape[0]), int(total_q),
         int(max_q_len), int(max_seq_len), int(num_blocks), int(n_q), int(n_kv), int(d), int(bs), float(scale),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def paged_attn_chunk_q8_append(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_table,
+                               seq_lens, max_q_len, max_seq_len, scale, workspace, stream=None):
+    """Chunk step over an 8-bit pool in one call: ``k_new``/``v_new`` bf16 ``[sum C, n_kv, d]``
+    quantised into the pool as the last C_s keys of each sequence, then :func:`paged_attn_chunk_q8`."""
+    _dev(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_table, seq_lens, workspace)
+    num_blocks, n_kv, bs, d = k_codes.shape
+    total_q, n_q, _ = q.shape
+    _check("paged_attn_chunk_q8_append", load_library().paged_attn_chunk_q8_append(
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(q_start), _ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale),
+        _ptr(k_new), _ptr(v_new), _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+        int(seq_lens.shape[0]), int(total_q), int(max_q_len), int(max_seq_len), int(num_blocks), int(n_q),
+        int(n_kv), int(d), int(bs), float(scale), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+        _stream(stream)))

@@ -162,11 +162,15 @@ class PagedKVCache:
         ``seq_lens``) and attend it, in one call."""
         if out is None:
             out = torch.empty_like(q)
-        if self.quantized:
-            raise NotImplementedError("no one-call chunk step over an 8-bit cache: call append() (kv_append_q8), "
-                                      "then chunk() (paged_attn_chunk_q8)")
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
                             chunk=(q_start.shape[0] - 1, max_q_len))
+        if self.quantized:
+            if split_tokens:
+                raise ValueError("chunks over an 8-bit cache use the balanced partition only (split_tokens=0)")
+            B.paged_attn_chunk_q8_append(out, lse, q, q_start, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
+                                         k_new, v_new, self.table_dev, seq_lens, max_q_len, max_seq_len, scale, ws,
+                                         stream=stream)
+            return out
         B.paged_attn_chunk_append(out, lse, q, q_start, self.k_cache, self.v_cache, k_new, v_new, self.table_dev,
                                   seq_lens, max_q_len, max_seq_len, scale, ws, split_tokens=split_tokens,
                                   stream=stream)

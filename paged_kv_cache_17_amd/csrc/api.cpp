@@ -715,24 +715,92 @@ extern "C" int paged_attn_chunk_append(void* out, float* lse, const void* q, con
 
 namespace {
 
-// paged_attn_chunk_q8 past 32 rows per kv head: the sequences' blocks
-// dequantised to bf16 into the workspace, then the bf16 matrix-core chunk
-// kernel over them (arguments already checked, except the workspace).
-int chunk_q8_staged(void* out, float* lse, const void* q, const int32_t* q_start, const void* k_codes,
-                    const void* v_codes, const float* k_scale, const float* v_scale, const int32_t* block_table,
-                    int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t total_q,
-                    int32_t max_q_len, int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv,
-                    int32_t head_dim, int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+// paged_attn_chunk_q8 and paged_attn_chunk_q8_append: every argument and the
+// workspace are checked before the first launch. Then either the balanced
+// pass (verification-sized chunks; the quantising append of the chunk's
+// rows at seq_lens - C_s launched first when k_new is set) or, past 32 rows
+// per kv head, the sequences' blocks dequantised to bf16 into the workspace
+// (the append fused into that pass) and the bf16 matrix-core chunk kernel
+// over them.
+int chunk_q8_impl(void* out, float* lse, const void* q, const int32_t* q_start, void* k_codes, void* v_codes,
+                  float* k_scale, float* v_scale, const void* k_new, const void* v_new, const int32_t* block_table,
+                  int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                  int32_t max_seq_len, int32_t num_blocks, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                  int32_t block_size, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size, table_stride, PKV_BF16,
+                         scale);
+    if (rc != PKV_OK) return rc;
+    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len) return PKV_ERR_INVALID_ARGUMENT;
+    if (total_q == 0) return PKV_OK;
+    if (num_seqs == 0 || max_q_len == 0) return PKV_ERR_INVALID_ARGUMENT;
+    if (!out || !q || !q_start || !k_codes || !v_codes || !k_scale || !v_scale || !block_table || !seq_lens)
+        return PKV_ERR_NULL_POINTER;
+    const bool append = k_new || v_new;
+    if (append && (!k_new || !v_new)) return PKV_ERR_NULL_POINTER;
+    const bool balanced = pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len);
+    if (!balanced && !pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size, max_seq_len))
+        return PKV_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scale) ||
+        !aligned16(v_scale))
+        return PKV_ERR_INVALID_ARGUMENT;
     if (!workspace) return PKV_ERR_NULL_POINTER;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
-    const StagingLayout l = staging_layout(num_seqs, max_seq_len, n_kv, head_dim, block_size);
-    if (static_cast<size_t>(num_seqs) * l.maxb > static_cast<size_t>(INT32_MAX)) return PKV_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < l.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
     char* ws = static_cast<char*>(workspace);
-    uint16_t* k_st = reinterpret_cast<uint16_t*>(ws);
-    uint16_t* v_st = reinterpret_cast<uint16_t*>(ws + l.v_offset);
-    int32_t* t_st = reinterpret_cast<int32_t*>(ws + l.table_offset);
+    pkv::AttnArgs a{};
+    a.q = q;
+    a.q_start = q_start;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_rows = total_q;
+    a.max_q_len = max_q_len;
+    a.max_seq_len = max_seq_len;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    StagingLayout l{};
+    if (balanced) {
+        a.waves = balanced_waves(n_q, n_kv, num_seqs, kChunkInt8);
+        if (a.waves < 1) return PKV_ERR_HIP;
+        const Layout w = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, a.waves);
+        if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+        a.k_cache = k_codes;
+        a.v_cache = v_codes;
+        a.k_scale = k_scale;
+        a.v_scale = v_scale;
+        a.table = block_table;
+        a.table_stride = table_stride;
+        a.num_blocks = num_blocks;
+        a.split_tokens = block_size;
+        a.max_splits = 1;
+        a.ws_ml = reinterpret_cast<pkv::PartialML*>(ws);
+        a.ws_o = reinterpret_cast<float*>(ws + w.o_offset);
+        a.prefix = reinterpret_cast<int*>(ws + w.prefix_offset);
+    } else {
+        l = staging_layout(num_seqs, max_seq_len, n_kv, head_dim, block_size);
+        if (static_cast<size_t>(num_seqs) * l.maxb > static_cast<size_t>(INT32_MAX)) return PKV_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < l.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+        a.k_cache = ws;                            // the chunk over the staged bf16 blocks
+        a.v_cache = ws + l.v_offset;
+        a.table = reinterpret_cast<int32_t*>(ws + l.table_offset);
+        a.table_stride = l.maxb;
+        a.num_blocks = num_seqs * l.maxb;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    // large chunks: the append fused into the block expansion below
+    const bool fused = append && !balanced && aligned16(k_new) && aligned16(v_new);
+    if (append && !fused)
+        e = pkv::launch_kv_append_q8(static_cast<int8_t*>(k_codes), static_cast<int8_t*>(v_codes), k_scale, v_scale,
+                                     k_new, v_new, true, block_table, table_stride, nullptr, q_start, num_seqs,
+                                     total_q, num_blocks, n_kv, head_dim, block_size, st, seq_lens, max_seq_len);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+    if (balanced) {
+        e = pkv::launch_chunk_balanced(a, st, profile_events());
+        if (e == hipSuccess) e = pkv::launch_merge(a, out, lse, true, st);
+        return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    }
     pkv::AttnArgs d{};   // the 8-bit pool, for the staging copy
     d.k_cache = k_codes;
     d.v_cache = v_codes;
@@ -747,26 +815,18 @@ int chunk_q8_staged(void* out, float* lse, const void* q, const int32_t* q_start
     d.n_kv = n_kv;
     d.head_dim = head_dim;
     d.block_size = block_size;
-    pkv::AttnArgs a{};   // the chunk over the staged bf16 blocks
-    a.q = q;
-    a.q_start = q_start;
-    a.k_cache = k_st;
-    a.v_cache = v_st;
-    a.table = t_st;
-    a.seq_lens = seq_lens;
-    a.table_stride = l.maxb;
-    a.num_seqs = num_seqs;
-    a.num_rows = total_q;
-    a.max_q_len = max_q_len;
-    a.max_seq_len = max_seq_len;
-    a.num_blocks = num_seqs * l.maxb;
-    a.n_q = n_q;
-    a.n_kv = n_kv;
-    a.head_dim = head_dim;
-    a.block_size = block_size;
-    a.scale_log2 = scale * 1.44269504088896340736f;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = pkv::launch_dequant_blocks(d, k_st, v_st, t_st, l.maxb, st);
+    if (fused) {
+        d.q_start = q_start;
+        d.k_new = k_new;
+        d.v_new = v_new;
+        d.k_app = k_codes;
+        d.v_app = v_codes;
+        d.ks_app = k_scale;
+        d.vs_app = v_scale;
+    }
+    e = pkv::launch_dequant_blocks(d, static_cast<uint16_t*>(const_cast<void*>(a.k_cache)),
+                                   static_cast<uint16_t*>(const_cast<void*>(a.v_cache)),
+                                   const_cast<int32_t*>(a.table), l.maxb, st);
     if (e == hipSuccess) e = pkv::launch_chunk_mfma(a, out, lse, st, profile_events());
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -797,58 +857,21 @@ extern "C" int paged_attn_chunk_q8(void* out, float* lse, const void* q, const i
                                    int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
                                    int32_t num_blocks, int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
                                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_shape(num_seqs, max_seq_len, num_blocks, n_q, n_kv, head_dim, block_size, table_stride, PKV_BF16,
-                         scale);
-    if (rc != PKV_OK) return rc;
-    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len) return PKV_ERR_INVALID_ARGUMENT;
-    if (total_q == 0) return PKV_OK;
-    if (num_seqs == 0 || max_q_len == 0) return PKV_ERR_INVALID_ARGUMENT;
-    if (!out || !q || !q_start || !k_codes || !v_codes || !k_scale || !v_scale || !block_table || !seq_lens)
-        return PKV_ERR_NULL_POINTER;
-    const bool balanced = pkv::chunk_balanced_supported(n_q, n_kv, head_dim, block_size, num_seqs, max_q_len);
-    if (!balanced && !pkv::chunk_mfma_supported(n_q, n_kv, head_dim, block_size, max_seq_len))
-        return PKV_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(out) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scale) ||
-        !aligned16(v_scale))
-        return PKV_ERR_INVALID_ARGUMENT;
-    if (!balanced) return chunk_q8_staged(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, block_table,
-                                          table_stride, seq_lens, num_seqs, total_q, max_q_len, max_seq_len,
-                                          num_blocks, n_q, n_kv, head_dim, block_size, scale, workspace,
-                                          workspace_bytes, stream);
-    pkv::AttnArgs a{};
-    a.waves = balanced_waves(n_q, n_kv, num_seqs, kChunkInt8);
-    if (a.waves < 1) return PKV_ERR_HIP;
-    a.q = q;
-    a.q_start = q_start;
-    a.k_cache = k_codes;
-    a.v_cache = v_codes;
-    a.k_scale = k_scale;
-    a.v_scale = v_scale;
-    a.table = block_table;
-    a.seq_lens = seq_lens;
-    a.table_stride = table_stride;
-    a.num_seqs = num_seqs;
-    a.num_rows = total_q;
-    a.max_q_len = max_q_len;
-    a.max_seq_len = max_seq_len;
-    a.num_blocks = num_blocks;
-    a.n_q = n_q;
-    a.n_kv = n_kv;
-    a.head_dim = head_dim;
-    a.block_size = block_size;
-    a.split_tokens = block_size;
-    a.max_splits = 1;
-    a.scale_log2 = scale * 1.44269504088896340736f;
-    if (!workspace) return PKV_ERR_NULL_POINTER;
-    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return PKV_ERR_INVALID_ARGUMENT;
-    const Layout w = ws_layout_balanced(num_seqs, pkv::kChunkSlotRows, n_kv, head_dim, a.waves);
-    if (workspace_bytes < w.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
-    char* ws = static_cast<char*>(workspace);
-    a.ws_ml = reinterpret_cast<pkv::PartialML*>(ws);
-    a.ws_o = reinterpret_cast<float*>(ws + w.o_offset);
-    a.prefix = reinterpret_cast<int*>(ws + w.prefix_offset);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = pkv::launch_chunk_balanced(a, st, profile_events());
-    if (e == hipSuccess) e = pkv::launch_merge(a, out, lse, true, st);
-    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    return chunk_q8_impl(out, lse, q, q_start, const_cast<void*>(k_codes), const_cast<void*>(v_codes),
+                         const_cast<float*>(k_scale), const_cast<float*>(v_scale), nullptr, nullptr, block_table,
+                         table_stride, seq_lens, num_seqs, total_q, max_q_len, max_seq_len, num_blocks, n_q, n_kv,
+                         head_dim, block_size, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attn_chunk_q8_append(void* out, float* lse, const void* q, const int32_t* q_start,
+                                          void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                                          const void* k_new, const void* v_new, const int32_t* block_table,
+                                          int32_t table_stride, const int32_t* seq_lens, int32_t num_seqs,
+                                          int32_t total_q, int32_t max_q_len, int32_t max_seq_len, int32_t num_blocks,
+                                          int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t block_size,
+                                          float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    if (total_q > 0 && (!k_new || !v_new)) return PKV_ERR_NULL_POINTER;
+    return chunk_q8_impl(out, lse, q, q_start, k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_table,
+                         table_stride, seq_lens, num_seqs, total_q, max_q_len, max_seq_len, num_blocks, n_q, n_kv,
+                         head_dim, block_size, scale, workspace, workspace_bytes, stream);
 }

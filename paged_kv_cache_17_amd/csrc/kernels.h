@@ -79,11 +79,13 @@ hipError_t launch_kv_append_q8_last(int8_t* k_codes, int8_t* v_codes, float* k_s
                                     const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_blocks, int n_kv,
                                     hipStream_t stream);
 
-// Quantising append (8-bit codes + one fp32 scale per token and kv head).
+// Quantising append (8-bit codes + one fp32 scale per token and kv head);
+// start_pos null: the chunk step's positions, as launch_kv_append.
 hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,
                                const void* v_new, bool bf16_in, const int32_t* table, int table_stride,
                                const int32_t* start_pos, const int32_t* new_start, int num_seqs, int total_new,
-                               int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream);
+                               int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream,
+                               const int32_t* seq_lens = nullptr, int max_seq_len = 0);
 
 // Token sampling after the LM head. Rows whose top-k set is small go
 // through a candidate pass (chunks of kSampleChunk logits, each keeping its
@@ -152,7 +154,11 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_i
 // hold, as bf16 scale x code, into a staging pool (block i of sequence s at
 // s * maxb + i, maxb = ceil(max_seq_len / block_size)) with a compact table
 // [num_seqs][maxb] naming those blocks (-1: no block there); the bf16 chunk
-// kernel then runs over them. a: the 8-bit call's arguments.
+// kernel then runs over them. a: the 8-bit call's arguments. With
+// a.k_new / a.v_new set (bf16 [total_q][n_kv][128], 16-byte aligned, rows
+// per sequence from a.q_start) the chunk's own tokens are quantised from
+// them into the pool (a.k_app / a.v_app codes, a.ks_app / a.vs_app scales)
+// on the way, as kv_append_q8 at seq_lens - C_s would.
 hipError_t launch_dequant_blocks(const AttnArgs& a, uint16_t* k_out, uint16_t* v_out, int32_t* table_out, int maxb,
                                  hipStream_t stream);
 

@@ -28,6 +28,17 @@ __host__ __device__ constexpr size_t staged_bytes(int num_seqs) {
     return num_seqs <= kStagedSeqs ? static_cast<size_t>(num_seqs + 1) * sizeof(int) : 0;
 }
 
+// Position of sequence s's first new token: start_pos[s], or (chunk step,
+// start_pos null) the last C_s of its seq_lens[s] keys; -1 for a sequence
+// whose length the chunk pass rejects (it gets no append).
+__device__ __forceinline__ int first_new_pos(const int32_t* start_pos, const int32_t* starts, int s,
+                                             const int32_t* seq_lens, int max_seq_len, int capacity) {
+    if (start_pos) return start_pos[s];
+    const int C = starts[s + 1] - starts[s];
+    const int L = seq_lens[s];
+    return seq_len_ok(L, C, max_seq_len, capacity) ? L - C : -1;
+}
+
 template <int UNIT>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     char* __restrict__ kc, char* __restrict__ vc,
@@ -59,15 +70,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     if (idx >= total) return;
     const int32_t* starts = staged ? s_start : new_start;
     const int s = seq_of_row(starts, num_seqs, t);
-    int first = 0;   // position of sequence s's first new token
-    if (start_pos) {
-        first = start_pos[s];
-    } else {         // chunk step: the chunk's C tokens are the last C of seq_lens[s]
-        const int C = starts[s + 1] - starts[s];
-        const int L = seq_lens[s];
-        if (!seq_len_ok(L, C, max_seq_len, table_stride * bs)) return;
-        first = L - C;
-    }
+    const int first = first_new_pos(start_pos, starts, s, seq_lens, max_seq_len, table_stride * bs);
+    if (first < 0) return;
     const int pos = first + (t - starts[s]);
     if (pos < 0 || pos / bs >= table_stride) return;
     const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     const TIn* __restrict__ kn, const TIn* __restrict__ vn, const int32_t* __restrict__ table, int table_stride,
     const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start, int num_seqs, int total_new,
-    int num_blocks, int n_kv, int d, int bs) {
+    int num_blocks, int n_kv, int d, int bs, const int32_t* __restrict__ seq_lens, int max_seq_len) {
     extern __shared__ int s_start[];
     const bool staged = num_seqs <= kStagedSeqs;
     if (staged)
@@ -119,7 +123,9 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(
     const int t = static_cast<int>(th / n_kv);
     const int32_t* starts = staged ? s_start : new_start;
     const int s = seq_of_row(starts, num_seqs, t);
-    const int pos = start_pos[s] + (t - starts[s]);
+    const int first = first_new_pos(start_pos, starts, s, seq_lens, max_seq_len, table_stride * bs);
+    if (first < 0) return;
+    const int pos = first + (t - starts[s]);
     if (pos < 0 || pos / bs >= table_stride) return;
     const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
     if (blk < 0 || blk >= num_blocks) return;                 // unmapped slot: nothing is written
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256) void kv_append_q8_d128_kernel(
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, const int32_t* __restrict__ table,
     int table_stride, const int32_t* __restrict__ start_pos, const int32_t* __restrict__ new_start, int num_seqs,
-    int total_new, int num_blocks, int n_kv, int bs) {
+    int total_new, int num_blocks, int n_kv, int bs, const int32_t* __restrict__ seq_lens, int max_seq_len) {
     constexpr int kD = 128, kLanes = 16;
     extern __shared__ int s_start[];
     const int c = threadIdx.x & (kLanes - 1);
@@ -166,7 +172,9 @@ __global__ __launch_bounds__(256) void kv_append_q8_d128_kernel(
     const int t = static_cast<int>(tc / n_kv);
     const int32_t* starts = staged ? s_start : new_start;
     const int s = seq_of_row(starts, num_seqs, t);
-    const int pos = start_pos[s] + (t - starts[s]);
+    const int first = first_new_pos(start_pos, starts, s, seq_lens, max_seq_len, table_stride * bs);
+    if (first < 0) return;
+    const int pos = first + (t - starts[s]);
     if (pos < 0 || pos / bs >= table_stride) return;
     const int blk = table[static_cast<size_t>(s) * table_stride + pos / bs];
     if (blk < 0 || blk >= num_blocks) return;                 // unmapped slot: nothing is written
@@ -277,7 +285,8 @@ __global__ __launch_bounds__(256) void kv_append_q8_last_kernel(int8_t* __restri
 hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale, const void* k_new,
                                const void* v_new, bool bf16_in, const int32_t* table, int table_stride,
                                const int32_t* start_pos, const int32_t* new_start, int num_seqs, int total_new,
-                               int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream) {
+                               int num_blocks, int n_kv, int head_dim, int block_size, hipStream_t stream,
+                               const int32_t* seq_lens, int max_seq_len) {
     const long long rows = 2LL * total_new * n_kv;
     const unsigned grid = static_cast<unsigned>((rows + 3) / 4);     // four waves per workgroup
     const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
@@ -287,17 +296,17 @@ hipError_t launch_kv_append_q8(int8_t* k_cache, int8_t* v_cache, float* k_scale,
         hipLaunchKernelGGL(kv_append_q8_d128_kernel, dim3(static_cast<unsigned>((pairs + 15) / 16)), dim3(256), lds,
                            stream, k_cache, v_cache, k_scale, v_scale, static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), table, table_stride, start_pos, new_start, num_seqs,
-                           total_new, num_blocks, n_kv, block_size);
+                           total_new, num_blocks, n_kv, block_size, seq_lens, max_seq_len);
     } else if (bf16_in)
         hipLaunchKernelGGL(kv_append_q8_kernel<uint16_t>, dim3(grid), dim3(256), lds, stream, k_cache, v_cache,
                            k_scale, v_scale, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                            table, table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv,
-                           head_dim, block_size);
+                           head_dim, block_size, seq_lens, max_seq_len);
     else
         hipLaunchKernelGGL(kv_append_q8_kernel<float>, dim3(grid), dim3(256), lds, stream, k_cache, v_cache, k_scale,
                            v_scale, static_cast<const float*>(k_new), static_cast<const float*>(v_new), table,
                            table_stride, start_pos, new_start, num_seqs, total_new, num_blocks, n_kv, head_dim,
-                           block_size);
+                           block_size, seq_lens, max_seq_len);
     return hipGetLastError();
 }
 

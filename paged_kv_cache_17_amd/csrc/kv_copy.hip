@@ -58,6 +58,16 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* __restr
 // block s * maxb + i, which the compact table names; -1 where the sequence
 // has no block i (past its length, or a length out of range) or its table
 // entry lies outside the pool.
+//
+// With the chunk's append fused in (FUSED, a.k_new set: the chunk step), the
+// rows of the chunk's own tokens (positions seq_lens[s] - C_s ..) are not
+// read from the pool: their bf16 values come from the new rows, are
+// quantised exactly as kv_append_q8 does (the row's absmax over 8 threads,
+// s = max(absmax, 1e-8) / 127, code = clamp(rint(x / s), -127, 127)), and
+// the codes and s go to the pool while bf16(s x code) goes to the staging
+// block - the values the separate append followed by this expansion gives.
+// A sequence the chunk pass rejects gets no append (its rows are NaN).
+template <bool FUSED>
 __global__ __launch_bounds__(kCopyThreads) void dequant_blocks_kernel(AttnArgs a, uint16_t* __restrict__ ko,
                                                                       uint16_t* __restrict__ vo,
                                                                       int32_t* __restrict__ to, int maxb) {
@@ -77,6 +87,116 @@ __global__ __launch_bounds__(kCopyThreads) void dequant_blocks_kernel(AttnArgs a
     if (id < 0) return;
     const int rows = a.n_kv * B;
     const int c = threadIdx.x & 7;
+    if constexpr (FUSED) {
+        const int qs = a.q_start[s];
+        const int C = a.q_start[s + 1] - qs;
+        const int P = L - C;                      // first new position
+        if (seq_len_ok(L, C, a.max_seq_len, a.table_stride * B) && B * i + B > P) {
+            // a block holding some of the chunk's tokens: slots below tp are
+            // cached keys, tp .. tl - 1 new ones (past tl: past the sequence,
+            // never read), eight threads (16 values each) per row
+            const int tp = min(max(P - B * i, 0), B);
+            const int tl = min(L - B * i, B);
+            auto row_of = [&](int k, int base, int cnt) { return (k / cnt) * B + base + k % cnt; };
+            constexpr int kStride = kCopyThreads / 8;
+            constexpr int kUnroll = 4;
+            const int n_c = a.n_kv * tp;
+            for (int k0 = threadIdx.x >> 3; k0 < n_c; k0 += kUnroll * kStride) {
+                u32x4 kc[kUnroll], vc[kUnroll];
+                float ks[kUnroll], vs[kUnroll];
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const size_t src = static_cast<size_t>(id) * rows + row_of(min(k0 + j * kStride, n_c - 1), 0, tp);
+                    kc[j] = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.k_cache) + src * kD + 16 * c);
+                    vc[j] = *reinterpret_cast<const u32x4*>(static_cast<const int8_t*>(a.v_cache) + src * kD + 16 * c);
+                    ks[j] = a.k_scale[src];
+                    vs[j] = a.v_scale[src];
+                }
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const size_t dst = cb * rows + row_of(min(k0 + j * kStride, n_c - 1), 0, tp);
+                    u32x4 kb[2], vb[2];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int sh = 16 * e;
+                            kb[w >> 1][2 * (w & 1) + e] =
+                                pack2_bf16(ks[j] * static_cast<float>(static_cast<int8_t>(kc[j][w] >> sh)),
+                                           ks[j] * static_cast<float>(static_cast<int8_t>(kc[j][w] >> (sh + 8))));
+                            vb[w >> 1][2 * (w & 1) + e] =
+                                pack2_bf16(vs[j] * static_cast<float>(static_cast<int8_t>(vc[j][w] >> sh)),
+                                           vs[j] * static_cast<float>(static_cast<int8_t>(vc[j][w] >> (sh + 8))));
+                        }
+                    u32x4* kd = reinterpret_cast<u32x4*>(ko + dst * kD + 16 * c);
+                    u32x4* vd = reinterpret_cast<u32x4*>(vo + dst * kD + 16 * c);
+                    kd[0] = kb[0];
+                    kd[1] = kb[1];
+                    vd[0] = vb[0];
+                    vd[1] = vb[1];
+                }
+            }
+            const int n_n = a.n_kv * (tl - tp);
+            for (int k0 = threadIdx.x >> 3; k0 < n_n; k0 += kUnroll * kStride) {
+                // every new row's values first (past the end: the last row
+                // again, the same bytes stored twice)
+                u32x4 x[kUnroll][2][2];
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const int k = min(k0 + j * kStride, n_n - 1);
+                    const int h = k / (tl - tp);
+                    const int key = B * i + tp + k % (tl - tp);
+                    const size_t nr = (static_cast<size_t>(qs) + (key - P)) * a.n_kv + h;   // its new row
+                    const u32x4* kn = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k_new) + nr * kD +
+                                                                     16 * c);
+                    const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.v_new) + nr * kD +
+                                                                     16 * c);
+                    x[j][0][0] = kn[0];
+                    x[j][0][1] = kn[1];
+                    x[j][1][0] = vn[0];
+                    x[j][1][1] = vn[1];
+                }
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const int r = row_of(min(k0 + j * kStride, n_n - 1), tp, tl - tp);
+                    const size_t src = static_cast<size_t>(id) * rows + r;
+                    const size_t dst = cb * rows + r;
+#pragma unroll
+                    for (int kv = 0; kv < 2; ++kv) {
+                        float f[16];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t w = x[j][kv][e >> 2][e & 3];
+                            f[2 * e] = __uint_as_float(w << 16);
+                            f[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+                        }
+                        float amax = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(f[e]));
+#pragma unroll
+                        for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+                        const float sc = fmaxf(amax, 1e-8f) / 127.0f;
+                        u32x4 codes = {0u, 0u, 0u, 0u};
+                        u32x4 st[2];
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            f[e] = fminf(fmaxf(rintf(f[e] / sc), -127.0f), 127.0f);
+                            codes[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(f[e])) & 0xffu) << (8 * (e & 3));
+                        }
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) st[e >> 2][e & 3] = pack2_bf16(sc * f[2 * e], sc * f[2 * e + 1]);
+                        int8_t* pc = static_cast<int8_t*>(kv ? a.v_app : a.k_app);
+                        *reinterpret_cast<u32x4*>(pc + src * kD + 16 * c) = codes;
+                        if (c == 0) (kv ? a.vs_app : a.ks_app)[src] = sc;
+                        u32x4* sd = reinterpret_cast<u32x4*>((kv ? vo : ko) + dst * kD + 16 * c);
+                        sd[0] = st[0];
+                        sd[1] = st[1];
+                    }
+                }
+            }
+            return;
+        }
+    }
     constexpr int kStride = kCopyThreads / 8;    // rows per pass of the workgroup
     constexpr int kUnroll = 4;                   // passes whose loads are in flight together
     for (int r0 = threadIdx.x >> 3; r0 < rows; r0 += kUnroll * kStride) {
@@ -140,8 +260,12 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_i
 
 hipError_t launch_dequant_blocks(const AttnArgs& a, uint16_t* k_out, uint16_t* v_out, int32_t* table_out, int maxb,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(dequant_blocks_kernel, dim3(maxb, a.num_seqs), dim3(kCopyThreads), 0, stream, a, k_out, v_out,
-                       table_out, maxb);
+    if (a.k_new)
+        hipLaunchKernelGGL(dequant_blocks_kernel<true>, dim3(maxb, a.num_seqs), dim3(kCopyThreads), 0, stream, a,
+                           k_out, v_out, table_out, maxb);
+    else
+        hipLaunchKernelGGL(dequant_blocks_kernel<false>, dim3(maxb, a.num_seqs), dim3(kCopyThreads), 0, stream, a,
+                           k_out, v_out, table_out, maxb);
     return hipGetLastError();
 }
 

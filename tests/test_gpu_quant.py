@@ -133,6 +133,54 @@ def test_q8_append_past_the_staged_sequence_prefix(dtype):
     _pools_match(c, oracle.build_quant_cache(wl))
 
 
+@pytest.mark.parametrize("n_q,n_kv,hist,new", [
+    (32, 8, [0, 17, 300, 2049], [5, 5, 3, 5]),          # verification-sized: the balanced pass
+    (32, 8, [0, 300, 1000, 2049], [512, 64, 100, 9]),   # past 32 rows per kv head: blocks staged as bf16
+    (8, 8, [5, 1500], [40, 33]),                        # one query head per kv head, staged
+])
+def test_q8_chunk_step_matches_the_two_calls(n_q, n_kv, hist, new):
+    """paged_attn_chunk_q8_append from the history-only state: codes, scales
+    and tables bit-exact against the oracle after the call, every row
+    bit-identical to kv_append_q8 + paged_attn_chunk_q8 and within the bar
+    of the oracle; a sequence with a table entry outside the pool gets NaN
+    rows while its other tokens are still written."""
+    hist, new = np.array(hist), np.array(new)
+    wl = build_workload(n_q=n_q, n_kv=n_kv, head_dim=128, block_size=16, dtype=BF16, hist_lens=hist,
+                        new_lens=new, seed=53)
+    say("q8 chunk step", n_q, n_kv, hist.tolist(), new.tolist())
+    c = build_gpu_cache(wl, quantized=True, with_new=False)
+    q = raw_to_torch(wl.q, BF16)
+    kn, vn = wl.packed_new_kv()
+    kn, vn = raw_to_torch(kn, BF16), raw_to_torch(vn, BF16)
+    lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.chunk_step(q, i32(wl.q_offsets), kn, vn, i32(wl.seq_lens), wl.max_new, wl.max_seq_len, wl.scale,
+                       lse=lse)
+    torch.cuda.synchronize()
+    ora = oracle.build_quant_cache(wl)
+    _pools_match(c, ora)
+    c2 = build_gpu_cache(wl, quantized=True)
+    out2, lse2 = run_chunk(c2, wl)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "not bit-identical to the two calls"
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    err = check_rows(out_f64(out, BF16), ref, BF16, "q8 chunk step")
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, BF16, "q8 chunk step lse")
+    say(f"  worst row rel err {err:.2e}")
+    # a bad table entry in the last sequence's first block: that sequence's
+    # rows NaN, its new tokens in valid blocks written all the same
+    c3 = build_gpu_cache(wl, quantized=True, with_new=False)
+    c3.table_dev[wl.num_seqs - 1, 0] = 10 ** 6
+    lse3 = torch.empty_like(lse)
+    out3 = c3.chunk_step(q, i32(wl.q_offsets), kn, vn, i32(wl.seq_lens), wl.max_new, wl.max_seq_len, wl.scale,
+                         lse=lse3)
+    torch.cuda.synchronize()
+    lo = int(wl.q_offsets[-2])
+    got3 = out_f64(out3, BF16)
+    assert np.isnan(got3[lo:]).all() and np.isnan(lse3[lo:].cpu().numpy()).all()
+    assert torch.equal(out3[:lo], out[:lo])
+    c3.table_dev[wl.num_seqs - 1, 0] = int(c3.table[wl.num_seqs - 1, 0])
+    _pools_match(c3, ora)
+
+
 def test_q8_invalid_rows_become_nan():
     L = np.array([40, 50, 60, 70, 80])
     wl = build_workload(n_q=8, n_kv=2, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - 1,

@@ -97,12 +97,13 @@ def test_random_shape_one_call_step(seed):
     """The one-call steps (append and attention in one call) from the
     history-only state: the decode step where it exists (bf16 or 8-bit,
     head_dim 128, block size 16; other shapes UNSUPPORTED) and the chunk step
-    on every bf16 / fp32 shape (there is none over an 8-bit pool). Pools
-    bit-exact after the call, every row within the bar."""
+    on every bf16 / fp32 shape and on 8-bit pools of head_dim 128 and block
+    size 16 (others UNSUPPORTED). Pools bit-exact after the call, every row
+    within the bar."""
     from paged_kv_cache_17_amd.binding import PagedKVError
     wl, mode, quant, split = draw_case(seed)
-    if mode == "chunk" and quant:
-        pytest.skip("no one-call chunk step over an 8-bit pool")
+    if quant:
+        split = 0
     name = (f"seed {seed}: {mode} step {'8-bit' if quant else wl.dtype} d{wl.head_dim} B{wl.block_size} "
             f"n_kv{wl.n_kv} G{wl.n_q // wl.n_kv} S{wl.num_seqs} split {split}")
     print(name, flush=True)
@@ -119,8 +120,11 @@ def test_random_shape_one_call_step(seed):
                                wl.scale, lse=lse, split_tokens=split)
         torch.cuda.synchronize()
     except PagedKVError as e:
-        assert mode == "decode" and e.status == UNSUPPORTED, name
-        assert (wl.head_dim, wl.block_size, wl.dtype) != (128, 16, BF16), name
+        assert e.status == UNSUPPORTED, name
+        if mode == "decode":
+            assert (wl.head_dim, wl.block_size, wl.dtype) != (128, 16, BF16), name
+        else:
+            assert quant and (wl.head_dim, wl.block_size) != (128, 16), name
         return
     if quant:
         ora = oracle.build_quant_cache(wl)

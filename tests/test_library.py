@@ -256,8 +256,9 @@ def test_one_call_steps_reject_bad_arguments_before_any_launch():
 
 
 def test_8bit_chunk_and_copy_reject_bad_arguments_before_any_launch():
-    """paged_attn_chunk_q8 and kv_copy_blocks_q8: shape, null-pointer,
-    support and alignment errors come back before any device call."""
+    """paged_attn_chunk_q8, paged_attn_chunk_q8_append and kv_copy_blocks_q8:
+    shape, null-pointer, support, alignment and workspace errors come back
+    before any device call."""
     lib = pkv.load_library()
     p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
 
@@ -280,6 +281,20 @@ def test_8bit_chunk_and_copy_reject_bad_arguments_before_any_launch():
     assert chunk(kc=24) == -2                         # codes not 16-byte aligned
     assert chunk(ks=20) == -2                         # scales not 16-byte aligned
     assert chunk(total_q=0) == 0
+
+    # the one-call chunk step over the 8-bit pool: the same checks, and the
+    # new rows' pointers, before its append could write anything
+    def step(kn=16, vn=16, max_q=9, total_q=9, ws=1 << 20, d=128):
+        return lib.paged_attn_chunk_q8_append(p(16), None, p(16), p(16), p(16), p(16), p(16), p(16), p(kn), p(vn),
+                                              p(16), 4096, p(16), 1, total_q, max_q, 64, 8, 32, 8, d, 16, 0.25,
+                                              p(256), ws, None)
+
+    need = ctypes.c_size_t(0)
+    assert lib.paged_attn_chunk_q8_workspace_size(1, 9, 9, 32, 8, 128, 16, 64, ctypes.byref(need)) == 0
+    assert step(kn=0) == -1 and step(vn=0) == -1
+    assert step(d=64) == -3
+    assert step(ws=need.value - 1) == -6
+    assert step(kn=0, vn=0, total_q=0) == 0
 
     def copy(kc=16, n=2, nb=8):
         return lib.kv_copy_blocks_q8(p(kc), p(16), p(16), p(16), p(16), p(16), n, nb, 8, 128, 16, None)
