@@ -678,6 +678,16 @@ def main():
         step(i, ev_dec[i], ev_chk[i])
     torch.cuda.synchronize()
     ms_step = total_ms / args.steps
+
+    # Region 3: the step's append alone (kv_append / kv_append_q8 of every
+    # new row, as its own launch), reported beside the step.
+    a_begin, a_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_begin.record(stream)
+    for i in range(args.steps):
+        caches[i % len(caches)].append(k_new, v_new, start_pos, new_start, stream=stream)
+    a_end.record(stream)
+    torch.cuda.synchronize()
+    append_ms = a_begin.elapsed_time(a_end) / args.steps
     tokens = int(wl.new_lens.sum())
 
     # Algorithmic work: decode rows read every cached K/V byte once
@@ -719,6 +729,7 @@ def main():
                    "partition": "balanced" if split == 0 else f"fixed split of {split} tokens"},
     }
     line["cold_start_ms"] = cold_ms
+    line["append_alone_ms"] = append_ms   # the step's appends as one separate launch (not part of `value`)
     if nd:
         kern_avg = float(np.mean([b.elapsed_time(a) for b, a in ev_dec]))
         achieved = dec_bytes / (kern_avg * 1e-3) / 1e9
