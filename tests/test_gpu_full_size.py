@@ -9,8 +9,11 @@ new tokens. Then the step runs exactly as the benchmark runs it:
   call (new rows appended, then paged decode attention over every cached
   key);
 * configuration 5 (48 decode rows + 16 prefill chunks of 512 queries):
-  ``kv_append`` of all new rows, ``paged_attn_decode`` over the decode rows,
-  ``paged_attn_chunk`` over the chunks.
+  ``paged_attn_decode_append`` over the decode rows and
+  ``paged_attn_chunk_append`` over the chunks (and, as ``--separate``,
+  ``kv_append`` of all new rows, ``paged_attn_decode``, ``paged_attn_chunk``);
+  over an 8-bit pool (``--kv int8``) ``paged_attn_decode_q8_append`` and
+  ``paged_attn_chunk_q8_append``, against attention over s * code.
 
 Bars (the lab page's closing checks: the cached result equals full
 recomputation for every served request; block tables and pool contents are
@@ -138,6 +141,50 @@ def test_full_size_chunked_prefill_mix_every_row(separate):
     worst, lworst, rows = _check_every_row(wl, out, lse)
     say(f"  {rows} rows (48 decode + 8192 chunk) x {wl.n_q} heads: worst row rel err {worst:.2e}, "
         f"lse {lworst:.2e}")
+
+
+def test_full_size_chunked_prefill_mix_8bit_every_row():
+    """Configuration 5 over an 8-bit pool through the benchmark's step: the
+    decode rows' one-call step (the quantising append folded into the split
+    pass) and the chunks' one-call step (their quantising append fused into
+    the expansion of their blocks to bf16). Codes, scales and tables
+    bit-exact; every row within the bar of the oracle's attention over s *
+    code."""
+    wl = config_workload(5)
+    nd = int(np.argmax(wl.new_lens != 1))
+    say(f"config 5, 8-bit pool: {nd} decode + {wl.num_seqs - nd} chunk seqs, {int(wl.seq_lens.sum())} keys")
+    c = build_gpu_cache(wl, fill_nan=True, quantized=True, with_new=False)
+    import paged_kv_cache_17_amd as pkv
+    q = raw_to_torch(wl.q, BF16)
+    kn, vn = wl.packed_new_kv()
+    kn, vn = raw_to_torch(kn, BF16), raw_to_torch(vn, BF16)
+    lens = i32(wl.seq_lens)
+    qd = int(wl.q_offsets[nd])
+    lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    ws = c.workspace(qd, wl.n_q, int(wl.seq_lens[:nd].max())).clone()
+    max_c, max_chk = int(wl.new_lens[nd:].max()), int(wl.seq_lens[nd:].max())
+    ws2 = c.workspace(q.shape[0] - qd, wl.n_q, max_chk, chunk=(wl.num_seqs - nd, max_c)).clone()
+    pkv.paged_attn_decode_q8_append(out[:qd], lse[:qd], q[:qd], c.k_cache, c.v_cache, c.k_scale, c.v_scale,
+                                    kn[:qd], vn[:qd], c.table_dev[:nd], lens[:nd], int(wl.seq_lens[:nd].max()),
+                                    wl.scale, ws)
+    pkv.paged_attn_chunk_q8_append(out[qd:], lse[qd:], q[qd:], i32(wl.q_offsets[nd:] - qd), c.k_cache, c.v_cache,
+                                   c.k_scale, c.v_scale, kn[qd:], vn[qd:], c.table_dev[nd:], lens[nd:], max_c,
+                                   max_chk, wl.scale, ws2)
+    torch.cuda.synchronize()
+    say("  step done; comparing codes, scales and tables")
+    ora = oracle.build_quant_cache(wl)
+    assert np.array_equal(c.table, ora.tables())
+    assert np.array_equal(c.k_cache.cpu().numpy(), ora.pool_k)
+    assert np.array_equal(c.v_cache.cpu().numpy(), ora.pool_v)
+    assert np.array_equal(c.k_scale.cpu().numpy().view(np.uint32), ora.scale_k.view(np.uint32))
+    assert np.array_equal(c.v_scale.cpu().numpy().view(np.uint32), ora.scale_v.view(np.uint32))
+    del c
+    say("  bit-exact; comparing every row")
+    ref, ref_lse = oracle.paged_attention_all(ora)
+    worst = check_rows(out_f64(out, BF16), ref, BF16, "config 5, 8-bit")
+    lworst = check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, BF16, "config 5, 8-bit")
+    say(f"  {out.shape[0]} rows x {wl.n_q} heads: worst row rel err {worst:.2e}, lse {lworst:.2e}")
 
 
 def test_row_error_budget_matrix_core_vs_vector_alu_c2():
