@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(char* __restr
 // s = max(absmax, 1e-8) / 127, code = clamp(rint(x / s), -127, 127)), and
 // the codes and s go to the pool while bf16(s x code) goes to the staging
 // block - the values the separate append followed by this expansion gives.
-// A sequence the chunk pass rejects gets no append (its rows are NaN).
+// Rows past the sequence's end are not staged (the chunk kernel never reads
+// them). A sequence the chunk pass rejects gets no append (its rows are NaN).
 template <bool FUSED>
 __global__ __launch_bounds__(kCopyThreads) void dequant_blocks_kernel(AttnArgs a, uint16_t* __restrict__ ko,
                                                                       uint16_t* __restrict__ vo,
