@@ -443,14 +443,14 @@ def bench_verify(args):
             if ev is not None:
                 pkv.pkv_set_profile_events(*ev)
             lens_d = i32_after[i % len(gpus)]   # device copies made once, outside the timed steps
-            if args.separate or quant:   # an 8-bit pool: kv_append_q8, then paged_attn_chunk_q8
+            if args.separate:   # two calls: kv_append (kv_append_q8), then the chunk pass
                 pkv.pkv_set_profile_events(None, None)
                 g.c.append(k, v, i32_lens[i % len(gpus)], g.q_start, stream=stream)
                 if ev is not None:
                     pkv.pkv_set_profile_events(*ev)
                 g.c.chunk(g.cyc[0][2], g.q_start, lens_d, g1, max_after, sw.scale, split_tokens=split,
                           stream=stream)
-            else:   # one call: the append, then the chunk pass
+            else:   # one call: the append, then the chunk pass (paged_attn_chunk_append / _q8_append)
                 g.c.chunk_step(g.cyc[0][2], g.q_start, k, v, lens_d, g1, max_after, sw.scale,
                                split_tokens=split, stream=stream)
             pkv.pkv_set_profile_events(None, None)
@@ -495,7 +495,10 @@ def bench_verify(args):
         "data": "synthetic",
         "config": {"workload": sw.name + ("-kv-int8" if quant else ""), "num_seqs": sw.num_seqs, "chunk": g1, "n_q": sw.n_q, "n_kv": sw.n_kv,
                    "head_dim": sw.head_dim, "block_size": sw.block_size, "context_tokens": int(lens.sum()),
-                   "kv_bytes": kv_bytes, "cache_copies": len(gpus)},
+                   "kv_bytes": kv_bytes, "cache_copies": len(gpus),
+                   "step": ("kv_append_q8 + paged_attn_chunk_q8" if quant else "kv_append + paged_attn_chunk")
+                   if args.separate else ("paged_attn_chunk_q8_append" if quant else "paged_attn_chunk_append")
+                   + " (one call)"},
         "roofline": {"kernel": "balanced split pass (matrix cores), 5-query chunks", "bound": "hbm",
                      "achieved": kv_bytes / (kern_m * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": kv_bytes / (kern_m * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
