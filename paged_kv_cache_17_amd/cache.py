@@ -159,7 +159,8 @@ class PagedKVCache:
     def chunk_step(self, q, q_start, k_new, v_new, seq_lens, max_q_len: int, max_seq_len: int, scale: float,
                    out=None, lse=None, split_tokens: int = 0, stream=None):
         """Append each sequence's chunk (``k_new``/``v_new`` ``[sum C, n_kv, d]``, the last C_s of
-        ``seq_lens``) and attend it, in one call."""
+        ``seq_lens``; bf16 and quantised for an 8-bit cache) and attend it, in one call
+        (``paged_attn_chunk_append`` / ``paged_attn_chunk_q8_append``)."""
         if out is None:
             out = torch.empty_like(q)
         ws = self.workspace(q.shape[0], q.shape[1], max_seq_len, split_tokens,
