@@ -242,14 +242,57 @@ def test_chunk_step_many_sequences():
 
 
 def test_chunk_step_large_chunks_and_decode_rows():
-    """Chunks of 40 (the matrix-core chunk kernel) beside 1-token rows: the
-    append launched first, then that kernel."""
+    """Chunks of 40 (the matrix-core chunk kernel, the append fused into it)
+    beside 1-token rows."""
     L = np.array([40, 57, 300, 1, 90])
     C = np.array([40, 40, 40, 1, 1])
     wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - C,
                         new_lens=C, seed=55)
     say("chunk step, chunks of 40")
     _check_chunk_step(wl, "chunk step 40")
+
+
+def test_chunk_step_fused_append_with_bad_rows():
+    """The matrix-core chunk step with its append fused in, where one
+    sequence's table names a block outside the pool (for a cached key) and
+    another's length is out of range: those sequences' rows are NaN; the
+    first still has its new tokens written (their blocks are valid), the
+    second gets no append; every other row and pool byte as the oracle."""
+    L = np.array([300, 200, 97, 150])
+    C = np.array([64, 40, 33, 50])
+    wl = build_workload(n_q=32, n_kv=8, head_dim=128, block_size=16, dtype=BF16, hist_lens=L - C,
+                        new_lens=C, seed=57)
+    say("fused chunk step, bad rows")
+    c = build_gpu_cache(wl, with_new=False)
+    c.table_dev[1, 0] = 10 ** 6                   # a cached key's block outside the pool
+    lens = wl.seq_lens.copy()
+    lens[2] = wl.table_stride * wl.block_size + 1  # longer than the table holds
+    q = raw_to_torch(wl.q, wl.dtype)
+    kn, vn = wl.packed_new_kv()
+    lse = torch.empty((q.shape[0], wl.n_q), dtype=torch.float32, device="cuda")
+    out = c.chunk_step(q, i32(wl.q_offsets), raw_to_torch(kn, wl.dtype), raw_to_torch(vn, wl.dtype), i32(lens),
+                       wl.max_new, int(lens.max()), wl.scale, lse=lse)
+    torch.cuda.synchronize()
+    got = out_f64(out, wl.dtype)
+    qo = wl.q_offsets
+    for s in (1, 2):
+        assert np.isnan(got[qo[s]:qo[s + 1]]).all() and np.isnan(lse[qo[s]:qo[s + 1]].cpu().numpy()).all()
+    ora = oracle.build_cache(wl)
+    ref, _ = oracle.paged_attention_all(ora)
+    for s in (0, 3):
+        check_rows(got[qo[s]:qo[s + 1]], ref[qo[s]:qo[s + 1]], wl.dtype, f"valid sequence {s}")
+    # pools: as the oracle's except sequence 2's new tokens, which stay as before the call
+    kp = torch_to_raw(c.k_cache, wl.dtype).view(np.uint16).copy()
+    vp = torch_to_raw(c.v_cache, wl.dtype).view(np.uint16).copy()
+    ok, ov = ora.pool_k.view(np.uint16).copy(), ora.pool_v.view(np.uint16).copy()
+    hist = build_gpu_cache(wl, with_new=False)
+    hk = torch_to_raw(hist.k_cache, wl.dtype).view(np.uint16)
+    hv = torch_to_raw(hist.v_cache, wl.dtype).view(np.uint16)
+    for p in range(int(wl.hist_lens[2]), int(wl.seq_lens[2])):
+        blk, slot = int(c.table[2, p // wl.block_size]), p % wl.block_size
+        ok[blk, :, slot] = hk[blk, :, slot]
+        ov[blk, :, slot] = hv[blk, :, slot]
+    assert np.array_equal(kp, ok) and np.array_equal(vp, ov)
 
 
 # ------------------------------------------------ errors before any write ---
