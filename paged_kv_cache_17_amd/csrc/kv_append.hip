@@ -242,10 +242,12 @@ __global__ __launch_bounds__(256) void kv_append_last_kernel(uint4* __restrict__
     vc[dst] = vn[src];
 }
 
-// The decode step's append into an 8-bit pool: one wave per (sequence, kv
-// head) row of K or of V at position seq_lens[s] - 1, bf16 input, quantised
-// exactly as kv_append_q8_kernel does; the same tokens as the decode pass
-// with the append folded in (head_dim 128, block_size 16).
+// The decode step's append into an 8-bit pool: one token per sequence at
+// position seq_lens[s] - 1, bf16 input, quantised exactly as
+// kv_append_q8_kernel does (head_dim 128, block_size 16): 16 lanes per
+// (sequence, kv head), each holding 8 values of its K row and 8 of its V row
+// (as kv_append_q8_d128_kernel). The same tokens as the decode pass with
+// the append folded in.
 __global__ __launch_bounds__(256) void kv_append_q8_last_kernel(int8_t* __restrict__ kc, int8_t* __restrict__ vc,
                                                                 float* __restrict__ ks, float* __restrict__ vs,
                                                                 const uint16_t* __restrict__ kn,
@@ -253,12 +255,14 @@ __global__ __launch_bounds__(256) void kv_append_q8_last_kernel(int8_t* __restri
                                                                 const int32_t* __restrict__ table, int table_stride,
                                                                 const int32_t* __restrict__ seq_lens, int num_seqs,
                                                                 int max_seq_len, int num_blocks, int n_kv) {
-    constexpr int kD = 128, kBS = 16;
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long row = static_cast<long long>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (row >= 2LL * num_seqs * n_kv) return;                 // whole wave exits together
-    const bool is_v = row & 1;
-    const long long th = row >> 1;
+    constexpr int kD = 128, kBS = 16, kLanes = 16;
+    const int c = threadIdx.x & (kLanes - 1);
+    const long long total = static_cast<long long>(num_seqs) * n_kv;
+    const long long th = static_cast<long long>(blockIdx.x) * (blockDim.x / kLanes) + threadIdx.x / kLanes;
+    if (th >= total) return;                                  // the 16 lanes of a row exit together
+    const size_t src = static_cast<size_t>(th) * kD + 8 * c;
+    const piece_u32x4 kx = *reinterpret_cast<const piece_u32x4*>(kn + src);
+    const piece_u32x4 vx = *reinterpret_cast<const piece_u32x4*>(vn + src);
     const int h = static_cast<int>(th % n_kv);
     const int s = static_cast<int>(th / n_kv);
     const int L = seq_lens[s];
@@ -266,18 +270,38 @@ __global__ __launch_bounds__(256) void kv_append_q8_last_kernel(int8_t* __restri
     const int pos = L - 1;
     const int blk = table[static_cast<size_t>(s) * table_stride + pos / kBS];
     if (blk < 0 || blk >= num_blocks) return;
-    const uint16_t* src = (is_v ? vn : kn) + static_cast<size_t>(th) * kD;
-    float amax = 0.0f;
-    for (int e = lane; e < kD; e += kWave) amax = fmaxf(amax, fabsf(Elem<uint16_t>::load(src + e)));
-    amax = wave_max(amax);
-    const float scale = fmaxf(amax, 1e-8f) / 127.0f;
     const size_t slot = (static_cast<size_t>(blk) * n_kv + h) * kBS + pos % kBS;
-    int8_t* dst = (is_v ? vc : kc) + slot * kD;
-    for (int e = lane; e < kD; e += kWave) {
-        const float c = fminf(fmaxf(rintf(Elem<uint16_t>::load(src + e) / scale), -127.0f), 127.0f);
-        dst[e] = static_cast<int8_t>(c);
+    float f[2][8], amax[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        f[0][2 * w] = __uint_as_float(kx[w] << 16);
+        f[0][2 * w + 1] = __uint_as_float(kx[w] & 0xffff0000u);
+        f[1][2 * w] = __uint_as_float(vx[w] << 16);
+        f[1][2 * w + 1] = __uint_as_float(vx[w] & 0xffff0000u);
     }
-    if (lane == 0) (is_v ? vs : ks)[slot] = scale;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax[r] = fmaxf(amax[r], fabsf(f[r][e]));
+#pragma unroll
+    for (int o = 1; o < kLanes; o <<= 1) {
+        const float mk = __shfl_xor(amax[0], o, kWave);
+        const float mv = __shfl_xor(amax[1], o, kWave);
+        amax[0] = fmaxf(amax[0], mk);
+        amax[1] = fmaxf(amax[1], mv);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const float scale = fmaxf(amax[r], 1e-8f) / 127.0f;
+        piece_u32x2 packed = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q = fminf(fmaxf(rintf(f[r][e] / scale), -127.0f), 127.0f);
+            packed[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xffu) << (8 * (e & 3));
+        }
+        *reinterpret_cast<piece_u32x2*>((r ? vc : kc) + slot * kD + 8 * c) = packed;
+        if (c == 0) (r ? vs : ks)[slot] = scale;
+    }
 }
 
 }  // namespace
@@ -343,8 +367,8 @@ hipError_t launch_kv_append_q8_last(int8_t* k_codes, int8_t* v_codes, float* k_s
                                     const void* k_new, const void* v_new, const int32_t* table, int table_stride,
                                     const int32_t* seq_lens, int num_seqs, int max_seq_len, int num_blocks, int n_kv,
                                     hipStream_t stream) {
-    const long long rows = 2LL * num_seqs * n_kv;            // one wave per row, 4 waves per workgroup
-    hipLaunchKernelGGL(kv_append_q8_last_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream,
+    const long long pairs = static_cast<long long>(num_seqs) * n_kv;   // 16 per workgroup
+    hipLaunchKernelGGL(kv_append_q8_last_kernel, dim3(static_cast<unsigned>((pairs + 15) / 16)), dim3(256), 0, stream,
                        k_codes, v_codes, k_scale, v_scale, static_cast<const uint16_t*>(k_new),
                        static_cast<const uint16_t*>(v_new), table, table_stride, seq_lens, num_seqs, max_seq_len,
                        num_blocks, n_kv);
