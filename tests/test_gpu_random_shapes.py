@@ -50,6 +50,7 @@ def draw_case(seed):
     else:
         new = rng.integers(1, int(rng.choice([3, 8, 40, 300])) + 1, size=S)
     split = int(rng.choice([16, 64, 256])) if (not quant and rng.random() < 0.3) else 0
+    split = -(-split // B) * B            # a fixed split is a whole number of blocks
     wl = build_workload(n_q=G * n_kv, n_kv=n_kv, head_dim=d, block_size=B, dtype=dtype, hist_lens=hist,
                         new_lens=new, seed=seed)
     return wl, mode, quant, split
